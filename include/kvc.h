@@ -1,0 +1,251 @@
+/*
+ * kvc.h -- C ABI of libkvc.so: score-and-select compression of a prompt's KV
+ * cache on AMD Instinct MI355X (gfx950).
+ *
+ * The path: for every KV head, the last w prompt queries (the observation
+ * window) attend to the prefix keys; each attention row is softmax-normalised
+ * over the prefix; the probabilities are averaged over the window into a
+ * per-token importance (optionally with Keyformer's Gumbel noise and
+ * temperature); ZigZag budgets may be allocated per layer from LMBA; each head
+ * keeps its top-k tokens plus a recent window; K and V are gathered into a
+ * compacted cache; ThinK may then prune key channels.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless marked "host".  The library never
+ *   allocates device memory on these paths and never frees caller memory; the
+ *   caller owns every buffer, including the workspace (sized by the matching
+ *   *_workspace_size function).  Inputs are read-only.
+ * - Every call is enqueued on `stream` (a hipStream_t passed as void*; NULL
+ *   means the null stream) and returns without synchronising.
+ * - Arguments are validated on the host before anything is enqueued.  On
+ *   KVC_E_ARG, KVC_E_SHAPE, KVC_E_WORKSPACE or KVC_E_UNSUPPORTED nothing is
+ *   enqueued and the outputs are untouched.  A failed launch returns
+ *   KVC_E_DEVICE.  Faults inside kernels surface at the caller's next
+ *   synchronisation.  No C++ exception crosses this boundary.
+ * - Tensors are row-major.  bf16 tensors are raw 16-bit patterns.  Element
+ *   strides are in elements.  bf16 pointers and the strides between rows that
+ *   the kernels read with 16-byte vectors must be 16-byte aligned / multiples
+ *   of 8 elements (checked; KVC_E_ARG otherwise).
+ * - Results are deterministic: the same inputs give the same bytes.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvc_status {
+  KVC_OK = 0,
+  KVC_E_ARG = 1,          /* invalid argument value or pointer                 */
+  KVC_E_SHAPE = 2,        /* inconsistent sizes                                */
+  KVC_E_WORKSPACE = 3,    /* workspace missing or smaller than required        */
+  KVC_E_DEVICE = 4,       /* a HIP call or kernel launch failed                */
+  KVC_E_UNSUPPORTED = 5   /* valid request this build does not implement       */
+} kvc_status;
+
+/* Static description of a status code; never NULL. */
+const char* kvc_status_str(int status);
+
+/* Version of this ABI (incremented on any incompatible change). */
+int kvc_abi_version(void);
+
+/* KV-cache size in bytes, 2 * B * S * L * N * D * elem_bytes: the size formula
+ * of the ThinK page (papercache summary of arXiv 2407.21018), preliminaries on
+ * KV-cache optimisation.  Returns -1 if an argument is negative or the product
+ * overflows int64. */
+int64_t kvc_cache_bytes(int64_t B, int64_t S, int64_t L, int64_t N, int64_t D, int64_t elem_bytes);
+
+/* Channels kept per head by ThinK: T = floor((1 - lambda) * D) evaluated in
+ * double (ThinK page, magnitude-based pruning).  Returns -1 unless
+ * 0 <= lambda < 1 and D > 0. */
+int kvc_think_channels(int D, double lambda);
+
+/* ------------------------------------------------------------------------ */
+/* kvc_score: observation-window importance.                                 */
+/* ------------------------------------------------------------------------ */
+/*
+ * Computes, for each layer l, KV head g and prefix token j in [0, n), n = S - w,
+ *
+ *   x[h,i,j] = alpha_l * <Q_obs[l,h,i,:], K[l,g,j,:]>,      h in group g
+ *   y        = x                          (gumbel == 0)
+ *   y        = (x + zeta[h,i,j]) / tau    (gumbel != 0; tau = +inf gives y = 0)
+ *   p[h,i,j] = exp(y[h,i,j] - max_j y[h,i,:]) / sum_j exp(...)   (over j < n)
+ *   I[l,g,j] = sum_{h in group g} (1/w) sum_i p[h,i,j]
+ *
+ * Sources: ZigZagKV blog page (qidao123 thread 109074), SnapKV section (window
+ * of the last prompt queries against the prefix, mean over the window's rows,
+ * per head); ThinK page, query-driven pruning (softmax(Q K^T / sqrt(D)));
+ * Keyformer blog page, Gumbel-distribution section (y = x + zeta with
+ * zeta ~ Gumbel(0,1), then division by the temperature tau); KVzap news page,
+ * architectural compression (grouped-query attention).
+ * Grouping: G = H / Hkv query heads share one KV head, query head h reads KV
+ * head floor(h / G), and a KV head's importance is the SUM of its G query
+ * heads' window means (each row of I sums to G).
+ * Noise (gumbel != 0): zeta = -ln(-ln u), u = (2*floor(X/2^9) + 1) * 2^-24,
+ * X = word (j mod 4) of Philox4x32-10 (Salmon et al., SC'11) with key
+ * (seed mod 2^32, seed >> 32) and counter (floor(j/4), S - w + i, h, 0).
+ *
+ * Layouts:
+ *   q_obs      bf16, element (l,h,i,d) at l*q_layer_stride + h*q_head_stride + i*D + d
+ *   k          bf16, element (l,g,j,d) at l*k_layer_stride + g*k_head_stride + j*D + d,
+ *              rows j in [0, S) must be readable (only j < n are used)
+ *   importance fp32 [L, Hkv, n] contiguous (written in full)
+ *   layer_scales: NULL, or device fp32 [L] of alpha_l (then `scale` is ignored)
+ * Limits: D == 128 (else KVC_E_UNSUPPORTED); 1 <= w < S; H % Hkv == 0;
+ *   G * w <= 4096; scale > 0 and finite (or every layer_scales entry, which
+ *   the library cannot check); tau > 0 (may be +inf) when gumbel != 0.
+ * Precision: bf16 products, fp32 accumulation and softmax statistics, fixed
+ *   reduction order; relative error of I well under 1e-3.
+ */
+typedef struct kvc_score_args {
+  int32_t L;                 /* layers scored by this call, >= 1                 */
+  int32_t H;                 /* query heads                                      */
+  int32_t Hkv;               /* KV heads                                         */
+  int32_t w;                 /* observation window (last w prompt queries)       */
+  int32_t S;                 /* prompt length                                    */
+  int32_t D;                 /* head dimension (128)                             */
+  int64_t q_head_stride;     /* elements between query heads (>= w*D)            */
+  int64_t q_layer_stride;    /* elements between layers of q_obs                 */
+  int64_t k_head_stride;     /* elements between KV heads (>= S*D)               */
+  int64_t k_layer_stride;    /* elements between layers of k                     */
+  float scale;               /* alpha when layer_scales == NULL (1/sqrt(D))       */
+  const float* layer_scales; /* device [L] or NULL                                */
+  int32_t gumbel;            /* 0: plain SnapKV scores; 1: Keyformer noise       */
+  float tau;                 /* temperature (gumbel only), > 0, +inf allowed     */
+  uint64_t seed;             /* Philox key (gumbel only)                         */
+} kvc_score_args;
+
+/* Workspace bytes kvc_score needs for these arguments (0 on invalid args). */
+size_t kvc_score_workspace_size(const kvc_score_args* args /* host */);
+
+kvc_status kvc_score(const kvc_score_args* args /* host */, const void* q_obs, const void* k,
+                     float* importance, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* kvc_lmba_budget: ZigZag per-layer budgets from importance.                */
+/* ------------------------------------------------------------------------ */
+/*
+ * For every layer l and KV head g: MBA[l,g] = the minimum m such that the m
+ * largest entries of I[l,g,:] hold at least `mass` of the row's total.  Then
+ * M_l = sum_g MBA[l,g] (LMBA_l = M_l / Hkv), R = total_budget - L*floor and
+ *   B_l = floor + q_l,   q_l = floor(R*M_l / sum M) plus one unit for each of
+ *   the R - sum q layers with the largest R*M_l mod sum M (ties: lower l),
+ * in exact integer arithmetic; a layer above `capacity` is clamped to it and
+ * the excess re-shared among the rest by the same rule.  If sum M == 0 every
+ * layer weighs 1.
+ * Sources: ZigZagKV blog page, section on ZigZagKV's new observations (MBA:
+ * fewest KV entries keeping 90% of a head's attention; LMBA: mean over the
+ * layer's heads) and section on ZigZag's space allocation (share of the total
+ * budget proportional to LMBA, with a minimum reserved per layer).
+ * Layout: importance fp32 [L, Hkv, n] contiguous, entries >= 0.  mba int32
+ *   [L, Hkv] or NULL; budgets int32 [L] (tokens per KV head, recent window
+ *   included).
+ * Errors: KVC_E_ARG unless 0 < mass <= 1, 0 <= floor <= capacity and
+ *   L*floor <= total_budget <= L*capacity.  L <= 65536.
+ * Mass sums are fp64, in a fixed order.
+ */
+size_t kvc_lmba_budget_workspace_size(int32_t L, int32_t Hkv, int32_t n);
+
+kvc_status kvc_lmba_budget(const float* importance, int32_t L, int32_t Hkv, int32_t n, double mass,
+                           int64_t total_budget, int32_t floor_per_layer, int32_t capacity,
+                           int32_t* mba, int32_t* budgets, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* kvc_select_topk: per-head top-k plus the recent window.                   */
+/* ------------------------------------------------------------------------ */
+/*
+ * Candidates C = [0, c), c = min(S - w, S - recent).  k_top = budget - recent.
+ * Each head keeps the k_top candidates first in the order (importance
+ * descending, position ascending) and every position of [S - recent, S);
+ * the `budget` kept positions are written ascending.
+ * Sources: ZigZagKV blog page, SnapKV section (per-head top-K by averaged
+ * score, plus every token of the last window) and ZigZag's token-selection
+ * section (the same with per-layer quotas); Keyformer blog page, prompt-phase
+ * paragraph (w recent tokens plus k - w of the other n - w).
+ * Layout: importance fp32, row g at importance + g * imp_head_stride (>= n =
+ *   S - w entries, only the first c are read; entries must not be NaN);
+ *   indices int32 [Hkv, budget] contiguous.
+ * Errors: KVC_E_ARG unless 0 <= recent <= S, 1 <= w < S,
+ *   recent <= budget <= c + recent.
+ */
+size_t kvc_select_topk_workspace_size(int32_t Hkv, int32_t n);
+
+kvc_status kvc_select_topk(const float* importance, int64_t imp_head_stride, int32_t Hkv, int32_t S,
+                           int32_t w, int32_t recent, int32_t budget, int32_t* indices,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* kvc_compact: gather kept K/V rows into a dense cache.                     */
+/* ------------------------------------------------------------------------ */
+/*
+ * k_out[g,t,:] = k[g, indices[g,t], :] and v_out likewise (raw bf16 bytes).
+ * Source: Keyformer blog page, prompt-phase paragraph (the kept tokens form the
+ * new, smaller cache); KVzap news page (cache of shape (2, L, H, T, D)).
+ * Layout: k, v bf16, row j of head g at base + g*head_stride + j*D; k_out,
+ *   v_out bf16 [Hkv, budget, D] contiguous.  v / v_out may both be NULL.
+ *   D % 8 == 0, D <= 1024.  An index outside [0, S) yields a row of 0xFFFF
+ *   (bf16 NaN) instead of a read out of bounds.
+ */
+kvc_status kvc_compact(const void* k, const void* v, int32_t Hkv, int32_t S, int32_t D,
+                       int64_t k_head_stride, int64_t v_head_stride, const int32_t* indices,
+                       int32_t budget, void* k_out, void* v_out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* kvc_channel_prune: ThinK key-channel pruning of a compacted cache.        */
+/* ------------------------------------------------------------------------ */
+/*
+ * With U = the first budget - recent rows of each head of k_c (the non-recent
+ * kept tokens, which precede the recent window): M[g,d] = (sum_{t in U}
+ * |k_c[g,t,d]|^p)^(1/p); T = floor((1 - lambda) D); channels[g] = the T
+ * channels first in the order (M descending, d ascending), written ascending;
+ * mask[g,d] = 1 for kept channels, else 0; k_pruned[g,t,c] =
+ * k_c[g,t,channels[g,c]] for t in U.  Recent rows keep all channels (they are
+ * not copied).
+ * Source: ThinK page, magnitude-based pruning (M = ||K[n,:,d]||_p, keep
+ * T = floor((1-lambda) D), I = Top_T) and THINK's implementation (recent keys
+ * unpruned, binary channel mask).
+ * Layout: k_c bf16 [Hkv, budget, D] contiguous; channels int32 [Hkv, T];
+ *   mask uint8 [Hkv, D] or NULL; k_pruned bf16 [Hkv, budget - recent, T].
+ * Errors: KVC_E_ARG unless 0 <= recent <= budget, 0 <= lambda < 1, T >= 1,
+ *   p in {1, 2}; D == 128 (else KVC_E_UNSUPPORTED).  Norms are fp32 sums in
+ *   a fixed order.
+ */
+size_t kvc_channel_prune_workspace_size(int32_t Hkv, int32_t budget, int32_t D);
+
+kvc_status kvc_channel_prune(const void* k_c, int32_t Hkv, int32_t budget, int32_t D,
+                             int32_t recent, double lambda, int32_t p, int32_t* channels,
+                             uint8_t* mask, void* k_pruned, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Kernel timing (measurement support).                                      */
+/* ------------------------------------------------------------------------ */
+/*
+ * While enabled, every kernel the library launches is bracketed by a pair of
+ * HIP events recorded on its launch stream.  kvc_timing_read synchronises on
+ * those events and reports, per kernel name, the number of launches and their
+ * summed duration in milliseconds.  Enabling clears earlier records.  Not
+ * thread-safe; meant for benchmarks, not for production paths.
+ */
+kvc_status kvc_timing_enable(int32_t enable);
+
+/* Number of distinct kernel names recorded so far. */
+int32_t kvc_timing_count(void);
+
+/* Entry `idx` (0-based): name copied into name_buf (NUL-terminated, truncated
+ * to name_len), launches and total milliseconds into *launches and *total_ms
+ * (host pointers). */
+kvc_status kvc_timing_read(int32_t idx, char* name_buf, int32_t name_len, int32_t* launches,
+                           double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

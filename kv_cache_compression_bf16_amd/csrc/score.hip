@@ -1,0 +1,415 @@
+// kvc_score: observation-window importance on gfx950.
+//
+// What is computed (ZigZagKV blog page, SnapKV section; ThinK page, query-driven
+// pruning; Keyformer blog page, Gumbel-distribution section): for every KV
+// head g the G*w window query rows of its query heads are scored against the
+// n = S - w prefix keys, each row is softmax-normalised over the prefix, and
+// the normalised rows are summed into a per-key importance (times 1/w).
+//
+// Design (two passes over the keys, same grid):
+//  * A workgroup owns 256 consecutive prefix keys of one KV head (4 waves x
+//    64 keys).  Each wave holds its 64 keys in registers, already in the A
+//    operand layout of v_mfma_f32_32x32x16_bf16, for the whole kernel: K is
+//    read from HBM exactly once per pass, straight into VGPRs.
+//  * The G*w query rows of the group stream through LDS in blocks of 32 rows
+//    (8 KB, double-buffered, 16-byte chunks XOR-swizzled by row so the MFMA
+//    B-operand reads are bank-conflict free).
+//  * The tile is computed as K x Q^T, so a lane owns ONE query row and 16 keys
+//    of each 32x32 tile: row statistics (pass 1) and the per-row softmax
+//    constant (pass 2) are per-lane scalars, and column sums over query rows
+//    accumulate in registers across all query blocks; the 32-lane reduction
+//    happens once per workgroup at the end.  Every key column has a single
+//    owner, so no atomics are used and results are bit-reproducible.
+//  * Pass 1 writes per-(row, workgroup) partials (max, sum of exp2) in log2
+//    units; a combine kernel folds them per row in a fixed order into
+//    rowc = m + log2(l); pass 2 recomputes the logits and accumulates
+//    exp2(t - rowc).
+//  * Keyformer noise: lane values come in groups of 4 consecutive, 4-aligned
+//    keys, which is exactly one Philox4x32-10 block, so every Philox call is
+//    fully used.
+#include <math.h>
+
+#include "common.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kChunks = kD / 8;                        // 16-byte chunks per row
+constexpr int kWaves = 4;
+constexpr int kTiles = 2;                              // 32-key tiles per wave
+constexpr int kKeysPerWave = 32 * kTiles;
+constexpr int kKeysPerBlock = kKeysPerWave * kWaves;   // 256
+constexpr int kQRows = 32;
+constexpr int kThreads = kWaves * kWave;
+
+struct ScoreParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t q_hs, q_ls, k_hs, k_ls;
+  float* imp;        // [L, Hkv, n]
+  float2* part;      // [L, Hkv, R, nblk] (max, sum) in log2 units
+  float* rowc;       // [L, Hkv, R]
+  const float* layer_scales;
+  float scale;
+  float tau_mul;     // log2(e) / tau, 0 for tau = +inf
+  float inv_w;
+  uint32_t seed_lo, seed_hi;
+  int L, Hkv, G, w, S, n, R, nblk, nqb;
+};
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
+// multiply-high/low S-box on words 0 and 2 with the key bumped by the Weyl
+// constants between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 x, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * x.z;
+    u32x4 y;
+    y.x = (uint32_t)(p1 >> 32) ^ x.y ^ k0;
+    y.y = (uint32_t)p1;
+    y.z = (uint32_t)(p0 >> 32) ^ x.w ^ k1;
+    y.w = (uint32_t)p0;
+    x = y;
+  }
+  return x;
+}
+
+// Gumbel(0,1) from one 32-bit word: u = (2*(X>>9)+1) * 2^-24 (exact in fp32),
+// zeta = -ln(-ln u); -ln u uses log1p(u-1) for u >= 1/2 (u-1 is exact there).
+__device__ __forceinline__ float gumbel_from_word(uint32_t x) {
+  const float u = (float)(((x >> 9) << 1) | 1u) * 0x1p-24f;
+  const float e = (u >= 0.5f) ? -log1pf(u - 1.0f) : -logf(u);
+  return -logf(e);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <bool kPass2, bool kGumbel>
+__global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
+  __shared__ u32x4 qs[2][kQRows * kChunks];   // 2 x 8 KB
+  __shared__ float2 red[2][kWaves][32];
+
+  const int blk = blockIdx.x, g = blockIdx.y, layer = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hb = lane >> 5, col = lane & 31;
+  const int key0 = blk * kKeysPerBlock + wave * kKeysPerWave;
+  const bool tail = blk * kKeysPerBlock + kKeysPerBlock > p.n;
+  const float alpha = p.layer_scales ? p.layer_scales[layer] : p.scale;
+  const float c = alpha * kLog2e;
+  const int64_t head_row0 = ((int64_t)layer * p.Hkv + g) * p.R;
+
+  // ---- K fragments: lane holds key (col) of tile t, 16-byte chunk (2s + hb).
+  bf16x8 kf[kTiles][8];
+  {
+    const uint16_t* kb = p.k + layer * p.k_ls + g * p.k_hs;
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      int j = key0 + t * 32 + col;
+      j = j < p.n ? j : p.n - 1;   // clamp: rows past the prefix are masked below
+      const bf16x8* row = reinterpret_cast<const bf16x8*>(kb + (int64_t)j * kD);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) kf[t][s] = row[2 * s + hb];
+    }
+  }
+
+  // ---- Q block staging: 512 16-byte chunks per 32-row block, 2 per thread.
+  const uint16_t* qb_base = p.q + layer * p.q_ls;
+  auto load_q = [&](int qb, u32x4 (&regs)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + u * kThreads, row = idx >> 4, ch = idx & 15;
+      const int r = qb * kQRows + row;
+      if (r < p.R) {
+        const int hh = r / p.w, i = r - hh * p.w;
+        const int h = g * p.G + hh;
+        regs[u] = *reinterpret_cast<const u32x4*>(qb_base + h * p.q_hs + (int64_t)i * kD + ch * 8);
+      } else {
+        regs[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_q = [&](int buf, const u32x4 (&regs)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + u * kThreads, row = idx >> 4, ch = idx & 15;
+      qs[buf][row * kChunks + (ch ^ (row & 15))] = regs[u];
+    }
+  };
+  auto load_rc = [&](int qb) -> float {
+    const int r = qb * kQRows + col;
+    return r < p.R ? p.rowc[head_row0 + r] : INFINITY;
+  };
+  // Pass 1: wave 0 folds the 4 waves' statistics of block qb into one partial.
+  auto store_partial = [&](int qb) {
+    if (wave == 0 && hb == 0) {
+      const int b = qb & 1;
+      float m = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) m = fmaxf(m, red[b][v][col].x);
+      float l = 0.f;
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+          const float2 a = red[b][v][col];
+          if (a.x != -INFINITY) l += a.y * fast_exp2(a.x - m);
+        }
+      }
+      const int r = qb * kQRows + col;
+      if (r < p.R) p.part[(head_row0 + r) * p.nblk + blk] = float2{m, l};
+    }
+  };
+
+  // Logits of this lane for query block qb, in log2 units (Keyformer path).
+  auto noisy = [&](f32x16 (&acc)[kTiles], int qb) {
+    const int r = qb * kQRows + col;
+    const int hh = r / p.w, i = r - hh * p.w;
+    const uint32_t h = (uint32_t)(g * p.G + hh);
+    const uint32_t pos = (uint32_t)(p.S - p.w + i);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const uint32_t j0 = (uint32_t)(key0 + t * 32 + 8 * r4 + 4 * hb);
+        const u32x4 x = philox4x32_10(u32x4{j0 >> 2, pos, h, 0u}, p.seed_lo, p.seed_hi);
+        acc[t][4 * r4 + 0] = fmaf(acc[t][4 * r4 + 0], alpha, gumbel_from_word(x.x)) * p.tau_mul;
+        acc[t][4 * r4 + 1] = fmaf(acc[t][4 * r4 + 1], alpha, gumbel_from_word(x.y)) * p.tau_mul;
+        acc[t][4 * r4 + 2] = fmaf(acc[t][4 * r4 + 2], alpha, gumbel_from_word(x.z)) * p.tau_mul;
+        acc[t][4 * r4 + 3] = fmaf(acc[t][4 * r4 + 3], alpha, gumbel_from_word(x.w)) * p.tau_mul;
+      }
+    }
+  };
+
+  u32x4 qreg[2];
+  load_q(0, qreg);
+  store_q(0, qreg);
+  float rc_next = kPass2 ? load_rc(0) : 0.f;
+  __syncthreads();
+
+  f32x16 colacc[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) colacc[t] = f32x16{};
+
+  for (int qb = 0; qb < p.nqb; ++qb) {
+    const int buf = qb & 1;
+    const bool more = qb + 1 < p.nqb;
+    if (!kPass2 && qb > 0) store_partial(qb - 1);
+    if (more) load_q(qb + 1, qreg);
+    const float rc = rc_next;
+    if (kPass2 && more) rc_next = load_rc(qb + 1);
+
+    f32x16 acc[kTiles];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) acc[t] = f32x16{};
+    const bf16x8* qsb = reinterpret_cast<const bf16x8*>(qs[buf]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 qf = qsb[col * kChunks + ((2 * s + hb) ^ (col & 15))];
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], qf, acc[t], 0, 0, 0);
+    }
+    // acc[t][r] = <K[key], Q[row]>, key = key0 + 32t + 8(r/4) + 4hb + (r%4), row = 32qb + col
+    if (kGumbel) noisy(acc, qb);
+
+    if (!kPass2) {
+      // masking: keys past the prefix, rows past the group
+      const bool row_ok = qb * kQRows + col < p.R;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + t * 32 + 8 * (r >> 2) + 4 * hb + (r & 3);
+          float v = acc[t][r];
+          if ((tail && key >= p.n) || !row_ok) v = -INFINITY;
+          acc[t][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      }
+      float mt, l = 0.f;
+      if (kGumbel) {
+        mt = mx;
+        if (mx != -INFINITY) {
+#pragma unroll
+          for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) l += fast_exp2(acc[t][r] - mt);
+        }
+      } else {
+        mt = mx * c;
+        if (mx != -INFINITY) {
+#pragma unroll
+          for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) l += fast_exp2(fmaf(acc[t][r], c, -mt));
+        }
+      }
+      // fold with the other half-wave (same query row, other 8 keys of each group)
+      const float mo = __shfl_xor(mt, 32), lo = __shfl_xor(l, 32);
+      const float m2 = fmaxf(mt, mo);
+      float l2 = 0.f;
+      if (m2 != -INFINITY) {
+        if (mt != -INFINITY) l2 += l * fast_exp2(mt - m2);
+        if (mo != -INFINITY) l2 += lo * fast_exp2(mo - m2);
+      }
+      if (hb == 0) red[buf][wave][col] = float2{m2, l2};
+    } else {
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float tt = kGumbel ? acc[t][r] - rc : fmaf(acc[t][r], c, -rc);
+          colacc[t][r] += fast_exp2(tt);
+        }
+      }
+    }
+
+    if (more) store_q(buf ^ 1, qreg);
+    __syncthreads();
+  }
+
+  if (!kPass2) {
+    store_partial(p.nqb - 1);
+    return;
+  }
+
+  // ---- pass 2: sum each key column over the 32 query lanes of its half-wave.
+  float* out = p.imp + ((int64_t)layer * p.Hkv + g) * p.n;
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    float mine = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = colacc[t][r];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 1);
+      if (col == r) mine = v;
+    }
+    if (col < 16) {
+      const int key = key0 + t * 32 + 8 * (col >> 2) + 4 * hb + (col & 3);
+      if (key < p.n) out[key] = mine * p.inv_w;
+    }
+  }
+}
+
+// Fold the per-workgroup partials of one query row (one wave per row, fixed
+// order): rowc = m + log2(sum_b l_b * 2^(m_b - m)).
+__global__ __launch_bounds__(256) void score_combine(ScoreParams p, int rows) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float2* pp = p.part + (int64_t)row * p.nblk;
+  float m = -INFINITY;
+  for (int b = lane; b < p.nblk; b += kWave) m = fmaxf(m, pp[b].x);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  float l = 0.f;
+  for (int b = lane; b < p.nblk; b += kWave) {
+    const float2 a = pp[b];
+    if (a.x != -INFINITY) l += a.y * fast_exp2(a.x - m);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+  if (lane == 0) p.rowc[row] = (l > 0.f) ? m + log2f(l) : INFINITY;
+}
+
+struct Plan {
+  int n, G, R, nblk, nqb;
+  size_t part_bytes, rowc_bytes, total;
+};
+
+kvc_status plan(const kvc_score_args* a, Plan* pl) {
+  if (!a) return KVC_E_ARG;
+  if (a->L < 1 || a->H < 1 || a->Hkv < 1 || a->w < 1 || a->S < 2 || a->D < 1) return KVC_E_ARG;
+  if (a->H % a->Hkv) return KVC_E_SHAPE;
+  if (a->w >= a->S) return KVC_E_SHAPE;
+  if (a->D != kD) return KVC_E_UNSUPPORTED;
+  if (a->L > 65535 || a->Hkv > 65535) return KVC_E_SHAPE;
+  const int64_t G = a->H / a->Hkv;
+  if (G * a->w > 65536) return KVC_E_SHAPE;
+  if (a->q_head_stride < (int64_t)a->w * kD || a->k_head_stride < (int64_t)a->S * kD) return KVC_E_SHAPE;
+  if (a->L > 1 && (a->q_layer_stride < a->H * a->q_head_stride ||
+                   a->k_layer_stride < a->Hkv * a->k_head_stride))
+    return KVC_E_SHAPE;
+  if ((a->q_head_stride | a->k_head_stride | a->q_layer_stride | a->k_layer_stride) & 7) return KVC_E_ARG;
+  if (!a->layer_scales && !(a->scale > 0.f && isfinite(a->scale))) return KVC_E_ARG;
+  if (a->gumbel && !(a->tau > 0.f)) return KVC_E_ARG;   // rejects NaN; +inf allowed
+  pl->n = a->S - a->w;
+  pl->G = (int)G;
+  pl->R = (int)(G * a->w);
+  pl->nblk = (pl->n + kKeysPerBlock - 1) / kKeysPerBlock;
+  pl->nqb = (pl->R + kQRows - 1) / kQRows;
+  const size_t rows = (size_t)a->L * a->Hkv * pl->R;
+  pl->part_bytes = align_up(rows * pl->nblk * sizeof(float2), 256);
+  pl->rowc_bytes = align_up(rows * sizeof(float), 256);
+  pl->total = pl->part_bytes + pl->rowc_bytes;
+  return KVC_OK;
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" size_t kvc_score_workspace_size(const kvc_score_args* args) {
+  kvc::Plan pl;
+  return kvc::plan(args, &pl) == KVC_OK ? pl.total : 0;
+}
+
+extern "C" kvc_status kvc_score(const kvc_score_args* a, const void* q_obs, const void* k,
+                                float* importance, void* ws, size_t ws_bytes, void* stream) {
+  using namespace kvc;
+  Plan pl;
+  kvc_status st = plan(a, &pl);
+  if (st != KVC_OK) return st;
+  if (!q_obs || !k || !importance) return KVC_E_ARG;
+  if (!aligned16(q_obs) || !aligned16(k) || (reinterpret_cast<uintptr_t>(importance) & 3)) return KVC_E_ARG;
+  if (!ws || ws_bytes < pl.total || !aligned16(ws)) return KVC_E_WORKSPACE;
+
+  ScoreParams p;
+  p.q = static_cast<const uint16_t*>(q_obs);
+  p.k = static_cast<const uint16_t*>(k);
+  p.q_hs = a->q_head_stride;
+  p.q_ls = a->q_layer_stride;
+  p.k_hs = a->k_head_stride;
+  p.k_ls = a->k_layer_stride;
+  p.imp = importance;
+  p.part = reinterpret_cast<float2*>(ws);
+  p.rowc = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.part_bytes);
+  p.layer_scales = a->layer_scales;
+  p.scale = a->scale;
+  p.tau_mul = a->gumbel ? (isinf(a->tau) ? 0.f : kLog2e / a->tau) : 0.f;
+  p.inv_w = 1.0f / (float)a->w;
+  p.seed_lo = (uint32_t)(a->seed & 0xFFFFFFFFull);
+  p.seed_hi = (uint32_t)(a->seed >> 32);
+  p.L = a->L;
+  p.Hkv = a->Hkv;
+  p.G = pl.G;
+  p.w = a->w;
+  p.S = a->S;
+  p.n = pl.n;
+  p.R = pl.R;
+  p.nblk = pl.nblk;
+  p.nqb = pl.nqb;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(pl.nblk, a->Hkv, a->L), block(kThreads);
+  const int rows = a->L * a->Hkv * pl.R;
+  if (a->gumbel) {
+    KVC_LAUNCH("score_pass1_gumbel", (score_pass<false, true>), grid, block, s, p);
+    KVC_LAUNCH("score_combine", score_combine, dim3((rows + 3) / 4), dim3(256), s, p, rows);
+    KVC_LAUNCH("score_pass2_gumbel", (score_pass<true, true>), grid, block, s, p);
+  } else {
+    KVC_LAUNCH("score_pass1", (score_pass<false, false>), grid, block, s, p);
+    KVC_LAUNCH("score_combine", score_combine, dim3((rows + 3) / 4), dim3(256), s, p, rows);
+    KVC_LAUNCH("score_pass2", (score_pass<true, false>), grid, block, s, p);
+  }
+  return KVC_OK;
+}

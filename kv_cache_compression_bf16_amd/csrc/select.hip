@@ -1,0 +1,155 @@
+// kvc_select_topk: per-head top-k of the importance plus the recent window.
+//
+// Selection rule (ZigZagKV blog page, SnapKV and token-selection sections;
+// Keyformer blog page, prompt phase): candidates are positions [0, c),
+// c = min(S - w, S - recent); the k_top = budget - recent candidates first in
+// (importance descending, position ascending) order are kept together with
+// every position of [S - recent, S); kept positions are written ascending.
+//
+// Design: one 1024-thread workgroup per head runs an exact MSB-first radix
+// select on order-preserving 32-bit keys of the fp32 scores (digits of 11, 11
+// and 10 bits, histograms in LDS with integer atomics, which are exact and
+// order-independent).  That yields the k-th key T and how many T-valued
+// candidates must be taken; a final ordered pass keeps every key > T and the
+// first such T-valued candidates by position, writing positions with two
+// block-wide prefix sums, so the output is ascending without a sort.
+#include "common.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kBins = 2048;
+
+// fp32 -> uint32 with the same order (-0 folded onto +0).
+__device__ __forceinline__ uint32_t order_key(uint32_t b) {
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Exclusive prefix sum over the workgroup; *total receives the sum of all x.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t v = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) wsum[wid] = v;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kSelWaves; ++i) {
+    const uint32_t s = wsum[i];
+    before += (i < wid) ? s : 0u;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + v - x;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* imp, int64_t hs, int c,
+                                                                 int k_top, int S, int recent, int budget,
+                                                                 int32_t* out) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t wsum[kSelWaves];
+  __shared__ uint32_t s_digit, s_above;
+
+  const int g = blockIdx.x, tid = threadIdx.x;
+  const uint32_t* v = reinterpret_cast<const uint32_t*>(imp + (int64_t)g * hs);
+  int32_t* o = out + (int64_t)g * budget;
+
+  for (int t = tid; t < recent; t += kSelThreads) o[k_top + t] = S - recent + t;
+  if (k_top == 0) return;
+  if (k_top >= c) {
+    for (int j = tid; j < c; j += kSelThreads) o[j] = j;
+    return;
+  }
+
+  // ---- radix select of the k_top-th largest key
+  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k_top;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t width_mask = (pass == 2) ? 0x3FFu : 0x7FFu;
+    for (int b = tid; b < kBins; b += kSelThreads) hist[b] = 0;
+    if (tid == 0) {
+      s_digit = 0;
+      s_above = 0;
+    }
+    __syncthreads();
+    for (int j = tid; j < c; j += kSelThreads) {
+      const uint32_t key = order_key(v[j]);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & width_mask], 1u);
+    }
+    __syncthreads();
+    // suffix counts: thread tid owns bins 2*rt and 2*rt+1, rt = 1023 - tid
+    const int rt = kSelThreads - 1 - tid;
+    const uint32_t h0 = hist[2 * rt], h1 = hist[2 * rt + 1];
+    uint32_t tot;
+    const uint32_t incl = block_excl_scan(h0 + h1, wsum, &tot) + h0 + h1;   // = sum of bins >= 2rt
+    const uint32_t suf1 = incl - h0;                                        // = sum of bins >= 2rt+1
+    if (suf1 >= krem && suf1 - h1 < krem) {
+      s_digit = 2 * rt + 1;
+      s_above = suf1 - h1;
+    } else if (incl >= krem && incl - h0 < krem) {
+      s_digit = 2 * rt;
+      s_above = incl - h0;
+    }
+    __syncthreads();
+    prefix |= s_digit << sh;
+    pmask |= width_mask << sh;
+    krem -= s_above;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;   // k_top-th largest key; take krem of the keys equal to T
+
+  // ---- ordered emission
+  uint32_t eq_carry = 0, out_carry = 0;
+  for (int base = 0; base < c; base += kSelThreads) {
+    const int j = base + tid;
+    const uint32_t key = j < c ? order_key(v[j]) : 0u;
+    const bool in = j < c;
+    const bool gt = in && key > T;
+    const bool eq = in && key == T;
+    uint32_t eq_tot;
+    const uint32_t eq_before = block_excl_scan(eq ? 1u : 0u, wsum, &eq_tot) + eq_carry;
+    const bool take = gt || (eq && eq_before < krem);
+    uint32_t take_tot;
+    const uint32_t pos = block_excl_scan(take ? 1u : 0u, wsum, &take_tot) + out_carry;
+    if (take && pos < (uint32_t)k_top) o[pos] = j;
+    eq_carry += eq_tot;
+    out_carry += take_tot;
+  }
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" size_t kvc_select_topk_workspace_size(int32_t Hkv, int32_t n) {
+  (void)Hkv;
+  (void)n;
+  return 0;
+}
+
+extern "C" kvc_status kvc_select_topk(const float* importance, int64_t imp_head_stride, int32_t Hkv,
+                                      int32_t S, int32_t w, int32_t recent, int32_t budget,
+                                      int32_t* indices, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (Hkv < 1 || S < 2 || w < 1 || w >= S || recent < 0 || recent > S) return KVC_E_ARG;
+  const int32_t n = S - w;
+  const int32_t c = n < S - recent ? n : S - recent;
+  if (budget < recent || budget - recent > c) return KVC_E_ARG;
+  if (imp_head_stride < n && Hkv > 1) return KVC_E_SHAPE;
+  if (!indices || (!importance && budget > recent)) return KVC_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(importance) & 3) || (reinterpret_cast<uintptr_t>(indices) & 3))
+    return KVC_E_ARG;
+  if (budget == 0) return KVC_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  KVC_LAUNCH("select_topk", kvc::select_topk_kernel, dim3(Hkv), dim3(kvc::kSelThreads), s, importance,
+             imp_head_stride, c, budget - recent, S, recent, budget, indices);
+  return KVC_OK;
+}

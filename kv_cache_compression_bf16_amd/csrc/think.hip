@@ -1,0 +1,151 @@
+// kvc_channel_prune: ThinK magnitude-based key-channel pruning.
+//
+// ThinK page (papercache summary of arXiv 2407.21018), magnitude-based pruning:
+// every head keeps the T = floor((1 - lambda) D) key channels with the largest
+// l_p norm over tokens; THINK's implementation section: recent keys are not
+// pruned and a binary mask records the pruned channels.  The norm here runs
+// over the non-recent kept rows (the rows that get pruned).
+//
+// Design (D = 128):
+//  * think_partial: grid (row chunks of 512, heads); 16 lanes cover one
+//    256-byte row with 16-byte loads, 16 rows in flight per workgroup; per-lane
+//    fp32 sums of |x|^p, folded over the 16 row lanes in a fixed order ->
+//    partial[g, chunk, d].
+//  * think_select: one 128-thread workgroup per head folds the chunk partials
+//    in order, ranks channels by (norm desc, index asc), writes the kept
+//    channels ascending and the mask.
+//  * think_gather: one wave per row; lane l holds bf16 channels 2l, 2l+1 of the
+//    row, output channel c takes its value with one cross-lane read from lane
+//    channels[c]/2 and the rows are written contiguously.
+#include "common.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kChunkRows = 512;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__global__ __launch_bounds__(256) void think_partial(const uint16_t* kc, int budget, int rows, int p,
+                                                    int nchunk, float* part) {
+  __shared__ float red[16][kD + 1];
+  const int chunk = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int cg = tid & 15, rl = tid >> 4;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  const int r0 = chunk * kChunkRows;
+  const int r1 = min(r0 + kChunkRows, rows);
+  const uint16_t* base = kc + (int64_t)g * budget * kD + cg * 8;
+  for (int r = r0 + rl; r < r1; r += 16) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(base + (int64_t)r * kD);
+    const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = bf16_lo(wv[e]), b = bf16_hi(wv[e]);
+      if (p == 2) {
+        acc[2 * e] = fmaf(a, a, acc[2 * e]);
+        acc[2 * e + 1] = fmaf(b, b, acc[2 * e + 1]);
+      } else {
+        acc[2 * e] += fabsf(a);
+        acc[2 * e + 1] += fabsf(b);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rl][cg * 8 + e] = acc[e];
+  __syncthreads();
+  if (tid < kD) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += red[i][tid];
+    part[((int64_t)g * nchunk + chunk) * kD + tid] = s;
+  }
+}
+
+__global__ __launch_bounds__(kD) void think_select(const float* part, int nchunk, int T, int32_t* channels,
+                                                  uint8_t* mask) {
+  __shared__ float sm[kD];
+  __shared__ int ssel[kD];
+  const int g = blockIdx.x, d = threadIdx.x;
+  float M = 0.f;
+  for (int c = 0; c < nchunk; ++c) M += part[((int64_t)g * nchunk + c) * kD + d];
+  sm[d] = M;
+  __syncthreads();
+  int rank = 0;
+  for (int e = 0; e < kD; ++e) {
+    const float o = sm[e];
+    rank += (o > M || (o == M && e < d)) ? 1 : 0;
+  }
+  const bool sel = rank < T;
+  ssel[d] = sel ? 1 : 0;
+  __syncthreads();
+  int pos = 0;
+  for (int e = 0; e < d; ++e) pos += ssel[e];
+  if (sel && pos < T) channels[(int64_t)g * T + pos] = d;   // pos < T unless norms are NaN
+  if (mask) mask[(int64_t)g * kD + d] = sel ? 1 : 0;
+}
+
+__global__ __launch_bounds__(256) void think_gather(const uint16_t* kc, int budget, int rows, int T,
+                                                   const int32_t* channels, uint16_t* out) {
+  const int g = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int32_t* ch = channels + (int64_t)g * T;
+  const int c0 = lane, c1 = lane + 64;
+  const int s0 = c0 < T ? ch[c0] : 0;
+  const int s1 = c1 < T ? ch[c1] : 0;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(kc + (int64_t)g * budget * kD);
+  uint16_t* dst = out + (int64_t)g * rows * T;
+  for (int r = blockIdx.x * 4 + wave; r < rows; r += gridDim.x * 4) {
+    const uint32_t x = src[(int64_t)r * (kD / 2) + lane];
+    const uint32_t y0 = __shfl(x, s0 >> 1);
+    const uint32_t y1 = __shfl(x, s1 >> 1);
+    if (c0 < T) dst[(int64_t)r * T + c0] = (uint16_t)((s0 & 1) ? (y0 >> 16) : (y0 & 0xFFFFu));
+    if (c1 < T) dst[(int64_t)r * T + c1] = (uint16_t)((s1 & 1) ? (y1 >> 16) : (y1 & 0xFFFFu));
+  }
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" size_t kvc_channel_prune_workspace_size(int32_t Hkv, int32_t budget, int32_t D) {
+  if (Hkv < 1 || budget < 0 || D != kvc::kD) return 0;
+  const size_t nchunk = ((size_t)budget + kvc::kChunkRows - 1) / kvc::kChunkRows;
+  return kvc::align_up((nchunk ? nchunk : 1) * Hkv * kvc::kD * sizeof(float), 256);
+}
+
+extern "C" kvc_status kvc_channel_prune(const void* k_c, int32_t Hkv, int32_t budget, int32_t D,
+                                        int32_t recent, double lambda, int32_t p, int32_t* channels,
+                                        uint8_t* mask, void* k_pruned, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  using namespace kvc;
+  if (Hkv < 1 || budget < 0 || recent < 0 || recent > budget) return KVC_E_ARG;
+  if (!(lambda >= 0.0 && lambda < 1.0) || (p != 1 && p != 2)) return KVC_E_ARG;
+  if (D != kD) return KVC_E_UNSUPPORTED;
+  if (Hkv > 65535) return KVC_E_SHAPE;
+  const int T = kvc_think_channels(D, lambda);
+  if (T < 1) return KVC_E_ARG;
+  const int rows = budget - recent;
+  if (!k_c || !channels || (rows > 0 && !k_pruned)) return KVC_E_ARG;
+  if (!aligned16(k_c) || (reinterpret_cast<uintptr_t>(channels) & 3) ||
+      (reinterpret_cast<uintptr_t>(k_pruned) & 1))
+    return KVC_E_ARG;
+  const size_t need = kvc_channel_prune_workspace_size(Hkv, budget, D);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return KVC_E_WORKSPACE;
+  int nchunk = (rows + kChunkRows - 1) / kChunkRows;
+  if (nchunk < 1) nchunk = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* part = static_cast<float*>(ws);
+  const uint16_t* kcp = static_cast<const uint16_t*>(k_c);
+  KVC_LAUNCH("think_partial", think_partial, dim3(nchunk, Hkv), dim3(256), s, kcp, budget, rows, p, nchunk,
+             part);
+  KVC_LAUNCH("think_select", think_select, dim3(Hkv), dim3(kD), s, part, nchunk, T, channels, mask);
+  if (rows > 0) {
+    int gx = (rows + 3) / 4;
+    if (gx > 2048) gx = 2048;
+    KVC_LAUNCH("think_gather", think_gather, dim3(gx, Hkv), dim3(256), s, kcp, budget, rows, T, channels,
+               static_cast<uint16_t*>(k_pruned));
+  }
+  return KVC_OK;
+}

@@ -1,0 +1,240 @@
+"""Thin Python binding of libkvc.so (C ABI declared in include/kvc.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libkvc.so.  Tensors are torch tensors on the GPU (torch provides device memory
+and the stream); each function takes the same name as the C entry point it
+calls.  Importing this module fails loudly if the library is missing; there is
+no CPU fallback.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvc.so")
+
+KVC_OK, KVC_E_ARG, KVC_E_SHAPE, KVC_E_WORKSPACE, KVC_E_DEVICE, KVC_E_UNSUPPORTED = range(6)
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {_lib.kvc_status_str(status).decode()}")
+
+
+class ScoreArgs(ctypes.Structure):
+    _fields_ = [
+        ("L", ctypes.c_int32), ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("w", ctypes.c_int32), ("S", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("q_head_stride", ctypes.c_int64), ("q_layer_stride", ctypes.c_int64),
+        ("k_head_stride", ctypes.c_int64), ("k_layer_stride", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("layer_scales", ctypes.c_void_p),
+        ("gumbel", ctypes.c_int32), ("tau", ctypes.c_float), ("seed", ctypes.c_uint64),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m kv_cache_compression_bf16_amd.build_lib` "
+                          "(or __graft_entry__.build()) first -- there is no CPU fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
+    sig = {
+        "kvc_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "kvc_abi_version": (ctypes.c_int, []),
+        "kvc_cache_bytes": (I64, [I64, I64, I64, I64, I64, I64]),
+        "kvc_think_channels": (ctypes.c_int, [ctypes.c_int, F64]),
+        "kvc_score_workspace_size": (SZ, [ctypes.POINTER(ScoreArgs)]),
+        "kvc_score": (ctypes.c_int, [ctypes.POINTER(ScoreArgs), P, P, P, P, SZ, P]),
+        "kvc_lmba_budget_workspace_size": (SZ, [I32, I32, I32]),
+        "kvc_lmba_budget": (ctypes.c_int, [P, I32, I32, I32, F64, I64, I32, I32, P, P, P, SZ, P]),
+        "kvc_select_topk_workspace_size": (SZ, [I32, I32]),
+        "kvc_select_topk": (ctypes.c_int, [P, I64, I32, I32, I32, I32, I32, P, P, SZ, P]),
+        "kvc_compact": (ctypes.c_int, [P, P, I32, I32, I32, I64, I64, P, I32, P, P, P]),
+        "kvc_channel_prune_workspace_size": (SZ, [I32, I32, I32]),
+        "kvc_channel_prune": (ctypes.c_int, [P, I32, I32, I32, I32, F64, I32, P, P, P, P, SZ, P]),
+        "kvc_timing_enable": (ctypes.c_int, [I32]),
+        "kvc_timing_count": (I32, []),
+        "kvc_timing_read": (ctypes.c_int, [I32, ctypes.c_char_p, I32, ctypes.POINTER(I32),
+                                           ctypes.POINTER(F64)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+lib = _lib
+
+
+def _check(status, where):
+    if status != KVC_OK:
+        raise KvcError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == 0:
+        return ws, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def _bf16(t, name):
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold raw bf16 (torch.bfloat16 / int16), got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+
+
+# ---------------------------------------------------------------- helpers
+def kvc_abi_version():
+    return _lib.kvc_abi_version()
+
+
+def kvc_cache_bytes(B, S, L, N, D, elem_bytes):
+    return _lib.kvc_cache_bytes(B, S, L, N, D, elem_bytes)
+
+
+def kvc_think_channels(D, lam):
+    return _lib.kvc_think_channels(D, lam)
+
+
+# ---------------------------------------------------------------- kvc_score
+def score_args(q_obs, k, *, w, S, scale=None, layer_scales=None, gumbel=False, tau=1.0, seed=0):
+    """ScoreArgs from tensors shaped q_obs [L?, H, w, D], k [L?, Hkv, S_alloc, D]."""
+    q4 = q_obs if q_obs.dim() == 4 else q_obs.unsqueeze(0)
+    k4 = k if k.dim() == 4 else k.unsqueeze(0)
+    L, H, wq, D = q4.shape
+    Lk, Hkv, Sk, Dk = k4.shape
+    if Lk != L or Dk != D or wq != w or Sk < S:
+        raise ValueError(f"shape mismatch: q_obs {tuple(q_obs.shape)}, k {tuple(k.shape)}, w={w}, S={S}")
+    if q4.stride(3) != 1 or q4.stride(2) != D or k4.stride(3) != 1 or k4.stride(2) != D:
+        raise ValueError("rows of q_obs and k must be contiguous with stride D")
+    a = ScoreArgs()
+    a.L, a.H, a.Hkv, a.w, a.S, a.D = L, H, Hkv, w, S, D
+    a.q_head_stride, a.q_layer_stride = q4.stride(1), q4.stride(0)
+    a.k_head_stride, a.k_layer_stride = k4.stride(1), k4.stride(0)
+    a.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    a.layer_scales = None if layer_scales is None else layer_scales.data_ptr()
+    a.gumbel = 1 if gumbel else 0
+    a.tau = float(tau)
+    a.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    return a
+
+
+def kvc_score_workspace_size(args):
+    return _lib.kvc_score_workspace_size(ctypes.byref(args))
+
+
+def kvc_score(q_obs, k, importance, *, w, S, scale=None, layer_scales=None, gumbel=False, tau=1.0, seed=0,
+              workspace=None, stream=None):
+    """Observation-window importance into ``importance`` (fp32 [L?, Hkv, S-w])."""
+    _bf16(q_obs, "q_obs")
+    _bf16(k, "k")
+    if layer_scales is not None and (layer_scales.dtype != torch.float32 or not layer_scales.is_cuda):
+        raise TypeError("layer_scales must be a float32 GPU tensor")
+    a = score_args(q_obs, k, w=w, S=S, scale=scale, layer_scales=layer_scales, gumbel=gumbel, tau=tau,
+                   seed=seed)
+    if importance.dtype != torch.float32 or not importance.is_contiguous() \
+            or importance.numel() != a.L * a.Hkv * (S - w):
+        raise ValueError("importance must be contiguous float32 with L*Hkv*(S-w) elements")
+    ws, nbytes = _workspace(_lib.kvc_score_workspace_size(ctypes.byref(a)), k.device, workspace)
+    _check(_lib.kvc_score(ctypes.byref(a), _ptr(q_obs), _ptr(k), _ptr(importance), _ptr(ws), nbytes,
+                          _stream(stream, k.device)), "kvc_score")
+    return importance
+
+
+# ---------------------------------------------------------------- kvc_lmba_budget
+def kvc_lmba_budget(importance, budgets, *, total_budget, floor_per_layer, capacity, mass=0.9, mba=None,
+                    workspace=None, stream=None):
+    """ZigZag budgets (int32 [L]) and optionally MBA (int32 [L, Hkv]) from importance [L, Hkv, n]."""
+    L, Hkv, n = importance.shape
+    if not importance.is_contiguous() or importance.dtype != torch.float32:
+        raise ValueError("importance must be contiguous float32 [L, Hkv, n]")
+    ws, nbytes = (workspace, 0)
+    if mba is None:
+        ws, nbytes = _workspace(_lib.kvc_lmba_budget_workspace_size(L, Hkv, n), importance.device, workspace)
+    _check(_lib.kvc_lmba_budget(_ptr(importance), L, Hkv, n, float(mass), int(total_budget),
+                                int(floor_per_layer), int(capacity), _ptr(mba), _ptr(budgets), _ptr(ws),
+                                nbytes, _stream(stream, importance.device)), "kvc_lmba_budget")
+    return budgets
+
+
+# ---------------------------------------------------------------- kvc_select_topk
+def kvc_select_topk(importance, indices, *, S, w, recent, budget, workspace=None, stream=None):
+    """Per-head kept positions (int32 [Hkv, budget], ascending) from importance [Hkv, n]."""
+    Hkv = importance.shape[0]
+    if importance.dtype != torch.float32 or importance.stride(-1) != 1:
+        raise ValueError("importance rows must be float32 with unit stride")
+    if indices.dtype != torch.int32 or not indices.is_contiguous() or indices.numel() != Hkv * budget:
+        raise ValueError("indices must be contiguous int32 [Hkv, budget]")
+    ws, nbytes = _workspace(_lib.kvc_select_topk_workspace_size(Hkv, S - w), importance.device, workspace)
+    _check(_lib.kvc_select_topk(_ptr(importance), importance.stride(0), Hkv, S, w, recent, budget,
+                                _ptr(indices), _ptr(ws), nbytes, _stream(stream, importance.device)),
+           "kvc_select_topk")
+    return indices
+
+
+# ---------------------------------------------------------------- kvc_compact
+def kvc_compact(k, v, indices, k_out, v_out, *, S, stream=None):
+    """k_out[g, t] = k[g, indices[g, t]] (and v likewise); k, v [Hkv, S_alloc, D]."""
+    _bf16(k, "k")
+    Hkv, _, D = k.shape
+    budget = indices.shape[1]
+    if k.stride(2) != 1 or k.stride(1) != D or not k_out.is_contiguous():
+        raise ValueError("k rows must be contiguous; k_out contiguous")
+    if v is not None and (v.stride(2) != 1 or v.stride(1) != D or not v_out.is_contiguous()):
+        raise ValueError("v rows must be contiguous; v_out contiguous")
+    _check(_lib.kvc_compact(_ptr(k), _ptr(v), Hkv, S, D, k.stride(0), 0 if v is None else v.stride(0),
+                            _ptr(indices), budget, _ptr(k_out), _ptr(v_out), _stream(stream, k.device)),
+           "kvc_compact")
+    return k_out, v_out
+
+
+# ---------------------------------------------------------------- kvc_channel_prune
+def kvc_channel_prune(k_c, channels, k_pruned, *, recent, lam, p=2, mask=None, workspace=None, stream=None):
+    """ThinK pruning of the compacted keys k_c [Hkv, budget, D]."""
+    _bf16(k_c, "k_c")
+    Hkv, budget, D = k_c.shape
+    if not k_c.is_contiguous():
+        raise ValueError("k_c must be contiguous")
+    ws, nbytes = _workspace(_lib.kvc_channel_prune_workspace_size(Hkv, budget, D), k_c.device, workspace)
+    _check(_lib.kvc_channel_prune(_ptr(k_c), Hkv, budget, D, recent, float(lam), int(p), _ptr(channels),
+                                  _ptr(mask), _ptr(k_pruned), _ptr(ws), nbytes, _stream(stream, k_c.device)),
+           "kvc_channel_prune")
+    return channels, k_pruned
+
+
+# ---------------------------------------------------------------- timing
+def kvc_timing_enable(enable=True):
+    _check(_lib.kvc_timing_enable(1 if enable else 0), "kvc_timing_enable")
+
+
+def kvc_timing_read():
+    """{kernel name: (launches, total_ms)} for launches since kvc_timing_enable."""
+    n = _lib.kvc_timing_count()
+    if n < 0:
+        raise KvcError(KVC_E_DEVICE, "kvc_timing_count")
+    out = {}
+    buf = ctypes.create_string_buffer(128)
+    for i in range(n):
+        cnt, ms = ctypes.c_int32(), ctypes.c_double()
+        _check(_lib.kvc_timing_read(i, buf, 128, ctypes.byref(cnt), ctypes.byref(ms)), "kvc_timing_read")
+        out[buf.value.decode()] = (cnt.value, ms.value)
+    return out

@@ -1,0 +1,98 @@
+"""Composition of the C-ABI calls into whole compression passes.
+
+Each pass is a fixed sequence of libkvc calls on one stream: score ->
+[ZigZag budgets] -> select -> compact -> [ThinK].  Buffers are allocated once
+per plan (through torch) so a pass itself allocates nothing on the device.
+No arithmetic happens here.
+"""
+
+import numpy as np
+import torch
+
+from . import kvc
+
+
+def bf16_to_device(bits, device):
+    """Raw bf16 bit patterns (numpy uint16) -> torch.bfloat16 tensor on ``device``."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+class CompressionPlan:
+    """Buffers and call sequence for one workload (see ``workload.Workload``)."""
+
+    def __init__(self, wl, device, tau=1.0):
+        self.wl = wl
+        self.device = device
+        self.tau = tau
+        f32, i32, bf = torch.float32, torch.int32, torch.bfloat16
+        L, Hkv, n, D = wl.L, wl.Hkv, wl.n, wl.D
+        self.importance = torch.empty((L, Hkv, n), dtype=f32, device=device)
+        self.zigzag = bool(wl.total_budget)
+        # workspace for kvc_score sized from a representative ScoreArgs
+        a = kvc.ScoreArgs()
+        a.L, a.H, a.Hkv, a.w, a.S, a.D = L, wl.H, Hkv, wl.w, wl.S, D
+        a.q_head_stride, a.q_layer_stride = wl.w * D, wl.H * wl.w * D
+        a.k_head_stride, a.k_layer_stride = wl.S * D, Hkv * wl.S * D
+        a.scale, a.gumbel, a.tau = 1.0, 1 if wl.gumbel else 0, 1.0
+        self.ws_score = torch.empty(max(kvc.kvc_score_workspace_size(a), 256), dtype=torch.uint8, device=device)
+        if self.zigzag:
+            self.budgets = torch.empty(L, dtype=i32, device=device)
+            self.mba = torch.empty((L, Hkv), dtype=i32, device=device)
+            tot = wl.total_budget
+            self.indices_flat = torch.empty(Hkv * tot, dtype=i32, device=device)
+            self.kc_flat = torch.empty(Hkv * tot * D, dtype=bf, device=device)
+            self.vc_flat = torch.empty(Hkv * tot * D, dtype=bf, device=device)
+        else:
+            B = wl.budget
+            self.indices = torch.empty((Hkv, B), dtype=i32, device=device)
+            self.kc = torch.empty((Hkv, B, D), dtype=bf, device=device)
+            self.vc = torch.empty((Hkv, B, D), dtype=bf, device=device)
+            sel_ws = kvc.lib.kvc_select_topk_workspace_size(Hkv, n)
+            self.ws_select = torch.empty(max(sel_ws, 256), dtype=torch.uint8, device=device)
+        self.think = wl.think_lambda >= 0
+        if self.think:
+            T = kvc.kvc_think_channels(D, wl.think_lambda)
+            rows = wl.budget - wl.recent
+            self.channels = torch.empty((Hkv, T), dtype=i32, device=device)
+            self.mask = torch.empty((Hkv, D), dtype=torch.uint8, device=device)
+            self.kp = torch.empty((Hkv, rows, T), dtype=bf, device=device)
+            self.ws_think = torch.empty(max(kvc.lib.kvc_channel_prune_workspace_size(Hkv, wl.budget, D), 256),
+                                        dtype=torch.uint8, device=device)
+
+    def score(self, q, k, layer_scales=None, stream=None):
+        wl = self.wl
+        kvc.kvc_score(q, k, self.importance if wl.L > 1 else self.importance[0], w=wl.w, S=wl.S,
+                      layer_scales=layer_scales, gumbel=wl.gumbel, tau=self.tau, seed=wl.noise_seed,
+                      workspace=self.ws_score, stream=stream)
+
+    def run(self, q, k, v, layer_scales=None, stream=None):
+        """One whole pass.  q [L?, H, w, D], k/v [L?, Hkv, S, D] (bf16 on device)."""
+        wl = self.wl
+        self.score(q, k, layer_scales, stream)
+        if not self.zigzag:
+            kvc.kvc_select_topk(self.importance[0], self.indices, S=wl.S, w=wl.w, recent=wl.recent,
+                                budget=wl.budget, workspace=self.ws_select, stream=stream)
+            kvc.kvc_compact(k if k.dim() == 3 else k[0], v if v.dim() == 3 else v[0], self.indices, self.kc,
+                            self.vc, S=wl.S, stream=stream)
+            if self.think:
+                kvc.kvc_channel_prune(self.kc, self.channels, self.kp, recent=wl.recent, lam=wl.think_lambda,
+                                      p=wl.think_p, mask=self.mask, workspace=self.ws_think, stream=stream)
+            return
+        kvc.kvc_lmba_budget(self.importance, self.budgets, total_budget=wl.total_budget,
+                            floor_per_layer=wl.floor, capacity=wl.capacity, mass=wl.mass, mba=self.mba,
+                            stream=stream)
+        budgets = self.budgets.cpu().tolist()      # sizes the per-layer outputs (one small D2H copy)
+        self.layer_budgets = budgets
+        off = 0
+        Hkv, D = wl.Hkv, wl.D
+        self.layer_views = []
+        for l, B in enumerate(budgets):
+            idx = self.indices_flat[off * Hkv:(off + B) * Hkv].view(Hkv, B)
+            kc = self.kc_flat[off * Hkv * D:(off + B) * Hkv * D].view(Hkv, B, D)
+            vc = self.vc_flat[off * Hkv * D:(off + B) * Hkv * D].view(Hkv, B, D)
+            kvc.kvc_select_topk(self.importance[l], idx, S=wl.S, w=wl.w, recent=wl.recent, budget=B,
+                                stream=stream)
+            kvc.kvc_compact(k[l], v[l], idx, kc, vc, S=wl.S, stream=stream)
+            self.layer_views.append((idx, kc, vc))
+            off += B

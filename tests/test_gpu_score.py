@@ -1,0 +1,121 @@
+"""kvc_score on the GPU against the oracle (element-wise, several tiles and
+ragged tails in both the key and the query-row directions)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_compression_bf16_amd import workload as wk
+
+from _parity import check_importance, dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _kvc():
+    from kv_cache_compression_bf16_amd import kvc
+    return kvc
+
+
+def _draw(H, Hkv, w, S, D=128, seed=0, outliers=0, L=None, pad_rows=0):
+    rng = np.random.default_rng(seed)
+    shp_q = (H, w, D) if L is None else (L, H, w, D)
+    shp_k = (Hkv, S + pad_rows, D) if L is None else (L, Hkv, S + pad_rows, D)
+    q = rng.standard_normal(shp_q, dtype=np.float32)
+    k = rng.standard_normal(shp_k, dtype=np.float32)
+    if outliers:
+        ch = rng.choice(D, outliers, replace=False)
+        k[..., ch] *= 8
+    return wk.f32_to_bf16_bits(q), wk.f32_to_bf16_bits(k)
+
+
+def _gpu_importance(qb, kb, *, w, S, L=None, **kw):
+    kvc = _kvc()
+    q, k = to_dev(qb), to_dev(kb)
+    Hkv = kb.shape[-3]
+    shape = (Hkv, S - w) if L is None else (L, Hkv, S - w)
+    imp = torch.full(shape, float("nan"), dtype=torch.float32, device=dev())
+    kvc.kvc_score(q, k, imp, w=w, S=S, **kw)
+    torch.cuda.synchronize()
+    return imp.cpu().numpy()
+
+
+def _oracle(qb, kb, *, w, S, scale, **kw):
+    return oracle.score.importance(oracle.score.bf16_bits_to_f64(qb), oracle.score.bf16_bits_to_f64(kb),
+                                   S=S, w=w, scale=scale, **kw)
+
+
+F32_ALPHA = float(np.float32(1 / math.sqrt(128)))
+
+
+@pytest.mark.parametrize("H,Hkv,w,S", [
+    (8, 8, 32, 2048),      # tiny SnapKV shape: 8 full key blocks
+    (8, 2, 20, 1000),      # G=4, 80 query rows (ragged 32-row blocks), 980 keys (ragged 256-key block)
+    (4, 4, 1, 300),        # single query row
+    (2, 1, 33, 290),       # G=2, 66 rows, n=257: one key past a block
+    (32, 8, 128, 4096 + 77),
+])
+def test_importance_matches_oracle(H, Hkv, w, S):
+    qb, kb = _draw(H, Hkv, w, S, seed=H * 1000 + S)
+    gpu = _gpu_importance(qb, kb, w=w, S=S)
+    ref = _oracle(qb, kb, w=w, S=S, scale=F32_ALPHA)
+    check_importance(gpu, ref, H // Hkv, f"H={H} Hkv={Hkv} w={w} S={S}")
+
+
+def test_outlier_channels_and_explicit_scale():
+    qb, kb = _draw(16, 4, 64, 3000, seed=5, outliers=4)
+    gpu = _gpu_importance(qb, kb, w=64, S=3000, scale=0.05)
+    ref = _oracle(qb, kb, w=64, S=3000, scale=float(np.float32(0.05)))
+    check_importance(gpu, ref, 4, "outliers")
+
+
+def test_minimal_prefix_of_one_key():
+    qb, kb = _draw(4, 2, 1, 2, seed=1)
+    gpu = _gpu_importance(qb, kb, w=1, S=2)
+    assert np.allclose(gpu, 2.0, rtol=1e-6, atol=0)
+
+
+def test_strided_keys_and_padding_rows_are_ignored():
+    # K lives in a [Hkv, S + 64, D] buffer; rows >= S hold huge values that must not matter
+    qb, kb = _draw(8, 4, 16, 700, seed=9, pad_rows=64)
+    kb[:, 700:, :] = wk.f32_to_bf16_bits(np.full((4, 64, 128), 1e4, np.float32))
+    gpu = _gpu_importance(qb, kb, w=16, S=700)
+    ref = _oracle(qb, kb[:, :700], w=16, S=700, scale=F32_ALPHA)
+    check_importance(gpu, ref, 2, "strided")
+
+
+def test_layers_with_per_layer_scales():
+    L, H, w, S = 3, 8, 128, 1500
+    qb, kb = _draw(H, H, w, S, seed=11, L=L)
+    scales = (np.random.default_rng(3).uniform(0.5, 3.0, L) / math.sqrt(128)).astype(np.float32)
+    gpu = _gpu_importance(qb, kb, w=w, S=S, L=L, layer_scales=torch.from_numpy(scales).to(dev()))
+    for l in range(L):
+        ref = _oracle(qb[l], kb[l], w=w, S=S, scale=float(scales[l]))
+        check_importance(gpu[l], ref, 1, f"layer {l}")
+
+
+@pytest.mark.parametrize("tau", [1.0, 1.0e4, math.inf, 0.25])
+def test_keyformer_noise(tau):
+    H, w, S, seed = 4, 64, 1500, 1234
+    qb, kb = _draw(H, H, w, S, seed=21)
+    gpu = _gpu_importance(qb, kb, w=w, S=S, gumbel=True, tau=tau, seed=seed)
+    ref = _oracle(qb, kb, w=w, S=S, scale=F32_ALPHA, gumbel=True, tau=tau, seed=seed)
+    check_importance(gpu, ref, 1, f"tau={tau}")
+
+
+def test_noise_seed_high_word_and_gqa():
+    H, Hkv, w, S, seed = 8, 2, 40, 777, (0xDEADBEEF << 32) | 12345
+    qb, kb = _draw(H, Hkv, w, S, seed=22)
+    gpu = _gpu_importance(qb, kb, w=w, S=S, gumbel=True, tau=1.0, seed=seed)
+    ref = _oracle(qb, kb, w=w, S=S, scale=F32_ALPHA, gumbel=True, tau=1.0, seed=seed)
+    check_importance(gpu, ref, 4, "gqa noise")
+
+
+def test_deterministic_bytes():
+    qb, kb = _draw(32, 8, 128, 5000, seed=31, outliers=4)
+    a = _gpu_importance(qb, kb, w=128, S=5000)
+    b = _gpu_importance(qb, kb, w=128, S=5000)
+    assert a.tobytes() == b.tobytes()

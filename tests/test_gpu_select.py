@@ -1,0 +1,191 @@
+"""kvc_select_topk, kvc_compact, kvc_lmba_budget and kvc_channel_prune on the
+GPU against the oracle, each in isolation on identical inputs (so every
+integer result must be bit-exact), including the degenerate cases."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_compression_bf16_amd import workload as wk
+
+from _parity import bits_of, check_channels, dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _kvc():
+    from kv_cache_compression_bf16_amd import kvc
+    return kvc
+
+
+# ---------------------------------------------------------------- select
+def _gpu_select(imp32, *, S, w, recent, budget):
+    kvc = _kvc()
+    t = torch.from_numpy(np.ascontiguousarray(imp32)).to(dev())
+    idx = torch.full((imp32.shape[0], budget), -7, dtype=torch.int32, device=dev())
+    kvc.kvc_select_topk(t, idx, S=S, w=w, recent=recent, budget=budget)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+def _ref_select(imp32, **kw):
+    return oracle.select.select_heads(imp32.astype(np.float64), **kw)
+
+
+@pytest.mark.parametrize("Hkv,S,w,recent,budget,kind", [
+    (8, 2048, 32, 32, 256, "exp"),
+    (8, 5000, 128, 64, 700, "exp"),
+    (3, 1025 + 16, 16, 16, 300, "ties3"),       # n = 1025: one element past a 1024 chunk
+    (4, 4000, 100, 300, 900, "exp"),            # recent > w: recent tokens leave the candidates
+    (4, 4000, 300, 100, 900, "exp"),            # recent < w: window-only tokens are dropped
+    (2, 3000, 10, 10, 10, "exp"),               # k_top = 0
+    (2, 3000, 10, 10, 3000, "exp"),             # k_top = |C|: keep everything
+    (2, 3000, 10, 10, 2999, "exp"),             # all but one
+    (2, 3000, 10, 0, 500, "equal"),             # all scores equal -> lowest positions
+    (2, 3000, 10, 5, 700, "zeros_denorm"),      # zeros and denormals
+    (8, 131072, 64, 64, 26214, "exp"),          # the 131072-token long-context shape
+])
+def test_select_bit_exact(Hkv, S, w, recent, budget, kind):
+    rng = np.random.default_rng(S + budget)
+    n = S - w
+    if kind == "exp":
+        imp = rng.exponential(size=(Hkv, n)).astype(np.float32)
+    elif kind == "ties3":
+        imp = (rng.integers(0, 3, size=(Hkv, n)) / 7.0).astype(np.float32)
+    elif kind == "equal":
+        imp = np.full((Hkv, n), 1.0 / n, dtype=np.float32)
+    else:
+        imp = rng.choice(np.array([0.0, 1e-42, 3e-40, 1e-38, 0.5], dtype=np.float32), size=(Hkv, n))
+    gpu = _gpu_select(imp, S=S, w=w, recent=recent, budget=budget)
+    ref = _ref_select(imp, S=S, w=w, recent=recent, budget=budget)
+    assert np.array_equal(gpu, ref)
+
+
+def test_select_reads_only_candidates_with_head_stride():
+    kvc = _kvc()
+    Hkv, S, w, recent, budget = 3, 2000, 50, 100, 400
+    n = S - w
+    rng = np.random.default_rng(4)
+    big = rng.exponential(size=(Hkv, n + 37)).astype(np.float32)
+    big[:, S - recent:] = 1e9          # beyond the candidates (r > w): must be ignored
+    t = torch.from_numpy(big).to(dev())[:, :n]
+    idx = torch.empty((Hkv, budget), dtype=torch.int32, device=dev())
+    kvc.kvc_select_topk(t, idx, S=S, w=w, recent=recent, budget=budget)
+    ref = _ref_select(big[:, :n], S=S, w=w, recent=recent, budget=budget)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------- compact
+def test_compact_bit_exact_and_bad_index_fill():
+    kvc = _kvc()
+    rng = np.random.default_rng(0)
+    Hkv, S, D, B = 4, 3000, 128, 333
+    k = rng.integers(0, 65536, size=(Hkv, S + 10, D), dtype=np.uint16)
+    v = rng.integers(0, 65536, size=(Hkv, S, D), dtype=np.uint16)
+    idx = np.stack([np.sort(rng.choice(S, B, replace=False)) for _ in range(Hkv)]).astype(np.int32)
+    idx[2, 5] = S + 3                  # out of range -> NaN row, no read
+    kd, vd = to_dev(k), to_dev(v)
+    idd = torch.from_numpy(idx).to(dev())
+    ko = torch.empty((Hkv, B, D), dtype=torch.bfloat16, device=dev())
+    vo = torch.empty((Hkv, B, D), dtype=torch.bfloat16, device=dev())
+    kvc.kvc_compact(kd, vd, idd, ko, vo, S=S)
+    kob, vob = bits_of(ko), bits_of(vo)
+    good = idx.copy(); good[2, 5] = 0
+    ref_k = oracle.compact.compact(k, good)
+    ref_v = oracle.compact.compact(v, good)
+    ref_k[2, 5] = 0xFFFF
+    ref_v[2, 5] = 0xFFFF
+    assert np.array_equal(kob, ref_k) and np.array_equal(vob, ref_v)
+    ko2 = torch.empty_like(ko)
+    kvc.kvc_compact(kd, None, idd, ko2, None, S=S)
+    assert np.array_equal(bits_of(ko2), ref_k)
+
+
+# ---------------------------------------------------------------- lmba budgets
+def _rows(L, Hkv, n, seed):
+    rng = np.random.default_rng(seed)
+    conc = rng.uniform(0.2, 6.0, size=(L, 1, 1))
+    x = rng.standard_normal((L, Hkv, n)) * conc
+    e = np.exp(x - x.max(axis=-1, keepdims=True))
+    return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
+def _gpu_budget(imp, **kw):
+    kvc = _kvc()
+    L, Hkv, n = imp.shape
+    t = torch.from_numpy(imp).to(dev())
+    b = torch.empty(L, dtype=torch.int32, device=dev())
+    m = torch.empty((L, Hkv), dtype=torch.int32, device=dev())
+    kvc.kvc_lmba_budget(t, b, mba=m, **kw)
+    torch.cuda.synchronize()
+    return m.cpu().numpy(), b.cpu().numpy()
+
+
+@pytest.mark.parametrize("L,Hkv,n,total,floor,cap,seed", [
+    (32, 8, 16256, 32 * 1024, 128, 16384, 0),
+    (5, 3, 1000, 2000, 50, 1000, 1),
+    (1, 2, 77, 40, 10, 77, 2),
+    (7, 4, 4096, 7 * 3000, 100, 3500, 3),     # forces capacity clamping
+])
+def test_budgets_bit_exact(L, Hkv, n, total, floor, cap, seed):
+    imp = _rows(L, Hkv, n, seed)
+    mba, bud = _gpu_budget(imp, total_budget=total, floor_per_layer=floor, capacity=cap)
+    ref_mba, ref_b = oracle.budget.zigzag_budgets(imp.astype(np.float64), total_budget=total, floor=floor,
+                                                  capacity=cap)
+    assert np.array_equal(mba, np.array(ref_mba))
+    assert bud.tolist() == ref_b
+    assert bud.sum() == total and bud.min() >= floor and bud.max() <= cap
+
+
+def test_budget_degenerate_rows():
+    n = 1000
+    imp = np.zeros((4, 2, n), dtype=np.float32)
+    imp[0] = 1.0 / n                     # uniform: ceil(0.9 n) = 900
+    imp[1, :, 17] = 1.0                  # one-hot: 1
+    imp[2, 0, :] = 0.0                   # all zero: 0
+    imp[2, 1, :10] = 0.1                 # ten equal values: 9
+    imp[3] = np.float32(1e-40)           # denormals only
+    mba, bud = _gpu_budget(imp, total_budget=1000, floor_per_layer=100, capacity=n)
+    ref_mba, ref_b = oracle.budget.zigzag_budgets(imp.astype(np.float64), total_budget=1000, floor=100,
+                                                  capacity=n)
+    assert mba.tolist() == ref_mba
+    assert bud.tolist() == ref_b
+
+
+def test_budget_equal_lmba_is_uniform():
+    imp = np.tile(_rows(1, 4, 2048, 9), (6, 1, 1))
+    _, bud = _gpu_budget(imp, total_budget=6 * 500, floor_per_layer=64, capacity=2048)
+    assert bud.tolist() == [500] * 6
+
+
+# ---------------------------------------------------------------- ThinK
+@pytest.mark.parametrize("Hkv,B,recent,lam,p", [
+    (8, 2000, 64, 0.4, 2),
+    (4, 1500, 32, 0.5, 1),
+    (2, 513, 1, 0.3, 2),
+    (3, 100, 100, 0.4, 2),      # no prunable rows
+    (2, 700, 0, 0.0, 2),        # lambda 0 keeps every channel
+])
+def test_channel_prune_bit_exact(Hkv, B, recent, lam, p):
+    kvc = _kvc()
+    rng = np.random.default_rng(B)
+    x = rng.standard_normal((Hkv, B, 128), dtype=np.float32)
+    x[:, :, [5, 66, 99, 127]] *= 8
+    kc = wk.f32_to_bf16_bits(x)
+    T = oracle.sizes.think_channels(128, lam)
+    rows = B - recent
+    ch = torch.empty((Hkv, T), dtype=torch.int32, device=dev())
+    mask = torch.empty((Hkv, 128), dtype=torch.uint8, device=dev())
+    kp = torch.empty((Hkv, rows, T), dtype=torch.bfloat16, device=dev())
+    kvc.kvc_channel_prune(to_dev(kc), ch, kp, recent=recent, lam=lam, p=p, mask=mask)
+    torch.cuda.synchronize()
+    ref_ch, ref_mask, _, norms = oracle.think.think_prune(oracle.score.bf16_bits_to_f64(kc), recent=recent,
+                                                         lam=lam, p=p)
+    gch = ch.cpu().numpy()
+    for g in range(Hkv):
+        check_channels(gch[g], norms[g], ref_ch[g], T)
+        assert np.array_equal(mask.cpu().numpy()[g], np.isin(np.arange(128), gch[g]).astype(np.uint8))
+    kpb = bits_of(kp)
+    for g in range(Hkv):
+        assert np.array_equal(kpb[g], kc[g, :rows][:, gch[g]])
