@@ -1,0 +1,202 @@
+"""Benchmark: prompt KV tokens compressed per second on one MI355X.
+
+One step = one whole compression pass (score -> [ZigZag budgets] -> select ->
+compact -> [ThinK]) over one synthetic prompt of the chosen workload, inputs
+already resident in HBM.  Default workload: the Llama-3-8B-shaped GQA layer
+(32 query / 8 KV heads, D 128, 32768-token prompt, window 128, budget 2048 per
+KV head incl. 64 recent, 4 outlier key channels x8).
+
+Prints ONE JSON line.  ``value`` = prompt tokens (layers x S) per second.
+The input set rotates over enough copies to exceed the 256 MB Infinity Cache,
+so every step reads its keys from HBM.  Per-kernel durations come from HIP
+events that libkvc records around each launch on the launch stream
+(kvc_timing_enable), in a second timed pass of the same steps.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prompt KV tokens compressed/sec (score+top-k+gather); % of HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+MALL_BYTES = 256 * 2 ** 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa32x8_s32768")
+    ap.add_argument("--tau", type=float, default=1.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
+    return ap.parse_args()
+
+
+def algorithmic(wl):
+    """Algorithmic bytes and flops of one step, and per-kernel figures."""
+    L, H, Hkv, S, w, D, G = wl.L, wl.H, wl.Hkv, wl.S, wl.w, wl.D, wl.G
+    n = S - w
+    R = G * w
+    q_bytes = L * H * w * D * 2
+    k_prefix = L * Hkv * n * D * 2
+    imp = L * Hkv * n * 4
+    B_total = wl.total_budget * Hkv if wl.total_budget else L * Hkv * wl.budget
+    rows = B_total * D * 2
+    flops_pass = 2.0 * L * Hkv * R * n * D
+    step_bytes = q_bytes + k_prefix + 2 * imp + B_total * 4 + 2 * rows * 2
+    if wl.think_lambda >= 0:
+        T = int(math.floor((1 - wl.think_lambda) * D))
+        kr = Hkv * (wl.budget - wl.recent)
+        step_bytes += kr * D * 2 + kr * T * 2
+    per_kernel = {
+        "score_pass1": ("mfma", flops_pass, q_bytes + k_prefix),
+        "score_pass2": ("mfma", flops_pass, q_bytes + k_prefix + imp),
+        "score_pass1_gumbel": ("mfma", flops_pass, q_bytes + k_prefix),
+        "score_pass2_gumbel": ("mfma", flops_pass, q_bytes + k_prefix + imp),
+        "select_topk": ("hbm", 0.0, imp + B_total * 4),
+        "compact": ("hbm", 0.0, 2 * rows * 2 + B_total * 4),
+    }
+    return step_bytes, flops_pass, per_kernel
+
+
+def cpu_baseline(wl, data, target_s, tau):
+    """The oracle, as it stands, on a bounded sample of the same workload (whole KV heads)."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    q, k, v = data
+    qf = oracle.score.bf16_bits_to_f64(q if wl.L == 1 else q[0])
+    kf = oracle.score.bf16_bits_to_f64(k if wl.L == 1 else k[0])
+    kraw = k if wl.L == 1 else k[0]
+    vraw = v if wl.L == 1 else v[0]
+    scale = float(np.float32(1.0 / math.sqrt(wl.D)))
+    heads, t0 = 0, time.perf_counter()
+    while heads < wl.Hkv:
+        g = heads
+        imp = oracle.score.importance(qf, kf, S=wl.S, w=wl.w, scale=scale, gumbel=wl.gumbel, tau=tau,
+                                      seed=wl.noise_seed, kv_heads=[g])
+        B = wl.budget if wl.budget else wl.total_budget // wl.L
+        idx = oracle.select.select(imp[g], S=wl.S, w=wl.w, recent=wl.recent, budget=B)
+        oracle.compact.compact(kraw[g:g + 1], idx[None])
+        oracle.compact.compact(vraw[g:g + 1], idx[None])
+        heads += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
+    tokens = wl.S * heads / wl.Hkv        # one layer's prompt, heads/Hkv of its work
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {wl.Hkv} KV heads of layer 0 (score+select+compact, fp64 numpy), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kv_cache_compression_bf16_amd import kvc, pipeline
+    from kv_cache_compression_bf16_amd import workload as wk
+
+    dev = torch.device("cuda:0")
+    wl = wk.WORKLOADS[args.workload]
+    print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    if wl.L == 1:
+        host = wk.gen_layer(wl)
+    else:
+        qs, ks, vs = zip(*(wk.gen_layer(wl, l) for l in range(wl.L)))
+        host = (np.stack(qs), np.stack(ks), np.stack(vs))
+    set_bytes = sum(x.nbytes for x in host)
+    copies = max(1, min(8, math.ceil(2 * MALL_BYTES / set_bytes)))
+    base = [pipeline.bf16_to_device(x, dev) for x in host]
+    sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+    ls = torch.from_numpy(wk.layer_scales(wl)).to(dev) if wl.scale_range else None
+    plan = pipeline.CompressionPlan(wl, dev, tau=args.tau)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        q, k, v = sets[i % copies]
+        plan.run(q, k, v, layer_scales=ls, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps between two events on the launch stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+
+    # ---- per-kernel durations: same steps again with libkvc's per-launch events
+    kvc.kvc_timing_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kt = kvc.kvc_timing_read()
+    kvc.kvc_timing_enable(False)
+
+    tokens = wl.L * wl.S
+    value = tokens / (ms_step / 1e3)
+    step_bytes, flops_pass, per_kernel = algorithmic(wl)
+    kernels = {name: {"launches": c, "avg_us": 1e3 * ms / c} for name, (c, ms) in kt.items()}
+    dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
+    avg_s = kernels[dom]["avg_us"] / 1e6
+    bound, flops, nbytes = per_kernel.get(dom, ("hbm", 0.0, 0))
+    if bound == "mfma":
+        achieved = flops / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+    else:
+        achieved = nbytes / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    roof["kernel"] = dom
+    for name, kk in kernels.items():
+        b, f, nb = per_kernel.get(name, ("", 0.0, 0))
+        kk["alg_TFLOPs"] = round(f / (kk["avg_us"] / 1e6) / 1e12, 2) if f else None
+        kk["alg_GBs"] = round(nb / (kk["avg_us"] / 1e6) / 1e9, 1) if nb else None
+        kk["avg_us"] = round(kk["avg_us"], 2)
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, host, args.cpu_seconds, args.tau)
+
+    config = {"workload": wl.name, "layers": wl.L, "q_heads": wl.H, "kv_heads": wl.Hkv, "seq_len": wl.S,
+              "head_dim": wl.D, "window": wl.w, "recent": wl.recent,
+              "budget_per_kv_head": wl.budget or None, "total_budget": wl.total_budget or None,
+              "gumbel_tau": args.tau if wl.gumbel else None, "input_copies_rotated": copies}
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, workload recipe)",
+        "config": config,
+        "hbm_frac_step": step_bytes / (ms_step / 1e3) / (HBM_PEAK_GBS * 1e9),
+        "alg_bytes_step": step_bytes, "alg_flops_score_pass": flops_pass,
+        "roofline": roof, "kernels": kernels, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
