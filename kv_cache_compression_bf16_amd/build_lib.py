@@ -26,6 +26,7 @@ COMMON_FLAGS = [
     "-fPIC",
     "-ffp-contract=off",          # explicit fmaf only: both score passes round identically
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",  # MFMA results stay in VGPRs: no AGPR copies before the exp epilogue
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]

@@ -100,6 +100,9 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
   const int hb = lane >> 5, col = lane & 31;
   const int key0 = blk * kKeysPerBlock + wave * kKeysPerWave;
   const bool tail = blk * kKeysPerBlock + kKeysPerBlock > p.n;
+  // w % 32 == 0: a 32-row query block never straddles two query heads and is
+  // never partial, so its head / window offset are block-uniform scalars.
+  const bool w32 = (p.w & 31) == 0;
   const float alpha = p.layer_scales ? p.layer_scales[layer] : p.scale;
   const float c = alpha * kLog2e;
   const int64_t head_row0 = ((int64_t)layer * p.Hkv + g) * p.R;
@@ -111,24 +114,31 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       int j = key0 + t * 32 + col;
-      j = j < p.n ? j : p.n - 1;   // clamp: rows past the prefix are masked below
+      j = j < p.n ? j : p.n - 1;   // clamp: keys past the prefix are masked in pass 1
       const bf16x8* row = reinterpret_cast<const bf16x8*>(kb + (int64_t)j * kD);
 #pragma unroll
       for (int s = 0; s < 8; ++s) kf[t][s] = row[2 * s + hb];
     }
   }
 
-  // ---- Q block staging: 512 16-byte chunks per 32-row block, 2 per thread.
-  const uint16_t* qb_base = p.q + layer * p.q_ls;
+  // ---- Q block staging: 512 16-byte chunks per 32-row block, 2 per thread
+  // (rows tid/16 and tid/16 + 16, chunk tid%16), coalesced 256-byte rows.
+  const uint16_t* qg = p.q + layer * p.q_ls + (int64_t)g * p.G * p.q_hs;
   auto load_q = [&](int qb, u32x4 (&regs)[2]) {
+    const int r0 = qb * kQRows;
+    if (w32) {
+      const int hh = r0 / p.w, i0 = r0 - hh * p.w;
+      const uint16_t* src = qg + hh * p.q_hs + (int64_t)(i0 + (tid >> 4)) * kD + (tid & 15) * 8;
+      regs[0] = *reinterpret_cast<const u32x4*>(src);
+      regs[1] = *reinterpret_cast<const u32x4*>(src + 16 * kD);
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int idx = tid + u * kThreads, row = idx >> 4, ch = idx & 15;
-      const int r = qb * kQRows + row;
+      const int r = r0 + (tid >> 4) + 16 * u;
       if (r < p.R) {
         const int hh = r / p.w, i = r - hh * p.w;
-        const int h = g * p.G + hh;
-        regs[u] = *reinterpret_cast<const u32x4*>(qb_base + h * p.q_hs + (int64_t)i * kD + ch * 8);
+        regs[u] = *reinterpret_cast<const u32x4*>(qg + hh * p.q_hs + (int64_t)i * kD + (tid & 15) * 8);
       } else {
         regs[u] = u32x4{0u, 0u, 0u, 0u};
       }
@@ -137,13 +147,13 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
   auto store_q = [&](int buf, const u32x4 (&regs)[2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int idx = tid + u * kThreads, row = idx >> 4, ch = idx & 15;
+      const int row = (tid >> 4) + 16 * u, ch = tid & 15;
       qs[buf][row * kChunks + (ch ^ (row & 15))] = regs[u];
     }
   };
   auto load_rc = [&](int qb) -> float {
     const int r = qb * kQRows + col;
-    return r < p.R ? p.rowc[head_row0 + r] : INFINITY;
+    return (w32 || r < p.R) ? p.rowc[head_row0 + r] : INFINITY;
   };
   // Pass 1: wave 0 folds the 4 waves' statistics of block qb into one partial.
   auto store_partial = [&](int qb) {
@@ -152,23 +162,43 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
       float m = -INFINITY;
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) m = fmaxf(m, red[b][v][col].x);
+      const float ms = (m == -INFINITY) ? 0.f : m;
       float l = 0.f;
-      if (m != -INFINITY) {
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-          const float2 a = red[b][v][col];
-          if (a.x != -INFINITY) l += a.y * fast_exp2(a.x - m);
-        }
+      for (int v = 0; v < kWaves; ++v) {
+        const float2 a = red[b][v][col];
+        l += a.y * fast_exp2(a.x - ms);
       }
       const int r = qb * kQRows + col;
-      if (r < p.R) p.part[(head_row0 + r) * p.nblk + blk] = float2{m, l};
+      if (w32 || r < p.R) p.part[(head_row0 + r) * p.nblk + blk] = float2{m, l};
     }
   };
-
-  // Logits of this lane for query block qb, in log2 units (Keyformer path).
+  // B operands from LDS, 8 k-steps x kTiles MFMAs: acc[t][r] = <K[key], Q[row]> with
+  // key = key0 + 32t + 8(r/4) + 4hb + (r%4), row = 32qb + col.
+  auto mfma_block = [&](int buf, f32x16 (&acc)[kTiles]) {
+    const bf16x8* qsb = reinterpret_cast<const bf16x8*>(qs[buf]);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) acc[t] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 qf = qsb[col * kChunks + ((2 * s + hb) ^ (col & 15))];
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], qf, acc[t], 0, 0, 0);
+    }
+  };
+  // Keyformer path: t = (alpha x + zeta) * log2(e)/tau, in place.
   auto noisy = [&](f32x16 (&acc)[kTiles], int qb) {
     const int r = qb * kQRows + col;
-    const int hh = r / p.w, i = r - hh * p.w;
+    int hh, i;
+    if (w32) {
+      const int r0 = qb * kQRows;
+      hh = r0 / p.w;
+      i = r0 - hh * p.w + col;
+    } else {
+      hh = r / p.w;
+      i = r - hh * p.w;
+    }
     const uint32_t h = (uint32_t)(g * p.G + hh);
     const uint32_t pos = (uint32_t)(p.S - p.w + i);
 #pragma unroll
@@ -185,93 +215,83 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
     }
   };
 
-  u32x4 qreg[2];
-  load_q(0, qreg);
-  store_q(0, qreg);
-  float rc_next = kPass2 ? load_rc(0) : 0.f;
-  __syncthreads();
-
   f32x16 colacc[kTiles];
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) colacc[t] = f32x16{};
 
-  for (int qb = 0; qb < p.nqb; ++qb) {
-    const int buf = qb & 1;
-    const bool more = qb + 1 < p.nqb;
-    if (!kPass2 && qb > 0) store_partial(qb - 1);
-    if (more) load_q(qb + 1, qreg);
-    const float rc = rc_next;
-    if (kPass2 && more) rc_next = load_rc(qb + 1);
-
-    f32x16 acc[kTiles];
+  // VALU half of one query block (overlaps the next block's MFMAs).
+  auto epilogue = [&](int qb, f32x16 (&acc)[kTiles], float rc) {
+    if (kGumbel) noisy(acc, qb);
+    // logit -> log2 units is fmaf(v, cc, -ref); the Keyformer path is already there
+    const float cc = kGumbel ? 1.0f : c;
+    if (!kPass2) {
+      const bool clean = !tail && (w32 || qb * kQRows + kQRows <= p.R);
+      if (!clean) {
+        const bool row_ok = qb * kQRows + col < p.R;
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) acc[t] = f32x16{};
-    const bf16x8* qsb = reinterpret_cast<const bf16x8*>(qs[buf]);
+        for (int t = 0; t < kTiles; ++t)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 qf = qsb[col * kChunks + ((2 * s + hb) ^ (col & 15))];
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + t * 32 + 8 * (r >> 2) + 4 * hb + (r & 3);
+            if (key >= p.n || !row_ok) acc[t][r] = -INFINITY;
+          }
+      }
+      float mx = acc[0][0];
 #pragma unroll
       for (int t = 0; t < kTiles; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], qf, acc[t], 0, 0, 0);
-    }
-    // acc[t][r] = <K[key], Q[row]>, key = key0 + 32t + 8(r/4) + 4hb + (r%4), row = 32qb + col
-    if (kGumbel) noisy(acc, qb);
-
-    if (!kPass2) {
-      // masking: keys past the prefix, rows past the group
-      const bool row_ok = qb * kQRows + col < p.R;
-      float mx = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t) {
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[t][r]);
+      const float mt = mx * cc;
+      const float mts = (mx == -INFINITY) ? 0.f : mt;
+      float l = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + t * 32 + 8 * (r >> 2) + 4 * hb + (r & 3);
-          float v = acc[t][r];
-          if ((tail && key >= p.n) || !row_ok) v = -INFINITY;
-          acc[t][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      }
-      float mt, l = 0.f;
-      if (kGumbel) {
-        mt = mx;
-        if (mx != -INFINITY) {
+      for (int t = 0; t < kTiles; ++t)
 #pragma unroll
-          for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) l += fast_exp2(acc[t][r] - mt);
-        }
-      } else {
-        mt = mx * c;
-        if (mx != -INFINITY) {
-#pragma unroll
-          for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) l += fast_exp2(fmaf(acc[t][r], c, -mt));
-        }
-      }
-      // fold with the other half-wave (same query row, other 8 keys of each group)
+        for (int r = 0; r < 16; ++r) l += fast_exp2(fmaf(acc[t][r], cc, -mts));
+      // fold with the other half-wave (same query row, the other keys of each group)
       const float mo = __shfl_xor(mt, 32), lo = __shfl_xor(l, 32);
       const float m2 = fmaxf(mt, mo);
-      float l2 = 0.f;
-      if (m2 != -INFINITY) {
-        if (mt != -INFINITY) l2 += l * fast_exp2(mt - m2);
-        if (mo != -INFINITY) l2 += lo * fast_exp2(mo - m2);
-      }
-      if (hb == 0) red[buf][wave][col] = float2{m2, l2};
+      const float m2s = (m2 == -INFINITY) ? 0.f : m2;
+      const float l2 = l * fast_exp2(mt - m2s) + lo * fast_exp2(mo - m2s);
+      if (hb == 0) red[qb & 1][wave][col] = float2{m2, l2};
     } else {
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t) {
+      for (int t = 0; t < kTiles; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float tt = kGumbel ? acc[t][r] - rc : fmaf(acc[t][r], c, -rc);
-          colacc[t][r] += fast_exp2(tt);
-        }
-      }
+        for (int r = 0; r < 16; ++r) colacc[t][r] += fast_exp2(fmaf(acc[t][r], cc, -rc));
     }
+  };
 
-    if (more) store_q(buf ^ 1, qreg);
+  u32x4 qreg[2];
+  load_q(0, qreg);
+  store_q(0, qreg);
+  if (p.nqb > 1) {
+    load_q(1, qreg);
+    store_q(1, qreg);
+  }
+  float rc_cur = kPass2 ? load_rc(0) : 0.f;
+  __syncthreads();
+
+  // Software pipeline: block qb+1's MFMAs are issued before block qb's VALU
+  // epilogue; block qb+2's Q rows are fetched from global memory meanwhile and
+  // land in the LDS buffer block qb has just vacated.
+  auto step = [&](int qb, f32x16 (&cur)[kTiles], f32x16 (&nxt)[kTiles]) {
+    const bool has_next = qb + 1 < p.nqb, has_next2 = qb + 2 < p.nqb;
+    if (!kPass2 && qb > 0) store_partial(qb - 1);
+    if (has_next2) load_q(qb + 2, qreg);
+    float rc_next = 0.f;
+    if (kPass2 && has_next) rc_next = load_rc(qb + 1);
+    if (has_next) mfma_block((qb + 1) & 1, nxt);
+    epilogue(qb, cur, rc_cur);
+    if (has_next2) store_q(qb & 1, qreg);
     __syncthreads();
+    rc_cur = rc_next;
+  };
+  f32x16 accA[kTiles], accB[kTiles];
+  mfma_block(0, accA);
+  for (int qb = 0; qb < p.nqb; qb += 2) {
+    step(qb, accA, accB);
+    if (qb + 1 < p.nqb) step(qb + 1, accB, accA);
   }
 
   if (!kPass2) {

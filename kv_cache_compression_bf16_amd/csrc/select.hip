@@ -11,16 +11,18 @@
 // and 10 bits, histograms in LDS with integer atomics, which are exact and
 // order-independent).  That yields the k-th key T and how many T-valued
 // candidates must be taken; a final ordered pass keeps every key > T and the
-// first such T-valued candidates by position, writing positions with two
-// block-wide prefix sums, so the output is ascending without a sort.
+// first such T-valued candidates by position.  Each thread owns a contiguous
+// run of 64 candidates held in registers, so the ascending output needs only
+// two workgroup prefix sums per 32768 candidates and no sort.
 #include "common.h"
 
 namespace kvc {
 namespace {
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kBins = 2048;
+constexpr int kBPT = kBins / kSelThreads;   // histogram bins per thread in the scan
 
 // fp32 -> uint32 with the same order (-0 folded onto +0).
 __device__ __forceinline__ uint32_t order_key(uint32_t b) {
@@ -51,6 +53,35 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, 
   return before + v - x;
 }
 
+// Scores are processed in rounds of kSelThreads * kVPT candidates; thread t owns
+// the contiguous segment [round_base + t*kVPT, round_base + (t+1)*kVPT), so the
+// ordered emission needs only two workgroup scans per round.  When the
+// candidates fit in one round they are loaded once and stay in registers for
+// every radix level.
+constexpr int kVPT = 64;
+constexpr int kRound = kSelThreads * kVPT;
+
+__device__ __forceinline__ void load_segment(const uint32_t* v, int c, int base, uint32_t (&key)[kVPT]) {
+  const int j0 = base + (int)threadIdx.x * kVPT;
+  if (j0 + kVPT <= c) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(v + j0);
+    const bool al = (reinterpret_cast<uintptr_t>(v + j0) & 15u) == 0;
+    if (al) {
+#pragma unroll
+      for (int i = 0; i < kVPT / 4; ++i) {
+        const u32x4 x = p[i];
+        key[4 * i + 0] = order_key(x.x);
+        key[4 * i + 1] = order_key(x.y);
+        key[4 * i + 2] = order_key(x.z);
+        key[4 * i + 3] = order_key(x.w);
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kVPT; ++i) key[i] = (j0 + i < c) ? order_key(v[j0 + i]) : 0u;
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* imp, int64_t hs, int c,
                                                                  int k_top, int S, int recent, int budget,
                                                                  int32_t* out) {
@@ -69,7 +100,12 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
     return;
   }
 
-  // ---- radix select of the k_top-th largest key
+  const int rounds = (c + kRound - 1) / kRound;
+  uint32_t key[kVPT];
+  if (rounds == 1) load_segment(v, c, 0, key);
+  const int seg0 = tid * kVPT;
+
+  // ---- radix select of the k_top-th largest key (11, 11, 10-bit digits)
   uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k_top;
   for (int pass = 0; pass < 3; ++pass) {
     const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
@@ -80,23 +116,33 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
       s_above = 0;
     }
     __syncthreads();
-    for (int j = tid; j < c; j += kSelThreads) {
-      const uint32_t key = order_key(v[j]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & width_mask], 1u);
+    for (int r = 0; r < rounds; ++r) {
+      if (rounds > 1) load_segment(v, c, r * kRound, key);
+      const int j0 = r * kRound + seg0;
+#pragma unroll
+      for (int i = 0; i < kVPT; ++i)
+        if (j0 + i < c && (key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> sh) & width_mask], 1u);
     }
     __syncthreads();
-    // suffix counts: thread tid owns bins 2*rt and 2*rt+1, rt = 1023 - tid
+    // suffix counts: thread tid owns bins [kBPT*rt, kBPT*rt + kBPT), rt = last - tid
     const int rt = kSelThreads - 1 - tid;
-    const uint32_t h0 = hist[2 * rt], h1 = hist[2 * rt + 1];
+    uint32_t hb[kBPT], a = 0;
+#pragma unroll
+    for (int i = 0; i < kBPT; ++i) {
+      hb[i] = hist[kBPT * rt + i];
+      a += hb[i];
+    }
     uint32_t tot;
-    const uint32_t incl = block_excl_scan(h0 + h1, wsum, &tot) + h0 + h1;   // = sum of bins >= 2rt
-    const uint32_t suf1 = incl - h0;                                        // = sum of bins >= 2rt+1
-    if (suf1 >= krem && suf1 - h1 < krem) {
-      s_digit = 2 * rt + 1;
-      s_above = suf1 - h1;
-    } else if (incl >= krem && incl - h0 < krem) {
-      s_digit = 2 * rt;
-      s_above = incl - h0;
+    const uint32_t incl = block_excl_scan(a, wsum, &tot) + a;   // = count of bins >= kBPT*rt
+    uint32_t below = 0;
+#pragma unroll
+    for (int i = 0; i < kBPT; ++i) {
+      const uint32_t suf = incl - below;                          // = count of bins >= kBPT*rt + i
+      if (suf >= krem && suf - hb[i] < krem) {
+        s_digit = kBPT * rt + i;
+        s_above = suf - hb[i];
+      }
+      below += hb[i];
     }
     __syncthreads();
     prefix |= s_digit << sh;
@@ -106,20 +152,35 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
   }
   const uint32_t T = prefix;   // k_top-th largest key; take krem of the keys equal to T
 
-  // ---- ordered emission
+  // ---- ordered emission: keys > T, then the first krem keys == T by position
   uint32_t eq_carry = 0, out_carry = 0;
-  for (int base = 0; base < c; base += kSelThreads) {
-    const int j = base + tid;
-    const uint32_t key = j < c ? order_key(v[j]) : 0u;
-    const bool in = j < c;
-    const bool gt = in && key > T;
-    const bool eq = in && key == T;
+  for (int r = 0; r < rounds; ++r) {
+    if (rounds > 1) load_segment(v, c, r * kRound, key);
+    const int j0 = r * kRound + seg0;
+    uint32_t n_eq = 0, n_gt = 0;
+#pragma unroll
+    for (int i = 0; i < kVPT; ++i) {
+      const bool in = j0 + i < c;
+      n_eq += (in && key[i] == T) ? 1u : 0u;
+      n_gt += (in && key[i] > T) ? 1u : 0u;
+    }
     uint32_t eq_tot;
-    const uint32_t eq_before = block_excl_scan(eq ? 1u : 0u, wsum, &eq_tot) + eq_carry;
-    const bool take = gt || (eq && eq_before < krem);
+    const uint32_t eq_before = block_excl_scan(n_eq, wsum, &eq_tot) + eq_carry;
+    // T-valued keys of this thread that still fit in the quota
+    const uint32_t eq_room = krem > eq_before ? krem - eq_before : 0u;
+    const uint32_t n_take = n_gt + (n_eq < eq_room ? n_eq : eq_room);
     uint32_t take_tot;
-    const uint32_t pos = block_excl_scan(take ? 1u : 0u, wsum, &take_tot) + out_carry;
-    if (take && pos < (uint32_t)k_top) o[pos] = j;
+    uint32_t pos = block_excl_scan(n_take, wsum, &take_tot) + out_carry;
+    uint32_t eq_seen = 0;
+#pragma unroll
+    for (int i = 0; i < kVPT; ++i) {
+      const bool in = j0 + i < c;
+      const bool eq = in && key[i] == T;
+      const bool take = (in && key[i] > T) || (eq && eq_seen < eq_room);
+      eq_seen += eq ? 1u : 0u;
+      if (take && pos < (uint32_t)k_top) o[pos] = j0 + i;
+      pos += take ? 1u : 0u;
+    }
     eq_carry += eq_tot;
     out_carry += take_tot;
   }
