@@ -38,7 +38,22 @@ def parse():
     ap.add_argument("--tau", type=float, default=1.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    """A plain copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counter readings."""
+    import torch
+
+    n = mib * 2 ** 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
 
 
 def algorithmic(wl):
@@ -105,6 +120,10 @@ def main():
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(see the sharding notes in DESIGN.md); rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import numpy as np
     import torch

@@ -12,8 +12,8 @@
 //    operand layout of v_mfma_f32_32x32x16_bf16, for the whole kernel: K is
 //    read from HBM exactly once per pass, straight into VGPRs.
 //  * The G*w query rows of the group stream through LDS in blocks of 32 rows
-//    (8 KB, double-buffered, 16-byte chunks XOR-swizzled by row so the MFMA
-//    B-operand reads are bank-conflict free).
+//    (8.5 KB, double-buffered, rows padded by 16 bytes so the MFMA B-operand
+//    reads are bank-conflict free and need no per-block address math).
 //  * The tile is computed as K x Q^T, so a lane owns ONE query row and 16 keys
 //    of each 32x32 tile: row statistics (pass 1) and the per-row softmax
 //    constant (pass 2) are per-lane scalars, and column sums over query rows
@@ -29,26 +29,36 @@
 //    fully used.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
+
+#ifndef KVC_SCORE_PIPELINE
+#define KVC_SCORE_PIPELINE 0
+#endif
 
 namespace kvc {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kChunks = kD / 8;                        // 16-byte chunks per row
 constexpr int kWaves = 4;
 constexpr int kTiles = 2;                              // 32-key tiles per wave
 constexpr int kKeysPerWave = 32 * kTiles;
 constexpr int kKeysPerBlock = kKeysPerWave * kWaves;   // 256
 constexpr int kQRows = 32;
 constexpr int kThreads = kWaves * kWave;
+// LDS row pitch of a staged query row: 256 bytes + 16 bytes of padding, so the
+// 16 lanes that read one 16-byte chunk of 16 different rows hit 16 distinct
+// bank groups, and the 8 chunk reads of a lane are one base + immediates.
+constexpr int kRowPitch = kD * 2 + 16;
+constexpr int kQBlockBytes = kQRows * kRowPitch;
 
 struct ScoreParams {
   const uint16_t* q;
   const uint16_t* k;
   int64_t q_hs, q_ls, k_hs, k_ls;
   float* imp;        // [L, Hkv, n]
-  float2* part;      // [L, Hkv, R, nblk] (max, sum) in log2 units
+  float2* part;      // [L, Hkv, nblk, R] (max, sum) in log2 units
   float* rowc;       // [L, Hkv, R]
   const float* layer_scales;
   float scale;
@@ -92,8 +102,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 template <bool kPass2, bool kGumbel>
 __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
-  __shared__ u32x4 qs[2][kQRows * kChunks];   // 2 x 8 KB
-  __shared__ float2 red[2][kWaves][32];
+  __shared__ __attribute__((aligned(16))) char qs[2][kQBlockBytes];   // 2 x 8.5 KB
+  __shared__ float2 red[2][kWaves][64];   // [.., 32 + col] is the unused half-wave copy
 
   const int blk = blockIdx.x, g = blockIdx.y, layer = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -124,13 +134,24 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
   // ---- Q block staging: 512 16-byte chunks per 32-row block, 2 per thread
   // (rows tid/16 and tid/16 + 16, chunk tid%16), coalesced 256-byte rows.
   const uint16_t* qg = p.q + layer * p.q_ls + (int64_t)g * p.G * p.q_hs;
+  const int q_toff = (tid >> 4) * kD + (tid & 15) * 8;           // element offset in a block
+  const int st_off = (tid >> 4) * kRowPitch + (tid & 15) * 16;    // LDS byte offset, row tid/16
+  const int rd_off = col * kRowPitch + hb * 16;                   // LDS byte offset of chunk hb
+  // Blocks are loaded strictly in order, so with w % 32 == 0 the (query head,
+  // window offset) of the next block to load is a running scalar pair: no
+  // integer division (which the compiler would expand on the VALU).
+  int ld_hh = 0, ld_i0 = 0;
   auto load_q = [&](int qb, u32x4 (&regs)[2]) {
     const int r0 = qb * kQRows;
     if (w32) {
-      const int hh = r0 / p.w, i0 = r0 - hh * p.w;
-      const uint16_t* src = qg + hh * p.q_hs + (int64_t)(i0 + (tid >> 4)) * kD + (tid & 15) * 8;
+      const uint16_t* src = qg + (ld_hh * p.q_hs + (int64_t)ld_i0 * kD) + q_toff;
       regs[0] = *reinterpret_cast<const u32x4*>(src);
       regs[1] = *reinterpret_cast<const u32x4*>(src + 16 * kD);
+      ld_i0 += kQRows;
+      if (ld_i0 == p.w) {
+        ld_i0 = 0;
+        ++ld_hh;
+      }
       return;
     }
 #pragma unroll
@@ -145,11 +166,8 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
     }
   };
   auto store_q = [&](int buf, const u32x4 (&regs)[2]) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int row = (tid >> 4) + 16 * u, ch = tid & 15;
-      qs[buf][row * kChunks + (ch ^ (row & 15))] = regs[u];
-    }
+    *reinterpret_cast<u32x4*>(qs[buf] + st_off) = regs[0];
+    *reinterpret_cast<u32x4*>(qs[buf] + st_off + 16 * kRowPitch) = regs[1];
   };
   auto load_rc = [&](int qb) -> float {
     const int r = qb * kQRows + col;
@@ -170,31 +188,36 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
         l += a.y * fast_exp2(a.x - ms);
       }
       const int r = qb * kQRows + col;
-      if (w32 || r < p.R) p.part[(head_row0 + r) * p.nblk + blk] = float2{m, l};
+      if (w32 || r < p.R) p.part[(head_row0 * p.nblk) + (int64_t)blk * p.R + r] = float2{m, l};
     }
   };
   // B operands from LDS, 8 k-steps x kTiles MFMAs: acc[t][r] = <K[key], Q[row]> with
   // key = key0 + 32t + 8(r/4) + 4hb + (r%4), row = 32qb + col.
   auto mfma_block = [&](int buf, f32x16 (&acc)[kTiles]) {
-    const bf16x8* qsb = reinterpret_cast<const bf16x8*>(qs[buf]);
+    const char* qsb = qs[buf] + rd_off;
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) acc[t] = f32x16{};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const bf16x8 qf = qsb[col * kChunks + ((2 * s + hb) ^ (col & 15))];
+      const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qsb + 32 * s);
 #pragma unroll
       for (int t = 0; t < kTiles; ++t)
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], qf, acc[t], 0, 0, 0);
     }
   };
   // Keyformer path: t = (alpha x + zeta) * log2(e)/tau, in place.
+  int ep_hh = 0, ep_i0 = 0;   // running (head, offset) of the block in the epilogue (w32 path)
   auto noisy = [&](f32x16 (&acc)[kTiles], int qb) {
     const int r = qb * kQRows + col;
     int hh, i;
     if (w32) {
-      const int r0 = qb * kQRows;
-      hh = r0 / p.w;
-      i = r0 - hh * p.w + col;
+      hh = ep_hh;
+      i = ep_i0 + col;
+      ep_i0 += kQRows;
+      if (ep_i0 == p.w) {
+        ep_i0 = 0;
+        ++ep_hh;
+      }
     } else {
       hh = r / p.w;
       i = r - hh * p.w;
@@ -220,13 +243,13 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
   for (int t = 0; t < kTiles; ++t) colacc[t] = f32x16{};
 
   // VALU half of one query block (overlaps the next block's MFMAs).
-  auto epilogue = [&](int qb, f32x16 (&acc)[kTiles], float rc) {
+  auto epilogue = [&](auto clean_c, int qb, f32x16 (&acc)[kTiles], float rc) {
+    constexpr bool kClean = decltype(clean_c)::value;
     if (kGumbel) noisy(acc, qb);
     // logit -> log2 units is fmaf(v, cc, -ref); the Keyformer path is already there
     const float cc = kGumbel ? 1.0f : c;
     if (!kPass2) {
-      const bool clean = !tail && (w32 || qb * kQRows + kQRows <= p.R);
-      if (!clean) {
+      if (!kClean) {
         const bool row_ok = qb * kQRows + col < p.R;
 #pragma unroll
         for (int t = 0; t < kTiles; ++t)
@@ -253,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
       const float m2 = fmaxf(mt, mo);
       const float m2s = (m2 == -INFINITY) ? 0.f : m2;
       const float l2 = l * fast_exp2(mt - m2s) + lo * fast_exp2(mo - m2s);
-      if (hb == 0) red[qb & 1][wave][col] = float2{m2, l2};
+      red[qb & 1][wave][lane] = float2{m2, l2};   // lanes col and 32+col hold the same pair
     } else {
 #pragma unroll
       for (int t = 0; t < kTiles; ++t)
@@ -263,41 +286,88 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
   };
 
   u32x4 qreg[2];
-  load_q(0, qreg);
-  store_q(0, qreg);
-  if (p.nqb > 1) {
-    load_q(1, qreg);
-    store_q(1, qreg);
-  }
-  float rc_cur = kPass2 ? load_rc(0) : 0.f;
-  __syncthreads();
-
-  // Software pipeline: block qb+1's MFMAs are issued before block qb's VALU
-  // epilogue; block qb+2's Q rows are fetched from global memory meanwhile and
-  // land in the LDS buffer block qb has just vacated.
-  auto step = [&](int qb, f32x16 (&cur)[kTiles], f32x16 (&nxt)[kTiles]) {
-    const bool has_next = qb + 1 < p.nqb, has_next2 = qb + 2 < p.nqb;
-    if (!kPass2 && qb > 0) store_partial(qb - 1);
-    if (has_next2) load_q(qb + 2, qreg);
-    float rc_next = 0.f;
-    if (kPass2 && has_next) rc_next = load_rc(qb + 1);
-    if (has_next) mfma_block((qb + 1) & 1, nxt);
-    epilogue(qb, cur, rc_cur);
-    if (has_next2) store_q(qb & 1, qreg);
+  float rc_cur = 0.f;
+  // The whole block loop, specialised for "clean" workgroups (no key past the
+  // prefix, query blocks never partial: no masking code at all) and the rest.
+  auto run = [&](auto clean_c) {
+    constexpr bool kClean = decltype(clean_c)::value;
+    load_q(0, qreg);
+    store_q(0, qreg);
+    if (p.nqb > 1) {
+      load_q(1, qreg);
+      store_q(1, qreg);
+    }
+    if (kPass2) rc_cur = load_rc(0);
     __syncthreads();
-    rc_cur = rc_next;
+#if KVC_SCORE_PIPELINE
+    // Software pipeline: block qb+1's MFMAs are issued in between block qb's
+    // exp/FMA epilogue (explicit instruction interleaving), so the matrix
+    // cores and the VALU work at the same time inside one wave; block qb+2's
+    // query rows are fetched meanwhile and land in the LDS buffer block qb
+    // vacated.  The steady-state loop is peeled: no conditionals in it.
+    auto step = [&](auto has_next_c, auto has_next2_c, int qb, f32x16 (&cur)[kTiles],
+                    f32x16 (&nxt)[kTiles]) {
+      constexpr bool kNext = decltype(has_next_c)::value, kNext2 = decltype(has_next2_c)::value;
+      if (kNext2) load_q(qb + 2, qreg);
+      float rc_next = 0.f;
+      if (kPass2 && kNext) rc_next = load_rc(qb + 1);
+      if (kNext) mfma_block((qb + 1) & 1, nxt);
+      epilogue(clean_c, qb, cur, rc_cur);
+      if constexpr (kClean && kNext) {
+        constexpr int kValuPerMfma = kPass2 ? (kGumbel ? 24 : 6) : (kGumbel ? 24 : 8);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the 8 LDS operand reads
+#pragma unroll
+        for (int i = 0; i < 8 * kTiles; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA ...
+          __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // ... then VALU work
+        }
+      }
+      if (kNext2) store_q(qb & 1, qreg);
+      __syncthreads();
+      if (!kPass2) store_partial(qb);
+      rc_cur = rc_next;
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    f32x16 accA[kTiles], accB[kTiles];
+    mfma_block(0, accA);
+    int qb = 0;
+    for (; qb + 3 < p.nqb; qb += 2) {
+      step(T_{}, T_{}, qb, accA, accB);
+      step(T_{}, T_{}, qb + 1, accB, accA);
+    }
+    const int left = p.nqb - qb;
+    if (left == 3) {
+      step(T_{}, T_{}, qb, accA, accB);
+      step(T_{}, F_{}, qb + 1, accB, accA);
+      step(F_{}, F_{}, qb + 2, accA, accB);
+    } else if (left == 2) {
+      step(T_{}, F_{}, qb, accA, accB);
+      step(F_{}, F_{}, qb + 1, accB, accA);
+    } else {
+      step(F_{}, F_{}, qb, accA, accB);
+    }
+#else
+    // Plain loop: MFMAs then epilogue per block; latency is hidden across waves.
+    for (int qb = 0; qb < p.nqb; ++qb) {
+      const bool has_next2 = qb + 2 < p.nqb;
+      if (has_next2) load_q(qb + 2, qreg);
+      f32x16 acc[kTiles];
+      mfma_block(qb & 1, acc);
+      epilogue(clean_c, qb, acc, rc_cur);
+      if (kPass2 && qb + 1 < p.nqb) rc_cur = load_rc(qb + 1);
+      __syncthreads();                          // every wave is done with buffer qb & 1
+      if (!kPass2) store_partial(qb);
+      if (has_next2) store_q(qb & 1, qreg);     // visible after the next iteration's barrier
+    }
+#endif
   };
-  f32x16 accA[kTiles], accB[kTiles];
-  mfma_block(0, accA);
-  for (int qb = 0; qb < p.nqb; qb += 2) {
-    step(qb, accA, accB);
-    if (qb + 1 < p.nqb) step(qb + 1, accB, accA);
-  }
+  if (!tail && w32)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
-  if (!kPass2) {
-    store_partial(p.nqb - 1);
-    return;
-  }
+  if (!kPass2) return;
 
   // ---- pass 2: sum each key column over the 32 query lanes of its half-wave.
   float* out = p.imp + ((int64_t)layer * p.Hkv + g) * p.n;
@@ -321,25 +391,41 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
   }
 }
 
-// Fold the per-workgroup partials of one query row (one wave per row, fixed
-// order): rowc = m + log2(sum_b l_b * 2^(m_b - m)).
-__global__ __launch_bounds__(256) void score_combine(ScoreParams p, int rows) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const float2* pp = p.part + (int64_t)row * p.nblk;
-  float m = -INFINITY;
-  for (int b = lane; b < p.nblk; b += kWave) m = fmaxf(m, pp[b].x);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  float l = 0.f;
-  for (int b = lane; b < p.nblk; b += kWave) {
-    const float2 a = pp[b];
-    if (a.x != -INFINITY) l += a.y * fast_exp2(a.x - m);
+// Fold the per-workgroup partials of each query row into
+// rowc = m + log2(sum_b l_b * 2^(m_b - m)).  A workgroup takes 32 consecutive
+// rows of one head; its 8 thread groups each fold every 8th key block online
+// (coalesced 256-byte reads), and the 8 group results are folded in a fixed
+// order, so the result is bit-reproducible.
+constexpr int kCombRows = 32, kCombGroups = 8;
+__global__ __launch_bounds__(256) void score_combine(ScoreParams p, int heads) {
+  __shared__ float2 sg[kCombGroups][kCombRows];
+  const int rr = threadIdx.x & (kCombRows - 1), q = threadIdx.x / kCombRows;
+  const int tiles = (p.R + kCombRows - 1) / kCombRows;
+  const int head = blockIdx.x / tiles, r = (blockIdx.x - head * tiles) * kCombRows + rr;
+  float m = -INFINITY, l = 0.f;
+  if (head < heads && r < p.R) {
+    const float2* pp = p.part + (int64_t)head * p.nblk * p.R + r;
+#pragma unroll 4
+    for (int b = q; b < p.nblk; b += kCombGroups) {
+      const float2 a = pp[(int64_t)b * p.R];
+      const float mn = fmaxf(m, a.x);
+      const float ms = (mn == -INFINITY) ? 0.f : mn;
+      l = l * fast_exp2(m - ms) + a.y * fast_exp2(a.x - ms);
+      m = mn;
+    }
   }
+  sg[q][rr] = float2{m, l};
+  __syncthreads();
+  if (q == 0 && head < heads && r < p.R) {
+    float mm = -INFINITY;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
-  if (lane == 0) p.rowc[row] = (l > 0.f) ? m + log2f(l) : INFINITY;
+    for (int i = 0; i < kCombGroups; ++i) mm = fmaxf(mm, sg[i][rr].x);
+    const float ms = (mm == -INFINITY) ? 0.f : mm;
+    float ll = 0.f;
+#pragma unroll
+    for (int i = 0; i < kCombGroups; ++i) ll += sg[i][rr].y * fast_exp2(sg[i][rr].x - ms);
+    p.rowc[(int64_t)head * p.R + r] = (ll > 0.f) ? mm + log2f(ll) : INFINITY;
+  }
 }
 
 struct Plan {
@@ -421,14 +507,15 @@ extern "C" kvc_status kvc_score(const kvc_score_args* a, const void* q_obs, cons
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(pl.nblk, a->Hkv, a->L), block(kThreads);
-  const int rows = a->L * a->Hkv * pl.R;
+  const int heads = a->L * a->Hkv;
+  const dim3 comb_grid(heads * ((pl.R + kCombRows - 1) / kCombRows));
   if (a->gumbel) {
     KVC_LAUNCH("score_pass1_gumbel", (score_pass<false, true>), grid, block, s, p);
-    KVC_LAUNCH("score_combine", score_combine, dim3((rows + 3) / 4), dim3(256), s, p, rows);
+    KVC_LAUNCH("score_combine", score_combine, comb_grid, dim3(256), s, p, heads);
     KVC_LAUNCH("score_pass2_gumbel", (score_pass<true, true>), grid, block, s, p);
   } else {
     KVC_LAUNCH("score_pass1", (score_pass<false, false>), grid, block, s, p);
-    KVC_LAUNCH("score_combine", score_combine, dim3((rows + 3) / 4), dim3(256), s, p, rows);
+    KVC_LAUNCH("score_combine", score_combine, comb_grid, dim3(256), s, p, heads);
     KVC_LAUNCH("score_pass2", (score_pass<true, false>), grid, block, s, p);
   }
   return KVC_OK;

@@ -6,14 +6,14 @@
 // (importance descending, position ascending) order are kept together with
 // every position of [S - recent, S); kept positions are written ascending.
 //
-// Design: one 1024-thread workgroup per head runs an exact MSB-first radix
+// Design: one 512-thread workgroup per head runs an exact MSB-first radix
 // select on order-preserving 32-bit keys of the fp32 scores (digits of 11, 11
-// and 10 bits, histograms in LDS with integer atomics, which are exact and
-// order-independent).  That yields the k-th key T and how many T-valued
-// candidates must be taken; a final ordered pass keeps every key > T and the
-// first such T-valued candidates by position.  Each thread owns a contiguous
-// run of 64 candidates held in registers, so the ascending output needs only
-// two workgroup prefix sums per 32768 candidates and no sort.
+// and 10 bits; LDS histograms with integer atomics, which are exact and
+// order-independent).  That yields the k_top-th key T and how many T-valued
+// candidates must be taken.  Each wave owns a contiguous range of candidates
+// loaded with coalesced 256-byte loads, 64 in flight per lane, and kept in
+// registers across all radix passes; the ordered output transposes them
+// through LDS so each thread owns 64 consecutive candidates (see below).
 #include "common.h"
 
 namespace kvc {
@@ -53,33 +53,28 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, 
   return before + v - x;
 }
 
-// Scores are processed in rounds of kSelThreads * kVPT candidates; thread t owns
-// the contiguous segment [round_base + t*kVPT, round_base + (t+1)*kVPT), so the
-// ordered emission needs only two workgroup scans per round.  When the
-// candidates fit in one round they are loaded once and stay in registers for
-// every radix level.
-constexpr int kVPT = 64;
-constexpr int kRound = kSelThreads * kVPT;
+// Candidates are handled in rounds of kRound = 512 * 64: in round r, wave w
+// owns the contiguous range [r*kRound + w*4096, +4096) and lane l holds
+// candidates base + 64*i + l (i < 64), so every load instruction reads 256
+// contiguous bytes and a lane keeps 64 loads in flight.  With one round (up to
+// 32768 candidates) the keys are loaded once and stay in registers for all
+// radix levels and both emission passes.
+constexpr int kVPL = 64;
+constexpr int kSpan = kVPL * kWave;                 // candidates per wave per round
+constexpr int kRound = kSelWaves * kSpan;
 
-__device__ __forceinline__ void load_segment(const uint32_t* v, int c, int base, uint32_t (&key)[kVPT]) {
-  const int j0 = base + (int)threadIdx.x * kVPT;
-  if (j0 + kVPT <= c) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(v + j0);
-    const bool al = (reinterpret_cast<uintptr_t>(v + j0) & 15u) == 0;
-    if (al) {
+__device__ __forceinline__ void load_round(const uint32_t* v, int c, int r, uint32_t (&key)[kVPL]) {
+  const int base = r * kRound + (int)(threadIdx.x >> 6) * kSpan + (int)(threadIdx.x & 63);
+  // Unconditional loads from a clamped address (then masked): a guarded load
+  // would be a branch, and the wait at each branch merge would serialize them.
+  uint32_t raw[kVPL];
 #pragma unroll
-      for (int i = 0; i < kVPT / 4; ++i) {
-        const u32x4 x = p[i];
-        key[4 * i + 0] = order_key(x.x);
-        key[4 * i + 1] = order_key(x.y);
-        key[4 * i + 2] = order_key(x.z);
-        key[4 * i + 3] = order_key(x.w);
-      }
-      return;
-    }
+  for (int i = 0; i < kVPL; ++i) {
+    const int j = base + 64 * i;
+    raw[i] = v[j < c ? j : c - 1];
   }
 #pragma unroll
-  for (int i = 0; i < kVPT; ++i) key[i] = (j0 + i < c) ? order_key(v[j0 + i]) : 0u;
+  for (int i = 0; i < kVPL; ++i) key[i] = (base + 64 * i < c) ? order_key(raw[i]) : 0u;
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* imp, int64_t hs, int c,
@@ -88,8 +83,9 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t wsum[kSelWaves];
   __shared__ uint32_t s_digit, s_above;
+  __shared__ uint32_t tr[kRound + kRound / 64];   // 130 KB transpose buffer of one round
 
-  const int g = blockIdx.x, tid = threadIdx.x;
+  const int g = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
   const uint32_t* v = reinterpret_cast<const uint32_t*>(imp + (int64_t)g * hs);
   int32_t* o = out + (int64_t)g * budget;
 
@@ -101,11 +97,11 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
   }
 
   const int rounds = (c + kRound - 1) / kRound;
-  uint32_t key[kVPT];
-  if (rounds == 1) load_segment(v, c, 0, key);
-  const int seg0 = tid * kVPT;
+  uint32_t key[kVPL];
+  if (rounds == 1) load_round(v, c, 0, key);
+  const int lbase = wave * kSpan + (tid & 63);   // candidate of key[0] in round 0
 
-  // ---- radix select of the k_top-th largest key (11, 11, 10-bit digits)
+  // ---- radix select of the k_top-th largest key
   uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k_top;
   for (int pass = 0; pass < 3; ++pass) {
     const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
@@ -117,11 +113,11 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
     }
     __syncthreads();
     for (int r = 0; r < rounds; ++r) {
-      if (rounds > 1) load_segment(v, c, r * kRound, key);
-      const int j0 = r * kRound + seg0;
+      if (rounds > 1) load_round(v, c, r, key);
+      const int j0 = r * kRound + lbase;
 #pragma unroll
-      for (int i = 0; i < kVPT; ++i)
-        if (j0 + i < c && (key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> sh) & width_mask], 1u);
+      for (int i = 0; i < kVPL; ++i)
+        if (j0 + 64 * i < c && (key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> sh) & width_mask], 1u);
     }
     __syncthreads();
     // suffix counts: thread tid owns bins [kBPT*rt, kBPT*rt + kBPT), rt = last - tid
@@ -152,33 +148,48 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
   }
   const uint32_t T = prefix;   // k_top-th largest key; take krem of the keys equal to T
 
-  // ---- ordered emission: keys > T, then the first krem keys == T by position
+  // ---- ordered emission, round by round.  The round's keys are transposed
+  // through LDS (word j at j + j/64: conflict-free both ways) so that thread t
+  // owns the 64 consecutive candidates [64t, 64t + 64); per-thread counts, two
+  // workgroup scans for the offsets, then each thread writes its kept positions
+  // in order: the output is ascending without a sort.
   uint32_t eq_carry = 0, out_carry = 0;
   for (int r = 0; r < rounds; ++r) {
-    if (rounds > 1) load_segment(v, c, r * kRound, key);
-    const int j0 = r * kRound + seg0;
-    uint32_t n_eq = 0, n_gt = 0;
-#pragma unroll
-    for (int i = 0; i < kVPT; ++i) {
-      const bool in = j0 + i < c;
-      n_eq += (in && key[i] == T) ? 1u : 0u;
-      n_gt += (in && key[i] > T) ? 1u : 0u;
+    if (rounds > 1) {
+      __syncthreads();   // the previous round's readers are done with `tr`
+      load_round(v, c, r, key);
     }
-    uint32_t eq_tot;
-    const uint32_t eq_before = block_excl_scan(n_eq, wsum, &eq_tot) + eq_carry;
-    // T-valued keys of this thread that still fit in the quota
-    const uint32_t eq_room = krem > eq_before ? krem - eq_before : 0u;
-    const uint32_t n_take = n_gt + (n_eq < eq_room ? n_eq : eq_room);
-    uint32_t take_tot;
-    uint32_t pos = block_excl_scan(n_take, wsum, &take_tot) + out_carry;
-    uint32_t eq_seen = 0;
+    const int j0 = r * kRound + lbase;
 #pragma unroll
-    for (int i = 0; i < kVPT; ++i) {
-      const bool in = j0 + i < c;
-      const bool eq = in && key[i] == T;
-      const bool take = (in && key[i] > T) || (eq && eq_seen < eq_room);
-      eq_seen += eq ? 1u : 0u;
-      if (take && pos < (uint32_t)k_top) o[pos] = j0 + i;
+    for (int i = 0; i < kVPL; ++i) {
+      const int jl = j0 - r * kRound + 64 * i;      // position within the round
+      tr[jl + (jl >> 6)] = key[i];
+    }
+    __syncthreads();
+    const int seg = tid * kVPL;                      // this thread's first position in the round
+    const int valid = min(kVPL, max(0, c - r * kRound - seg));
+    uint32_t mine[kVPL];
+    uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int e = 0; e < kVPL; ++e) {
+      mine[e] = tr[seg + e + tid];                   // = position seg + e, padded
+      n_gt += (e < valid && mine[e] > T) ? 1u : 0u;
+      n_eq += (e < valid && mine[e] == T) ? 1u : 0u;
+    }
+    uint32_t eq_tot, take_tot;
+    const uint32_t eq_b = block_excl_scan(n_eq, wsum, &eq_tot) + eq_carry;
+    const uint32_t room = krem > eq_b ? krem - eq_b : 0u;
+    const uint32_t n_take = n_gt + (n_eq < room ? n_eq : room);
+    uint32_t pos = block_excl_scan(n_take, wsum, &take_tot) + out_carry;
+    uint32_t eq_left = n_eq < room ? n_eq : room;    // T-valued candidates this thread keeps
+    const int jb = r * kRound + seg;
+#pragma unroll
+    for (int e = 0; e < kVPL; ++e) {
+      const bool in = e < valid;
+      const bool eq = in && mine[e] == T;
+      const bool take = (in && mine[e] > T) || (eq && eq_left > 0);
+      eq_left -= (eq && eq_left > 0) ? 1u : 0u;
+      if (take && pos < (uint32_t)k_top) o[pos] = jb + e;
       pos += take ? 1u : 0u;
     }
     eq_carry += eq_tot;
@@ -208,6 +219,7 @@ extern "C" kvc_status kvc_select_topk(const float* importance, int64_t imp_head_
   if (!indices || (!importance && budget > recent)) return KVC_E_ARG;
   if ((reinterpret_cast<uintptr_t>(importance) & 3) || (reinterpret_cast<uintptr_t>(indices) & 3))
     return KVC_E_ARG;
+  if (Hkv > 65535) return KVC_E_SHAPE;
   if (budget == 0) return KVC_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   KVC_LAUNCH("select_topk", kvc::select_topk_kernel, dim3(Hkv), dim3(kvc::kSelThreads), s, importance,

@@ -14,7 +14,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvc.so")
+# KVC_LIBRARY may name an alternative build of the same library (A/B timing).
+LIB_PATH = os.environ.get("KVC_LIBRARY") or os.path.join(_PKG, "libkvc.so")
 
 KVC_OK, KVC_E_ARG, KVC_E_SHAPE, KVC_E_WORKSPACE, KVC_E_DEVICE, KVC_E_UNSUPPORTED = range(6)
 

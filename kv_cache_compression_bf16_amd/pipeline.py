@@ -36,6 +36,8 @@ class CompressionPlan:
         a.k_head_stride, a.k_layer_stride = wl.S * D, Hkv * wl.S * D
         a.scale, a.gumbel, a.tau = 1.0, 1 if wl.gumbel else 0, 1.0
         self.ws_score = torch.empty(max(kvc.kvc_score_workspace_size(a), 256), dtype=torch.uint8, device=device)
+        sel_ws = kvc.lib.kvc_select_topk_workspace_size(Hkv, n)
+        self.ws_select = torch.empty(max(sel_ws, 256), dtype=torch.uint8, device=device)
         if self.zigzag:
             self.budgets = torch.empty(L, dtype=i32, device=device)
             self.mba = torch.empty((L, Hkv), dtype=i32, device=device)
@@ -48,8 +50,6 @@ class CompressionPlan:
             self.indices = torch.empty((Hkv, B), dtype=i32, device=device)
             self.kc = torch.empty((Hkv, B, D), dtype=bf, device=device)
             self.vc = torch.empty((Hkv, B, D), dtype=bf, device=device)
-            sel_ws = kvc.lib.kvc_select_topk_workspace_size(Hkv, n)
-            self.ws_select = torch.empty(max(sel_ws, 256), dtype=torch.uint8, device=device)
         self.think = wl.think_lambda >= 0
         if self.think:
             T = kvc.kvc_think_channels(D, wl.think_lambda)
@@ -92,7 +92,7 @@ class CompressionPlan:
             kc = self.kc_flat[off * Hkv * D:(off + B) * Hkv * D].view(Hkv, B, D)
             vc = self.vc_flat[off * Hkv * D:(off + B) * Hkv * D].view(Hkv, B, D)
             kvc.kvc_select_topk(self.importance[l], idx, S=wl.S, w=wl.w, recent=wl.recent, budget=B,
-                                stream=stream)
+                                workspace=self.ws_select, stream=stream)
             kvc.kvc_compact(k[l], v[l], idx, kc, vc, S=wl.S, stream=stream)
             self.layer_views.append((idx, kc, vc))
             off += B
