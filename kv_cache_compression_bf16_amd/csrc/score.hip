@@ -33,9 +33,6 @@
 
 #include "common.h"
 
-#ifndef KVC_SCORE_PIPELINE
-#define KVC_SCORE_PIPELINE 0
-#endif
 
 namespace kvc {
 namespace {
@@ -62,7 +59,7 @@ struct ScoreParams {
   float* rowc;       // [L, Hkv, R]
   const float* layer_scales;
   float scale;
-  float tau_mul;     // log2(e) / tau, 0 for tau = +inf
+  float inv_tau;     // 1 / tau, 0 for tau = +inf
   float inv_w;
   uint32_t seed_lo, seed_hi;
   int L, Hkv, G, w, S, n, R, nblk, nqb;
@@ -90,12 +87,13 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 x, uint32_t k0, uint32_t k1
   return x;
 }
 
-// Gumbel(0,1) from one 32-bit word: u = (2*(X>>9)+1) * 2^-24 (exact in fp32),
-// zeta = -ln(-ln u); -ln u uses log1p(u-1) for u >= 1/2 (u-1 is exact there).
-__device__ __forceinline__ float gumbel_from_word(uint32_t x) {
+// Gumbel(0,1) noise from one 32-bit word, in log2 units: u = (2*(X>>9)+1) * 2^-24
+// (exact in fp32) and zeta * log2(e) = -log2(-ln u) = -log2(-log2 u) - log2(ln 2).
+// The hardware log2 is within 1.2e-7 relative of the exact value on every u of
+// this grid, u -> 1 included, so the noise is good to about 1e-6 absolute.
+__device__ __forceinline__ float gumbel_log2_from_word(uint32_t x) {
   const float u = (float)(((x >> 9) << 1) | 1u) * 0x1p-24f;
-  const float e = (u >= 0.5f) ? -log1pf(u - 1.0f) : -logf(u);
-  return -logf(e);
+  return -__builtin_amdgcn_logf(-__builtin_amdgcn_logf(u)) + 0.52876637f;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -205,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], qf, acc[t], 0, 0, 0);
     }
   };
-  // Keyformer path: t = (alpha x + zeta) * log2(e)/tau, in place.
+  // Keyformer path: t = (alpha x + zeta) * log2(e) / tau, in place.
   int ep_hh = 0, ep_i0 = 0;   // running (head, offset) of the block in the epilogue (w32 path)
   auto noisy = [&](f32x16 (&acc)[kTiles], int qb) {
     const int r = qb * kQRows + col;
@@ -230,10 +228,10 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
       for (int r4 = 0; r4 < 4; ++r4) {
         const uint32_t j0 = (uint32_t)(key0 + t * 32 + 8 * r4 + 4 * hb);
         const u32x4 x = philox4x32_10(u32x4{j0 >> 2, pos, h, 0u}, p.seed_lo, p.seed_hi);
-        acc[t][4 * r4 + 0] = fmaf(acc[t][4 * r4 + 0], alpha, gumbel_from_word(x.x)) * p.tau_mul;
-        acc[t][4 * r4 + 1] = fmaf(acc[t][4 * r4 + 1], alpha, gumbel_from_word(x.y)) * p.tau_mul;
-        acc[t][4 * r4 + 2] = fmaf(acc[t][4 * r4 + 2], alpha, gumbel_from_word(x.z)) * p.tau_mul;
-        acc[t][4 * r4 + 3] = fmaf(acc[t][4 * r4 + 3], alpha, gumbel_from_word(x.w)) * p.tau_mul;
+        acc[t][4 * r4 + 0] = fmaf(acc[t][4 * r4 + 0], c, gumbel_log2_from_word(x.x)) * p.inv_tau;
+        acc[t][4 * r4 + 1] = fmaf(acc[t][4 * r4 + 1], c, gumbel_log2_from_word(x.y)) * p.inv_tau;
+        acc[t][4 * r4 + 2] = fmaf(acc[t][4 * r4 + 2], c, gumbel_log2_from_word(x.z)) * p.inv_tau;
+        acc[t][4 * r4 + 3] = fmaf(acc[t][4 * r4 + 3], c, gumbel_log2_from_word(x.w)) * p.inv_tau;
       }
     }
   };
@@ -242,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) colacc[t] = f32x16{};
 
-  // VALU half of one query block (overlaps the next block's MFMAs).
+  // VALU half of one query block (other waves' MFMAs run meanwhile).
   auto epilogue = [&](auto clean_c, int qb, f32x16 (&acc)[kTiles], float rc) {
     constexpr bool kClean = decltype(clean_c)::value;
     if (kGumbel) noisy(acc, qb);
@@ -290,7 +288,6 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
   // The whole block loop, specialised for "clean" workgroups (no key past the
   // prefix, query blocks never partial: no masking code at all) and the rest.
   auto run = [&](auto clean_c) {
-    constexpr bool kClean = decltype(clean_c)::value;
     load_q(0, qreg);
     store_q(0, qreg);
     if (p.nqb > 1) {
@@ -299,55 +296,6 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
     }
     if (kPass2) rc_cur = load_rc(0);
     __syncthreads();
-#if KVC_SCORE_PIPELINE
-    // Software pipeline: block qb+1's MFMAs are issued in between block qb's
-    // exp/FMA epilogue (explicit instruction interleaving), so the matrix
-    // cores and the VALU work at the same time inside one wave; block qb+2's
-    // query rows are fetched meanwhile and land in the LDS buffer block qb
-    // vacated.  The steady-state loop is peeled: no conditionals in it.
-    auto step = [&](auto has_next_c, auto has_next2_c, int qb, f32x16 (&cur)[kTiles],
-                    f32x16 (&nxt)[kTiles]) {
-      constexpr bool kNext = decltype(has_next_c)::value, kNext2 = decltype(has_next2_c)::value;
-      if (kNext2) load_q(qb + 2, qreg);
-      float rc_next = 0.f;
-      if (kPass2 && kNext) rc_next = load_rc(qb + 1);
-      if (kNext) mfma_block((qb + 1) & 1, nxt);
-      epilogue(clean_c, qb, cur, rc_cur);
-      if constexpr (kClean && kNext) {
-        constexpr int kValuPerMfma = kPass2 ? (kGumbel ? 24 : 6) : (kGumbel ? 24 : 8);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the 8 LDS operand reads
-#pragma unroll
-        for (int i = 0; i < 8 * kTiles; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA ...
-          __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // ... then VALU work
-        }
-      }
-      if (kNext2) store_q(qb & 1, qreg);
-      __syncthreads();
-      if (!kPass2) store_partial(qb);
-      rc_cur = rc_next;
-    };
-    using T_ = std::true_type;
-    using F_ = std::false_type;
-    f32x16 accA[kTiles], accB[kTiles];
-    mfma_block(0, accA);
-    int qb = 0;
-    for (; qb + 3 < p.nqb; qb += 2) {
-      step(T_{}, T_{}, qb, accA, accB);
-      step(T_{}, T_{}, qb + 1, accB, accA);
-    }
-    const int left = p.nqb - qb;
-    if (left == 3) {
-      step(T_{}, T_{}, qb, accA, accB);
-      step(T_{}, F_{}, qb + 1, accB, accA);
-      step(F_{}, F_{}, qb + 2, accA, accB);
-    } else if (left == 2) {
-      step(T_{}, F_{}, qb, accA, accB);
-      step(F_{}, F_{}, qb + 1, accB, accA);
-    } else {
-      step(F_{}, F_{}, qb, accA, accB);
-    }
-#else
     // Plain loop: MFMAs then epilogue per block; latency is hidden across waves.
     for (int qb = 0; qb < p.nqb; ++qb) {
       const bool has_next2 = qb + 2 < p.nqb;
@@ -360,7 +308,6 @@ __global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
       if (!kPass2) store_partial(qb);
       if (has_next2) store_q(qb & 1, qreg);     // visible after the next iteration's barrier
     }
-#endif
   };
   if (!tail && w32)
     run(std::true_type{});
@@ -491,7 +438,7 @@ extern "C" kvc_status kvc_score(const kvc_score_args* a, const void* q_obs, cons
   p.rowc = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.part_bytes);
   p.layer_scales = a->layer_scales;
   p.scale = a->scale;
-  p.tau_mul = a->gumbel ? (isinf(a->tau) ? 0.f : kLog2e / a->tau) : 0.f;
+  p.inv_tau = a->gumbel ? (isinf(a->tau) ? 0.f : 1.0f / a->tau) : 0.f;
   p.inv_w = 1.0f / (float)a->w;
   p.seed_lo = (uint32_t)(a->seed & 0xFFFFFFFFull);
   p.seed_hi = (uint32_t)(a->seed >> 32);
