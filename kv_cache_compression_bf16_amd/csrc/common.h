@@ -27,12 +27,14 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 }  // namespace kvc
 
-// Launch `kernel<<<grid, block, 0, stream>>>(args...)` with timing and error
+// Launch `kernel<<<grid, block, shm, stream>>>(args...)` with timing and error
 // mapping; returns from the calling function on failure.
-#define KVC_LAUNCH(name, kernel, grid, block, stream, ...)                      \
+#define KVC_LAUNCH_SHM(name, kernel, grid, block, shm, stream, ...)             \
   do {                                                                         \
     int kvc_slot_ = ::kvc::launch_begin(name, stream);                         \
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);           \
+    hipLaunchKernelGGL(kernel, grid, block, shm, stream, __VA_ARGS__);         \
     kvc_status kvc_st_ = ::kvc::launch_end(kvc_slot_, stream);                 \
     if (kvc_st_ != KVC_OK) return kvc_st_;                                     \
   } while (0)
+#define KVC_LAUNCH(name, kernel, grid, block, stream, ...) \
+  KVC_LAUNCH_SHM(name, kernel, grid, block, 0, stream, __VA_ARGS__)

@@ -7,22 +7,27 @@
 // the normalised rows are summed into a per-key importance (times 1/w).
 //
 // Design (two passes over the keys, same grid):
-//  * A workgroup owns 256 consecutive prefix keys of one KV head (4 waves x
-//    64 keys).  Each wave holds its 64 keys in registers, already in the A
-//    operand layout of v_mfma_f32_32x32x16_bf16, for the whole kernel: K is
-//    read from HBM exactly once per pass, straight into VGPRs.
-//  * The G*w query rows of the group stream through LDS in blocks of 32 rows
-//    (8.5 KB, double-buffered, rows padded by 16 bytes so the MFMA B-operand
-//    reads are bank-conflict free and need no per-block address math).
+//  * A workgroup owns 32*kW consecutive prefix keys of one KV head, 32 per
+//    wave.  Each wave holds its 32 keys in registers, already in the A operand
+//    layout of v_mfma_f32_32x32x16_bf16, for the whole kernel: K is read from
+//    HBM exactly once per pass, straight into VGPRs.
+//  * The G*w query rows of the group are staged in LDS once per workgroup, in
+//    chunks of up to 32*kW rows (rows padded by 16 bytes so the MFMA B-operand
+//    reads are bank-conflict free).  After that one barrier every wave walks
+//    the query blocks on its own: no barrier and no shared state inside the
+//    block loop, so the 4 waves of each SIMD drift apart and hide each
+//    other's MFMA, LDS and transcendental latencies.  kW is picked so that
+//    LDS holds 4 waves per SIMD (16 waves for 512 rows, 4 for 128 rows).
 //  * The tile is computed as K x Q^T, so a lane owns ONE query row and 16 keys
 //    of each 32x32 tile: row statistics (pass 1) and the per-row softmax
 //    constant (pass 2) are per-lane scalars, and column sums over query rows
 //    accumulate in registers across all query blocks; the 32-lane reduction
-//    happens once per workgroup at the end.  Every key column has a single
-//    owner, so no atomics are used and results are bit-reproducible.
-//  * Pass 1 writes per-(row, workgroup) partials (max, sum of exp2) in log2
-//    units; a combine kernel folds them per row in a fixed order into
-//    rowc = m + log2(l); pass 2 recomputes the logits and accumulates
+//    happens once per wave at the end.  Every key column has a single owner,
+//    so no atomics are used and results are bit-reproducible.
+//  * Pass 1 keeps each wave's per-row (max, sum of exp2) in registers and
+//    folds the waves once per chunk, in a fixed order, into per-(row,
+//    workgroup) partials in log2 units; a combine kernel folds those per row
+//    into rowc = m + log2(l); pass 2 recomputes the logits and accumulates
 //    exp2(t - rowc).
 //  * Keyformer noise: lane values come in groups of 4 consecutive, 4-aligned
 //    keys, which is exactly one Philox4x32-10 block, so every Philox call is
@@ -38,17 +43,27 @@ namespace kvc {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kWaves = 4;
-constexpr int kTiles = 2;                              // 32-key tiles per wave
-constexpr int kKeysPerWave = 32 * kTiles;
-constexpr int kKeysPerBlock = kKeysPerWave * kWaves;   // 256
-constexpr int kQRows = 32;
-constexpr int kThreads = kWaves * kWave;
 // LDS row pitch of a staged query row: 256 bytes + 16 bytes of padding, so the
 // 16 lanes that read one 16-byte chunk of 16 different rows hit 16 distinct
 // bank groups, and the 8 chunk reads of a lane are one base + immediates.
 constexpr int kRowPitch = kD * 2 + 16;
-constexpr int kQBlockBytes = kQRows * kRowPitch;
+
+// Waves per workgroup and staged rows per chunk (32 per wave, so LDS holds 4
+// waves per SIMD: 160 KB per CU).  The Keyformer passes need more registers
+// for Philox (about 150 VGPRs, 3 waves per SIMD), so they always use 4 waves
+// and 128-row chunks.
+#ifndef KVC_SCORE_MAX_WAVES
+#define KVC_SCORE_MAX_WAVES 16
+#endif
+inline int score_waves(int R, bool gumbel) {
+  if (gumbel) return 4;
+  const int kw = R <= 128 ? 4 : (R <= 256 ? 8 : 16);
+  return kw < KVC_SCORE_MAX_WAVES ? kw : KVC_SCORE_MAX_WAVES;
+}
+inline int score_chunk_rows(int R, int kw) { return min((R + 31) / 32 * 32, 32 * kw); }
+inline size_t score_lds_bytes(int rows, bool pass2) {
+  return (size_t)rows * kRowPitch + (pass2 ? (size_t)rows * sizeof(float) : 0);
+}
 
 struct ScoreParams {
   const uint16_t* q;
@@ -62,7 +77,7 @@ struct ScoreParams {
   float inv_tau;     // 1 / tau, 0 for tau = +inf
   float inv_w;
   uint32_t seed_lo, seed_hi;
-  int L, Hkv, G, w, S, n, R, nblk, nqb;
+  int L, Hkv, G, w, S, n, R, nblk, chunk_rows;
 };
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
@@ -98,243 +113,211 @@ __device__ __forceinline__ float gumbel_log2_from_word(uint32_t x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <bool kPass2, bool kGumbel>
-__global__ __launch_bounds__(kThreads) void score_pass(ScoreParams p) {
-  __shared__ __attribute__((aligned(16))) char qs[2][kQBlockBytes];   // 2 x 8.5 KB
-  __shared__ float2 red[2][kWaves][64];   // [.., 32 + col] is the unused half-wave copy
+template <bool kPass2, bool kGumbel, int kW>
+__global__ __launch_bounds__(kW * kWave) void score_pass(ScoreParams p) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];   // [rows][kRowPitch] (+ [rows] rowc)
+  constexpr int kThreads = kW * kWave;
+  constexpr int kKeysPerBlock = 32 * kW;
 
   const int blk = blockIdx.x, g = blockIdx.y, layer = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hb = lane >> 5, col = lane & 31;
-  const int key0 = blk * kKeysPerBlock + wave * kKeysPerWave;
-  const bool tail = blk * kKeysPerBlock + kKeysPerBlock > p.n;
-  // w % 32 == 0: a 32-row query block never straddles two query heads and is
-  // never partial, so its head / window offset are block-uniform scalars.
-  const bool w32 = (p.w & 31) == 0;
+  const int key0 = blk * kKeysPerBlock + wave * 32;
+  const bool wave_full = key0 + 32 <= p.n;      // no key of this wave past the prefix
   const float alpha = p.layer_scales ? p.layer_scales[layer] : p.scale;
   const float c = alpha * kLog2e;
   const int64_t head_row0 = ((int64_t)layer * p.Hkv + g) * p.R;
+  const int rows_alloc = p.chunk_rows;
+  float* rcs = reinterpret_cast<float*>(lds + (size_t)rows_alloc * kRowPitch);
 
-  // ---- K fragments: lane holds key (col) of tile t, 16-byte chunk (2s + hb).
-  bf16x8 kf[kTiles][8];
+  // ---- K fragments: lane holds key (col), 16-byte chunk (2s + hb).
+  bf16x8 kf[8];
   {
     const uint16_t* kb = p.k + layer * p.k_ls + g * p.k_hs;
+    const int j = min(key0 + col, p.n - 1);   // clamp: keys past the prefix are masked
+    const bf16x8* row = reinterpret_cast<const bf16x8*>(kb + (int64_t)j * kD);
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-      int j = key0 + t * 32 + col;
-      j = j < p.n ? j : p.n - 1;   // clamp: keys past the prefix are masked in pass 1
-      const bf16x8* row = reinterpret_cast<const bf16x8*>(kb + (int64_t)j * kD);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) kf[t][s] = row[2 * s + hb];
-    }
+    for (int s = 0; s < 8; ++s) kf[s] = row[2 * s + hb];
   }
 
-  // ---- Q block staging: 512 16-byte chunks per 32-row block, 2 per thread
-  // (rows tid/16 and tid/16 + 16, chunk tid%16), coalesced 256-byte rows.
+  // ---- stage query rows [c0, c0 + nrows) into LDS (zero rows past R), 8
+  // independent 16-byte loads in flight per thread, addresses clamped.
   const uint16_t* qg = p.q + layer * p.q_ls + (int64_t)g * p.G * p.q_hs;
-  const int q_toff = (tid >> 4) * kD + (tid & 15) * 8;           // element offset in a block
-  const int st_off = (tid >> 4) * kRowPitch + (tid & 15) * 16;    // LDS byte offset, row tid/16
-  const int rd_off = col * kRowPitch + hb * 16;                   // LDS byte offset of chunk hb
-  // Blocks are loaded strictly in order, so with w % 32 == 0 the (query head,
-  // window offset) of the next block to load is a running scalar pair: no
-  // integer division (which the compiler would expand on the VALU).
-  int ld_hh = 0, ld_i0 = 0;
-  auto load_q = [&](int qb, u32x4 (&regs)[2]) {
-    const int r0 = qb * kQRows;
-    if (w32) {
-      const uint16_t* src = qg + (ld_hh * p.q_hs + (int64_t)ld_i0 * kD) + q_toff;
-      regs[0] = *reinterpret_cast<const u32x4*>(src);
-      regs[1] = *reinterpret_cast<const u32x4*>(src + 16 * kD);
-      ld_i0 += kQRows;
-      if (ld_i0 == p.w) {
-        ld_i0 = 0;
-        ++ld_hh;
+  // row r -> (query head r / w, window offset r % w): a float estimate of the
+  // quotient, then one exact integer correction (r < 2^16, so the estimate is
+  // off by at most one).
+  const float inv_w = 1.0f / (float)p.w;
+  auto split_row = [&](int r, int& hh, int& ii) {
+    hh = (int)((float)r * inv_w);
+    ii = r - hh * p.w;
+    if (ii < 0) { --hh; ii += p.w; }
+    if (ii >= p.w) { ++hh; ii -= p.w; }
+  };
+  auto stage = [&](int c0, int nrows) {
+    const int total = nrows * 16;
+    for (int base = 0; base < total; base += 8 * kThreads) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * kThreads + tid;
+        const int r = min(c0 + (i >> 4), p.R - 1);
+        int hh, ii;
+        split_row(r, hh, ii);
+        v[u] = *reinterpret_cast<const u32x4*>(qg + hh * p.q_hs + (int64_t)ii * kD + (i & 15) * 8);
       }
-      return;
-    }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int r = r0 + (tid >> 4) + 16 * u;
-      if (r < p.R) {
-        const int hh = r / p.w, i = r - hh * p.w;
-        regs[u] = *reinterpret_cast<const u32x4*>(qg + hh * p.q_hs + (int64_t)i * kD + (tid & 15) * 8);
-      } else {
-        regs[u] = u32x4{0u, 0u, 0u, 0u};
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * kThreads + tid;
+        if (i < total) {
+          const bool ok = c0 + (i >> 4) < p.R;
+          *reinterpret_cast<u32x4*>(lds + (i >> 4) * kRowPitch + (i & 15) * 16) = ok ? v[u] : u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
-  };
-  auto store_q = [&](int buf, const u32x4 (&regs)[2]) {
-    *reinterpret_cast<u32x4*>(qs[buf] + st_off) = regs[0];
-    *reinterpret_cast<u32x4*>(qs[buf] + st_off + 16 * kRowPitch) = regs[1];
-  };
-  auto load_rc = [&](int qb) -> float {
-    const int r = qb * kQRows + col;
-    return (w32 || r < p.R) ? p.rowc[head_row0 + r] : INFINITY;
-  };
-  // Pass 1: wave 0 folds the 4 waves' statistics of block qb into one partial.
-  auto store_partial = [&](int qb) {
-    if (wave == 0 && hb == 0) {
-      const int b = qb & 1;
-      float m = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < kWaves; ++v) m = fmaxf(m, red[b][v][col].x);
-      const float ms = (m == -INFINITY) ? 0.f : m;
-      float l = 0.f;
-#pragma unroll
-      for (int v = 0; v < kWaves; ++v) {
-        const float2 a = red[b][v][col];
-        l += a.y * fast_exp2(a.x - ms);
+    if (kPass2)
+      for (int i = tid; i < nrows; i += kThreads) {
+        const int r = c0 + i;
+        rcs[i] = r < p.R ? p.rowc[head_row0 + r] : INFINITY;
       }
-      const int r = qb * kQRows + col;
-      if (w32 || r < p.R) p.part[(head_row0 * p.nblk) + (int64_t)blk * p.R + r] = float2{m, l};
-    }
   };
-  // B operands from LDS, 8 k-steps x kTiles MFMAs: acc[t][r] = <K[key], Q[row]> with
-  // key = key0 + 32t + 8(r/4) + 4hb + (r%4), row = 32qb + col.
-  auto mfma_block = [&](int buf, f32x16 (&acc)[kTiles]) {
-    const char* qsb = qs[buf] + rd_off;
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) acc[t] = f32x16{};
+
+  // A operand from registers, B operand (32 query rows) from LDS:
+  // acc[r] = <K[key], Q[row]>, key = key0 + 8(r/4) + 4hb + (r%4), row = 32qb + col.
+  auto mfma_block = [&](int qb) -> f32x16 {
+    const char* qsb = lds + (qb * 32 + col) * kRowPitch + hb * 16;
+    f32x16 acc = f32x16{};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qsb + 32 * s);
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], qf, acc[t], 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf, acc, 0, 0, 0);
     }
+    return acc;
   };
-  // Keyformer path: t = (alpha x + zeta) * log2(e) / tau, in place.
-  int ep_hh = 0, ep_i0 = 0;   // running (head, offset) of the block in the epilogue (w32 path)
-  auto noisy = [&](f32x16 (&acc)[kTiles], int qb) {
-    const int r = qb * kQRows + col;
+  // Keyformer path: t = (alpha x + zeta) * log2(e) / tau, in place, for row r.
+  auto noisy = [&](f32x16& acc, int r) {
     int hh, i;
-    if (w32) {
-      hh = ep_hh;
-      i = ep_i0 + col;
-      ep_i0 += kQRows;
-      if (ep_i0 == p.w) {
-        ep_i0 = 0;
-        ++ep_hh;
-      }
-    } else {
-      hh = r / p.w;
-      i = r - hh * p.w;
-    }
+    split_row(r, hh, i);
     const uint32_t h = (uint32_t)(g * p.G + hh);
     const uint32_t pos = (uint32_t)(p.S - p.w + i);
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const uint32_t j0 = (uint32_t)(key0 + t * 32 + 8 * r4 + 4 * hb);
-        const u32x4 x = philox4x32_10(u32x4{j0 >> 2, pos, h, 0u}, p.seed_lo, p.seed_hi);
-        acc[t][4 * r4 + 0] = fmaf(acc[t][4 * r4 + 0], c, gumbel_log2_from_word(x.x)) * p.inv_tau;
-        acc[t][4 * r4 + 1] = fmaf(acc[t][4 * r4 + 1], c, gumbel_log2_from_word(x.y)) * p.inv_tau;
-        acc[t][4 * r4 + 2] = fmaf(acc[t][4 * r4 + 2], c, gumbel_log2_from_word(x.z)) * p.inv_tau;
-        acc[t][4 * r4 + 3] = fmaf(acc[t][4 * r4 + 3], c, gumbel_log2_from_word(x.w)) * p.inv_tau;
-      }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const uint32_t j0 = (uint32_t)(key0 + 8 * r4 + 4 * hb);
+      const u32x4 x = philox4x32_10(u32x4{j0 >> 2, pos, h, 0u}, p.seed_lo, p.seed_hi);
+      acc[4 * r4 + 0] = fmaf(acc[4 * r4 + 0], c, gumbel_log2_from_word(x.x)) * p.inv_tau;
+      acc[4 * r4 + 1] = fmaf(acc[4 * r4 + 1], c, gumbel_log2_from_word(x.y)) * p.inv_tau;
+      acc[4 * r4 + 2] = fmaf(acc[4 * r4 + 2], c, gumbel_log2_from_word(x.z)) * p.inv_tau;
+      acc[4 * r4 + 3] = fmaf(acc[4 * r4 + 3], c, gumbel_log2_from_word(x.w)) * p.inv_tau;
     }
   };
+  // logit -> log2 units is fmaf(v, cc, -ref); the Keyformer path is already there
+  const float cc = kGumbel ? 1.0f : c;
 
-  f32x16 colacc[kTiles];
-#pragma unroll
-  for (int t = 0; t < kTiles; ++t) colacc[t] = f32x16{};
-
-  // VALU half of one query block (other waves' MFMAs run meanwhile).
-  auto epilogue = [&](auto clean_c, int qb, f32x16 (&acc)[kTiles], float rc) {
+  // Pass 1, one query block: this wave's (max, sum of exp2) of the lane's row
+  // over its 32 keys; lanes of half-wave 0 return the max, half-wave 1 the sum.
+  auto row_stats = [&](auto clean_c, f32x16 acc, int r) -> float {
     constexpr bool kClean = decltype(clean_c)::value;
-    if (kGumbel) noisy(acc, qb);
-    // logit -> log2 units is fmaf(v, cc, -ref); the Keyformer path is already there
-    const float cc = kGumbel ? 1.0f : c;
-    if (!kPass2) {
-      if (!kClean) {
-        const bool row_ok = qb * kQRows + col < p.R;
+    if (!kClean) {
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + t * 32 + 8 * (r >> 2) + 4 * hb + (r & 3);
-            if (key >= p.n || !row_ok) acc[t][r] = -INFINITY;
-          }
+      for (int e = 0; e < 16; ++e) {
+        const int key = key0 + 8 * (e >> 2) + 4 * hb + (e & 3);
+        if (key >= p.n || r >= p.R) acc[e] = -INFINITY;
       }
-      float mx = acc[0][0];
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[t][r]);
-      const float mt = mx * cc;
-      const float mts = (mx == -INFINITY) ? 0.f : mt;
-      float l = 0.f;
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) l += fast_exp2(fmaf(acc[t][r], cc, -mts));
-      // fold with the other half-wave (same query row, the other keys of each group)
-      const float mo = __shfl_xor(mt, 32), lo = __shfl_xor(l, 32);
-      const float m2 = fmaxf(mt, mo);
-      const float m2s = (m2 == -INFINITY) ? 0.f : m2;
-      const float l2 = l * fast_exp2(mt - m2s) + lo * fast_exp2(mo - m2s);
-      red[qb & 1][wave][lane] = float2{m2, l2};   // lanes col and 32+col hold the same pair
-    } else {
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) colacc[t][r] += fast_exp2(fmaf(acc[t][r], cc, -rc));
     }
+    float mx = acc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, acc[e]);
+    const float mt = mx * cc;
+    const float mts = (mx == -INFINITY) ? 0.f : mt;
+    float l = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) l += fast_exp2(fmaf(acc[e], cc, -mts));
+    // fold with the other half-wave (same query row, the other 16 keys)
+    const float mo = __shfl_xor(mt, 32), lo = __shfl_xor(l, 32);
+    const float m2 = fmaxf(mt, mo);
+    const float m2s = (m2 == -INFINITY) ? 0.f : m2;
+    const float l2 = l * fast_exp2(mt - m2s) + lo * fast_exp2(mo - m2s);
+    return hb ? l2 : m2;
   };
 
-  u32x4 qreg[2];
-  float rc_cur = 0.f;
-  // The whole block loop, specialised for "clean" workgroups (no key past the
-  // prefix, query blocks never partial: no masking code at all) and the rest.
-  auto run = [&](auto clean_c) {
-    load_q(0, qreg);
-    store_q(0, qreg);
-    if (p.nqb > 1) {
-      load_q(1, qreg);
-      store_q(1, qreg);
-    }
-    if (kPass2) rc_cur = load_rc(0);
+  f32x16 colacc = f32x16{};
+  for (int c0 = 0; c0 < p.R; c0 += rows_alloc) {
+    const int nrows = min(rows_alloc, (p.R - c0 + 31) / 32 * 32);
+    const int nb = nrows / 32;
+    const bool rows_full = c0 + nrows <= p.R;
+    stage(c0, nrows);
     __syncthreads();
-    // Plain loop: MFMAs then epilogue per block; latency is hidden across waves.
-    for (int qb = 0; qb < p.nqb; ++qb) {
-      const bool has_next2 = qb + 2 < p.nqb;
-      if (has_next2) load_q(qb + 2, qreg);
-      f32x16 acc[kTiles];
-      mfma_block(qb & 1, acc);
-      epilogue(clean_c, qb, acc, rc_cur);
-      if (kPass2 && qb + 1 < p.nqb) rc_cur = load_rc(qb + 1);
-      __syncthreads();                          // every wave is done with buffer qb & 1
-      if (!kPass2) store_partial(qb);
-      if (has_next2) store_q(qb & 1, qreg);     // visible after the next iteration's barrier
+    if (!kPass2) {
+      // per-block partials stay in registers until the chunk is done
+      float st[kW];
+      auto blocks = [&](auto clean_c) {
+#pragma unroll
+        for (int qb = 0; qb < kW; ++qb) {
+          st[qb] = 0.f;
+          if (qb < nb) {
+            f32x16 acc = mfma_block(qb);
+            const int r = c0 + qb * 32 + col;
+            if (kGumbel) noisy(acc, r);
+            st[qb] = row_stats(clean_c, acc, r);
+          }
+        }
+      };
+      if (wave_full && rows_full)
+        blocks(std::true_type{});
+      else
+        blocks(std::false_type{});
+      __syncthreads();   // every wave is done with the staged rows: reuse them
+      float* red = reinterpret_cast<float*>(lds);   // [kW][nrows][2] = (max, sum)
+#pragma unroll
+      for (int qb = 0; qb < kW; ++qb)
+        if (qb < nb) red[(wave * nrows + qb * 32 + col) * 2 + hb] = st[qb];
+      __syncthreads();
+      for (int i = tid; i < nrows; i += kThreads) {
+        const int r = c0 + i;
+        if (r >= p.R) continue;
+        float m = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < kW; ++v) m = fmaxf(m, red[(v * nrows + i) * 2]);
+        const float ms = (m == -INFINITY) ? 0.f : m;
+        float l = 0.f;
+#pragma unroll
+        for (int v = 0; v < kW; ++v) l += red[(v * nrows + i) * 2 + 1] * fast_exp2(red[(v * nrows + i) * 2] - ms);
+        p.part[head_row0 * p.nblk + (int64_t)blk * p.R + r] = float2{m, l};
+      }
+    } else {
+      auto blocks = [&](auto clean_c) {
+        constexpr bool kClean = decltype(clean_c)::value;
+        (void)kClean;
+        for (int qb = 0; qb < nb; ++qb) {
+          f32x16 acc = mfma_block(qb);
+          if (kGumbel) noisy(acc, c0 + qb * 32 + col);
+          const float rc = rcs[qb * 32 + col];   // +inf for rows past R: adds 0
+#pragma unroll
+          for (int e = 0; e < 16; ++e) colacc[e] += fast_exp2(fmaf(acc[e], cc, -rc));
+        }
+      };
+      blocks(std::true_type{});
     }
-  };
-  if (!tail && w32)
-    run(std::true_type{});
-  else
-    run(std::false_type{});
+    __syncthreads();   // before the next chunk overwrites the staged rows
+  }
 
   if (!kPass2) return;
 
   // ---- pass 2: sum each key column over the 32 query lanes of its half-wave.
   float* out = p.imp + ((int64_t)layer * p.Hkv + g) * p.n;
+  float mine = 0.f;
 #pragma unroll
-  for (int t = 0; t < kTiles; ++t) {
-    float mine = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float v = colacc[t][r];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 1);
-      if (col == r) mine = v;
-    }
-    if (col < 16) {
-      const int key = key0 + t * 32 + 8 * (col >> 2) + 4 * hb + (col & 3);
-      if (key < p.n) out[key] = mine * p.inv_w;
-    }
+  for (int e = 0; e < 16; ++e) {
+    float v = colacc[e];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 8);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 1);
+    if (col == e) mine = v;
+  }
+  if (col < 16) {
+    const int key = key0 + 8 * (col >> 2) + 4 * hb + (col & 3);
+    if (key < p.n) out[key] = mine * p.inv_w;
   }
 }
 
@@ -376,7 +359,7 @@ __global__ __launch_bounds__(256) void score_combine(ScoreParams p, int heads) {
 }
 
 struct Plan {
-  int n, G, R, nblk, nqb;
+  int n, G, R, kw, nblk, chunk_rows;
   size_t part_bytes, rowc_bytes, total;
 };
 
@@ -399,12 +382,36 @@ kvc_status plan(const kvc_score_args* a, Plan* pl) {
   pl->n = a->S - a->w;
   pl->G = (int)G;
   pl->R = (int)(G * a->w);
-  pl->nblk = (pl->n + kKeysPerBlock - 1) / kKeysPerBlock;
-  pl->nqb = (pl->R + kQRows - 1) / kQRows;
+  pl->kw = score_waves(pl->R, a->gumbel != 0);
+  pl->nblk = (pl->n + 32 * pl->kw - 1) / (32 * pl->kw);
+  pl->chunk_rows = score_chunk_rows(pl->R, pl->kw);
   const size_t rows = (size_t)a->L * a->Hkv * pl->R;
   pl->part_bytes = align_up(rows * pl->nblk * sizeof(float2), 256);
   pl->rowc_bytes = align_up(rows * sizeof(float), 256);
   pl->total = pl->part_bytes + pl->rowc_bytes;
+  return KVC_OK;
+}
+
+// Pass 1, combine, pass 2 on one stream, kW waves per scoring workgroup.
+template <int kW>
+kvc_status launch_score(const ScoreParams& p, const Plan& pl, bool gumbel, hipStream_t s) {
+  const dim3 grid(pl.nblk, p.Hkv, p.L), block(kW * kWave);
+  const int heads = p.L * p.Hkv;
+  const dim3 comb_grid(heads * ((pl.R + kCombRows - 1) / kCombRows));
+  const size_t lds1 = score_lds_bytes(pl.chunk_rows, false), lds2 = score_lds_bytes(pl.chunk_rows, true);
+  if (gumbel) {
+    if constexpr (kW == 4) {   // the only shape the Keyformer passes are built for
+      KVC_LAUNCH_SHM("score_pass1_gumbel", (score_pass<false, true, kW>), grid, block, lds1, s, p);
+      KVC_LAUNCH("score_combine", score_combine, comb_grid, dim3(256), s, p, heads);
+      KVC_LAUNCH_SHM("score_pass2_gumbel", (score_pass<true, true, kW>), grid, block, lds2, s, p);
+    } else {
+      return KVC_E_UNSUPPORTED;
+    }
+  } else {
+    KVC_LAUNCH_SHM("score_pass1", (score_pass<false, false, kW>), grid, block, lds1, s, p);
+    KVC_LAUNCH("score_combine", score_combine, comb_grid, dim3(256), s, p, heads);
+    KVC_LAUNCH_SHM("score_pass2", (score_pass<true, false, kW>), grid, block, lds2, s, p);
+  }
   return KVC_OK;
 }
 
@@ -450,20 +457,12 @@ extern "C" kvc_status kvc_score(const kvc_score_args* a, const void* q_obs, cons
   p.n = pl.n;
   p.R = pl.R;
   p.nblk = pl.nblk;
-  p.nqb = pl.nqb;
+  p.chunk_rows = pl.chunk_rows;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(pl.nblk, a->Hkv, a->L), block(kThreads);
-  const int heads = a->L * a->Hkv;
-  const dim3 comb_grid(heads * ((pl.R + kCombRows - 1) / kCombRows));
-  if (a->gumbel) {
-    KVC_LAUNCH("score_pass1_gumbel", (score_pass<false, true>), grid, block, s, p);
-    KVC_LAUNCH("score_combine", score_combine, comb_grid, dim3(256), s, p, heads);
-    KVC_LAUNCH("score_pass2_gumbel", (score_pass<true, true>), grid, block, s, p);
-  } else {
-    KVC_LAUNCH("score_pass1", (score_pass<false, false>), grid, block, s, p);
-    KVC_LAUNCH("score_combine", score_combine, comb_grid, dim3(256), s, p, heads);
-    KVC_LAUNCH("score_pass2", (score_pass<true, false>), grid, block, s, p);
+  switch (pl.kw) {
+    case 4: return launch_score<4>(p, pl, a->gumbel != 0, s);
+    case 8: return launch_score<8>(p, pl, a->gumbel != 0, s);
+    default: return launch_score<16>(p, pl, a->gumbel != 0, s);
   }
-  return KVC_OK;
 }

@@ -7,13 +7,18 @@
 // every position of [S - recent, S); kept positions are written ascending.
 //
 // Design: one 512-thread workgroup per head runs an exact MSB-first radix
-// select on order-preserving 32-bit keys of the fp32 scores (digits of 11, 11
-// and 10 bits; LDS histograms with integer atomics, which are exact and
-// order-independent).  That yields the k_top-th key T and how many T-valued
-// candidates must be taken.  Each wave owns a contiguous range of candidates
-// loaded with coalesced 256-byte loads, 64 in flight per lane, and kept in
-// registers across all radix passes; the ordered output transposes them
-// through LDS so each thread owns 64 consecutive candidates (see below).
+// select on order-preserving 32-bit keys of the fp32 scores, relative to the
+// head's smallest key: d = key - min, and each level histograms the next (up
+// to) 11 bits below the highest set bit of max - min.  Scores of one head
+// usually span a narrow key range (similar exponents), so the first level
+// already spreads them over the bins (few LDS-atomic collisions) and often
+// two levels suffice.  Integer atomics are exact and order-independent.  The
+// select yields the k_top-th key T and how many T-valued candidates must be
+// taken.  Each wave owns a contiguous range of candidates loaded with
+// coalesced 256-byte loads, 64 in flight per lane, and kept in registers
+// across all levels; the ordered output transposes them through LDS so each
+// thread owns 64 consecutive candidates, and the kept positions are staged
+// in LDS and written out coalesced.
 #include "common.h"
 
 namespace kvc {
@@ -53,6 +58,27 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, 
   return before + v - x;
 }
 
+// Workgroup-wide (min, max); every thread receives the result.
+__device__ __forceinline__ void block_min_max(uint32_t& lo, uint32_t& hi, uint32_t* wlo, uint32_t* whi) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor(lo, o));
+    hi = max(hi, (uint32_t)__shfl_xor(hi, o));
+  }
+  if (lane == 0) {
+    wlo[wid] = lo;
+    whi[wid] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kSelWaves; ++i) {
+    lo = min(lo, wlo[i]);
+    hi = max(hi, whi[i]);
+  }
+  __syncthreads();
+}
+
 // Candidates are handled in rounds of kRound = 512 * 64: in round r, wave w
 // owns the contiguous range [r*kRound + w*4096, +4096) and lane l holds
 // candidates base + 64*i + l (i < 64), so every load instruction reads 256
@@ -81,9 +107,9 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
                                                                  int k_top, int S, int recent, int budget,
                                                                  int32_t* out) {
   __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t wsum[kSelWaves];
+  __shared__ uint32_t wsum[kSelWaves], wsum2[kSelWaves];
   __shared__ uint32_t s_digit, s_above;
-  __shared__ uint32_t tr[kRound + kRound / 64];   // 130 KB transpose buffer of one round
+  __shared__ uint32_t tr[kRound + kRound / 64];   // 130 KB: transposed keys, then kept positions
 
   const int g = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
   const uint32_t* v = reinterpret_cast<const uint32_t*>(imp + (int64_t)g * hs);
@@ -101,11 +127,30 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
   if (rounds == 1) load_round(v, c, 0, key);
   const int lbase = wave * kSpan + (tid & 63);   // candidate of key[0] in round 0
 
-  // ---- radix select of the k_top-th largest key
-  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k_top;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t width_mask = (pass == 2) ? 0x3FFu : 0x7FFu;
+  // ---- key range of the candidates
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int r = 0; r < rounds; ++r) {
+    if (rounds > 1) load_round(v, c, r, key);
+    const int j0 = r * kRound + lbase;
+#pragma unroll
+    for (int i = 0; i < kVPL; ++i) {
+      const bool in = j0 + 64 * i < c;
+      kmin = min(kmin, in ? key[i] : 0xFFFFFFFFu);
+      kmax = max(kmax, in ? key[i] : 0u);
+    }
+  }
+  block_min_max(kmin, kmax, wsum, wsum2);
+
+  // ---- radix select on d = key - kmin, MSB first.  Bits [top, 32) of the
+  // k_top-th largest d are known (= hi); each level resolves up to 11 more.
+  int top = 32 - __clz(kmax - kmin);   // 0 when every candidate has the same key
+  uint32_t hi = 0, krem = (uint32_t)k_top;
+  while (top > 0) {
+    const int width = top < 11 ? top : 11;
+    const int sh = top - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    const uint32_t hmask = top >= 32 ? 0u : (0xFFFFFFFFu << top);   // bits already resolved
+    const uint32_t hval = top >= 32 ? 0u : (hi << top);
     for (int b = tid; b < kBins; b += kSelThreads) hist[b] = 0;
     if (tid == 0) {
       s_digit = 0;
@@ -116,8 +161,11 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
       if (rounds > 1) load_round(v, c, r, key);
       const int j0 = r * kRound + lbase;
 #pragma unroll
-      for (int i = 0; i < kVPL; ++i)
-        if (j0 + 64 * i < c && (key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> sh) & width_mask], 1u);
+      for (int i = 0; i < kVPL; ++i) {
+        const uint32_t d = key[i] - kmin;
+        const bool live = j0 + 64 * i < c && (d & hmask) == hval;
+        if (live) atomicAdd(&hist[(d >> sh) & dmask], 1u);
+      }
     }
     __syncthreads();
     // suffix counts: thread tid owns bins [kBPT*rt, kBPT*rt + kBPT), rt = last - tid
@@ -141,22 +189,23 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
       below += hb[i];
     }
     __syncthreads();
-    prefix |= s_digit << sh;
-    pmask |= width_mask << sh;
+    hi = (hi << width) | s_digit;
     krem -= s_above;
+    top = sh;
     __syncthreads();
   }
-  const uint32_t T = prefix;   // k_top-th largest key; take krem of the keys equal to T
+  const uint32_t T = kmin + hi;   // k_top-th largest key; take krem of the keys equal to T
 
   // ---- ordered emission, round by round.  The round's keys are transposed
   // through LDS (word j at j + j/64: conflict-free both ways) so that thread t
-  // owns the 64 consecutive candidates [64t, 64t + 64); per-thread counts, two
-  // workgroup scans for the offsets, then each thread writes its kept positions
-  // in order: the output is ascending without a sort.
+  // owns the 64 consecutive candidates [64t, 64t + 64); per-thread counts and
+  // two workgroup scans give each thread its output offset; the kept
+  // positions go to LDS in order and then out with coalesced stores, so the
+  // output is ascending without a sort.
   uint32_t eq_carry = 0, out_carry = 0;
   for (int r = 0; r < rounds; ++r) {
     if (rounds > 1) {
-      __syncthreads();   // the previous round's readers are done with `tr`
+      __syncthreads();   // the previous round's copy-out is done with `tr`
       load_round(v, c, r, key);
     }
     const int j0 = r * kRound + lbase;
@@ -177,21 +226,24 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
       n_eq += (e < valid && mine[e] == T) ? 1u : 0u;
     }
     uint32_t eq_tot, take_tot;
-    const uint32_t eq_b = block_excl_scan(n_eq, wsum, &eq_tot) + eq_carry;
+    const uint32_t eq_b = block_excl_scan(n_eq, wsum, &eq_tot) + eq_carry;   // also orders tr reads before writes
     const uint32_t room = krem > eq_b ? krem - eq_b : 0u;
     const uint32_t n_take = n_gt + (n_eq < room ? n_eq : room);
-    uint32_t pos = block_excl_scan(n_take, wsum, &take_tot) + out_carry;
+    uint32_t pos = block_excl_scan(n_take, wsum, &take_tot);   // offset within this round's output
     uint32_t eq_left = n_eq < room ? n_eq : room;    // T-valued candidates this thread keeps
-    const int jb = r * kRound + seg;
+    const uint32_t jb = (uint32_t)(r * kRound + seg);
 #pragma unroll
     for (int e = 0; e < kVPL; ++e) {
       const bool in = e < valid;
       const bool eq = in && mine[e] == T;
       const bool take = (in && mine[e] > T) || (eq && eq_left > 0);
       eq_left -= (eq && eq_left > 0) ? 1u : 0u;
-      if (take && pos < (uint32_t)k_top) o[pos] = jb + e;
+      if (take) tr[pos] = jb + e;                    // pos < take_tot <= kRound
       pos += take ? 1u : 0u;
     }
+    __syncthreads();
+    const uint32_t n_out = min(take_tot, (uint32_t)k_top - min(out_carry, (uint32_t)k_top));
+    for (uint32_t t = tid; t < n_out; t += kSelThreads) o[out_carry + t] = (int32_t)tr[t];
     eq_carry += eq_tot;
     out_carry += take_tot;
   }

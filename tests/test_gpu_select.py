@@ -45,6 +45,10 @@ def _ref_select(imp32, **kw):
     (2, 3000, 10, 0, 500, "equal"),             # all scores equal -> lowest positions
     (2, 3000, 10, 5, 700, "zeros_denorm"),      # zeros and denormals
     (8, 131072, 64, 64, 26214, "exp"),          # the 131072-token long-context shape
+    (4, 40000, 64, 64, 5000, "narrow"),         # near-uniform scores: a tiny key range, 2 rounds
+    (4, 9000, 64, 64, 2000, "signed"),          # negative and positive scores
+    (2, 9000, 64, 64, 1000, "wide"),            # keys spanning all 32 bits, +-inf included
+    (2, 70016, 16, 16, 30000, "ties3"),         # three rounds; equal keys straddle round borders
 ])
 def test_select_bit_exact(Hkv, S, w, recent, budget, kind):
     rng = np.random.default_rng(S + budget)
@@ -55,6 +59,13 @@ def test_select_bit_exact(Hkv, S, w, recent, budget, kind):
         imp = (rng.integers(0, 3, size=(Hkv, n)) / 7.0).astype(np.float32)
     elif kind == "equal":
         imp = np.full((Hkv, n), 1.0 / n, dtype=np.float32)
+    elif kind == "narrow":
+        imp = ((1.0 + 1e-4 * rng.standard_normal(size=(Hkv, n))) / n).astype(np.float32)
+    elif kind == "signed":
+        imp = rng.standard_normal(size=(Hkv, n)).astype(np.float32)
+    elif kind == "wide":
+        imp = rng.choice(np.array([-np.inf, -1e30, -1.0, -0.0, 0.0, 1e-30, 1.0, 1e30, np.inf],
+                                  dtype=np.float32), size=(Hkv, n))
     else:
         imp = rng.choice(np.array([0.0, 1e-42, 3e-40, 1e-38, 0.5], dtype=np.float32), size=(Hkv, n))
     gpu = _gpu_select(imp, S=S, w=w, recent=recent, budget=budget)
