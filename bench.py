@@ -14,9 +14,11 @@ events that libkvc records around each launch on the launch stream
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -72,6 +74,7 @@ def algorithmic(wl):
         T = int(math.floor((1 - wl.think_lambda) * D))
         kr = Hkv * (wl.budget - wl.recent)
         step_bytes += kr * D * 2 + kr * T * 2
+    # per step (bench divides by the launches per step): bound, flops, algorithmic bytes
     per_kernel = {
         "score_pass1": ("mfma", flops_pass, q_bytes + k_prefix),
         "score_pass2": ("mfma", flops_pass, q_bytes + k_prefix + imp),
@@ -79,8 +82,39 @@ def algorithmic(wl):
         "score_pass2_gumbel": ("mfma", flops_pass, q_bytes + k_prefix + imp),
         "select_topk": ("hbm", 0.0, imp + B_total * 4),
         "compact": ("hbm", 0.0, 2 * rows * 2 + B_total * 4),
+        "lmba_mba": ("hbm", 0.0, imp),
     }
+    if wl.think_lambda >= 0:
+        T = int(math.floor((1 - wl.think_lambda) * D))
+        kr = Hkv * (wl.budget - wl.recent)
+        per_kernel["think_partial"] = ("hbm", 0.0, kr * D * 2)
+        per_kernel["think_gather"] = ("hbm", 0.0, kr * D * 2 + kr * T * 2)
     return step_bytes, flops_pass, per_kernel
+
+
+KERNEL_SOURCE = {"score": "score.hip", "select": "select.hip", "compact": "compact.hip", "lmba": "budget.hip",
+                 "think": "think.hip"}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (profiles/hbm_traffic_<workload>.md), or None if there is none or the kernel's
+    source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    csrc = os.path.join(ROOT, "kv_cache_compression_bf16_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("common.h", KERNEL_SOURCE[kernel.split("_")[0]]):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    for line in open(path):
+        m = re.match(r"traffic kernel=(\S+) read_bytes=(\d+) write_bytes=(\d+) source=\S+ sha256_16=([0-9a-f]+)", line)
+        if m and m.group(1) == kernel:
+            if m.group(4) != h.hexdigest()[:16]:
+                return None
+            return int(m.group(2)) + int(m.group(3))
+    return None
 
 
 def cpu_baseline(wl, data, target_s, tau):
@@ -95,12 +129,13 @@ def cpu_baseline(wl, data, target_s, tau):
     kraw = k if wl.L == 1 else k[0]
     vraw = v if wl.L == 1 else v[0]
     scale = float(np.float32(1.0 / math.sqrt(wl.D)))
+    B = wl.budget if wl.budget else wl.total_budget // wl.L
+    # whole KV heads of layer 0, cycling over the heads until the time target
     heads, t0 = 0, time.perf_counter()
-    while heads < wl.Hkv:
-        g = heads
+    while True:
+        g = heads % wl.Hkv
         imp = oracle.score.importance(qf, kf, S=wl.S, w=wl.w, scale=scale, gumbel=wl.gumbel, tau=tau,
                                       seed=wl.noise_seed, kv_heads=[g])
-        B = wl.budget if wl.budget else wl.total_budget // wl.L
         idx = oracle.select.select(imp[g], S=wl.S, w=wl.w, recent=wl.recent, budget=B)
         oracle.compact.compact(kraw[g:g + 1], idx[None])
         oracle.compact.compact(vraw[g:g + 1], idx[None])
@@ -109,9 +144,10 @@ def cpu_baseline(wl, data, target_s, tau):
             break
     dt = time.perf_counter() - t0
     threads = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
-    tokens = wl.S * heads / wl.Hkv        # one layer's prompt, heads/Hkv of its work
+    tokens = wl.S * heads / wl.Hkv        # one layer's prompt per Hkv heads of work
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{heads} of {wl.Hkv} KV heads of layer 0 (score+select+compact, fp64 numpy), {dt:.1f} s"}
+            "sample": f"{heads} KV-head passes over layer 0 ({wl.Hkv} heads per layer; score+select+compact, "
+                      f"fp64 numpy), {dt:.1f} s"}
 
 
 def main():
@@ -180,20 +216,24 @@ def main():
     kernels = {name: {"launches": c, "avg_us": 1e3 * ms / c} for name, (c, ms) in kt.items()}
     dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
     avg_s = kernels[dom]["avg_us"] / 1e6
+    per_launch = args.steps / kernels[dom]["launches"]     # one step's figure -> one launch's
     bound, flops, nbytes = per_kernel.get(dom, ("hbm", 0.0, 0))
+    traffic = measured_traffic(dom, wl.name)
     if bound == "mfma":
-        achieved = flops / avg_s / 1e12
+        achieved = flops * per_launch / avg_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
     else:
-        achieved = nbytes / avg_s / 1e9
+        achieved = nbytes * per_launch / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
     roof["kernel"] = dom
+    roof["alg_bytes_per_launch"] = nbytes * per_launch
     for name, kk in kernels.items():
         b, f, nb = per_kernel.get(name, ("", 0.0, 0))
-        kk["alg_TFLOPs"] = round(f / (kk["avg_us"] / 1e6) / 1e12, 2) if f else None
-        kk["alg_GBs"] = round(nb / (kk["avg_us"] / 1e6) / 1e9, 1) if nb else None
+        pl = args.steps / kk["launches"]
+        kk["alg_TFLOPs"] = round(f * pl / (kk["avg_us"] / 1e6) / 1e12, 2) if f else None
+        kk["alg_GBs"] = round(nb * pl / (kk["avg_us"] / 1e6) / 1e9, 1) if nb else None
         kk["avg_us"] = round(kk["avg_us"], 2)
 
     cpu = None
