@@ -23,6 +23,10 @@ int launch_begin(const char* name, hipStream_t s);
 kvc_status launch_end(int slot, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Compute units of the current device (queried once per device), or 0 if the
+// query fails.
+int device_cu_count();
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace kvc

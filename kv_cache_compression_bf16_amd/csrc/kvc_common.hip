@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
 #include <map>
 #include <string>
 #include <vector>
@@ -10,6 +11,21 @@
 #include "common.h"
 
 namespace kvc {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];   // per device id; 0 = not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 namespace {
 
 struct Record {

@@ -48,21 +48,27 @@ constexpr int kD = 128;
 // bank groups, and the 8 chunk reads of a lane are one base + immediates.
 constexpr int kRowPitch = kD * 2 + 16;
 
-// Waves per workgroup and staged rows per chunk (32 per wave, so LDS holds 4
-// waves per SIMD: 160 KB per CU).  The Keyformer passes need more registers
-// for Philox (about 150 VGPRs, 3 waves per SIMD), so they always use 4 waves
-// and 128-row chunks.
-#ifndef KVC_SCORE_MAX_WAVES
-#define KVC_SCORE_MAX_WAVES 16
-#endif
-inline int score_waves(int R, bool gumbel) {
-  if (gumbel) return 4;
-  const int kw = R <= 128 ? 4 : (R <= 256 ? 8 : 16);
-  return kw < KVC_SCORE_MAX_WAVES ? kw : KVC_SCORE_MAX_WAVES;
+// Shape of a scoring workgroup: kw waves, kt 32-key tiles per wave, and up to
+// 32*cb staged query rows per chunk.  A unit of work is 32*kw*kt consecutive
+// prefix keys of one KV head.
+//  * R > 256: 8 waves x 2 tiles, 512-row chunks (one workgroup per CU, 2 waves
+//    per SIMD, each with two independent MFMA chains and room for the next
+//    unit's keys in registers);
+//  * R <= 256: 4 waves x 2 tiles, chunks of up to 256 rows;
+//  * Keyformer noise: 4 waves x 1 tile, 128-row chunks (Philox needs the
+//    registers).
+struct Shape {
+  int kw, kt, cb;
+};
+inline Shape score_shape(int R, bool gumbel) {
+  if (gumbel) return {4, 1, 4};
+  if (R > 256) return {8, 2, 16};
+  return {4, 2, 8};
 }
-inline int score_chunk_rows(int R, int kw) { return min((R + 31) / 32 * 32, 32 * kw); }
-inline size_t score_lds_bytes(int rows, bool pass2) {
-  return (size_t)rows * kRowPitch + (pass2 ? (size_t)rows * sizeof(float) : 0);
+inline int score_chunk_rows(int R, const Shape& sh) { return min((R + 31) / 32 * 32, 32 * sh.cb); }
+inline size_t score_lds_bytes(int rows, int kw, bool pass2) {
+  // staged rows, then the row constants (pass 2) or the 4-block fold strip (pass 1)
+  return (size_t)rows * kRowPitch + (pass2 ? (size_t)rows * sizeof(float) : (size_t)4 * 32 * kw * 2 * sizeof(float));
 }
 
 struct ScoreParams {
@@ -113,39 +119,23 @@ __device__ __forceinline__ float gumbel_log2_from_word(uint32_t x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <bool kPass2, bool kGumbel, int kW>
-__global__ __launch_bounds__(kW * kWave) void score_pass(ScoreParams p) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];   // [rows][kRowPitch] (+ [rows] rowc)
+template <bool kPass2, bool kGumbel, int kW, int kT, int kCB>
+__global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreParams p) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int kThreads = kW * kWave;
-  constexpr int kKeysPerBlock = 32 * kW;
+  constexpr int kKeysPerWave = 32 * kT;
+  constexpr int kKeysPerUnit = kKeysPerWave * kW;
+  constexpr int kFoldBlocks = 4;
 
-  const int blk = blockIdx.x, g = blockIdx.y, layer = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hb = lane >> 5, col = lane & 31;
-  const int key0 = blk * kKeysPerBlock + wave * 32;
-  const bool wave_full = key0 + 32 <= p.n;      // no key of this wave past the prefix
-  const float alpha = p.layer_scales ? p.layer_scales[layer] : p.scale;
-  const float c = alpha * kLog2e;
-  const int64_t head_row0 = ((int64_t)layer * p.Hkv + g) * p.R;
   const int rows_alloc = p.chunk_rows;
-  float* rcs = reinterpret_cast<float*>(lds + (size_t)rows_alloc * kRowPitch);
+  float* rcs = reinterpret_cast<float*>(lds + (size_t)rows_alloc * kRowPitch);    // pass 2: [rows]
+  float* fold = reinterpret_cast<float*>(lds + (size_t)rows_alloc * kRowPitch);   // pass 1: [kW][128][2]
 
-  // ---- K fragments: lane holds key (col), 16-byte chunk (2s + hb).
-  bf16x8 kf[8];
-  {
-    const uint16_t* kb = p.k + layer * p.k_ls + g * p.k_hs;
-    const int j = min(key0 + col, p.n - 1);   // clamp: keys past the prefix are masked
-    const bf16x8* row = reinterpret_cast<const bf16x8*>(kb + (int64_t)j * kD);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) kf[s] = row[2 * s + hb];
-  }
-
-  // ---- stage query rows [c0, c0 + nrows) into LDS (zero rows past R), 8
-  // independent 16-byte loads in flight per thread, addresses clamped.
-  const uint16_t* qg = p.q + layer * p.q_ls + (int64_t)g * p.G * p.q_hs;
   // row r -> (query head r / w, window offset r % w): a float estimate of the
-  // quotient, then one exact integer correction (r < 2^16, so the estimate is
-  // off by at most one).
+  // quotient, then one exact integer correction (r < 2^16 + 32, so the
+  // estimate is off by at most one).
   const float inv_w = 1.0f / (float)p.w;
   auto split_row = [&](int r, int& hh, int& ii) {
     hh = (int)((float)r * inv_w);
@@ -153,171 +143,247 @@ __global__ __launch_bounds__(kW * kWave) void score_pass(ScoreParams p) {
     if (ii < 0) { --hh; ii += p.w; }
     if (ii >= p.w) { ++hh; ii -= p.w; }
   };
-  auto stage = [&](int c0, int nrows) {
-    const int total = nrows * 16;
-    for (int base = 0; base < total; base += 8 * kThreads) {
-      u32x4 v[8];
+
+  // This workgroup's contiguous range of units u = (layer*Hkv + g)*nblk + blk.
+  const int total = p.L * p.Hkv * p.nblk;
+  const int per = total / (int)gridDim.x, extra = total % (int)gridDim.x;
+  const int u0 = (int)blockIdx.x * per + min((int)blockIdx.x, extra);
+  const int u1 = u0 + per + ((int)blockIdx.x < extra ? 1 : 0);
+
+  // K fragments of unit u: lane holds key (32t + col) of its wave's tiles,
+  // 16-byte chunk (2s + hb), already in the MFMA A-operand layout.
+  auto load_k = [&](int u, bf16x8 (&dst)[kT][8]) {
+    const int head = u / p.nblk, blk = u - head * p.nblk;
+    const int layer = head / p.Hkv, g = head - layer * p.Hkv;
+    const uint16_t* kb = p.k + layer * p.k_ls + g * p.k_hs;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * kThreads + tid;
-        const int r = min(c0 + (i >> 4), p.R - 1);
-        int hh, ii;
-        split_row(r, hh, ii);
-        v[u] = *reinterpret_cast<const u32x4*>(qg + hh * p.q_hs + (int64_t)ii * kD + (i & 15) * 8);
-      }
+    for (int t = 0; t < kT; ++t) {
+      const int j = min(blk * kKeysPerUnit + wave * kKeysPerWave + t * 32 + col, p.n - 1);   // clamp; masked
+      const bf16x8* row = reinterpret_cast<const bf16x8*>(kb + (int64_t)j * kD);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * kThreads + tid;
-        if (i < total) {
-          const bool ok = c0 + (i >> 4) < p.R;
-          *reinterpret_cast<u32x4*>(lds + (i >> 4) * kRowPitch + (i & 15) * 16) = ok ? v[u] : u32x4{0u, 0u, 0u, 0u};
+      for (int s = 0; s < 8; ++s) dst[t][s] = row[2 * s + hb];
+    }
+  };
+
+  // The next unit's keys are prefetched into a second register set while a
+  // unit computes; the Keyformer passes skip that (their Philox registers
+  // would cost a wave per SIMD) and load each unit's keys at its start.
+  constexpr bool kPrefetch = !kGumbel;
+  bf16x8 kf[kT][8], kn[kPrefetch ? kT : 1][8];
+  if (u0 < u1) load_k(u0, kf);
+  int staged = -1;   // head whose query rows are in LDS (single-chunk case)
+  for (int u = u0; u < u1; ++u) {
+    const int head = u / p.nblk, blk = u - head * p.nblk;
+    const int layer = head / p.Hkv, g = head - layer * p.Hkv;
+    const bool has_next = u + 1 < u1;
+    if constexpr (kPrefetch) {
+      if (has_next) load_k(u + 1, kn);   // lands while this unit computes
+    } else {
+      if (u != u0) load_k(u, kf);
+    }
+    const int key0 = blk * kKeysPerUnit + wave * kKeysPerWave;
+    const bool wave_full = key0 + kKeysPerWave <= p.n;   // no key of this wave past the prefix
+    const float alpha = p.layer_scales ? p.layer_scales[layer] : p.scale;
+    const float c = alpha * kLog2e;
+    // logit -> log2 units is fmaf(v, cc, -ref); the Keyformer path is already there
+    const float cc = kGumbel ? 1.0f : c;
+    const int64_t head_row0 = (int64_t)head * p.R;
+    const uint16_t* qg = p.q + layer * p.q_ls + (int64_t)g * p.G * p.q_hs;
+
+    // stage query rows [c0, c0 + nrows) into LDS (zero rows past R), 8
+    // independent 16-byte loads in flight per thread, addresses clamped.
+    auto stage = [&](int c0, int nrows) {
+      const int tot = nrows * 16;
+      for (int base = 0; base < tot; base += 8 * kThreads) {
+        u32x4 v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = base + e * kThreads + tid;
+          const int r = min(c0 + (i >> 4), p.R - 1);
+          int hh, ii;
+          split_row(r, hh, ii);
+          v[e] = *reinterpret_cast<const u32x4*>(qg + hh * p.q_hs + (int64_t)ii * kD + (i & 15) * 8);
         }
-      }
-    }
-    if (kPass2)
-      for (int i = tid; i < nrows; i += kThreads) {
-        const int r = c0 + i;
-        rcs[i] = r < p.R ? p.rowc[head_row0 + r] : INFINITY;
-      }
-  };
-
-  // A operand from registers, B operand (32 query rows) from LDS:
-  // acc[r] = <K[key], Q[row]>, key = key0 + 8(r/4) + 4hb + (r%4), row = 32qb + col.
-  auto mfma_block = [&](int qb) -> f32x16 {
-    const char* qsb = lds + (qb * 32 + col) * kRowPitch + hb * 16;
-    f32x16 acc = f32x16{};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qsb + 32 * s);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf, acc, 0, 0, 0);
-    }
-    return acc;
-  };
-  // Keyformer path: t = (alpha x + zeta) * log2(e) / tau, in place, for row r.
-  auto noisy = [&](f32x16& acc, int r) {
-    int hh, i;
-    split_row(r, hh, i);
-    const uint32_t h = (uint32_t)(g * p.G + hh);
-    const uint32_t pos = (uint32_t)(p.S - p.w + i);
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const uint32_t j0 = (uint32_t)(key0 + 8 * r4 + 4 * hb);
-      const u32x4 x = philox4x32_10(u32x4{j0 >> 2, pos, h, 0u}, p.seed_lo, p.seed_hi);
-      acc[4 * r4 + 0] = fmaf(acc[4 * r4 + 0], c, gumbel_log2_from_word(x.x)) * p.inv_tau;
-      acc[4 * r4 + 1] = fmaf(acc[4 * r4 + 1], c, gumbel_log2_from_word(x.y)) * p.inv_tau;
-      acc[4 * r4 + 2] = fmaf(acc[4 * r4 + 2], c, gumbel_log2_from_word(x.z)) * p.inv_tau;
-      acc[4 * r4 + 3] = fmaf(acc[4 * r4 + 3], c, gumbel_log2_from_word(x.w)) * p.inv_tau;
-    }
-  };
-  // logit -> log2 units is fmaf(v, cc, -ref); the Keyformer path is already there
-  const float cc = kGumbel ? 1.0f : c;
-
-  // Pass 1, one query block: this wave's (max, sum of exp2) of the lane's row
-  // over its 32 keys; lanes of half-wave 0 return the max, half-wave 1 the sum.
-  auto row_stats = [&](auto clean_c, f32x16 acc, int r) -> float {
-    constexpr bool kClean = decltype(clean_c)::value;
-    if (!kClean) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = key0 + 8 * (e >> 2) + 4 * hb + (e & 3);
-        if (key >= p.n || r >= p.R) acc[e] = -INFINITY;
-      }
-    }
-    float mx = acc[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, acc[e]);
-    const float mt = mx * cc;
-    const float mts = (mx == -INFINITY) ? 0.f : mt;
-    float l = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) l += fast_exp2(fmaf(acc[e], cc, -mts));
-    // fold with the other half-wave (same query row, the other 16 keys)
-    const float mo = __shfl_xor(mt, 32), lo = __shfl_xor(l, 32);
-    const float m2 = fmaxf(mt, mo);
-    const float m2s = (m2 == -INFINITY) ? 0.f : m2;
-    const float l2 = l * fast_exp2(mt - m2s) + lo * fast_exp2(mo - m2s);
-    return hb ? l2 : m2;
-  };
-
-  f32x16 colacc = f32x16{};
-  for (int c0 = 0; c0 < p.R; c0 += rows_alloc) {
-    const int nrows = min(rows_alloc, (p.R - c0 + 31) / 32 * 32);
-    const int nb = nrows / 32;
-    const bool rows_full = c0 + nrows <= p.R;
-    stage(c0, nrows);
-    __syncthreads();
-    if (!kPass2) {
-      // per-block partials stay in registers until the chunk is done
-      float st[kW];
-      auto blocks = [&](auto clean_c) {
-#pragma unroll
-        for (int qb = 0; qb < kW; ++qb) {
-          st[qb] = 0.f;
-          if (qb < nb) {
-            f32x16 acc = mfma_block(qb);
-            const int r = c0 + qb * 32 + col;
-            if (kGumbel) noisy(acc, r);
-            st[qb] = row_stats(clean_c, acc, r);
+        for (int e = 0; e < 8; ++e) {
+          const int i = base + e * kThreads + tid;
+          if (i < tot) {
+            const bool ok = c0 + (i >> 4) < p.R;
+            *reinterpret_cast<u32x4*>(lds + (i >> 4) * kRowPitch + (i & 15) * 16) = ok ? v[e] : u32x4{0u, 0u, 0u, 0u};
           }
         }
-      };
-      if (wave_full && rows_full)
-        blocks(std::true_type{});
-      else
-        blocks(std::false_type{});
-      __syncthreads();   // every wave is done with the staged rows: reuse them
-      float* red = reinterpret_cast<float*>(lds);   // [kW][nrows][2] = (max, sum)
-#pragma unroll
-      for (int qb = 0; qb < kW; ++qb)
-        if (qb < nb) red[(wave * nrows + qb * 32 + col) * 2 + hb] = st[qb];
-      __syncthreads();
-      for (int i = tid; i < nrows; i += kThreads) {
-        const int r = c0 + i;
-        if (r >= p.R) continue;
-        float m = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < kW; ++v) m = fmaxf(m, red[(v * nrows + i) * 2]);
-        const float ms = (m == -INFINITY) ? 0.f : m;
-        float l = 0.f;
-#pragma unroll
-        for (int v = 0; v < kW; ++v) l += red[(v * nrows + i) * 2 + 1] * fast_exp2(red[(v * nrows + i) * 2] - ms);
-        p.part[head_row0 * p.nblk + (int64_t)blk * p.R + r] = float2{m, l};
       }
-    } else {
-      auto blocks = [&](auto clean_c) {
-        constexpr bool kClean = decltype(clean_c)::value;
-        (void)kClean;
+      if (kPass2)
+        for (int i = tid; i < nrows; i += kThreads) {
+          const int r = c0 + i;
+          rcs[i] = r < p.R ? p.rowc[head_row0 + r] : INFINITY;
+        }
+    };
+    // A operands from registers, B operand (32 query rows) from LDS:
+    // acc[t][e] = <K[key], Q[row]>, key = key0 + 32t + 8(e/4) + 4hb + (e%4), row = 32qb + col.
+    auto mfma_block = [&](int qb, f32x16 (&acc)[kT]) {
+      const char* qsb = lds + (qb * 32 + col) * kRowPitch + hb * 16;
+#pragma unroll
+      for (int t = 0; t < kT; ++t) acc[t] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qsb + 32 * s);
+#pragma unroll
+        for (int t = 0; t < kT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], qf, acc[t], 0, 0, 0);
+      }
+    };
+    // Keyformer path: t = (alpha x + zeta) * log2(e) / tau, in place, for row r.
+    auto noisy = [&](f32x16 (&acc)[kT], int r) {
+      int hh, i;
+      split_row(r, hh, i);
+      const uint32_t h = (uint32_t)(g * p.G + hh);
+      const uint32_t pos = (uint32_t)(p.S - p.w + i);
+#pragma unroll
+      for (int t = 0; t < kT; ++t)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const uint32_t j0 = (uint32_t)(key0 + 32 * t + 8 * r4 + 4 * hb);
+          const u32x4 x = philox4x32_10(u32x4{j0 >> 2, pos, h, 0u}, p.seed_lo, p.seed_hi);
+          acc[t][4 * r4 + 0] = fmaf(acc[t][4 * r4 + 0], c, gumbel_log2_from_word(x.x)) * p.inv_tau;
+          acc[t][4 * r4 + 1] = fmaf(acc[t][4 * r4 + 1], c, gumbel_log2_from_word(x.y)) * p.inv_tau;
+          acc[t][4 * r4 + 2] = fmaf(acc[t][4 * r4 + 2], c, gumbel_log2_from_word(x.z)) * p.inv_tau;
+          acc[t][4 * r4 + 3] = fmaf(acc[t][4 * r4 + 3], c, gumbel_log2_from_word(x.w)) * p.inv_tau;
+        }
+    };
+    // Pass 1, one query block: this wave's (max, sum of exp2) of the lane's row
+    // over its keys; lanes of half-wave 0 return the max, half-wave 1 the sum.
+    auto row_stats = [&](auto clean_c, f32x16 (&acc)[kT], int r) -> float {
+      constexpr bool kClean = decltype(clean_c)::value;
+      if (!kClean) {
+#pragma unroll
+        for (int t = 0; t < kT; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = key0 + 32 * t + 8 * (e >> 2) + 4 * hb + (e & 3);
+            if (key >= p.n || r >= p.R) acc[t][e] = -INFINITY;
+          }
+      }
+      float mx = acc[0][0];
+#pragma unroll
+      for (int t = 0; t < kT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[t][e]);
+      const float mt = mx * cc;
+      const float mts = (mx == -INFINITY) ? 0.f : mt;
+      float l = 0.f;
+#pragma unroll
+      for (int t = 0; t < kT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) l += fast_exp2(fmaf(acc[t][e], cc, -mts));
+      // fold with the other half-wave (same query row, the other keys of each group)
+      const float mo = __shfl_xor(mt, 32), lo = __shfl_xor(l, 32);
+      const float m2 = fmaxf(mt, mo);
+      const float m2s = (m2 == -INFINITY) ? 0.f : m2;
+      const float l2 = l * fast_exp2(mt - m2s) + lo * fast_exp2(mo - m2s);
+      return hb ? l2 : m2;
+    };
+
+    f32x16 colacc[kT];
+#pragma unroll
+    for (int t = 0; t < kT; ++t) colacc[t] = f32x16{};
+    for (int c0 = 0; c0 < p.R; c0 += rows_alloc) {
+      const int nrows = min(rows_alloc, (p.R - c0 + 31) / 32 * 32);
+      const int nb = nrows / 32;
+      const bool rows_full = c0 + nrows <= p.R;
+      if (p.R > rows_alloc || head != staged) {
+        __syncthreads();   // every wave is done with the previous rows
+        stage(c0, nrows);
+        __syncthreads();
+        staged = head;
+      }
+      if (!kPass2) {
+        float st[kCB];   // per-block partials stay in registers until the chunk is done
+        auto blocks = [&](auto clean_c) {
+#pragma unroll
+          for (int qb = 0; qb < kCB; ++qb) {
+            st[qb] = 0.f;
+            if (qb < nb) {
+              f32x16 acc[kT];
+              mfma_block(qb, acc);
+              const int r = c0 + qb * 32 + col;
+              if (kGumbel) noisy(acc, r);
+              st[qb] = row_stats(clean_c, acc, r);
+            }
+          }
+        };
+        if (wave_full && rows_full)
+          blocks(std::true_type{});
+        else
+          blocks(std::false_type{});
+        // fold the waves, kFoldBlocks query blocks at a time, in a fixed order
+#pragma unroll
+        for (int f0 = 0; f0 < kCB; f0 += kFoldBlocks) {
+          if (f0 < nb) {
+#pragma unroll
+            for (int qq = 0; qq < kFoldBlocks; ++qq)
+              if (f0 + qq < kCB && f0 + qq < nb) fold[((wave * kFoldBlocks + qq) * 32 + col) * 2 + hb] = st[f0 + qq];
+            __syncthreads();
+            for (int i = tid; i < kFoldBlocks * 32; i += kThreads) {
+              const int rr = f0 * 32 + i, r = c0 + rr;
+              if (rr < nrows && r < p.R) {
+                float m = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < kW; ++v) m = fmaxf(m, fold[(v * kFoldBlocks * 32 + i) * 2]);
+                const float ms = (m == -INFINITY) ? 0.f : m;
+                float l = 0.f;
+#pragma unroll
+                for (int v = 0; v < kW; ++v)
+                  l += fold[(v * kFoldBlocks * 32 + i) * 2 + 1] * fast_exp2(fold[(v * kFoldBlocks * 32 + i) * 2] - ms);
+                p.part[head_row0 * p.nblk + (int64_t)blk * p.R + r] = float2{m, l};
+              }
+            }
+            __syncthreads();
+          }
+        }
+      } else {
         for (int qb = 0; qb < nb; ++qb) {
-          f32x16 acc = mfma_block(qb);
+          f32x16 acc[kT];
+          mfma_block(qb, acc);
           if (kGumbel) noisy(acc, c0 + qb * 32 + col);
           const float rc = rcs[qb * 32 + col];   // +inf for rows past R: adds 0
 #pragma unroll
-          for (int e = 0; e < 16; ++e) colacc[e] += fast_exp2(fmaf(acc[e], cc, -rc));
-        }
-      };
-      blocks(std::true_type{});
-    }
-    __syncthreads();   // before the next chunk overwrites the staged rows
-  }
-
-  if (!kPass2) return;
-
-  // ---- pass 2: sum each key column over the 32 query lanes of its half-wave.
-  float* out = p.imp + ((int64_t)layer * p.Hkv + g) * p.n;
-  float mine = 0.f;
+          for (int t = 0; t < kT; ++t)
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    float v = colacc[e];
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 8);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 1);
-    if (col == e) mine = v;
-  }
-  if (col < 16) {
-    const int key = key0 + 8 * (col >> 2) + 4 * hb + (col & 3);
-    if (key < p.n) out[key] = mine * p.inv_w;
+            for (int e = 0; e < 16; ++e) colacc[t][e] += fast_exp2(fmaf(acc[t][e], cc, -rc));
+        }
+      }
+    }
+
+    if (kPass2) {
+      // sum each key column over the 32 query lanes of its half-wave
+      float* out = p.imp + (int64_t)head * p.n;
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        float mine = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float v = colacc[t][e];
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 8);
+          v += __shfl_xor(v, 4);
+          v += __shfl_xor(v, 2);
+          v += __shfl_xor(v, 1);
+          if (col == e) mine = v;
+        }
+        if (col < 16) {
+          const int key = key0 + 32 * t + 8 * (col >> 2) + 4 * hb + (col & 3);
+          if (key < p.n) out[key] = mine * p.inv_w;
+        }
+      }
+    }
+    if constexpr (kPrefetch) {
+      if (has_next) {
+#pragma unroll
+        for (int t = 0; t < kT; ++t)
+#pragma unroll
+          for (int s = 0; s < 8; ++s) kf[t][s] = kn[t][s];
+      }
+    }
   }
 }
 
@@ -359,7 +425,8 @@ __global__ __launch_bounds__(256) void score_combine(ScoreParams p, int heads) {
 }
 
 struct Plan {
-  int n, G, R, kw, nblk, chunk_rows;
+  int n, G, R, nblk, chunk_rows;
+  Shape shape;
   size_t part_bytes, rowc_bytes, total;
 };
 
@@ -382,9 +449,10 @@ kvc_status plan(const kvc_score_args* a, Plan* pl) {
   pl->n = a->S - a->w;
   pl->G = (int)G;
   pl->R = (int)(G * a->w);
-  pl->kw = score_waves(pl->R, a->gumbel != 0);
-  pl->nblk = (pl->n + 32 * pl->kw - 1) / (32 * pl->kw);
-  pl->chunk_rows = score_chunk_rows(pl->R, pl->kw);
+  pl->shape = score_shape(pl->R, a->gumbel != 0);
+  const int unit = 32 * pl->shape.kw * pl->shape.kt;
+  pl->nblk = (pl->n + unit - 1) / unit;
+  pl->chunk_rows = score_chunk_rows(pl->R, pl->shape);
   const size_t rows = (size_t)a->L * a->Hkv * pl->R;
   pl->part_bytes = align_up(rows * pl->nblk * sizeof(float2), 256);
   pl->rowc_bytes = align_up(rows * sizeof(float), 256);
@@ -392,26 +460,37 @@ kvc_status plan(const kvc_score_args* a, Plan* pl) {
   return KVC_OK;
 }
 
-// Pass 1, combine, pass 2 on one stream, kW waves per scoring workgroup.
-template <int kW>
-kvc_status launch_score(const ScoreParams& p, const Plan& pl, bool gumbel, hipStream_t s) {
-  const dim3 grid(pl.nblk, p.Hkv, p.L), block(kW * kWave);
+// Persistent grid for one scoring pass: as many workgroups as fit on the
+// device at once (occupancy x CUs), at most one per unit.
+template <typename K>
+kvc_status score_grid(K kernel, int threads, size_t lds, int units, int* grid) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu < 1)
+    return KVC_E_DEVICE;
+  const int cus = device_cu_count();
+  if (cus < 1) return KVC_E_DEVICE;
+  *grid = units < per_cu * cus ? units : per_cu * cus;
+  return KVC_OK;
+}
+
+// Pass 1, combine, pass 2 on one stream.
+template <bool kGumbel, int kW, int kT, int kCB>
+kvc_status launch_score(const ScoreParams& p, const Plan& pl, hipStream_t s) {
+  constexpr int kThreads = kW * kWave;
+  const int units = p.L * p.Hkv * pl.nblk;
   const int heads = p.L * p.Hkv;
   const dim3 comb_grid(heads * ((pl.R + kCombRows - 1) / kCombRows));
-  const size_t lds1 = score_lds_bytes(pl.chunk_rows, false), lds2 = score_lds_bytes(pl.chunk_rows, true);
-  if (gumbel) {
-    if constexpr (kW == 4) {   // the only shape the Keyformer passes are built for
-      KVC_LAUNCH_SHM("score_pass1_gumbel", (score_pass<false, true, kW>), grid, block, lds1, s, p);
-      KVC_LAUNCH("score_combine", score_combine, comb_grid, dim3(256), s, p, heads);
-      KVC_LAUNCH_SHM("score_pass2_gumbel", (score_pass<true, true, kW>), grid, block, lds2, s, p);
-    } else {
-      return KVC_E_UNSUPPORTED;
-    }
-  } else {
-    KVC_LAUNCH_SHM("score_pass1", (score_pass<false, false, kW>), grid, block, lds1, s, p);
-    KVC_LAUNCH("score_combine", score_combine, comb_grid, dim3(256), s, p, heads);
-    KVC_LAUNCH_SHM("score_pass2", (score_pass<true, false, kW>), grid, block, lds2, s, p);
-  }
+  const size_t lds1 = score_lds_bytes(pl.chunk_rows, kW, false), lds2 = score_lds_bytes(pl.chunk_rows, kW, true);
+  auto k1 = score_pass<false, kGumbel, kW, kT, kCB>;
+  auto k2 = score_pass<true, kGumbel, kW, kT, kCB>;
+  int g1 = 0, g2 = 0;
+  kvc_status st = score_grid(k1, kThreads, lds1, units, &g1);
+  if (st != KVC_OK) return st;
+  st = score_grid(k2, kThreads, lds2, units, &g2);
+  if (st != KVC_OK) return st;
+  KVC_LAUNCH_SHM(kGumbel ? "score_pass1_gumbel" : "score_pass1", k1, dim3(g1), dim3(kThreads), lds1, s, p);
+  KVC_LAUNCH("score_combine", score_combine, comb_grid, dim3(256), s, p, heads);
+  KVC_LAUNCH_SHM(kGumbel ? "score_pass2_gumbel" : "score_pass2", k2, dim3(g2), dim3(kThreads), lds2, s, p);
   return KVC_OK;
 }
 
@@ -460,9 +539,7 @@ extern "C" kvc_status kvc_score(const kvc_score_args* a, const void* q_obs, cons
   p.chunk_rows = pl.chunk_rows;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (pl.kw) {
-    case 4: return launch_score<4>(p, pl, a->gumbel != 0, s);
-    case 8: return launch_score<8>(p, pl, a->gumbel != 0, s);
-    default: return launch_score<16>(p, pl, a->gumbel != 0, s);
-  }
+  if (a->gumbel) return launch_score<true, 4, 1, 4>(p, pl, s);
+  if (pl.shape.kw == 8) return launch_score<false, 8, 2, 16>(p, pl, s);
+  return launch_score<false, 4, 2, 8>(p, pl, s);
 }

@@ -6,7 +6,7 @@
 // (importance descending, position ascending) order are kept together with
 // every position of [S - recent, S); kept positions are written ascending.
 //
-// Design: one 512-thread workgroup per head runs an exact MSB-first radix
+// Design: one 1024-thread workgroup per head runs an exact MSB-first radix
 // select on order-preserving 32-bit keys of the fp32 scores, relative to the
 // head's smallest key: d = key - min, and each level histograms the next (up
 // to) 11 bits below the highest set bit of max - min.  Scores of one head
@@ -24,7 +24,10 @@
 namespace kvc {
 namespace {
 
-constexpr int kSelThreads = 512;
+#ifndef KVC_SEL_THREADS
+#define KVC_SEL_THREADS 1024
+#endif
+constexpr int kSelThreads = KVC_SEL_THREADS;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kBins = 2048;
 constexpr int kBPT = kBins / kSelThreads;   // histogram bins per thread in the scan
@@ -79,13 +82,13 @@ __device__ __forceinline__ void block_min_max(uint32_t& lo, uint32_t& hi, uint32
   __syncthreads();
 }
 
-// Candidates are handled in rounds of kRound = 512 * 64: in round r, wave w
-// owns the contiguous range [r*kRound + w*4096, +4096) and lane l holds
-// candidates base + 64*i + l (i < 64), so every load instruction reads 256
-// contiguous bytes and a lane keeps 64 loads in flight.  With one round (up to
-// 32768 candidates) the keys are loaded once and stay in registers for all
+// Candidates are handled in rounds of kRound = 32768: in round r, wave w owns
+// the contiguous range [r*kRound + w*kSpan, +kSpan) and lane l holds
+// candidates base + 64*i + l (i < kVPL), so every load instruction reads 256
+// contiguous bytes and a lane keeps kVPL loads in flight.  With one round (up
+// to 32768 candidates) the keys are loaded once and stay in registers for all
 // radix levels and both emission passes.
-constexpr int kVPL = 64;
+constexpr int kVPL = 32768 / kSelThreads;          // candidates per lane per round
 constexpr int kSpan = kVPL * kWave;                 // candidates per wave per round
 constexpr int kRound = kSelWaves * kSpan;
 
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
     uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
     for (int e = 0; e < kVPL; ++e) {
-      mine[e] = tr[seg + e + tid];                   // = position seg + e, padded
+      mine[e] = tr[seg + e + ((seg + e) >> 6)];      // = position seg + e, padded
       n_gt += (e < valid && mine[e] > T) ? 1u : 0u;
       n_eq += (e < valid && mine[e] == T) ? 1u : 0u;
     }
