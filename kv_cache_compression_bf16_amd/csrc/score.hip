@@ -6,29 +6,31 @@
 // n = S - w prefix keys, each row is softmax-normalised over the prefix, and
 // the normalised rows are summed into a per-key importance (times 1/w).
 //
-// Design (two passes over the keys, same grid):
-//  * A workgroup owns 32*kW consecutive prefix keys of one KV head, 32 per
-//    wave.  Each wave holds its 32 keys in registers, already in the A operand
-//    layout of v_mfma_f32_32x32x16_bf16, for the whole kernel: K is read from
-//    HBM exactly once per pass, straight into VGPRs.
-//  * The G*w query rows of the group are staged in LDS once per workgroup, in
-//    chunks of up to 32*kW rows (rows padded by 16 bytes so the MFMA B-operand
-//    reads are bank-conflict free).  After that one barrier every wave walks
-//    the query blocks on its own: no barrier and no shared state inside the
-//    block loop, so the 4 waves of each SIMD drift apart and hide each
-//    other's MFMA, LDS and transcendental latencies.  kW is picked so that
-//    LDS holds 4 waves per SIMD (16 waves for 512 rows, 4 for 128 rows).
+// Design (two passes over the keys):
+//  * Work is split into units of 32*kW*kT consecutive prefix keys of one KV
+//    head.  A persistent grid (as many workgroups as fit on the device) gives
+//    each workgroup a contiguous range of units.  Each wave holds its 32*kT
+//    keys of the unit in registers, already in the A operand layout of
+//    v_mfma_f32_32x32x16_bf16: K is read from HBM exactly once per pass,
+//    straight into VGPRs.
+//  * The G*w query rows of the unit's group are staged in LDS in chunks of up
+//    to 32*cb rows (rows padded by 16 bytes so the MFMA B-operand reads are
+//    bank-conflict free) and stay there for the next unit of the same head.
+//    After the staging barrier every wave walks the query blocks on its own:
+//    no barrier and no shared state inside the block loop.  A block's 8 query
+//    fragments are read before its MFMA chains, so LDS latency is paid once
+//    per block.  With kT = 2 each wave runs two independent MFMA chains.
 //  * The tile is computed as K x Q^T, so a lane owns ONE query row and 16 keys
 //    of each 32x32 tile: row statistics (pass 1) and the per-row softmax
 //    constant (pass 2) are per-lane scalars, and column sums over query rows
 //    accumulate in registers across all query blocks; the 32-lane reduction
-//    happens once per wave at the end.  Every key column has a single owner,
-//    so no atomics are used and results are bit-reproducible.
+//    happens once per unit.  Every key column has a single owner, so no
+//    atomics are used and results are bit-reproducible.
 //  * Pass 1 keeps each wave's per-row (max, sum of exp2) in registers and
-//    folds the waves once per chunk, in a fixed order, into per-(row,
-//    workgroup) partials in log2 units; a combine kernel folds those per row
-//    into rowc = m + log2(l); pass 2 recomputes the logits and accumulates
-//    exp2(t - rowc).
+//    folds the waves in a fixed order, 4 query blocks at a time through a
+//    small LDS strip, into per-(row, unit) partials in log2 units; a combine
+//    kernel folds those per row into rowc = m + log2(l); pass 2 recomputes
+//    the logits and accumulates exp2(t - rowc).
 //  * Keyformer noise: lane values come in groups of 4 consecutive, 4-aligned
 //    keys, which is exactly one Philox4x32-10 block, so every Philox call is
 //    fully used.
@@ -52,8 +54,7 @@ constexpr int kRowPitch = kD * 2 + 16;
 // 32*cb staged query rows per chunk.  A unit of work is 32*kw*kt consecutive
 // prefix keys of one KV head.
 //  * R > 256: 8 waves x 2 tiles, 512-row chunks (one workgroup per CU, 2 waves
-//    per SIMD, each with two independent MFMA chains and room for the next
-//    unit's keys in registers);
+//    per SIMD, each with two independent MFMA chains);
 //  * R <= 256: 4 waves x 2 tiles, chunks of up to 256 rows;
 //  * Keyformer noise: 4 waves x 1 tile, 128-row chunks (Philox needs the
 //    registers).
@@ -165,22 +166,13 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
     }
   };
 
-  // The next unit's keys are prefetched into a second register set while a
-  // unit computes; the Keyformer passes skip that (their Philox registers
-  // would cost a wave per SIMD) and load each unit's keys at its start.
-  constexpr bool kPrefetch = !kGumbel;
-  bf16x8 kf[kT][8], kn[kPrefetch ? kT : 1][8];
+  bf16x8 kf[kT][8];
   if (u0 < u1) load_k(u0, kf);
   int staged = -1;   // head whose query rows are in LDS (single-chunk case)
   for (int u = u0; u < u1; ++u) {
     const int head = u / p.nblk, blk = u - head * p.nblk;
     const int layer = head / p.Hkv, g = head - layer * p.Hkv;
-    const bool has_next = u + 1 < u1;
-    if constexpr (kPrefetch) {
-      if (has_next) load_k(u + 1, kn);   // lands while this unit computes
-    } else {
-      if (u != u0) load_k(u, kf);
-    }
+    if (u != u0) load_k(u, kf);   // issued before this unit's staging, if any
     const int key0 = blk * kKeysPerUnit + wave * kKeysPerWave;
     const bool wave_full = key0 + kKeysPerWave <= p.n;   // no key of this wave past the prefix
     const float alpha = p.layer_scales ? p.layer_scales[layer] : p.scale;
@@ -221,16 +213,19 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
     };
     // A operands from registers, B operand (32 query rows) from LDS:
     // acc[t][e] = <K[key], Q[row]>, key = key0 + 32t + 8(e/4) + 4hb + (e%4), row = 32qb + col.
+    // All 8 fragments of the block are read first, so the LDS latency is paid
+    // once per block rather than once per k-step.
     auto mfma_block = [&](int qb, f32x16 (&acc)[kT]) {
       const char* qsb = lds + (qb * 32 + col) * kRowPitch + hb * 16;
+      bf16x8 qf[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qsb + 32 * s);
 #pragma unroll
       for (int t = 0; t < kT; ++t) acc[t] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qsb + 32 * s);
+      for (int s = 0; s < 8; ++s)
 #pragma unroll
-        for (int t = 0; t < kT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], qf, acc[t], 0, 0, 0);
-      }
+        for (int t = 0; t < kT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], qf[s], acc[t], 0, 0, 0);
     };
     // Keyformer path: t = (alpha x + zeta) * log2(e) / tau, in place, for row r.
     auto noisy = [&](f32x16 (&acc)[kT], int r) {
@@ -374,14 +369,6 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
           const int key = key0 + 32 * t + 8 * (col >> 2) + 4 * hb + (col & 3);
           if (key < p.n) out[key] = mine * p.inv_w;
         }
-      }
-    }
-    if constexpr (kPrefetch) {
-      if (has_next) {
-#pragma unroll
-        for (int t = 0; t < kT; ++t)
-#pragma unroll
-          for (int s = 0; s < 8; ++s) kf[t][s] = kn[t][s];
       }
     }
   }
