@@ -6,31 +6,32 @@
 // (importance descending, position ascending) order are kept together with
 // every position of [S - recent, S); kept positions are written ascending.
 //
-// Design: one 1024-thread workgroup per head runs an exact MSB-first radix
-// select on order-preserving 32-bit keys of the fp32 scores, relative to the
-// head's smallest key: d = key - min, and each level histograms the next (up
-// to) 11 bits below the highest set bit of max - min.  Scores of one head
-// usually span a narrow key range (similar exponents), so the first level
-// already spreads them over the bins (few LDS-atomic collisions) and often
-// two levels suffice.  Integer atomics are exact and order-independent.  The
-// select yields the k_top-th key T and how many T-valued candidates must be
-// taken.  Each wave owns a contiguous range of candidates loaded with
-// coalesced 256-byte loads, 64 in flight per lane, and kept in registers
-// across all levels; the ordered output transposes them through LDS so each
-// thread owns 64 consecutive candidates, and the kept positions are staged
-// in LDS and written out coalesced.
+// Both designs below run an exact MSB-first radix select on order-preserving
+// 32-bit keys of the fp32 scores with LDS histograms and integer atomics
+// (exact and order-independent), then write the kept positions in order
+// (each thread owns consecutive candidates; workgroup scans give the output
+// offsets), so the output is ascending without a sort and bit-reproducible.
+//
+//  * Up to 32768 candidates per head (one launch): one 1024-thread workgroup
+//    per head keeps all keys in registers; its levels work on key - min, each
+//    taking the next (up to) 11 bits below the top set bit of max - min, so
+//    scores of similar magnitude still spread over the bins.
+//  * More candidates (four launches, each ordered after the previous one on
+//    the stream): every head is cut into chunks of at most 4096 and each
+//    (chunk, head) gets a 256-thread workgroup.  Levels of 11, 11 and 10 bits;
+//    level L's workgroups first resolve level L-1's digit by a binary search
+//    over the per-chunk inclusive suffix counts the previous launch stored
+//    (11 sums over the chunks), histogram their chunk, and store its suffix
+//    counts; the last launch resolves T, counts the kept candidates of the
+//    earlier chunks from their suffix counts and emits its chunk.  Launches
+//    cost several microseconds each, so this only pays off where one
+//    workgroup per head would leave most of the chip idle for long.
 #include "common.h"
 
 namespace kvc {
 namespace {
 
-#ifndef KVC_SEL_THREADS
-#define KVC_SEL_THREADS 1024
-#endif
-constexpr int kSelThreads = KVC_SEL_THREADS;
-constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kBins = 2048;
-constexpr int kBPT = kBins / kSelThreads;   // histogram bins per thread in the scan
 
 // fp32 -> uint32 with the same order (-0 folded onto +0).
 __device__ __forceinline__ uint32_t order_key(uint32_t b) {
@@ -38,8 +39,11 @@ __device__ __forceinline__ uint32_t order_key(uint32_t b) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Exclusive prefix sum over the workgroup; *total receives the sum of all x.
+// Exclusive prefix sum over a workgroup of kThreadsT threads; *total receives
+// the sum of all x.
+template <int kThreadsT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, uint32_t* total) {
+  constexpr int kWavesT = kThreadsT / kWave;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   uint32_t v = x;
 #pragma unroll
@@ -51,7 +55,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, 
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) {
+  for (int i = 0; i < kWavesT; ++i) {
     const uint32_t s = wsum[i];
     before += (i < wid) ? s : 0u;
     tot += s;
@@ -60,6 +64,13 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, 
   *total = tot;
   return before + v - x;
 }
+
+// ======================================================== one workgroup per head
+namespace one {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kBPT = kBins / kSelThreads;   // histogram bins per thread in the scan
 
 // Workgroup-wide (min, max); every thread receives the result.
 __device__ __forceinline__ void block_min_max(uint32_t& lo, uint32_t& hi, uint32_t* wlo, uint32_t* whi) {
@@ -180,7 +191,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
       a += hb[i];
     }
     uint32_t tot;
-    const uint32_t incl = block_excl_scan(a, wsum, &tot) + a;   // = count of bins >= kBPT*rt
+    const uint32_t incl = block_excl_scan<kSelThreads>(a, wsum, &tot) + a;   // = count of bins >= kBPT*rt
     uint32_t below = 0;
 #pragma unroll
     for (int i = 0; i < kBPT; ++i) {
@@ -229,10 +240,10 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
       n_eq += (e < valid && mine[e] == T) ? 1u : 0u;
     }
     uint32_t eq_tot, take_tot;
-    const uint32_t eq_b = block_excl_scan(n_eq, wsum, &eq_tot) + eq_carry;   // also orders tr reads before writes
+    const uint32_t eq_b = block_excl_scan<kSelThreads>(n_eq, wsum, &eq_tot) + eq_carry;   // also orders tr reads before writes
     const uint32_t room = krem > eq_b ? krem - eq_b : 0u;
     const uint32_t n_take = n_gt + (n_eq < room ? n_eq : room);
-    uint32_t pos = block_excl_scan(n_take, wsum, &take_tot);   // offset within this round's output
+    uint32_t pos = block_excl_scan<kSelThreads>(n_take, wsum, &take_tot);   // offset within this round's output
     uint32_t eq_left = n_eq < room ? n_eq : room;    // T-valued candidates this thread keeps
     const uint32_t jb = (uint32_t)(r * kRound + seg);
 #pragma unroll
@@ -252,20 +263,228 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
   }
 }
 
+
+}  // namespace one
+
+// ================================================= several workgroups per head
+namespace many {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kBPT = kBins / kThreads;           // histogram bins per thread in a scan
+constexpr int kMaxChunk = 4096;                  // candidates per workgroup
+constexpr int kSegment = kMaxChunk / kThreads;   // candidates per thread in the emission
+constexpr int kTargetGroups = 256;               // workgroups aimed for over all heads
+
+// Level L: digit = (key >> level_shift(L)) & level_mask(L).
+__host__ __device__ constexpr int level_shift(int L) { return L == 0 ? 21 : (L == 1 ? 10 : 0); }
+__host__ __device__ constexpr uint32_t level_mask(int L) { return L == 2 ? 0x3FFu : 0x7FFu; }
+
+// Per-head state passed between launches: resolved digits and the rank of T
+// still to place after each level.
+enum : int { kD0 = 0, kD1 = 1, kKrem1 = 2, kKrem2 = 3, kStateWords = 4 };
+
+struct SelArgs {
+  const uint32_t* imp;   // fp32 bit patterns
+  int64_t hs;            // head stride (elements)
+  int c, k_top, S, recent, budget;
+  int chunk, nchunk;     // candidates per chunk, chunks per head
+  int32_t* out;          // [Hkv, budget]
+  uint32_t* suf;         // [3][Hkv][nchunk][kBins]: inclusive suffix counts per chunk
+  uint32_t* state;       // [Hkv][kStateWords]
+};
+
+__device__ __forceinline__ const uint32_t* chunk_suffix(const SelArgs& a, int L, int g, int q) {
+  return a.suf + (((int64_t)L * gridDim.y + g) * a.nchunk + q) * kBins;
+}
+
+// Sum over the head's chunks of level L's suffix count at bin b (all threads).
+__device__ __forceinline__ uint32_t suffix_total(const SelArgs& a, int L, int g, int b, uint32_t* wsum) {
+  uint32_t x = 0;
+  for (int q = threadIdx.x; q < a.nchunk; q += kThreads) x += chunk_suffix(a, L, g, q)[b];
+  uint32_t tot;
+  (void)block_excl_scan<kThreads>(x, wsum, &tot);
+  return tot;
+}
+
+// Level L's digit: the largest d with total suffix count >= krem (the count
+// at bin 0, all live keys, is >= krem), and the count above it.
+__device__ __forceinline__ void resolve_digit(const SelArgs& a, int L, int g, uint32_t krem, uint32_t* wsum,
+                                              uint32_t& digit, uint32_t& above) {
+  int lo = 0, hi = kBins - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (suffix_total(a, L, g, mid, wsum) >= krem)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  digit = (uint32_t)lo;
+  above = lo + 1 < kBins ? suffix_total(a, L, g, lo + 1, wsum) : 0u;
+}
+
+template <int kLevel>
+__global__ __launch_bounds__(kThreads) void select_level(SelArgs a) {
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t wsum[kWaves];
+  const int p = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  uint32_t* st = a.state + g * kStateWords;
+
+  // digits resolved so far: (key & pmask) == prefix marks the keys still live
+  uint32_t prefix = 0, pmask = 0;
+  if (kLevel >= 1) {
+    const uint32_t krem = kLevel == 1 ? (uint32_t)a.k_top : st[kKrem1];
+    if (kLevel == 2) {
+      prefix = st[kD0] << level_shift(0);
+      pmask = level_mask(0) << level_shift(0);
+    }
+    uint32_t d, above;
+    resolve_digit(a, kLevel - 1, g, krem, wsum, d, above);
+    prefix |= d << level_shift(kLevel - 1);
+    pmask |= level_mask(kLevel - 1) << level_shift(kLevel - 1);
+    if (p == 0 && tid == 0) {
+      st[kLevel == 1 ? kD0 : kD1] = d;
+      st[kLevel == 1 ? kKrem1 : kKrem2] = krem - above;
+    }
+  }
+
+  for (int b = tid; b < kBins; b += kThreads) h[b] = 0u;
+  __syncthreads();
+  const int j0 = p * a.chunk, j1 = min(a.c, j0 + a.chunk);
+  const uint32_t* v = a.imp + (int64_t)g * a.hs;
+#pragma unroll 4
+  for (int j = j0 + tid; j < j1; j += kThreads) {
+    const uint32_t key = order_key(v[j]);
+    if ((key & pmask) == prefix) atomicAdd(&h[(key >> level_shift(kLevel)) & level_mask(kLevel)], 1u);
+  }
+  __syncthreads();
+
+  // inclusive suffix counts: the thread owns kBPT bins from base = kBPT*(last - tid)
+  const int base = kBPT * (kThreads - 1 - tid);
+  uint32_t hb[kBPT], sum = 0;
+#pragma unroll
+  for (int i = 0; i < kBPT; ++i) {
+    hb[i] = h[base + i];
+    sum += hb[i];
+  }
+  uint32_t tot;
+  uint32_t s = block_excl_scan<kThreads>(sum, wsum, &tot);   // count in bins >= base + kBPT
+  uint32_t* my = a.suf + (((int64_t)kLevel * gridDim.y + g) * a.nchunk + p) * kBins;
+#pragma unroll
+  for (int i = kBPT - 1; i >= 0; --i) {
+    s += hb[i];
+    my[base + i] = s;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void select_emit(SelArgs a) {
+  __shared__ uint32_t keys[kMaxChunk + kMaxChunk / 64];   // candidate j at j + j/64
+  __shared__ uint32_t wsum[kWaves];
+  const int p = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const uint32_t* st = a.state + g * kStateWords;
+  int32_t* o = a.out + (int64_t)g * a.budget;
+  if (p == 0)
+    for (int t = tid; t < a.recent; t += kThreads) o[a.k_top + t] = a.S - a.recent + t;
+  const int j0 = p * a.chunk, cnt = min(a.c, j0 + a.chunk) - j0;
+  const uint32_t* v = a.imp + (int64_t)g * a.hs + j0;
+  for (int j = tid; j < cnt; j += kThreads) keys[j + (j >> 6)] = order_key(v[j]);
+
+  // T = the k_top-th key; krem of the T-valued candidates are taken
+  const uint32_t d0 = st[kD0], d1 = st[kD1], krem2 = st[kKrem2];
+  uint32_t d2, above2;
+  resolve_digit(a, 2, g, krem2, wsum, d2, above2);   // its barriers also publish `keys`
+  const uint32_t T = (d0 << level_shift(0)) | (d1 << level_shift(1)) | d2;
+  const uint32_t krem = krem2 - above2;
+
+  // candidates kept before this chunk, from the earlier chunks' suffix counts
+  uint32_t gt_q = 0, eq_q = 0;
+  for (int q = tid; q < p; q += kThreads) {
+    const uint32_t* s0 = chunk_suffix(a, 0, g, q);
+    const uint32_t* s1 = chunk_suffix(a, 1, g, q);
+    const uint32_t* s2 = chunk_suffix(a, 2, g, q);
+    const uint32_t up0 = d0 + 1 < (uint32_t)kBins ? s0[d0 + 1] : 0u;
+    const uint32_t up1 = d1 + 1 < (uint32_t)kBins ? s1[d1 + 1] : 0u;
+    const uint32_t up2 = d2 + 1 < (uint32_t)kBins ? s2[d2 + 1] : 0u;
+    gt_q += up0 + up1 + up2;
+    eq_q += s2[d2] - up2;
+  }
+  uint32_t gt_before, eq_before;
+  (void)block_excl_scan<kThreads>(gt_q, wsum, &gt_before);
+  (void)block_excl_scan<kThreads>(eq_q, wsum, &eq_before);
+  const uint32_t eq_room = krem > eq_before ? krem - eq_before : 0u;
+  const uint32_t out0 = gt_before + (eq_before < krem ? eq_before : krem);
+
+  // this chunk: the thread owns candidates [kSegment*tid, kSegment*tid + kSegment)
+  const int seg = tid * kSegment;
+  const int valid = min(kSegment, max(0, cnt - seg));
+  uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int e = 0; e < kSegment; ++e) {
+    const int j = seg + e;
+    const uint32_t k = e < valid ? keys[j + (j >> 6)] : 0u;
+    n_gt += (e < valid && k > T) ? 1u : 0u;
+    n_eq += (e < valid && k == T) ? 1u : 0u;
+  }
+  uint32_t eq_tot, take_tot;
+  const uint32_t eqx = block_excl_scan<kThreads>(n_eq, wsum, &eq_tot);
+  const uint32_t room = eq_room > eqx ? eq_room - eqx : 0u;
+  uint32_t eq_left = n_eq < room ? n_eq : room;   // T-valued candidates this thread keeps
+  uint32_t pos = out0 + block_excl_scan<kThreads>(n_gt + eq_left, wsum, &take_tot);
+#pragma unroll
+  for (int e = 0; e < kSegment; ++e) {
+    const int j = seg + e;
+    const uint32_t k = e < valid ? keys[j + (j >> 6)] : 0u;
+    const bool eq = e < valid && k == T && eq_left > 0;
+    const bool take = (e < valid && k > T) || eq;
+    eq_left -= eq ? 1u : 0u;
+    if (take && pos < (uint32_t)a.k_top) o[pos] = j0 + j;
+    pos += take ? 1u : 0u;
+  }
+}
+
+// Chunking of c candidates over Hkv heads: about kTargetGroups workgroups, in
+// chunks of 256..4096 candidates (multiples of 256).
+void plan_chunks(int32_t Hkv, int32_t c, int* chunk, int* nchunk) {
+  const int goal = (kTargetGroups + Hkv - 1) / Hkv;
+  int ch = (c + goal - 1) / goal;
+  ch = (ch + kThreads - 1) / kThreads * kThreads;
+  ch = ch < kThreads ? kThreads : (ch > kMaxChunk ? kMaxChunk : ch);
+  *chunk = ch;
+  *nchunk = c > 0 ? (c + ch - 1) / ch : 1;
+}
+
+// Workspace words for nchunk chunks per head.
+size_t workspace_words(int32_t Hkv, int nchunk) {
+  return (size_t)3 * Hkv * nchunk * kBins + (size_t)Hkv * kStateWords;
+}
+
+// Most chunks any c <= n is cut into: at most the target count while the
+// chunk size is free to grow, else n / 4096 rounded up.
+int max_chunks(int32_t Hkv, int32_t n) {
+  const int goal = (kTargetGroups + Hkv - 1) / Hkv;
+  const int big = (n + kMaxChunk - 1) / kMaxChunk;
+  return goal > big ? goal : big;
+}
+
+}  // namespace many
+
+// Candidate counts up to one round of the single-workgroup kernel use it.
+bool use_one_workgroup(int c) { return c <= one::kRound; }
+
 }  // namespace
 }  // namespace kvc
 
+// Enough for every call with Hkv heads and at most n candidates.
 extern "C" size_t kvc_select_topk_workspace_size(int32_t Hkv, int32_t n) {
-  (void)Hkv;
-  (void)n;
-  return 0;
+  if (Hkv < 1 || n < 1) return 0;
+  if (kvc::use_one_workgroup(n)) return 0;
+  return kvc::many::workspace_words(Hkv, kvc::many::max_chunks(Hkv, n)) * sizeof(uint32_t);
 }
 
 extern "C" kvc_status kvc_select_topk(const float* importance, int64_t imp_head_stride, int32_t Hkv,
                                       int32_t S, int32_t w, int32_t recent, int32_t budget,
                                       int32_t* indices, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
+  using namespace kvc;
   if (Hkv < 1 || S < 2 || w < 1 || w >= S || recent < 0 || recent > S) return KVC_E_ARG;
   const int32_t n = S - w;
   const int32_t c = n < S - recent ? n : S - recent;
@@ -277,7 +496,35 @@ extern "C" kvc_status kvc_select_topk(const float* importance, int64_t imp_head_
   if (Hkv > 65535) return KVC_E_SHAPE;
   if (budget == 0) return KVC_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  KVC_LAUNCH("select_topk", kvc::select_topk_kernel, dim3(Hkv), dim3(kvc::kSelThreads), s, importance,
-             imp_head_stride, c, budget - recent, S, recent, budget, indices);
+  const int k_top = budget - recent;
+  if (use_one_workgroup(c) || k_top == 0 || k_top >= c) {
+    KVC_LAUNCH("select_topk", one::select_topk_kernel, dim3(Hkv), dim3(one::kSelThreads), s, importance,
+               imp_head_stride, c, k_top, S, recent, budget, indices);
+    return KVC_OK;
+  }
+
+  int chunk, nchunk;
+  many::plan_chunks(Hkv, c, &chunk, &nchunk);
+  if (!ws || ws_bytes < many::workspace_words(Hkv, nchunk) * sizeof(uint32_t) ||
+      (reinterpret_cast<uintptr_t>(ws) & 3))
+    return KVC_E_WORKSPACE;
+  many::SelArgs a;
+  a.imp = reinterpret_cast<const uint32_t*>(importance);
+  a.hs = imp_head_stride;
+  a.c = c;
+  a.k_top = k_top;
+  a.S = S;
+  a.recent = recent;
+  a.budget = budget;
+  a.chunk = chunk;
+  a.nchunk = nchunk;
+  a.out = indices;
+  a.suf = static_cast<uint32_t*>(ws);
+  a.state = a.suf + (size_t)3 * Hkv * nchunk * kBins;
+  const dim3 grid(nchunk, Hkv);
+  KVC_LAUNCH("select_level0", many::select_level<0>, grid, dim3(many::kThreads), s, a);
+  KVC_LAUNCH("select_level1", many::select_level<1>, grid, dim3(many::kThreads), s, a);
+  KVC_LAUNCH("select_level2", many::select_level<2>, grid, dim3(many::kThreads), s, a);
+  KVC_LAUNCH("select_emit", many::select_emit, grid, dim3(many::kThreads), s, a);
   return KVC_OK;
 }

@@ -118,6 +118,21 @@ def test_select_validation(S, w, recent, budget, status):
     assert st == status
 
 
+def test_select_workspace():
+    # up to 32768 candidates per head: one workgroup per head, no workspace
+    assert lib.kvc_select_topk_workspace_size(8, 32640) == 0
+    need = lib.kvc_select_topk_workspace_size(8, 131008)
+    assert need > 0 and lib.kvc_select_topk_workspace_size(0, 100) == 0
+    # the size for n covers every smaller candidate count (the chunking is not monotone in c)
+    for Hkv in (1, 3, 8, 32):
+        big = lib.kvc_select_topk_workspace_size(Hkv, 140000)
+        assert all(lib.kvc_select_topk_workspace_size(Hkv, n) <= big for n in range(1, 140000, 997))
+    # too small or missing: rejected before anything is enqueued
+    args = (FAKE, 131008, 8, 131072, 64, 64, 26214, FAKE)
+    assert lib.kvc_select_topk(*args, None, need, None) == E.KVC_E_WORKSPACE
+    assert lib.kvc_select_topk(*args, FAKE, 4, None) == E.KVC_E_WORKSPACE
+
+
 def test_compact_validation():
     assert lib.kvc_compact(FAKE, FAKE, 4, 100, 12, 1200, 1200, FAKE, 10, FAKE, FAKE, None) == E.KVC_E_ARG
     assert lib.kvc_compact(FAKE, None, 4, 100, 128, 12800, 0, FAKE, 10, FAKE, FAKE, None) == E.KVC_E_ARG

@@ -49,6 +49,9 @@ def _ref_select(imp32, **kw):
     (4, 9000, 64, 64, 2000, "signed"),          # negative and positive scores
     (2, 9000, 64, 64, 1000, "wide"),            # keys spanning all 32 bits, +-inf included
     (2, 70016, 16, 16, 30000, "ties3"),         # three rounds; equal keys straddle round borders
+    (3, 40016, 16, 16, 9000, "equal"),          # chunked path: one key everywhere -> lowest positions
+    (2, 50064, 64, 64, 7000, "wide"),           # chunked path: full key range, +-inf
+    (2, 45000, 10, 5, 20000, "zeros_denorm"),   # chunked path: zeros and denormals
 ])
 def test_select_bit_exact(Hkv, S, w, recent, budget, kind):
     rng = np.random.default_rng(S + budget)
