@@ -24,7 +24,7 @@
 namespace kvc {
 namespace {
 
-constexpr int kMbaThreads = 256;
+constexpr int kMbaThreads = 1024;
 constexpr int kMbaWaves = kMbaThreads / kWave;
 constexpr int kAllocThreads = 1024;
 constexpr int kMaxLayers = 1024;
@@ -57,6 +57,7 @@ __global__ __launch_bounds__(kMbaThreads) void mba_kernel(const float* imp, int 
   const uint32_t* v = reinterpret_cast<const uint32_t*>(imp + (int64_t)row * n);
 
   double part = 0.0;
+#pragma unroll 4
   for (int j = tid; j < n; j += kMbaThreads) part += (double)__uint_as_float(v[j]);
   const double total = block_sum_f64(part, sred);
   const double target = mass * total;
@@ -77,6 +78,7 @@ __global__ __launch_bounds__(kMbaThreads) void mba_kernel(const float* imp, int 
       bm[d] = 0.0;
       bc[d] = 0u;
     }
+#pragma unroll 4
     for (int j = tid; j < n; j += kMbaThreads) {
       const uint32_t key = v[j];   // scores are >= 0: raw bits already order-preserving
       const bool live = (sh == 28) || ((key >> (sh + 4)) == (prefix >> (sh + 4)));
