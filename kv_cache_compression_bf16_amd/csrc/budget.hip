@@ -6,15 +6,17 @@
 // and the rest of the total budget is shared in proportion to LMBA.
 //
 // Design:
-//  * mba_kernel, one workgroup per (layer, head): the row's total mass is an
-//    fp64 sum in a fixed order; the threshold key T (the largest score whose
-//    "at least T" mass reaches mass*total) is found by an 8-level, 16-way
-//    search over the order-preserving 32-bit keys of the scores.  At each level
-//    every thread accumulates the mass and count of each of the 16 digit
-//    buckets in registers, and buckets are combined across the workgroup in a
-//    fixed tree order, so the result is bit-reproducible (no floating-point
-//    atomics).  MBA = (#scores > T) + the fewest T-valued scores that close the
-//    remaining gap.
+//  * mba_kernel, one workgroup per (layer, head).  Masses are exact 64-bit
+//    fixed-point integers x_fix = floor(x * 2^shift), with shift chosen so that
+//    n copies of the row's largest score still fit in 62 bits; integer sums
+//    are exact and order-independent, so LDS atomics keep the result
+//    bit-reproducible.  (Truncation loses less than n * 2^-shift of the total,
+//    about 1e-10 of the largest score for n = 16K.)  The threshold key T (the
+//    largest score whose "at least T" mass reaches mass*total) is found by a
+//    radix search on key - min over the order-preserving 32-bit keys, each
+//    level taking the next (up to) 11 bits below the top set bit of max - min
+//    and histogramming count and mass per bin.  MBA = (#scores > T) + the
+//    fewest T-valued scores that close the remaining gap.
 //  * allocate_kernel, one workgroup: exact int64 largest-remainder shares with
 //    the floor, capacity clamping and re-sharing (water-filling).
 #include <math.h>
@@ -29,139 +31,160 @@ constexpr int kMbaWaves = kMbaThreads / kWave;
 constexpr int kAllocThreads = 1024;
 constexpr int kMaxLayers = 1024;
 
-__device__ __forceinline__ double shfl_xor_f64(double x, int o) {
-  return __shfl_xor(x, o);
+// Workgroup-wide exclusive prefix sum of uint64 values; *total gets the sum.
+__device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t x, uint64_t* wsum, uint64_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint64_t v = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) wsum[wid] = v;
+  __syncthreads();
+  uint64_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kMbaWaves; ++i) {
+    const uint64_t s = wsum[i];
+    before += (i < wid) ? s : 0ull;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + v - x;
 }
 
-// Fixed-order workgroup sum of one double per thread (all threads get it).
-__device__ double block_sum_f64(double x, double* scratch) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += shfl_xor_f64(x, o);
-  if (lane == 0) scratch[wid] = x;
-  __syncthreads();
-  double t = 0.0;
-#pragma unroll
-  for (int i = 0; i < kMbaWaves; ++i) t += scratch[i];
-  __syncthreads();
-  return t;
-}
+constexpr int kMbaBins = 2048;
+constexpr int kMbaBPT = kMbaBins / kMbaThreads;   // bins per thread in the suffix scans
 
 __global__ __launch_bounds__(kMbaThreads) void mba_kernel(const float* imp, int n, double mass,
                                                          int32_t* mba_out) {
-  __shared__ double sm[kMbaWaves][16];
-  __shared__ uint32_t sc[kMbaWaves][16];
-  __shared__ double sred[kMbaWaves];
+  __shared__ uint32_t hc[kMbaBins];   // count per bin
+  __shared__ uint64_t hm[kMbaBins];   // fixed-point mass per bin
+  __shared__ uint64_t wsum[kMbaWaves];
+  __shared__ uint32_t wlo[kMbaWaves], whi[kMbaWaves];
+  __shared__ uint32_t s_bin;
+  __shared__ uint64_t s_above_m;
+  __shared__ uint32_t s_above_c;
 
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const uint32_t* v = reinterpret_cast<const uint32_t*>(imp + (int64_t)row * n);
 
-  double part = 0.0;
+  // key range (scores are >= 0, so the raw bits are order-preserving keys)
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll 4
-  for (int j = tid; j < n; j += kMbaThreads) part += (double)__uint_as_float(v[j]);
-  const double total = block_sum_f64(part, sred);
-  const double target = mass * total;
-  if (!(target > 0.0)) {
+  for (int j = tid; j < n; j += kMbaThreads) {
+    const uint32_t k = v[j];
+    kmin = min(kmin, k);
+    kmax = max(kmax, k);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor(kmin, o));
+    kmax = max(kmax, (uint32_t)__shfl_xor(kmax, o));
+  }
+  if (lane == 0) {
+    wlo[wid] = kmin;
+    whi[wid] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kMbaWaves; ++i) {
+    kmin = min(kmin, wlo[i]);
+    kmax = max(kmax, whi[i]);
+  }
+  if (kmax == 0u) {   // every score is zero: nothing to keep
     if (tid == 0) mba_out[row] = 0;
     return;
   }
 
-  uint32_t prefix = 0;       // digits of T fixed so far
-  double above_m = 0.0;      // mass of scores whose key exceeds every key still in play
-  int64_t above_c = 0;
-  uint32_t eq_count = 0;
-  for (int sh = 28; sh >= 0; sh -= 4) {
-    double bm[16];
-    uint32_t bc[16];
-#pragma unroll
-    for (int d = 0; d < 16; ++d) {
-      bm[d] = 0.0;
-      bc[d] = 0u;
+  // fixed point: max < 2^e_max, n < 2^l_n, shift = 62 - l_n - e_max
+  int e_max;
+  (void)frexp((double)__uint_as_float(kmax), &e_max);
+  const int l_n = 32 - __clz((uint32_t)n);
+  const int shift = 62 - l_n - e_max;
+  auto fix = [&](uint32_t key) -> uint64_t { return (uint64_t)ldexp((double)__uint_as_float(key), shift); };
+
+  uint64_t part = 0;
+#pragma unroll 4
+  for (int j = tid; j < n; j += kMbaThreads) part += fix(v[j]);
+  uint64_t total;
+  (void)block_excl_scan_u64(part, wsum, &total);
+  const uint64_t target = (uint64_t)ceil((double)total * mass);   // keep at least this much
+  if (target == 0) {
+    if (tid == 0) mba_out[row] = 0;
+    return;
+  }
+
+  // radix search on d = key - kmin, MSB first: bits [top, 32) of T - kmin are
+  // known (= hi); the keys above T hold above_m / above_c
+  int top = 32 - __clz(kmax - kmin);
+  uint32_t hi = 0, above_c = 0, eq = (uint32_t)n;   // eq: keys equal to T (all, if they are all equal)
+  uint64_t above_m = 0;
+  while (top > 0) {
+    const int width = top < 11 ? top : 11;
+    const int sh = top - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    const uint32_t hmask = top >= 32 ? 0u : (0xFFFFFFFFu << top);
+    const uint32_t hval = top >= 32 ? 0u : (hi << top);
+    for (int b = tid; b < kMbaBins; b += kMbaThreads) {
+      hc[b] = 0u;
+      hm[b] = 0ull;
     }
+    if (tid == 0) s_bin = 0u;
+    __syncthreads();
 #pragma unroll 4
     for (int j = tid; j < n; j += kMbaThreads) {
-      const uint32_t key = v[j];   // scores are >= 0: raw bits already order-preserving
-      const bool live = (sh == 28) || ((key >> (sh + 4)) == (prefix >> (sh + 4)));
-      if (live) {
-        const uint32_t d = (key >> sh) & 15u;
-        const double x = (double)__uint_as_float(key);
-#pragma unroll
-        for (int dd = 0; dd < 16; ++dd) {
-          bm[dd] += (d == (uint32_t)dd) ? x : 0.0;
-          bc[dd] += (d == (uint32_t)dd) ? 1u : 0u;
-        }
-      }
-    }
-    // fixed-order reduction of the 16 buckets: wave butterfly, then waves 0..3
-#pragma unroll
-    for (int d = 0; d < 16; ++d) {
-      double m = bm[d];
-      uint32_t cnt = bc[d];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        m += shfl_xor_f64(m, o);
-        cnt += __shfl_xor(cnt, o);
-      }
-      if (lane == 0) {
-        sm[wid][d] = m;
-        sc[wid][d] = cnt;
+      const uint32_t k = v[j];
+      const uint32_t d = k - kmin;
+      if ((d & hmask) == hval) {
+        const uint32_t b = (d >> sh) & dmask;
+        atomicAdd(&hc[b], 1u);
+        atomicAdd(reinterpret_cast<unsigned long long*>(&hm[b]), (unsigned long long)fix(k));
       }
     }
     __syncthreads();
-    // every thread walks the 16 digits from the top (identical, uniform result):
-    // T's digit is the highest one whose bucket brings the mass to the target
-    bool found = false;
-    int dstar = -1, dlow = -1;
-    double cum = above_m, mlow = 0.0;
-    int64_t cumc = above_c;
-    uint32_t clow = 0;
+    // suffix sums of mass and count: the thread owns kMbaBPT bins from base
+    const int base = kMbaBPT * (kMbaThreads - 1 - tid);
+    uint64_t m_own = 0;
+    uint32_t c_own = 0;
 #pragma unroll
-    for (int d = 15; d >= 0; --d) {
-      double m = 0.0;
-      uint32_t cnt = 0;
+    for (int i = 0; i < kMbaBPT; ++i) {
+      m_own += hm[base + i];
+      c_own += hc[base + i];
+    }
+    uint64_t mtot;
+    const uint64_t m_higher = block_excl_scan_u64(m_own, wsum, &mtot);   // mass in bins >= base + kMbaBPT
+    const uint64_t c_higher = block_excl_scan_u64(c_own, wsum, &mtot);
+    // the crossing bin: the highest b with above_m + mass(bins >= b) >= target
+    uint64_t sm = m_higher;
+    uint64_t sc = c_higher;
 #pragma unroll
-      for (int w = 0; w < kMbaWaves; ++w) {
-        m += sm[w][d];
-        cnt += sc[w][d];
-      }
-      if (!found && cnt > 0) {
-        if (cum + m >= target) {
-          found = true;
-          dstar = d;
-          eq_count = cnt;
-        } else {
-          cum += m;
-          cumc += cnt;
-          dlow = d;
-          mlow = m;
-          clow = cnt;
-        }
+    for (int i = kMbaBPT - 1; i >= 0; --i) {
+      const uint64_t up_m = sm, up_c = sc;   // bins > base + i
+      sm += hm[base + i];
+      sc += hc[base + i];
+      if (above_m + sm >= target && above_m + up_m < target) {
+        s_bin = (uint32_t)(base + i);
+        s_above_m = up_m;
+        s_above_c = (uint32_t)up_c;
       }
     }
-    if (!found) {   // rounding kept the target out of reach: T lies in the lowest live bucket
-      dstar = dlow;
-      cum -= mlow;
-      cumc -= clow;
-      eq_count = clow;
-    }
-    above_m = cum;
-    above_c = cumc;
-    prefix |= (uint32_t)dstar << sh;
+    __syncthreads();
+    hi = (hi << width) | s_bin;
+    above_m += s_above_m;
+    above_c += s_above_c;
+    eq = hc[s_bin];   // after the last level: the keys equal to T
+    top = sh;
     __syncthreads();
   }
   if (tid == 0) {
-    const double t = (double)__uint_as_float(prefix);
-    const double need = target - above_m;
-    int64_t e;
-    if (!(t > 0.0)) {
-      e = eq_count;
-    } else {
-      e = (int64_t)ceil(need / t);
-      if (e < 1) e = 1;
-      if (e > (int64_t)eq_count) e = eq_count;
-      while (e > 1 && above_m + (double)(e - 1) * t >= target) --e;
-      while (e < (int64_t)eq_count && above_m + (double)e * t < target) ++e;
-    }
+    // the eq keys equal to T = kmin + hi close the gap
+    const uint64_t xt = fix(kmin + hi);
+    const uint64_t need = target - above_m;   // > 0 by construction
+    uint64_t e = xt > 0 ? (need + xt - 1) / xt : (uint64_t)eq;
+    if (e < 1) e = 1;
+    if (e > eq) e = eq;
     mba_out[row] = (int32_t)(above_c + e);
   }
 }

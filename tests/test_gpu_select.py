@@ -167,6 +167,24 @@ def test_budget_degenerate_rows():
     assert bud.tolist() == ref_b
 
 
+def test_budget_mixed_magnitudes():
+    # the 90% crossing lands among thousands of tiny scores below one large one,
+    # and rows span many decades (the MBA search keeps masses in 64-bit fixed point)
+    n = 16256
+    rng = np.random.default_rng(7)
+    imp = np.zeros((3, 4, n), dtype=np.float32)
+    imp[0, :, :] = 3e-5
+    imp[0, :, 123] = 0.5
+    imp[1] = (10.0 ** rng.uniform(-12, 0, size=(4, n))).astype(np.float32)
+    imp[2] = rng.exponential(size=(4, n)).astype(np.float32) ** 6
+    imp /= imp.sum(axis=-1, keepdims=True)
+    mba, bud = _gpu_budget(imp, total_budget=3 * 4000, floor_per_layer=128, capacity=n)
+    ref_mba, ref_b = oracle.budget.zigzag_budgets(imp.astype(np.float64), total_budget=3 * 4000, floor=128,
+                                                  capacity=n)
+    assert mba.tolist() == ref_mba
+    assert bud.tolist() == ref_b
+
+
 def test_budget_equal_lmba_is_uniform():
     imp = np.tile(_rows(1, 4, 2048, 9), (6, 1, 1))
     _, bud = _gpu_budget(imp, total_budget=6 * 500, floor_per_layer=64, capacity=2048)
