@@ -189,8 +189,9 @@ kvc_status kvc_select_topk(const float* importance, int64_t imp_head_stride, int
  * new, smaller cache); KVzap news page (cache of shape (2, L, H, T, D)).
  * Layout: k, v bf16, row j of head g at base + g*head_stride + j*D; k_out,
  *   v_out bf16 [Hkv, budget, D] contiguous.  v / v_out may both be NULL.
- *   D % 8 == 0, D <= 1024.  An index outside [0, S) yields a row of 0xFFFF
- *   (bf16 NaN) instead of a read out of bounds.
+ *   D % 8 == 0, D <= 1024, budget * D / 8 < 2^31 (else KVC_E_SHAPE).  An
+ *   index outside [0, S) yields a row of 0xFFFF (bf16 NaN) instead of a read
+ *   out of bounds.
  */
 kvc_status kvc_compact(const void* k, const void* v, int32_t Hkv, int32_t S, int32_t D,
                        int64_t k_head_stride, int64_t v_head_stride, const int32_t* indices,

@@ -2,15 +2,52 @@
 //
 // Keyformer blog page, prompt-phase paragraph: the kept tokens form the new,
 // smaller cache; KVzap news page: the cache is (2, L, H, T, D).  The copy is of
-// raw bf16 bytes.  Each lane moves 16 bytes, so a 128-dim row is 16 lanes and
-// a wave copies 4 full rows per instruction (coalesced 256-byte segments); K
-// and V are two planes of the same grid.
+// raw bf16 bytes.  Each lane moves 16-byte chunks, consecutive lanes on
+// consecutive chunks of a row (coalesced 256-byte segments for D = 128), 4 rows
+// per thread so that 4 loads are in flight; K and V are two planes of one
+// grid.
 #include "common.h"
 
 namespace kvc {
 namespace {
 
-__global__ __launch_bounds__(256) void compact_kernel(const uint16_t* k, const uint16_t* v, int S, int D,
+// One 16-byte chunk per lane, consecutive lanes on consecutive chunks of a row
+// (a 128-dim row is 16 lanes: coalesced 256-byte segments), and kRPT rows per
+// thread, kRPT independent loads in flight.  kChunks = D / 8 divides 256.
+template <int kRPT>
+__global__ __launch_bounds__(256) void compact_rows(const uint16_t* k, const uint16_t* v, int S, int D,
+                                                     int64_t khs, int64_t vhs, const int32_t* idx,
+                                                     int budget, uint16_t* ko, uint16_t* vo) {
+  const int g = blockIdx.y;
+  const bool isv = blockIdx.z != 0;
+  const uint16_t* src = (isv ? v : k) + g * (isv ? vhs : khs);
+  uint16_t* dst = (isv ? vo : ko) + (int64_t)g * budget * D;
+  const int32_t* ix = idx + (int64_t)g * budget;
+  const int chunks = D >> 3, rpp = 256 / chunks;   // rows per pass of the workgroup
+  const int ch = threadIdx.x % chunks;
+  const int r0 = blockIdx.x * rpp * kRPT + threadIdx.x / chunks;
+  int j[kRPT];
+#pragma unroll
+  for (int q = 0; q < kRPT; ++q) {
+    const int t = r0 + q * rpp;
+    j[q] = t < budget ? ix[t] : -1;
+  }
+  u32x4 val[kRPT];
+#pragma unroll
+  for (int q = 0; q < kRPT; ++q) {
+    const bool ok = j[q] >= 0 && j[q] < S;
+    val[q] = *reinterpret_cast<const u32x4*>(src + (int64_t)(ok ? j[q] : 0) * D + ch * 8);
+    if (!ok) val[q] = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  }
+#pragma unroll
+  for (int q = 0; q < kRPT; ++q) {
+    const int t = r0 + q * rpp;
+    if (t < budget) *reinterpret_cast<u32x4*>(dst + (int64_t)t * D + ch * 8) = val[q];
+  }
+}
+
+// Any D % 8 == 0: one chunk per thread.
+__global__ __launch_bounds__(256) void compact_chunks(const uint16_t* k, const uint16_t* v, int S, int D,
                                                        int64_t khs, int64_t vhs, const int32_t* idx,
                                                        int budget, uint16_t* ko, uint16_t* vo) {
   const int g = blockIdx.y;
@@ -19,17 +56,15 @@ __global__ __launch_bounds__(256) void compact_kernel(const uint16_t* k, const u
   uint16_t* dst = (isv ? vo : ko) + (int64_t)g * budget * D;
   const int32_t* ix = idx + (int64_t)g * budget;
   const int chunks = D >> 3;
-  const int64_t total = (int64_t)budget * chunks;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int t = (int)(e / chunks), ch = (int)(e - (int64_t)t * chunks);
-    const int j = ix[t];
-    u32x4 val;
-    if (j >= 0 && j < S)
-      val = *reinterpret_cast<const u32x4*>(src + (int64_t)j * D + ch * 8);
-    else
-      val = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-    *reinterpret_cast<u32x4*>(dst + (int64_t)t * D + ch * 8) = val;
-  }
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int t = e / chunks;
+  if (t >= budget) return;
+  const int ch = e - t * chunks;
+  const int j = ix[t];
+  const bool ok = j >= 0 && j < S;
+  u32x4 val = *reinterpret_cast<const u32x4*>(src + (int64_t)(ok ? j : 0) * D + ch * 8);
+  if (!ok) val = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  *reinterpret_cast<u32x4*>(dst + (int64_t)t * D + ch * 8) = val;
 }
 
 }  // namespace
@@ -48,12 +83,22 @@ extern "C" kvc_status kvc_compact(const void* k, const void* v, int32_t Hkv, int
   if (!aligned16(k) || !aligned16(k_out) || (v && (!aligned16(v) || !aligned16(v_out)))) return KVC_E_ARG;
   if (reinterpret_cast<uintptr_t>(indices) & 3) return KVC_E_ARG;
   if (budget == 0) return KVC_OK;
-  const int64_t total = (int64_t)budget * (D / 8);
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  if ((int64_t)budget * (D / 8) > 0x7FFFFFFF - 256) return KVC_E_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  KVC_LAUNCH("compact", compact_kernel, dim3((unsigned)blocks, Hkv, v ? 2 : 1), dim3(256), s,
-             static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), S, D, k_head_stride,
-             v_head_stride, indices, budget, static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out));
+  const dim3 block(256);
+  const uint16_t *kp = static_cast<const uint16_t*>(k), *vp = static_cast<const uint16_t*>(v);
+  uint16_t *kop = static_cast<uint16_t*>(k_out), *vop = static_cast<uint16_t*>(v_out);
+  const int planes = v ? 2 : 1;
+  const int chunks = D / 8;
+  if (256 % chunks == 0) {   // 4 rows per thread
+    constexpr int kRPT = 4;
+    const int rows_per_wg = 256 / chunks * kRPT;
+    KVC_LAUNCH("compact", compact_rows<kRPT>, dim3((budget + rows_per_wg - 1) / rows_per_wg, Hkv, planes), block, s,
+               kp, vp, S, D, k_head_stride, v_head_stride, indices, budget, kop, vop);
+  } else {
+    const int threads = budget * chunks;
+    KVC_LAUNCH("compact", compact_chunks, dim3((threads + 255) / 256, Hkv, planes), block, s, kp, vp, S, D,
+               k_head_stride, v_head_stride, indices, budget, kop, vop);
+  }
   return KVC_OK;
 }

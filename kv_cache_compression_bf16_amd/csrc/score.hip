@@ -374,22 +374,24 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
   }
 }
 
-// Fold the per-workgroup partials of each query row into
-// rowc = m + log2(sum_b l_b * 2^(m_b - m)).  A workgroup takes 32 consecutive
-// rows of one head; its 8 thread groups each fold every 8th key block online
-// (coalesced 256-byte reads), and the 8 group results are folded in a fixed
-// order, so the result is bit-reproducible.
-constexpr int kCombRows = 32, kCombGroups = 8;
+// Fold the per-unit partials of each query row into
+// rowc = m + log2(sum_b l_b * 2^(m_b - m)).  A workgroup takes kRows
+// consecutive rows of one head; its 256/kRows thread groups each fold every
+// (256/kRows)-th unit online (coalesced reads along the rows), and the group
+// results are folded in a fixed order, so the result is bit-reproducible.
+// Rows with many units use 8 rows x 32 groups, the rest 32 rows x 8 groups.
+template <int kRows>
 __global__ __launch_bounds__(256) void score_combine(ScoreParams p, int heads) {
-  __shared__ float2 sg[kCombGroups][kCombRows];
-  const int rr = threadIdx.x & (kCombRows - 1), q = threadIdx.x / kCombRows;
-  const int tiles = (p.R + kCombRows - 1) / kCombRows;
-  const int head = blockIdx.x / tiles, r = (blockIdx.x - head * tiles) * kCombRows + rr;
+  constexpr int kGroups = 256 / kRows;
+  __shared__ float2 sg[kGroups][kRows];
+  const int rr = threadIdx.x % kRows, q = threadIdx.x / kRows;
+  const int tiles = (p.R + kRows - 1) / kRows;
+  const int head = blockIdx.x / tiles, r = (blockIdx.x - head * tiles) * kRows + rr;
   float m = -INFINITY, l = 0.f;
   if (head < heads && r < p.R) {
     const float2* pp = p.part + (int64_t)head * p.nblk * p.R + r;
 #pragma unroll 4
-    for (int b = q; b < p.nblk; b += kCombGroups) {
+    for (int b = q; b < p.nblk; b += kGroups) {
       const float2 a = pp[(int64_t)b * p.R];
       const float mn = fmaxf(m, a.x);
       const float ms = (mn == -INFINITY) ? 0.f : mn;
@@ -402,11 +404,11 @@ __global__ __launch_bounds__(256) void score_combine(ScoreParams p, int heads) {
   if (q == 0 && head < heads && r < p.R) {
     float mm = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kCombGroups; ++i) mm = fmaxf(mm, sg[i][rr].x);
+    for (int i = 0; i < kGroups; ++i) mm = fmaxf(mm, sg[i][rr].x);
     const float ms = (mm == -INFINITY) ? 0.f : mm;
     float ll = 0.f;
 #pragma unroll
-    for (int i = 0; i < kCombGroups; ++i) ll += sg[i][rr].y * fast_exp2(sg[i][rr].x - ms);
+    for (int i = 0; i < kGroups; ++i) ll += sg[i][rr].y * fast_exp2(sg[i][rr].x - ms);
     p.rowc[(int64_t)head * p.R + r] = (ll > 0.f) ? mm + log2f(ll) : INFINITY;
   }
 }
@@ -466,7 +468,10 @@ kvc_status launch_score(const ScoreParams& p, const Plan& pl, hipStream_t s) {
   constexpr int kThreads = kW * kWave;
   const int units = p.L * p.Hkv * pl.nblk;
   const int heads = p.L * p.Hkv;
-  const dim3 comb_grid(heads * ((pl.R + kCombRows - 1) / kCombRows));
+  const bool wide = pl.nblk >= 128;   // many units per row: more groups per row
+  const int comb_rows = wide ? 8 : 32;
+  const dim3 comb_grid(heads * ((pl.R + comb_rows - 1) / comb_rows));
+  auto kc = wide ? score_combine<8> : score_combine<32>;
   const size_t lds1 = score_lds_bytes(pl.chunk_rows, kW, false), lds2 = score_lds_bytes(pl.chunk_rows, kW, true);
   auto k1 = score_pass<false, kGumbel, kW, kT, kCB>;
   auto k2 = score_pass<true, kGumbel, kW, kT, kCB>;
@@ -476,7 +481,7 @@ kvc_status launch_score(const ScoreParams& p, const Plan& pl, hipStream_t s) {
   st = score_grid(k2, kThreads, lds2, units, &g2);
   if (st != KVC_OK) return st;
   KVC_LAUNCH_SHM(kGumbel ? "score_pass1_gumbel" : "score_pass1", k1, dim3(g1), dim3(kThreads), lds1, s, p);
-  KVC_LAUNCH("score_combine", score_combine, comb_grid, dim3(256), s, p, heads);
+  KVC_LAUNCH("score_combine", kc, comb_grid, dim3(256), s, p, heads);
   KVC_LAUNCH_SHM(kGumbel ? "score_pass2_gumbel" : "score_pass2", k2, dim3(g2), dim3(kThreads), lds2, s, p);
   return KVC_OK;
 }

@@ -91,10 +91,11 @@ def test_select_reads_only_candidates_with_head_stride():
 
 
 # ---------------------------------------------------------------- compact
-def test_compact_bit_exact_and_bad_index_fill():
+@pytest.mark.parametrize("D", [128, 96, 8])   # 4-rows-per-thread path (128, 8) and chunk path (96)
+def test_compact_bit_exact_and_bad_index_fill(D):
     kvc = _kvc()
     rng = np.random.default_rng(0)
-    Hkv, S, D, B = 4, 3000, 128, 333
+    Hkv, S, B = 4, 3000, 333
     k = rng.integers(0, 65536, size=(Hkv, S + 10, D), dtype=np.uint16)
     v = rng.integers(0, 65536, size=(Hkv, S, D), dtype=np.uint16)
     idx = np.stack([np.sort(rng.choice(S, B, replace=False)) for _ in range(Hkv)]).astype(np.int32)
