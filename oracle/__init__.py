@@ -18,6 +18,7 @@ written in the order and notation of the pages it cites:
                  uniform mapping and the Gumbel(0,1) transform.
 * ``budget``  -- MBA, LMBA and ZigZag's proportional per-layer allocation with
                  a floor (ZigZagKV blog, observation and allocation sections).
+* ``pool``    -- SnapKV's 1D pooling of the importance along the keys.
 * ``select``  -- per-head top-k plus the recent window.
 * ``compact`` -- gather of the kept K/V rows.
 * ``think``   -- ThinK magnitude-based key-channel pruning.
@@ -27,4 +28,4 @@ Parity status of each function (what pins it) is listed in each module's
 docstring; every function here has at least one pin in ``tests/``.
 """
 
-from . import budget, compact, philox, score, select, sizes, think  # noqa: F401
+from . import budget, compact, philox, pool, score, select, sizes, think  # noqa: F401
