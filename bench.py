@@ -74,6 +74,8 @@ def algorithmic(wl):
         T = int(math.floor((1 - wl.think_lambda) * D))
         kr = Hkv * (wl.budget - wl.recent)
         step_bytes += kr * D * 2 + kr * T * 2
+    if wl.pool_kernel:
+        step_bytes += 2 * imp
     # per step (bench divides by the launches per step): bound, flops, algorithmic bytes
     per_kernel = {
         "score_pass1": ("mfma", flops_pass, q_bytes + k_prefix),
@@ -83,6 +85,7 @@ def algorithmic(wl):
         "select_topk": ("hbm", 0.0, imp + B_total * 4),
         "compact": ("hbm", 0.0, 2 * rows * 2 + B_total * 4),
         "lmba_mba": ("hbm", 0.0, imp),
+        "pool_importance": ("hbm", 0.0, 2 * imp),
     }
     if wl.think_lambda >= 0:
         T = int(math.floor((1 - wl.think_lambda) * D))
@@ -93,6 +96,7 @@ def algorithmic(wl):
 
 
 KERNEL_SOURCE = {"score": "score.hip", "select": "select.hip", "compact": "compact.hip", "lmba": "budget.hip",
+                 "pool": "pool.hip",
                  "think": "think.hip"}
 
 
@@ -244,7 +248,8 @@ def main():
     config = {"workload": wl.name, "layers": wl.L, "q_heads": wl.H, "kv_heads": wl.Hkv, "seq_len": wl.S,
               "head_dim": wl.D, "window": wl.w, "recent": wl.recent,
               "budget_per_kv_head": wl.budget or None, "total_budget": wl.total_budget or None,
-              "gumbel_tau": args.tau if wl.gumbel else None, "input_copies_rotated": copies}
+              "gumbel_tau": args.tau if wl.gumbel else None, "pool_kernel": wl.pool_kernel or None,
+              "input_copies_rotated": copies}
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",

@@ -157,6 +157,29 @@ kvc_status kvc_lmba_budget(const float* importance, int32_t L, int32_t Hkv, int3
                            void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* kvc_pool_importance: SnapKV 1D pooling of the importance.                 */
+/* ------------------------------------------------------------------------ */
+/*
+ * For every row g (layer x KV head) and key j < n, with h = kernel / 2:
+ *   KVC_POOL_AVG: out[g,j] = (1/kernel) * sum_{i=j-h}^{j+h} in[g,i], positions
+ *                 outside [0, n) counting as 0 (zero padding);
+ *   KVC_POOL_MAX: out[g,j] = max of in[g,i] over i in [j-h, j+h] and [0, n).
+ * Source: ZigZagKV blog page, SnapKV section (the averaged scores are pooled
+ * along the keys so the neighbours of a strong token are kept with it).  The
+ * page gives no kernel size or type; kernel odd in [1, 255], stride 1.
+ * Layout: fp32, row g at in + g*in_stride and out + g*out_stride (>= n when
+ *   rows > 1); out must not alias in.  Sums run in a fixed order: the result
+ *   is bit-reproducible.
+ * Errors: KVC_E_ARG unless rows >= 1, n >= 1, kernel odd in [1, 255], mode
+ *   KVC_POOL_AVG or KVC_POOL_MAX, in != out, both 4-byte aligned;
+ *   KVC_E_SHAPE for a stride < n or rows > 65535.
+ */
+typedef enum kvc_pool_mode { KVC_POOL_AVG = 0, KVC_POOL_MAX = 1 } kvc_pool_mode;
+
+kvc_status kvc_pool_importance(const float* in, int64_t in_stride, float* out, int64_t out_stride,
+                               int32_t rows, int32_t n, int32_t kernel, int32_t mode, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* kvc_select_topk: per-head top-k plus the recent window.                   */
 /* ------------------------------------------------------------------------ */
 /*

@@ -52,6 +52,7 @@ def _load():
         "kvc_score": (ctypes.c_int, [ctypes.POINTER(ScoreArgs), P, P, P, P, SZ, P]),
         "kvc_lmba_budget_workspace_size": (SZ, [I32, I32, I32]),
         "kvc_lmba_budget": (ctypes.c_int, [P, I32, I32, I32, F64, I64, I32, I32, P, P, P, SZ, P]),
+        "kvc_pool_importance": (ctypes.c_int, [P, I64, P, I64, I32, I32, I32, I32, P]),
         "kvc_select_topk_workspace_size": (SZ, [I32, I32]),
         "kvc_select_topk": (ctypes.c_int, [P, I64, I32, I32, I32, I32, I32, P, P, SZ, P]),
         "kvc_compact": (ctypes.c_int, [P, P, I32, I32, I32, I64, I64, P, I32, P, P, P]),
@@ -175,6 +176,25 @@ def kvc_lmba_budget(importance, budgets, *, total_budget, floor_per_layer, capac
                                 int(floor_per_layer), int(capacity), _ptr(mba), _ptr(budgets), _ptr(ws),
                                 nbytes, _stream(stream, importance.device)), "kvc_lmba_budget")
     return budgets
+
+
+# ---------------------------------------------------------------- kvc_pool_importance
+POOL_AVG, POOL_MAX = 0, 1
+
+
+def kvc_pool_importance(importance, pooled, *, kernel, mode=POOL_AVG, stream=None):
+    """SnapKV 1D pooling along the keys of every row of importance [..., n] into pooled (same shape)."""
+    if importance.dtype != torch.float32 or pooled.dtype != torch.float32:
+        raise ValueError("importance and pooled must be float32")
+    if importance.shape != pooled.shape or importance.stride(-1) != 1 or pooled.stride(-1) != 1:
+        raise ValueError("importance and pooled must have the same shape and unit-stride rows")
+    n = importance.shape[-1]
+    src = importance.reshape(-1, n)
+    dst = pooled.view(-1, n)
+    _check(_lib.kvc_pool_importance(_ptr(src), src.stride(0), _ptr(dst), dst.stride(0), src.shape[0], n,
+                                    int(kernel), int(mode), _stream(stream, importance.device)),
+           "kvc_pool_importance")
+    return pooled
 
 
 # ---------------------------------------------------------------- kvc_select_topk

@@ -1,7 +1,7 @@
 """Composition of the C-ABI calls into whole compression passes.
 
 Each pass is a fixed sequence of libkvc calls on one stream: score ->
-[ZigZag budgets] -> select -> compact -> [ThinK].  Buffers are allocated once
+[SnapKV pooling] -> [ZigZag budgets] -> select -> compact -> [ThinK].  Buffers are allocated once
 per plan (through torch) so a pass itself allocates nothing on the device.
 No arithmetic happens here.
 """
@@ -28,6 +28,9 @@ class CompressionPlan:
         f32, i32, bf = torch.float32, torch.int32, torch.bfloat16
         L, Hkv, n, D = wl.L, wl.Hkv, wl.n, wl.D
         self.importance = torch.empty((L, Hkv, n), dtype=f32, device=device)
+        # scores the selection ranks: the importance, or its SnapKV pooling
+        self.pooled = torch.empty_like(self.importance) if wl.pool_kernel else None
+        self.scores = self.pooled if wl.pool_kernel else self.importance
         self.zigzag = bool(wl.total_budget)
         # workspace for kvc_score sized from a representative ScoreArgs
         a = kvc.ScoreArgs()
@@ -70,8 +73,11 @@ class CompressionPlan:
         """One whole pass.  q [L?, H, w, D], k/v [L?, Hkv, S, D] (bf16 on device)."""
         wl = self.wl
         self.score(q, k, layer_scales, stream)
+        if wl.pool_kernel:
+            kvc.kvc_pool_importance(self.importance, self.pooled, kernel=wl.pool_kernel, mode=wl.pool_mode,
+                                    stream=stream)
         if not self.zigzag:
-            kvc.kvc_select_topk(self.importance[0], self.indices, S=wl.S, w=wl.w, recent=wl.recent,
+            kvc.kvc_select_topk(self.scores[0], self.indices, S=wl.S, w=wl.w, recent=wl.recent,
                                 budget=wl.budget, workspace=self.ws_select, stream=stream)
             kvc.kvc_compact(k if k.dim() == 3 else k[0], v if v.dim() == 3 else v[0], self.indices, self.kc,
                             self.vc, S=wl.S, stream=stream)
@@ -91,7 +97,7 @@ class CompressionPlan:
             idx = self.indices_flat[off * Hkv:(off + B) * Hkv].view(Hkv, B)
             kc = self.kc_flat[off * Hkv * D:(off + B) * Hkv * D].view(Hkv, B, D)
             vc = self.vc_flat[off * Hkv * D:(off + B) * Hkv * D].view(Hkv, B, D)
-            kvc.kvc_select_topk(self.importance[l], idx, S=wl.S, w=wl.w, recent=wl.recent, budget=B,
+            kvc.kvc_select_topk(self.scores[l], idx, S=wl.S, w=wl.w, recent=wl.recent, budget=B,
                                 workspace=self.ws_select, stream=stream)
             kvc.kvc_compact(k[l], v[l], idx, kc, vc, S=wl.S, stream=stream)
             self.layer_views.append((idx, kc, vc))

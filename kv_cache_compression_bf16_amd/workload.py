@@ -50,6 +50,8 @@ class Workload:
     noise_seed: int = 0
     think_lambda: float = -1.0      # < 0: no channel pruning
     think_p: int = 2
+    pool_kernel: int = 0            # SnapKV 1D pooling of the importance before top-k (0: off)
+    pool_mode: int = 0              # 0: average (zero padding, / kernel), 1: max
     seed: int = 0
     notes: str = field(default="", compare=False)
 
@@ -81,6 +83,10 @@ WORKLOADS = {
         name="gqa32x8_s32768", cfg_id=1, L=1, H=32, Hkv=8, S=32768, w=128, recent=64, budget=2048,
         outliers=4,
         notes="Llama-3-8B-shaped layer, GQA 32/8, 4 outlier key channels x8, budget 2048 incl. 64 recent"),
+    "gqa32x8_s32768_pool7": Workload(
+        name="gqa32x8_s32768_pool7", cfg_id=1, L=1, H=32, Hkv=8, S=32768, w=128, recent=64, budget=2048,
+        outliers=4, pool_kernel=7, pool_mode=0,
+        notes="the GQA layer above (same inputs) with SnapKV's average pooling (kernel 7) before top-k"),
     "zigzag_l32_s16384": Workload(
         name="zigzag_l32_s16384", cfg_id=2, L=32, H=8, Hkv=8, S=16384, w=128, recent=128,
         total_budget=32 * 1024, floor=128, scale_range=(0.5, 3.0),

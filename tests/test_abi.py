@@ -73,6 +73,7 @@ def _args(**over):
 
 
 FAKE = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(1 << 21)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -131,6 +132,22 @@ def test_select_workspace():
     args = (FAKE, 131008, 8, 131072, 64, 64, 26214, FAKE)
     assert lib.kvc_select_topk(*args, None, need, None) == E.KVC_E_WORKSPACE
     assert lib.kvc_select_topk(*args, FAKE, 4, None) == E.KVC_E_WORKSPACE
+
+
+@pytest.mark.parametrize("rows,n,kernel,mode,status", [
+    (0, 10, 3, 0, E.KVC_E_ARG),
+    (2, 0, 3, 0, E.KVC_E_ARG),
+    (2, 10, 4, 0, E.KVC_E_ARG),        # even kernel
+    (2, 10, 257, 0, E.KVC_E_ARG),      # beyond 255
+    (2, 10, 3, 2, E.KVC_E_ARG),        # unknown mode
+])
+def test_pool_validation(rows, n, kernel, mode, status):
+    assert lib.kvc_pool_importance(FAKE, n, FAKE2, n, rows, n, kernel, mode, None) == status
+
+
+def test_pool_aliasing_and_strides():
+    assert lib.kvc_pool_importance(FAKE, 10, FAKE, 10, 2, 10, 3, 0, None) == E.KVC_E_ARG     # in == out
+    assert lib.kvc_pool_importance(FAKE, 9, FAKE2, 10, 2, 10, 3, 0, None) == E.KVC_E_SHAPE   # stride < n
 
 
 def test_compact_validation():

@@ -90,6 +90,33 @@ def test_select_reads_only_candidates_with_head_stride():
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+# ---------------------------------------------------------------- pooling
+@pytest.mark.parametrize("rows,n,kernel,mode", [
+    (8, 32640, 7, 0), (8, 32640, 7, 1),
+    (3, 1025, 1, 0), (3, 1025, 255, 0), (3, 1025, 255, 1),   # identity and the widest window
+    (2, 5, 9, 0), (2, 5, 9, 1),                              # window wider than the row
+    (5, 131008, 31, 0),
+])
+def test_pool_matches_oracle(rows, n, kernel, mode):
+    kvc = _kvc()
+    rng = np.random.default_rng(n + kernel + mode)
+    x = rng.exponential(size=(rows, n)).astype(np.float32) / n
+    if mode == 1:
+        x -= np.float32(1.0 / n)                             # signed values: max must ignore the padding
+    t = torch.from_numpy(x).to(dev())
+    out = torch.full_like(t, float("nan"))
+    kvc.kvc_pool_importance(t, out, kernel=kernel, mode=mode)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = oracle.pool.pool(x.astype(np.float64), kernel, mode)
+    if mode == 1:
+        assert np.array_equal(got, ref)                      # a max picks an input value exactly
+    else:
+        # fp32: kernel - 1 sequential additions of positive terms and one division
+        rel = (kernel + 2) * 2.0 ** -24
+        assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-38)
+
+
 # ---------------------------------------------------------------- compact
 @pytest.mark.parametrize("D", [128, 96, 8])   # 4-rows-per-thread path (128, 8) and chunk path (96)
 def test_compact_bit_exact_and_bad_index_fill(D):

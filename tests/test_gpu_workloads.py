@@ -50,6 +50,12 @@ def _oracle_imp(wl, q, k, scale, heads, tau=1.0):
 
 def _check_uniform_budget_layer(wl, plan, q, k, v, scale, heads, tau=1.0):
     imp = plan.importance[0].cpu().numpy()
+    scores = plan.scores[0].cpu().numpy()              # what the selection ranks (pooled or not)
+    if wl.pool_kernel:
+        # pooling in isolation on the GPU's own importance
+        ref_pool = oracle.pool.pool(imp.astype(np.float64), wl.pool_kernel, wl.pool_mode)
+        rel = (wl.pool_kernel + 2) * 2.0 ** -24
+        assert np.all(np.abs(scores - ref_pool) <= rel * np.abs(ref_pool) + 1e-38)
     idx = plan.indices.cpu().numpy()
     # any-size properties, every head
     check_importance_sums = np.allclose(imp.astype(np.float64).sum(axis=1), wl.G, rtol=1e-5, atol=0)
@@ -60,7 +66,7 @@ def _check_uniform_budget_layer(wl, plan, q, k, v, scale, heads, tau=1.0):
     assert np.array_equal(bits_of(plan.kc), oracle.compact.compact(k, idx))
     assert np.array_equal(bits_of(plan.vc), oracle.compact.compact(v, idx))
     # selection in isolation on the GPU's scores, every head
-    ref_iso = oracle.select.select_heads(imp.astype(np.float64), S=wl.S, w=wl.w, recent=wl.recent,
+    ref_iso = oracle.select.select_heads(scores.astype(np.float64), S=wl.S, w=wl.w, recent=wl.recent,
                                          budget=wl.budget)
     assert np.array_equal(idx, ref_iso)
     # sampled heads against the oracle's own scores
@@ -68,8 +74,9 @@ def _check_uniform_budget_layer(wl, plan, q, k, v, scale, heads, tau=1.0):
     kinds = []
     for g in heads:
         check_importance(imp[g][None], ref[g][None], wl.G, f"{wl.name} head {g}")
-        ref_idx = oracle.select.select(ref[g], S=wl.S, w=wl.w, recent=wl.recent, budget=wl.budget)
-        kinds.append(check_selection(idx[g], ref[g], ref_idx, S=wl.S, w=wl.w, recent=wl.recent,
+        ref_s = oracle.pool.pool_row(ref[g], wl.pool_kernel, wl.pool_mode) if wl.pool_kernel else ref[g]
+        ref_idx = oracle.select.select(ref_s, S=wl.S, w=wl.w, recent=wl.recent, budget=wl.budget)
+        kinds.append(check_selection(idx[g], ref_s, ref_idx, S=wl.S, w=wl.w, recent=wl.recent,
                                      budget=wl.budget))
     return kinds
 
@@ -85,6 +92,13 @@ def test_gqa32x8_s32768():
     wl = wk.WORKLOADS["gqa32x8_s32768"]
     plan, (q, k, v), sc = _run(wl)
     kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=[0, 5])
+    print("selection:", kinds)
+
+
+def test_gqa32x8_s32768_pool7():
+    wl = wk.WORKLOADS["gqa32x8_s32768_pool7"]
+    plan, (q, k, v), sc = _run(wl)
+    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=[3])
     print("selection:", kinds)
 
 
