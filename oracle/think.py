@@ -1,4 +1,4 @@
-"""ThinK magnitude-based key-channel pruning.
+"""ThinK key-channel pruning: magnitude-based and query-driven.
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
@@ -8,12 +8,18 @@ Source: ThinK page (papercache summary of arXiv 2407.21018, ICLR 2025):
   channel d; with pruning ratio lambda every head keeps T = floor((1 - lambda) D)
   channels, I = Top_T(M, T), I in Z^{N x T};
 * section on THINK's implementation: recent tokens' keys are not pruned, and a
-  binary mask records which channels were pruned.
+  binary mask records which channels were pruned;
+* sections on query-driven pruning, the greedy algorithm and the observation
+  window: channel j of head i scores Score_i[j] = ||Q_i[-S_obs:, j] K_i[:, j]^T||_F
+  (the Frobenius norm of the outer product of the channel's window-query column
+  and key column), and the T highest-scoring channels are kept.
 
 Readings: the norm runs over the non-recent kept rows (the rows that get
 pruned), i.e. the first budget - r rows of the compacted cache, whose positions
 all precede the recent window; ties in M go to the lower channel; the kept
-channel list is ascending; V is not touched.
+channel list is ascending; V is not touched.  For the query-driven score of a
+KV head shared by G query heads, the window queries of those G heads are
+stacked (G*w rows); the key side is the same non-recent kept rows.
 """
 
 import numpy as np
@@ -50,3 +56,41 @@ def think_prune(kc, *, recent, lam, p=2):
         mask[g, c] = 1
         pruned[g] = kc[g, :rows][:, c]
     return chans, mask, pruned, norms
+
+
+def query_scores(q_group, kc_head_rows):
+    """Score[d] = ||Q[:, d] K[:, d]^T||_F, straight from the definition.
+
+    q_group: [G*w, D] window queries of the KV head's query heads; kc_head_rows:
+    [rows, D] non-recent kept keys (both float64).  Returns float64 [D].
+    """
+    q = np.asarray(q_group, dtype=np.float64)
+    k = np.asarray(kc_head_rows, dtype=np.float64)
+    return np.array([np.linalg.norm(np.outer(q[:, d], k[:, d]), "fro") for d in range(q.shape[1])])
+
+
+def think_prune_query(kc, q_obs, *, recent, lam):
+    """Query-driven ThinK.  kc: [Hkv, B, D] float64 compacted keys (recent rows
+    last); q_obs: [H, w, D] float64 window queries, H = G * Hkv, head h in group h // G.
+
+    Returns (channels [Hkv, T] ascending, mask [Hkv, D], pruned [Hkv, B - recent, T], scores [Hkv, D]).
+    """
+    Hkv, B, D = kc.shape
+    H = q_obs.shape[0]
+    G = H // Hkv
+    T = kept_channels(D, lam)
+    rows = B - recent
+    chans = np.empty((Hkv, T), dtype=np.int64)
+    mask = np.zeros((Hkv, D), dtype=np.uint8)
+    scores = np.empty((Hkv, D))
+    pruned = np.empty((Hkv, rows, T))
+    for g in range(Hkv):
+        qg = q_obs[g * G:(g + 1) * G].reshape(-1, D)
+        sc = query_scores(qg, kc[g, :rows])
+        scores[g] = sc
+        order = np.lexsort((np.arange(D), -sc))
+        c = np.sort(order[:T])
+        chans[g] = c
+        mask[g, c] = 1
+        pruned[g] = kc[g, :rows][:, c]
+    return chans, mask, pruned, scores

@@ -78,3 +78,29 @@ def test_channel_ties_go_to_lower_index():
     kc = np.ones((1, 6, 16))
     chans, _, _, _ = think.think_prune(kc, recent=0, lam=0.75, p=1)
     assert chans[0].tolist() == [0, 1, 2, 3]
+
+
+def test_query_score_is_product_of_column_norms():
+    # rank-1 Frobenius identity: ||q k^T||_F = ||q||_2 ||k||_2, per channel
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((12, 16))
+    k = rng.standard_normal((40, 16))
+    got = oracle.think.query_scores(q, k)
+    assert np.allclose(got, np.linalg.norm(q, axis=0) * np.linalg.norm(k, axis=0), rtol=1e-12)
+
+
+def test_query_driven_prefers_channels_the_queries_use():
+    # equal key norms everywhere: the query side alone decides; a channel with no
+    # query energy is never kept, the loud query channels always are
+    rng = np.random.default_rng(12)
+    Hkv, G, w, B, D, recent = 2, 2, 3, 20, 16, 4
+    kc = np.sign(rng.standard_normal((Hkv, B, D)))          # |K| = 1: every key column has norm sqrt(rows)
+    q = rng.standard_normal((Hkv * G, w, D)) * 0.1
+    q[:, :, 5] = 0.0
+    q[:, :, [2, 9]] *= 100.0
+    ch, mask, pruned, sc = oracle.think.think_prune_query(kc, q, recent=recent, lam=0.5)
+    assert ch.shape == (Hkv, 8)
+    for g in range(Hkv):
+        assert 5 not in ch[g] and {2, 9} <= set(ch[g].tolist())
+        assert np.array_equal(pruned[g], kc[g, :B - recent][:, ch[g]])
+        assert mask[g].sum() == 8
