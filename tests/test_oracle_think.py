@@ -7,6 +7,8 @@
   kept; ties go to the lower channel; the gather keeps the selected columns.
 * KV-cache size formula against the two sizes the pages print (13 GB on the
   ThinK page, about 335 GB on the KVzap page).
+* Query-driven score (outer-product Frobenius norm) against the rank-1
+  identity ||q k^T||_F = ||q|| ||k||, and a case the query side decides.
 """
 
 import json
@@ -85,7 +87,7 @@ def test_query_score_is_product_of_column_norms():
     rng = np.random.default_rng(11)
     q = rng.standard_normal((12, 16))
     k = rng.standard_normal((40, 16))
-    got = oracle.think.query_scores(q, k)
+    got = think.query_scores(q, k)
     assert np.allclose(got, np.linalg.norm(q, axis=0) * np.linalg.norm(k, axis=0), rtol=1e-12)
 
 
@@ -98,7 +100,7 @@ def test_query_driven_prefers_channels_the_queries_use():
     q = rng.standard_normal((Hkv * G, w, D)) * 0.1
     q[:, :, 5] = 0.0
     q[:, :, [2, 9]] *= 100.0
-    ch, mask, pruned, sc = oracle.think.think_prune_query(kc, q, recent=recent, lam=0.5)
+    ch, mask, pruned, sc = think.think_prune_query(kc, q, recent=recent, lam=0.5)
     assert ch.shape == (Hkv, 8)
     for g in range(Hkv):
         assert 5 not in ch[g] and {2, 9} <= set(ch[g].tolist())
