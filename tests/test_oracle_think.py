@@ -99,10 +99,12 @@ def test_query_driven_prefers_channels_the_queries_use():
     kc = np.sign(rng.standard_normal((Hkv, B, D)))          # |K| = 1: every key column has norm sqrt(rows)
     q = rng.standard_normal((Hkv * G, w, D)) * 0.1
     q[:, :, 5] = 0.0
-    q[:, :, [2, 9]] *= 100.0
+    loud = {0: [2, 9], 1: [4, 7]}                             # group g = query heads [g*G, g*G + G)
+    for g, cols in loud.items():
+        q[g * G:(g + 1) * G][:, :, cols] *= 100.0
     ch, mask, pruned, sc = think.think_prune_query(kc, q, recent=recent, lam=0.5)
     assert ch.shape == (Hkv, 8)
     for g in range(Hkv):
-        assert 5 not in ch[g] and {2, 9} <= set(ch[g].tolist())
+        assert 5 not in ch[g] and set(loud[g]) <= set(ch[g].tolist())
         assert np.array_equal(pruned[g], kc[g, :B - recent][:, ch[g]])
         assert mask[g].sum() == 8
