@@ -74,6 +74,8 @@ def algorithmic(wl):
         T = int(math.floor((1 - wl.think_lambda) * D))
         kr = Hkv * (wl.budget - wl.recent)
         step_bytes += kr * D * 2 + kr * T * 2
+    if wl.think_lambda >= 0 and wl.think_query:
+        step_bytes += q_bytes
     if wl.pool_kernel:
         step_bytes += 2 * imp
     # per step (bench divides by the launches per step): bound, flops, algorithmic bytes
@@ -92,6 +94,8 @@ def algorithmic(wl):
         kr = Hkv * (wl.budget - wl.recent)
         per_kernel["think_partial"] = ("hbm", 0.0, kr * D * 2)
         per_kernel["think_gather"] = ("hbm", 0.0, kr * D * 2 + kr * T * 2)
+        if wl.think_query:
+            per_kernel["think_qpartial"] = ("hbm", 0.0, q_bytes)
     return step_bytes, flops_pass, per_kernel
 
 
@@ -140,17 +144,26 @@ def cpu_baseline(wl, data, target_s, tau):
         g = heads % wl.Hkv
         imp = oracle.score.importance(qf, kf, S=wl.S, w=wl.w, scale=scale, gumbel=wl.gumbel, tau=tau,
                                       seed=wl.noise_seed, kv_heads=[g])
-        idx = oracle.select.select(imp[g], S=wl.S, w=wl.w, recent=wl.recent, budget=B)
-        oracle.compact.compact(kraw[g:g + 1], idx[None])
+        sc = oracle.pool.pool(imp[g:g + 1], wl.pool_kernel, wl.pool_mode)[0] if wl.pool_kernel else imp[g]
+        idx = oracle.select.select(sc, S=wl.S, w=wl.w, recent=wl.recent, budget=B)
+        kc = oracle.compact.compact(kraw[g:g + 1], idx[None])
         oracle.compact.compact(vraw[g:g + 1], idx[None])
+        if wl.think_lambda >= 0 and wl.think_query:
+            oracle.think.think_prune_query(oracle.score.bf16_bits_to_f64(kc), qf[g * wl.G:(g + 1) * wl.G],
+                                           recent=wl.recent, lam=wl.think_lambda)
+        elif wl.think_lambda >= 0:
+            oracle.think.think_prune(oracle.score.bf16_bits_to_f64(kc), recent=wl.recent, lam=wl.think_lambda,
+                                     p=wl.think_p)
         heads += 1
         if time.perf_counter() - t0 >= target_s:
             break
     dt = time.perf_counter() - t0
     threads = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
     tokens = wl.S * heads / wl.Hkv        # one layer's prompt per Hkv heads of work
+    steps = "+".join(["score"] + (["pool"] if wl.pool_kernel else []) + ["select", "compact"]
+                     + (["think"] if wl.think_lambda >= 0 else []))
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{heads} KV-head passes over layer 0 ({wl.Hkv} heads per layer; score+select+compact, "
+            "sample": f"{heads} KV-head passes over layer 0 ({wl.Hkv} heads per layer; {steps}, "
                       f"fp64 numpy), {dt:.1f} s"}
 
 

@@ -248,6 +248,35 @@ kvc_status kvc_channel_prune(const void* k_c, int32_t Hkv, int32_t budget, int32
                              size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* kvc_channel_prune_query: query-driven ThinK key-channel pruning.          */
+/* ------------------------------------------------------------------------ */
+/*
+ * As kvc_channel_prune with p = 2, except for the channel score.  A KV head g
+ * is queried by the G query heads g*G .. g*G + G - 1; Q_g stacks their w
+ * observation-window rows (G*w rows).  score[g,d] = ||Q_g[:,d] K_U[:,d]^T||_F,
+ * which for the rank-1 outer product equals ||Q_g[:,d]||_2 ||K_U[:,d]||_2
+ * (U as in kvc_channel_prune); the kernel ranks by the square of this
+ * product, which orders channels the same way.  channels, mask and k_pruned
+ * are then as for kvc_channel_prune.
+ * Source: ThinK page, query-driven pruning (per-channel Frobenius norm of
+ * Q[-S_obs:, d] K[:, d]^T, greedy top-T over channels), its observation-window
+ * section (the last S_obs queries), and THINK's implementation (recent keys
+ * unpruned, binary channel mask).
+ * Layout: q_obs bf16, row r of query head h at q_obs + h*q_head_stride + r*D
+ *   (q_head_stride in elements, a multiple of 8, >= w*D: the [H, w, D] tensor
+ *   the scoring call reads); the rest as for kvc_channel_prune.
+ * Errors: as kvc_channel_prune; KVC_E_ARG if q_obs is NULL or not 16-byte
+ *   aligned, G < 1 or w < 1; KVC_E_SHAPE if Hkv*G > 65535 or q_head_stride is
+ *   out of range.  fp32 sums in a fixed order.
+ */
+size_t kvc_channel_prune_query_workspace_size(int32_t Hkv, int32_t G, int32_t budget, int32_t D);
+
+kvc_status kvc_channel_prune_query(const void* k_c, const void* q_obs, int32_t Hkv, int32_t G, int32_t w,
+                                   int64_t q_head_stride, int32_t budget, int32_t D, int32_t recent,
+                                   double lambda, int32_t* channels, uint8_t* mask, void* k_pruned,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Kernel timing (measurement support).                                      */
 /* ------------------------------------------------------------------------ */
 /*

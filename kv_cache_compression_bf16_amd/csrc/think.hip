@@ -1,19 +1,25 @@
-// kvc_channel_prune: ThinK magnitude-based key-channel pruning.
+// kvc_channel_prune / kvc_channel_prune_query: ThinK key-channel pruning.
 //
-// ThinK page (papercache summary of arXiv 2407.21018), magnitude-based pruning:
-// every head keeps the T = floor((1 - lambda) D) key channels with the largest
-// l_p norm over tokens; THINK's implementation section: recent keys are not
-// pruned and a binary mask records the pruned channels.  The norm here runs
-// over the non-recent kept rows (the rows that get pruned).
+// ThinK page (papercache summary of arXiv 2407.21018): magnitude-based pruning
+// keeps, per head, the T = floor((1 - lambda) D) key channels with the largest
+// l_p norm over tokens; query-driven pruning keeps the T channels with the
+// largest ||Q[-S_obs:, j] K[:, j]^T||_F = ||Q[:, j]|| ||K[:, j]|| (rank-1
+// outer product) over the observation-window queries; THINK's implementation
+// section: recent keys are not pruned and a binary mask records the pruned
+// channels.  The key norms here run over the non-recent kept rows (the rows
+// that get pruned); a KV head's query side stacks its G query heads' windows.
 //
 // Design (D = 128):
 //  * think_partial: grid (row chunks of 512, heads); 16 lanes cover one
 //    256-byte row with 16-byte loads, 16 rows in flight per workgroup; per-lane
 //    fp32 sums of |x|^p, folded over the 16 row lanes in a fixed order ->
 //    partial[g, chunk, d].
+//  * think_qpartial (query-driven only): grid (G, heads), the same row layout
+//    over one query head's w window rows -> per-channel sums of q^2.
 //  * think_select: one 128-thread workgroup per head folds the chunk partials
-//    in order, ranks channels by (norm desc, index asc), writes the kept
-//    channels ascending and the mask.
+//    in order (times the folded query sums, query-driven: ||Q|| ||K|| and its
+//    square rank alike), ranks channels by (score desc, index asc), writes the
+//    kept channels ascending and the mask.
 //  * think_gather: one wave per row; lane l holds bf16 channels 2l, 2l+1 of the
 //    row, output channel c takes its value with one cross-lane read from lane
 //    channels[c]/2 and the rows are written contiguously.
@@ -65,13 +71,49 @@ __global__ __launch_bounds__(256) void think_partial(const uint16_t* kc, int bud
   }
 }
 
-__global__ __launch_bounds__(kD) void think_select(const float* part, int nchunk, int T, int32_t* channels,
-                                                  uint8_t* mask) {
+__global__ __launch_bounds__(256) void think_qpartial(const uint16_t* q, int64_t q_hs, int G, int w,
+                                                     float* qpart) {
+  __shared__ float red[16][kD + 1];
+  const int hh = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int cg = tid & 15, rl = tid >> 4;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  const uint16_t* base = q + (int64_t)(g * G + hh) * q_hs + cg * 8;
+  for (int r = rl; r < w; r += 16) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(base + (int64_t)r * kD);
+    const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = bf16_lo(wv[e]), b = bf16_hi(wv[e]);
+      acc[2 * e] = fmaf(a, a, acc[2 * e]);
+      acc[2 * e + 1] = fmaf(b, b, acc[2 * e + 1]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rl][cg * 8 + e] = acc[e];
+  __syncthreads();
+  if (tid < kD) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += red[i][tid];
+    qpart[((int64_t)g * G + hh) * kD + tid] = s;
+  }
+}
+
+// qpart == nullptr: magnitude score; else the query-driven score (squared).
+__global__ __launch_bounds__(kD) void think_select(const float* part, int nchunk, const float* qpart, int G,
+                                                  int T, int32_t* channels, uint8_t* mask) {
   __shared__ float sm[kD];
   __shared__ int ssel[kD];
   const int g = blockIdx.x, d = threadIdx.x;
   float M = 0.f;
   for (int c = 0; c < nchunk; ++c) M += part[((int64_t)g * nchunk + c) * kD + d];
+  if (qpart) {
+    float qn = 0.f;
+    for (int hh = 0; hh < G; ++hh) qn += qpart[((int64_t)g * G + hh) * kD + d];
+    M *= qn;
+  }
   sm[d] = M;
   __syncthreads();
   int rank = 0;
@@ -109,17 +151,18 @@ __global__ __launch_bounds__(256) void think_gather(const uint16_t* kc, int budg
 }  // namespace
 }  // namespace kvc
 
-extern "C" size_t kvc_channel_prune_workspace_size(int32_t Hkv, int32_t budget, int32_t D) {
-  if (Hkv < 1 || budget < 0 || D != kvc::kD) return 0;
-  const size_t nchunk = ((size_t)budget + kvc::kChunkRows - 1) / kvc::kChunkRows;
-  return kvc::align_up((nchunk ? nchunk : 1) * Hkv * kvc::kD * sizeof(float), 256);
+namespace kvc {
+namespace {
+
+size_t think_chunks(int32_t budget) {
+  const size_t nchunk = ((size_t)budget + kChunkRows - 1) / kChunkRows;
+  return nchunk ? nchunk : 1;
 }
 
-extern "C" kvc_status kvc_channel_prune(const void* k_c, int32_t Hkv, int32_t budget, int32_t D,
-                                        int32_t recent, double lambda, int32_t p, int32_t* channels,
-                                        uint8_t* mask, void* k_pruned, void* ws, size_t ws_bytes,
-                                        void* stream) {
-  using namespace kvc;
+// Shared body of both entry points; q == nullptr selects the magnitude score.
+kvc_status channel_prune(const void* k_c, const void* q, int32_t G, int32_t w, int64_t q_hs, int32_t Hkv,
+                         int32_t budget, int32_t D, int32_t recent, double lambda, int32_t p, int32_t* channels,
+                         uint8_t* mask, void* k_pruned, void* ws, size_t ws_bytes, size_t need, void* stream) {
   if (Hkv < 1 || budget < 0 || recent < 0 || recent > budget) return KVC_E_ARG;
   if (!(lambda >= 0.0 && lambda < 1.0) || (p != 1 && p != 2)) return KVC_E_ARG;
   if (D != kD) return KVC_E_UNSUPPORTED;
@@ -131,16 +174,18 @@ extern "C" kvc_status kvc_channel_prune(const void* k_c, int32_t Hkv, int32_t bu
   if (!aligned16(k_c) || (reinterpret_cast<uintptr_t>(channels) & 3) ||
       (reinterpret_cast<uintptr_t>(k_pruned) & 1))
     return KVC_E_ARG;
-  const size_t need = kvc_channel_prune_workspace_size(Hkv, budget, D);
   if (!ws || ws_bytes < need || !aligned16(ws)) return KVC_E_WORKSPACE;
-  int nchunk = (rows + kChunkRows - 1) / kChunkRows;
-  if (nchunk < 1) nchunk = 1;
+  const int nchunk = (int)think_chunks(rows);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* part = static_cast<float*>(ws);
+  float* qpart = q ? part + align_up(think_chunks(budget) * Hkv * kD, 64) : nullptr;
   const uint16_t* kcp = static_cast<const uint16_t*>(k_c);
-  KVC_LAUNCH("think_partial", think_partial, dim3(nchunk, Hkv), dim3(256), s, kcp, budget, rows, p, nchunk,
-             part);
-  KVC_LAUNCH("think_select", think_select, dim3(Hkv), dim3(kD), s, part, nchunk, T, channels, mask);
+  KVC_LAUNCH("think_partial", think_partial, dim3(nchunk, Hkv), dim3(256), s, kcp, budget, rows, q ? 2 : p,
+             nchunk, part);
+  if (q)
+    KVC_LAUNCH("think_qpartial", think_qpartial, dim3(G, Hkv), dim3(256), s, static_cast<const uint16_t*>(q),
+               q_hs, G, w, qpart);
+  KVC_LAUNCH("think_select", think_select, dim3(Hkv), dim3(kD), s, part, nchunk, qpart, G, T, channels, mask);
   if (rows > 0) {
     int gx = (rows + 3) / 4;
     if (gx > 2048) gx = 2048;
@@ -148,4 +193,38 @@ extern "C" kvc_status kvc_channel_prune(const void* k_c, int32_t Hkv, int32_t bu
                static_cast<uint16_t*>(k_pruned));
   }
   return KVC_OK;
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" size_t kvc_channel_prune_workspace_size(int32_t Hkv, int32_t budget, int32_t D) {
+  if (Hkv < 1 || budget < 0 || D != kvc::kD) return 0;
+  return kvc::align_up(kvc::think_chunks(budget) * Hkv * kvc::kD * sizeof(float), 256);
+}
+
+extern "C" kvc_status kvc_channel_prune(const void* k_c, int32_t Hkv, int32_t budget, int32_t D,
+                                        int32_t recent, double lambda, int32_t p, int32_t* channels,
+                                        uint8_t* mask, void* k_pruned, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  return kvc::channel_prune(k_c, nullptr, 0, 0, 0, Hkv, budget, D, recent, lambda, p, channels, mask, k_pruned,
+                            ws, ws_bytes, kvc_channel_prune_workspace_size(Hkv, budget, D), stream);
+}
+
+extern "C" size_t kvc_channel_prune_query_workspace_size(int32_t Hkv, int32_t G, int32_t budget, int32_t D) {
+  if (Hkv < 1 || G < 1 || budget < 0 || D != kvc::kD) return 0;
+  const size_t keys = kvc::align_up(kvc::think_chunks(budget) * Hkv * kvc::kD, 64);
+  return kvc::align_up((keys + (size_t)Hkv * G * kvc::kD) * sizeof(float), 256);
+}
+
+extern "C" kvc_status kvc_channel_prune_query(const void* k_c, const void* q_obs, int32_t Hkv, int32_t G,
+                                              int32_t w, int64_t q_head_stride, int32_t budget, int32_t D,
+                                              int32_t recent, double lambda, int32_t* channels, uint8_t* mask,
+                                              void* k_pruned, void* ws, size_t ws_bytes, void* stream) {
+  using namespace kvc;
+  if (G < 1 || w < 1 || !q_obs || !aligned16(q_obs)) return KVC_E_ARG;
+  if ((int64_t)Hkv * G > 65535) return KVC_E_SHAPE;
+  if (q_head_stride < (int64_t)w * D || (q_head_stride & 7)) return KVC_E_SHAPE;
+  return channel_prune(k_c, q_obs, G, w, q_head_stride, Hkv, budget, D, recent, lambda, 2, channels, mask,
+                       k_pruned, ws, ws_bytes, kvc_channel_prune_query_workspace_size(Hkv, G, budget, D), stream);
 }

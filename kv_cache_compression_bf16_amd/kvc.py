@@ -58,6 +58,9 @@ def _load():
         "kvc_compact": (ctypes.c_int, [P, P, I32, I32, I32, I64, I64, P, I32, P, P, P]),
         "kvc_channel_prune_workspace_size": (SZ, [I32, I32, I32]),
         "kvc_channel_prune": (ctypes.c_int, [P, I32, I32, I32, I32, F64, I32, P, P, P, P, SZ, P]),
+        "kvc_channel_prune_query_workspace_size": (SZ, [I32, I32, I32, I32]),
+        "kvc_channel_prune_query": (ctypes.c_int, [P, P, I32, I32, I32, I64, I32, I32, I32, F64, P, P, P, P, SZ,
+                                                   P]),
         "kvc_timing_enable": (ctypes.c_int, [I32]),
         "kvc_timing_count": (I32, []),
         "kvc_timing_read": (ctypes.c_int, [I32, ctypes.c_char_p, I32, ctypes.POINTER(I32),
@@ -239,6 +242,26 @@ def kvc_channel_prune(k_c, channels, k_pruned, *, recent, lam, p=2, mask=None, w
     _check(_lib.kvc_channel_prune(_ptr(k_c), Hkv, budget, D, recent, float(lam), int(p), _ptr(channels),
                                   _ptr(mask), _ptr(k_pruned), _ptr(ws), nbytes, _stream(stream, k_c.device)),
            "kvc_channel_prune")
+    return channels, k_pruned
+
+
+def kvc_channel_prune_query(k_c, q_obs, channels, k_pruned, *, recent, lam, mask=None, workspace=None,
+                            stream=None):
+    """Query-driven ThinK pruning of k_c [Hkv, budget, D] by the window queries q_obs [H, w, D]."""
+    _bf16(k_c, "k_c")
+    _bf16(q_obs, "q_obs")
+    Hkv, budget, D = k_c.shape
+    H, w, Dq = q_obs.shape
+    if not k_c.is_contiguous():
+        raise ValueError("k_c must be contiguous")
+    if Dq != D or H % Hkv or q_obs.stride(1) != D or q_obs.stride(2) != 1:
+        raise ValueError(f"shape mismatch: q_obs {tuple(q_obs.shape)}, k_c {tuple(k_c.shape)}")
+    G = H // Hkv
+    ws, nbytes = _workspace(_lib.kvc_channel_prune_query_workspace_size(Hkv, G, budget, D), k_c.device,
+                            workspace)
+    _check(_lib.kvc_channel_prune_query(_ptr(k_c), _ptr(q_obs), Hkv, G, w, q_obs.stride(0), budget, D, recent,
+                                        float(lam), _ptr(channels), _ptr(mask), _ptr(k_pruned), _ptr(ws), nbytes,
+                                        _stream(stream, k_c.device)), "kvc_channel_prune_query")
     return channels, k_pruned
 
 

@@ -1,7 +1,8 @@
 """Composition of the C-ABI calls into whole compression passes.
 
 Each pass is a fixed sequence of libkvc calls on one stream: score ->
-[SnapKV pooling] -> [ZigZag budgets] -> select -> compact -> [ThinK].  Buffers are allocated once
+[SnapKV pooling] -> [ZigZag budgets] -> select -> compact -> [ThinK, by key norms or by
+the window queries].  Buffers are allocated once
 per plan (through torch) so a pass itself allocates nothing on the device.
 No arithmetic happens here.
 """
@@ -60,8 +61,11 @@ class CompressionPlan:
             self.channels = torch.empty((Hkv, T), dtype=i32, device=device)
             self.mask = torch.empty((Hkv, D), dtype=torch.uint8, device=device)
             self.kp = torch.empty((Hkv, rows, T), dtype=bf, device=device)
-            self.ws_think = torch.empty(max(kvc.lib.kvc_channel_prune_workspace_size(Hkv, wl.budget, D), 256),
-                                        dtype=torch.uint8, device=device)
+            if wl.think_query:
+                nb = kvc.lib.kvc_channel_prune_query_workspace_size(Hkv, wl.G, wl.budget, D)
+            else:
+                nb = kvc.lib.kvc_channel_prune_workspace_size(Hkv, wl.budget, D)
+            self.ws_think = torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
 
     def score(self, q, k, layer_scales=None, stream=None):
         wl = self.wl
@@ -81,7 +85,11 @@ class CompressionPlan:
                                 budget=wl.budget, workspace=self.ws_select, stream=stream)
             kvc.kvc_compact(k if k.dim() == 3 else k[0], v if v.dim() == 3 else v[0], self.indices, self.kc,
                             self.vc, S=wl.S, stream=stream)
-            if self.think:
+            if self.think and wl.think_query:
+                kvc.kvc_channel_prune_query(self.kc, q if q.dim() == 3 else q[0], self.channels, self.kp,
+                                            recent=wl.recent, lam=wl.think_lambda, mask=self.mask,
+                                            workspace=self.ws_think, stream=stream)
+            elif self.think:
                 kvc.kvc_channel_prune(self.kc, self.channels, self.kp, recent=wl.recent, lam=wl.think_lambda,
                                       p=wl.think_p, mask=self.mask, workspace=self.ws_think, stream=stream)
             return

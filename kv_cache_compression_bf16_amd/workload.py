@@ -50,6 +50,7 @@ class Workload:
     noise_seed: int = 0
     think_lambda: float = -1.0      # < 0: no channel pruning
     think_p: int = 2
+    think_query: bool = False       # query-driven ThinK score (window queries x keys) instead of l_p norms
     pool_kernel: int = 0            # SnapKV 1D pooling of the importance before top-k (0: off)
     pool_mode: int = 0              # 0: average (zero padding, / kernel), 1: max
     seed: int = 0
@@ -99,6 +100,10 @@ WORKLOADS = {
         name="think_s131072", cfg_id=4, L=1, H=8, Hkv=8, S=131072, w=64, recent=64,
         budget=int(0.2 * 131072), outliers=4, think_lambda=0.4, think_p=2,
         notes="long context, top 20% then ThinK l2 key-channel pruning lambda 0.4"),
+    "think_s131072_query": Workload(
+        name="think_s131072_query", cfg_id=4, L=1, H=8, Hkv=8, S=131072, w=64, recent=64,
+        budget=int(0.2 * 131072), outliers=4, think_lambda=0.4, think_query=True,
+        notes="the long-context case above (same inputs) with ThinK's query-driven channel score"),
 }
 
 

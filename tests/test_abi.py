@@ -180,6 +180,36 @@ def test_channel_prune_validation():
     assert f(FAKE, 8, 100, 128, 10, 0.999, 2, FAKE, None, FAKE, FAKE, ws, None) == E.KVC_E_ARG  # T = 0
 
 
+def test_channel_prune_query_validation():
+    f = lib.kvc_channel_prune_query
+    ws = lib.kvc_channel_prune_query_workspace_size(8, 4, 100, 128)
+    assert ws >= lib.kvc_channel_prune_workspace_size(8, 100, 128) + 8 * 4 * 128 * 4
+    assert lib.kvc_channel_prune_query_workspace_size(8, 0, 100, 128) == 0
+    assert lib.kvc_channel_prune_query_workspace_size(8, 4, 100, 64) == 0
+    qs = 16 * 128
+    ok = (FAKE, FAKE, 8, 4, 16, qs, 100, 128, 10, 0.4, FAKE, None, FAKE, FAKE, ws, None)
+
+    def call(**kw):
+        names = ["k", "q", "Hkv", "G", "w", "qs", "budget", "D", "recent", "lam", "ch", "mask", "kp", "ws",
+                 "nbytes", "stream"]
+        a = dict(zip(names, ok))
+        a.update(kw)
+        return f(*[a[n] for n in names])
+
+    assert call(q=None) == E.KVC_E_ARG
+    assert call(q=ctypes.c_void_p((1 << 21) + 8)) == E.KVC_E_ARG   # q not 16-byte aligned
+    assert call(G=0) == E.KVC_E_ARG
+    assert call(w=0) == E.KVC_E_ARG
+    assert call(qs=16 * 128 - 8) == E.KVC_E_SHAPE              # window rows overlap the next head
+    assert call(qs=16 * 128 + 4) == E.KVC_E_SHAPE              # head stride not a multiple of 8
+    assert call(Hkv=8192, G=16) == E.KVC_E_SHAPE               # Hkv * G > 65535
+    assert call(recent=101) == E.KVC_E_ARG
+    assert call(lam=1.0) == E.KVC_E_ARG
+    assert call(D=64) == E.KVC_E_UNSUPPORTED
+    assert call(ws=None) == E.KVC_E_WORKSPACE
+    assert call(nbytes=ws - 256) == E.KVC_E_WORKSPACE          # the magnitude path's size is not enough
+
+
 def test_timing_api_without_launches():
     assert lib.kvc_timing_enable(1) == E.KVC_OK
     assert lib.kvc_timing_count() == 0

@@ -249,3 +249,43 @@ def test_channel_prune_bit_exact(Hkv, B, recent, lam, p):
     kpb = bits_of(kp)
     for g in range(Hkv):
         assert np.array_equal(kpb[g], kc[g, :rows][:, gch[g]])
+
+
+@pytest.mark.parametrize("Hkv,G,w,wpad,B,recent,lam,loud", [
+    (8, 4, 32, 0, 2000, 64, 0.4, False),
+    (2, 1, 17, 0, 513, 1, 0.3, False),        # w not a multiple of the 16 row lanes
+    (3, 2, 8, 0, 100, 100, 0.4, False),       # no prunable rows: every score is 0, lowest channels win
+    (2, 8, 16, 0, 700, 0, 0.0, False),        # lambda 0 keeps every channel
+    (4, 4, 24, 40, 1500, 32, 0.5, True),      # window rows a slice of a longer query block; per-group loud channels
+])
+def test_channel_prune_query(Hkv, G, w, wpad, B, recent, lam, loud):
+    kvc = _kvc()
+    rng = np.random.default_rng(B + w)
+    x = rng.standard_normal((Hkv, B, 128), dtype=np.float32)
+    x[:, :, [5, 66, 99, 127]] *= 8
+    qf = rng.standard_normal((Hkv * G, w + wpad, 128), dtype=np.float32)
+    if loud:
+        qf[:, :, 66] = 0.0                                    # an outlier key channel no query uses
+        for g in range(Hkv):
+            qf[g * G:(g + 1) * G, :, [10 + g, 40 + 2 * g]] *= 16.0
+    kc, qb = wk.f32_to_bf16_bits(x), wk.f32_to_bf16_bits(qf)
+    T = oracle.sizes.think_channels(128, lam)
+    rows = B - recent
+    ch = torch.empty((Hkv, T), dtype=torch.int32, device=dev())
+    mask = torch.empty((Hkv, 128), dtype=torch.uint8, device=dev())
+    kp = torch.empty((Hkv, rows, T), dtype=torch.bfloat16, device=dev())
+    qd = to_dev(qb)[:, wpad:, :]                              # head stride (w + wpad) * D
+    kvc.kvc_channel_prune_query(to_dev(kc), qd, ch, kp, recent=recent, lam=lam, mask=mask)
+    torch.cuda.synchronize()
+    ref_ch, _, _, scores = oracle.think.think_prune_query(oracle.score.bf16_bits_to_f64(kc),
+                                                          oracle.score.bf16_bits_to_f64(qb[:, wpad:, :]),
+                                                          recent=recent, lam=lam)
+    gch = ch.cpu().numpy()
+    gmask = mask.cpu().numpy()
+    kpb = bits_of(kp)
+    for g in range(Hkv):
+        check_channels(gch[g], scores[g], ref_ch[g], T)
+        assert np.array_equal(gmask[g], np.isin(np.arange(128), gch[g]).astype(np.uint8))
+        assert np.array_equal(kpb[g], kc[g, :rows][:, gch[g]])
+        if loud:
+            assert 66 not in gch[g] and {10 + g, 40 + 2 * g} <= set(gch[g].tolist())

@@ -131,6 +131,28 @@ def test_think_s131072():
     assert np.array_equal(plan.mask.cpu().numpy().sum(axis=1), np.full(wl.Hkv, T))
 
 
+def test_think_s131072_query():
+    wl = wk.WORKLOADS["think_s131072_query"]
+    plan, (q, k, v), sc = _run(wl)
+    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=[5])
+    print("selection:", kinds)
+    # query-driven ThinK on the GPU's compacted keys and the window queries, every head
+    kc = bits_of(plan.kc)
+    T = oracle.sizes.think_channels(wl.D, wl.think_lambda)
+    ref_ch, _, _, scores = oracle.think.think_prune_query(oracle.score.bf16_bits_to_f64(kc),
+                                                          oracle.score.bf16_bits_to_f64(q),
+                                                          recent=wl.recent, lam=wl.think_lambda)
+    ch = plan.channels.cpu().numpy()
+    kp = bits_of(plan.kp)
+    rows = wl.budget - wl.recent
+    out = []
+    for g in range(wl.Hkv):
+        out.append(check_channels(ch[g], scores[g], ref_ch[g], T))
+        assert np.array_equal(kp[g], kc[g, :rows][:, ch[g]])
+    print("channels:", out)
+    assert np.array_equal(plan.mask.cpu().numpy().sum(axis=1), np.full(wl.Hkv, T))
+
+
 def test_zigzag_l32_s16384():
     wl = wk.WORKLOADS["zigzag_l32_s16384"]
     plan, (q, k, v), scales = _run(wl)
