@@ -20,12 +20,14 @@ written in the order and notation of the pages it cites:
                  a floor (ZigZagKV blog, observation and allocation sections).
 * ``pool``    -- SnapKV's 1D pooling of the importance along the keys.
 * ``select``  -- per-head top-k plus the recent window.
+* ``threshold`` -- KVzap's threshold rule with a sliding window (variable
+                 kept count per head, packed output) and the packed gather.
 * ``compact`` -- gather of the kept K/V rows.
-* ``think``   -- ThinK magnitude-based key-channel pruning.
+* ``think``   -- ThinK key-channel pruning, magnitude-based and query-driven.
 * ``sizes``   -- the KV-cache size formula and ThinK's kept-channel count.
 
 Parity status of each function (what pins it) is listed in each module's
 docstring; every function here has at least one pin in ``tests/``.
 """
 
-from . import budget, compact, philox, pool, score, select, sizes, think  # noqa: F401
+from . import budget, compact, philox, pool, score, select, sizes, think, threshold  # noqa: F401
