@@ -58,15 +58,19 @@ def calibrate_copy(mib):
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
 
 
-def algorithmic(wl):
-    """Algorithmic bytes and flops of one step, and per-kernel figures."""
+def algorithmic(wl, kept_rows=None):
+    """Algorithmic bytes and flops of one step, and per-kernel figures.  kept_rows:
+    the kept (head, token) rows of a threshold selection, which depend on the data."""
     L, H, Hkv, S, w, D, G = wl.L, wl.H, wl.Hkv, wl.S, wl.w, wl.D, wl.G
     n = S - w
     R = G * w
     q_bytes = L * H * w * D * 2
     k_prefix = L * Hkv * n * D * 2
     imp = L * Hkv * n * 4
-    B_total = wl.total_budget * Hkv if wl.total_budget else L * Hkv * wl.budget
+    if wl.threshold > 0:
+        B_total = kept_rows
+    else:
+        B_total = wl.total_budget * Hkv if wl.total_budget else L * Hkv * wl.budget
     rows = B_total * D * 2
     flops_pass = 2.0 * L * Hkv * R * n * D
     step_bytes = q_bytes + k_prefix + 2 * imp + B_total * 4 + 2 * rows * 2
@@ -85,6 +89,9 @@ def algorithmic(wl):
         "score_pass1_gumbel": ("mfma", flops_pass, q_bytes + k_prefix),
         "score_pass2_gumbel": ("mfma", flops_pass, q_bytes + k_prefix + imp),
         "select_topk": ("hbm", 0.0, imp + B_total * 4),
+        "threshold_count": ("hbm", 0.0, imp),
+        "threshold_emit": ("hbm", 0.0, imp + B_total * 4),
+        "compact_ragged": ("hbm", 0.0, 2 * rows * 2 + B_total * 4),
         "compact": ("hbm", 0.0, 2 * rows * 2 + B_total * 4),
         "lmba_mba": ("hbm", 0.0, imp),
         "pool_importance": ("hbm", 0.0, 2 * imp),
@@ -100,7 +107,7 @@ def algorithmic(wl):
 
 
 KERNEL_SOURCE = {"score": "score.hip", "select": "select.hip", "compact": "compact.hip", "lmba": "budget.hip",
-                 "pool": "pool.hip",
+                 "pool": "pool.hip", "threshold": "threshold.hip",
                  "think": "think.hip"}
 
 
@@ -145,7 +152,10 @@ def cpu_baseline(wl, data, target_s, tau):
         imp = oracle.score.importance(qf, kf, S=wl.S, w=wl.w, scale=scale, gumbel=wl.gumbel, tau=tau,
                                       seed=wl.noise_seed, kv_heads=[g])
         sc = oracle.pool.pool(imp[g:g + 1], wl.pool_kernel, wl.pool_mode)[0] if wl.pool_kernel else imp[g]
-        idx = oracle.select.select(sc, S=wl.S, w=wl.w, recent=wl.recent, budget=B)
+        if wl.threshold > 0:
+            idx = oracle.threshold.select_threshold(sc, S=wl.S, w=wl.w, recent=wl.recent, theta=wl.theta)
+        else:
+            idx = oracle.select.select(sc, S=wl.S, w=wl.w, recent=wl.recent, budget=B)
         kc = oracle.compact.compact(kraw[g:g + 1], idx[None])
         oracle.compact.compact(vraw[g:g + 1], idx[None])
         if wl.think_lambda >= 0 and wl.think_query:
@@ -160,7 +170,8 @@ def cpu_baseline(wl, data, target_s, tau):
     dt = time.perf_counter() - t0
     threads = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
     tokens = wl.S * heads / wl.Hkv        # one layer's prompt per Hkv heads of work
-    steps = "+".join(["score"] + (["pool"] if wl.pool_kernel else []) + ["select", "compact"]
+    steps = "+".join(["score"] + (["pool"] if wl.pool_kernel else [])
+                     + (["threshold", "compact"] if wl.threshold > 0 else ["select", "compact"])
                      + (["think"] if wl.think_lambda >= 0 else []))
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{heads} KV-head passes over layer 0 ({wl.Hkv} heads per layer; {steps}, "
@@ -229,7 +240,8 @@ def main():
 
     tokens = wl.L * wl.S
     value = tokens / (ms_step / 1e3)
-    step_bytes, flops_pass, per_kernel = algorithmic(wl)
+    kept_rows = int(plan.offsets[-1].item()) if wl.threshold > 0 else None   # after the timed region
+    step_bytes, flops_pass, per_kernel = algorithmic(wl, kept_rows)
     kernels = {name: {"launches": c, "avg_us": 1e3 * ms / c} for name, (c, ms) in kt.items()}
     dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
     avg_s = kernels[dom]["avg_us"] / 1e6
@@ -262,6 +274,7 @@ def main():
               "head_dim": wl.D, "window": wl.w, "recent": wl.recent,
               "budget_per_kv_head": wl.budget or None, "total_budget": wl.total_budget or None,
               "gumbel_tau": args.tau if wl.gumbel else None, "pool_kernel": wl.pool_kernel or None,
+              "threshold_x_uniform": wl.threshold or None, "kept_rows": kept_rows,
               "input_copies_rotated": copies}
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

@@ -204,6 +204,34 @@ kvc_status kvc_select_topk(const float* importance, int64_t imp_head_stride, int
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* kvc_select_threshold: keep every candidate scoring >= threshold.          */
+/* ------------------------------------------------------------------------ */
+/*
+ * Candidates C = [0, c), c = min(S - w, S - recent), as for kvc_select_topk.
+ * Head g keeps each candidate j with scores[g, j] >= threshold (compared in
+ * fp32; a NaN score is never kept), ascending, then every position of
+ * [S - recent, S).  The kept count varies per head and per prompt.  Heads are
+ * packed: head g's positions are indices[offsets[g] .. offsets[g + 1]),
+ * offsets[0] = 0, offsets[Hkv] = the total.
+ * Source: KVzap news page, inference section (thresholding plus a sliding
+ * window of recent tokens, giving a compression ratio that follows the
+ * prompt's information density).
+ * Layout: scores fp32, row g at scores + g * score_head_stride (>= S - w
+ *   entries, only the first c read); indices int32 with room for
+ *   Hkv * (c + recent) entries (the most that can be kept); offsets int32
+ *   [Hkv + 1].  Both are written on the device; read offsets[Hkv] back to
+ *   learn the total.
+ * Errors: KVC_E_ARG unless 0 <= recent <= S, 1 <= w < S and threshold is not
+ *   NaN (+-inf allowed); KVC_E_SHAPE if Hkv * (c + recent) >= 2^31.
+ *   Integer sums only: the output is deterministic.
+ */
+size_t kvc_select_threshold_workspace_size(int32_t Hkv, int32_t S, int32_t w, int32_t recent);
+
+kvc_status kvc_select_threshold(const float* scores, int64_t score_head_stride, int32_t Hkv, int32_t S,
+                                int32_t w, int32_t recent, float threshold, int32_t* indices,
+                                int32_t* offsets, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* kvc_compact: gather kept K/V rows into a dense cache.                     */
 /* ------------------------------------------------------------------------ */
 /*
@@ -219,6 +247,30 @@ kvc_status kvc_select_topk(const float* importance, int64_t imp_head_stride, int
 kvc_status kvc_compact(const void* k, const void* v, int32_t Hkv, int32_t S, int32_t D,
                        int64_t k_head_stride, int64_t v_head_stride, const int32_t* indices,
                        int32_t budget, void* k_out, void* v_out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* kvc_compact_ragged: gather kept rows of packed heads.                     */
+/* ------------------------------------------------------------------------ */
+/*
+ * For each head g and each t in [offsets[g], offsets[g + 1]) ∩ [0, max_rows):
+ * k_out[t, :] = k[g, indices[t], :] and v_out likewise (raw bf16 bytes): the
+ * compressed cache of a selection whose kept count varies per head, packed
+ * head after head as kvc_select_threshold writes it.
+ * Source: as kvc_compact (the kept tokens form the new, smaller cache), with
+ * the KVzap news page's variable per-prompt kept count.
+ * Layout: k, v as for kvc_compact; indices int32 and offsets int32 [Hkv + 1]
+ *   on the device (only the device reads them); k_out, v_out bf16
+ *   [max_rows, D].  indices must hold max_rows entries.  Whatever offsets
+ *   holds, no access leaves [0, max_rows) or [0, S) (an index outside [0, S)
+ *   yields a row of 0xFFFF).
+ * Errors: KVC_E_ARG for null or misaligned pointers, D % 8 != 0 or D > 1024;
+ *   KVC_E_UNSUPPORTED unless D / 8 divides 256; KVC_E_SHAPE if
+ *   max_rows * D / 8 >= 2^31.
+ */
+kvc_status kvc_compact_ragged(const void* k, const void* v, int32_t Hkv, int32_t S, int32_t D,
+                              int64_t k_head_stride, int64_t v_head_stride, const int32_t* indices,
+                              const int32_t* offsets, int32_t max_rows, void* k_out, void* v_out,
+                              void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* kvc_channel_prune: ThinK key-channel pruning of a compacted cache.        */

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvc.so")
 
-SOURCES = ["kvc_common.hip", "score.hip", "pool.hip", "select.hip", "compact.hip", "budget.hip", "think.hip"]
+SOURCES = ["kvc_common.hip", "score.hip", "pool.hip", "select.hip", "threshold.hip", "compact.hip", "budget.hip",
+           "think.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

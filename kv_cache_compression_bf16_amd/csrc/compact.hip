@@ -1,4 +1,6 @@
 // kvc_compact: gather the kept K and V rows into a dense per-head cache.
+// kvc_compact_ragged: the same for per-head kept counts that vary (packed
+// heads, as the threshold selection writes them).
 //
 // Keyformer blog page, prompt-phase paragraph: the kept tokens form the new,
 // smaller cache; KVzap news page: the cache is (2, L, H, T, D).  The copy is of
@@ -67,6 +69,47 @@ __global__ __launch_bounds__(256) void compact_chunks(const uint16_t* k, const u
   *reinterpret_cast<u32x4*>(dst + (int64_t)t * D + ch * 8) = val;
 }
 
+// Packed heads: head g's rows are [offsets[g], offsets[g + 1]) of indices and
+// of the outputs.  grid (row blocks, Hkv, planes); a workgroup strides over
+// its head's rows (the counts live on the device).  Every access is bounded
+// by max_rows and [0, S) whatever the offsets hold.
+template <int kRPT>
+__global__ __launch_bounds__(256) void compact_ragged_rows(const uint16_t* k, const uint16_t* v, int S, int D,
+                                                            int64_t khs, int64_t vhs, const int32_t* idx,
+                                                            const int32_t* offsets, int max_rows,
+                                                            uint16_t* ko, uint16_t* vo) {
+  const int g = blockIdx.y;
+  const bool isv = blockIdx.z != 0;
+  const uint16_t* src = (isv ? v : k) + g * (isv ? vhs : khs);
+  uint16_t* dst = isv ? vo : ko;
+  const int a = offsets[g], b = offsets[g + 1];
+  const int lo = max(a, 0), hi = min(b, max_rows);
+  const int chunks = D >> 3, rpp = 256 / chunks;
+  const int ch = threadIdx.x % chunks;
+  const int step = gridDim.x * rpp * kRPT;
+  for (int r0 = lo + blockIdx.x * rpp * kRPT + threadIdx.x / chunks; r0 - (int)(threadIdx.x / chunks) < hi;
+       r0 += step) {
+    int j[kRPT];
+#pragma unroll
+    for (int q = 0; q < kRPT; ++q) {
+      const int t = r0 + q * rpp;
+      j[q] = t < hi ? idx[t] : -1;
+    }
+    u32x4 val[kRPT];
+#pragma unroll
+    for (int q = 0; q < kRPT; ++q) {
+      const bool ok = j[q] >= 0 && j[q] < S;
+      val[q] = *reinterpret_cast<const u32x4*>(src + (int64_t)(ok ? j[q] : 0) * D + ch * 8);
+      if (!ok) val[q] = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    }
+#pragma unroll
+    for (int q = 0; q < kRPT; ++q) {
+      const int t = r0 + q * rpp;
+      if (t < hi) *reinterpret_cast<u32x4*>(dst + (int64_t)t * D + ch * 8) = val[q];
+    }
+  }
+}
+
 }  // namespace
 }  // namespace kvc
 
@@ -100,5 +143,36 @@ extern "C" kvc_status kvc_compact(const void* k, const void* v, int32_t Hkv, int
     KVC_LAUNCH("compact", compact_chunks, dim3((threads + 255) / 256, Hkv, planes), block, s, kp, vp, S, D,
                k_head_stride, v_head_stride, indices, budget, kop, vop);
   }
+  return KVC_OK;
+}
+
+extern "C" kvc_status kvc_compact_ragged(const void* k, const void* v, int32_t Hkv, int32_t S, int32_t D,
+                                         int64_t k_head_stride, int64_t v_head_stride, const int32_t* indices,
+                                         const int32_t* offsets, int32_t max_rows, void* k_out, void* v_out,
+                                         void* stream) {
+  using namespace kvc;
+  if (Hkv < 1 || S < 1 || max_rows < 0 || D < 8 || D > 1024 || (D & 7)) return KVC_E_ARG;
+  if (256 % (D / 8)) return KVC_E_UNSUPPORTED;
+  if (Hkv > 65535) return KVC_E_SHAPE;
+  if (!k || !k_out || !offsets || (max_rows > 0 && !indices)) return KVC_E_ARG;
+  if ((v == nullptr) != (v_out == nullptr)) return KVC_E_ARG;
+  if (k_head_stride < (int64_t)S * D || (v && v_head_stride < (int64_t)S * D)) return KVC_E_SHAPE;
+  if ((k_head_stride & 7) || (v && (v_head_stride & 7))) return KVC_E_ARG;
+  if (!aligned16(k) || !aligned16(k_out) || (v && (!aligned16(v) || !aligned16(v_out)))) return KVC_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(indices) & 3) || (reinterpret_cast<uintptr_t>(offsets) & 3)) return KVC_E_ARG;
+  if (max_rows == 0) return KVC_OK;
+  if ((int64_t)max_rows * (D / 8) > 0x7FFFFFFF - 256) return KVC_E_SHAPE;
+  constexpr int kRPT = 4;
+  const int rows_per_wg = 256 / (D / 8) * kRPT;
+  // rows per head are known only on the device: enough workgroups for an even
+  // share of max_rows per head, at most 256 per head, striding beyond that
+  int64_t per_head = ((int64_t)max_rows + Hkv - 1) / Hkv;
+  int gx = (int)((per_head + rows_per_wg - 1) / rows_per_wg);
+  gx = gx < 1 ? 1 : (gx > 256 ? 256 : gx);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  KVC_LAUNCH("compact_ragged", compact_ragged_rows<kRPT>, dim3(gx, Hkv, v ? 2 : 1), dim3(256), s,
+             static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), S, D, k_head_stride,
+             v_head_stride, indices, offsets, max_rows, static_cast<uint16_t*>(k_out),
+             static_cast<uint16_t*>(v_out));
   return KVC_OK;
 }

@@ -56,6 +56,9 @@ def _load():
         "kvc_select_topk_workspace_size": (SZ, [I32, I32]),
         "kvc_select_topk": (ctypes.c_int, [P, I64, I32, I32, I32, I32, I32, P, P, SZ, P]),
         "kvc_compact": (ctypes.c_int, [P, P, I32, I32, I32, I64, I64, P, I32, P, P, P]),
+        "kvc_select_threshold_workspace_size": (SZ, [I32, I32, I32, I32]),
+        "kvc_select_threshold": (ctypes.c_int, [P, I64, I32, I32, I32, I32, ctypes.c_float, P, P, P, SZ, P]),
+        "kvc_compact_ragged": (ctypes.c_int, [P, P, I32, I32, I32, I64, I64, P, P, I32, P, P, P]),
         "kvc_channel_prune_workspace_size": (SZ, [I32, I32, I32]),
         "kvc_channel_prune": (ctypes.c_int, [P, I32, I32, I32, I32, F64, I32, P, P, P, P, SZ, P]),
         "kvc_channel_prune_query_workspace_size": (SZ, [I32, I32, I32, I32]),
@@ -228,6 +231,44 @@ def kvc_compact(k, v, indices, k_out, v_out, *, S, stream=None):
     _check(_lib.kvc_compact(_ptr(k), _ptr(v), Hkv, S, D, k.stride(0), 0 if v is None else v.stride(0),
                             _ptr(indices), budget, _ptr(k_out), _ptr(v_out), _stream(stream, k.device)),
            "kvc_compact")
+    return k_out, v_out
+
+
+# ---------------------------------------------------------------- kvc_select_threshold
+def kvc_select_threshold(scores, indices, offsets, *, S, w, recent, threshold, workspace=None, stream=None):
+    """Keep candidates with score >= threshold plus the recent window; packed heads.
+    scores [Hkv, >= S - w] fp32; indices int32 with Hkv * (c + recent) entries; offsets int32 [Hkv + 1]."""
+    if scores.dtype != torch.float32 or indices.dtype != torch.int32 or offsets.dtype != torch.int32:
+        raise TypeError("scores must be float32, indices and offsets int32")
+    if scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be [Hkv, n] with unit stride along n")
+    Hkv = scores.shape[0]
+    c = min(S - w, S - recent)
+    if offsets.numel() != Hkv + 1 or indices.numel() < Hkv * (c + recent):
+        raise ValueError(f"offsets needs {Hkv + 1} entries and indices {Hkv * (c + recent)}")
+    ws, nbytes = _workspace(_lib.kvc_select_threshold_workspace_size(Hkv, S, w, recent), scores.device, workspace)
+    _check(_lib.kvc_select_threshold(_ptr(scores), scores.stride(0), Hkv, S, w, recent, float(threshold),
+                                     _ptr(indices), _ptr(offsets), _ptr(ws), nbytes,
+                                     _stream(stream, scores.device)), "kvc_select_threshold")
+    return indices, offsets
+
+
+def kvc_compact_ragged(k, v, indices, offsets, k_out, v_out, *, S, stream=None):
+    """Gather packed heads: k [Hkv, S_alloc, D] -> k_out [max_rows, D] (v likewise, or None)."""
+    _bf16(k, "k")
+    Hkv, _, D = k.shape
+    max_rows = k_out.shape[0]
+    if k.stride(1) != D or k.stride(2) != 1 or not k_out.is_contiguous() or k_out.shape[-1] != D:
+        raise ValueError("k rows must be contiguous with stride D and k_out [max_rows, D] contiguous")
+    if indices.numel() < max_rows or offsets.numel() != Hkv + 1:
+        raise ValueError("indices needs max_rows entries and offsets Hkv + 1")
+    if v is not None:
+        _bf16(v, "v")
+        if v.shape != k.shape or v.stride(1) != D or v_out.shape != k_out.shape or not v_out.is_contiguous():
+            raise ValueError("v / v_out must match k / k_out")
+    _check(_lib.kvc_compact_ragged(_ptr(k), _ptr(v), Hkv, S, D, k.stride(0), 0 if v is None else v.stride(0),
+                                   _ptr(indices), _ptr(offsets), max_rows, _ptr(k_out), _ptr(v_out),
+                                   _stream(stream, k.device)), "kvc_compact_ragged")
     return k_out, v_out
 
 

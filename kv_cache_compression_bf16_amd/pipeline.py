@@ -1,8 +1,8 @@
 """Composition of the C-ABI calls into whole compression passes.
 
 Each pass is a fixed sequence of libkvc calls on one stream: score ->
-[SnapKV pooling] -> [ZigZag budgets] -> select -> compact -> [ThinK, by key norms or by
-the window queries].  Buffers are allocated once
+[SnapKV pooling] -> [ZigZag budgets] -> select (top-k, or KVzap's threshold with packed
+heads) -> compact -> [ThinK, by key norms or by the window queries].  Buffers are allocated once
 per plan (through torch) so a pass itself allocates nothing on the device.
 No arithmetic happens here.
 """
@@ -49,6 +49,14 @@ class CompressionPlan:
             self.indices_flat = torch.empty(Hkv * tot, dtype=i32, device=device)
             self.kc_flat = torch.empty(Hkv * tot * D, dtype=bf, device=device)
             self.vc_flat = torch.empty(Hkv * tot * D, dtype=bf, device=device)
+        elif wl.threshold > 0:
+            cap = Hkv * wl.capacity                  # the most a threshold can keep
+            self.ws_thr = torch.empty(max(kvc.lib.kvc_select_threshold_workspace_size(Hkv, wl.S, wl.w, wl.recent),
+                                          256), dtype=torch.uint8, device=device)
+            self.indices_flat = torch.empty(cap, dtype=i32, device=device)
+            self.offsets = torch.empty(Hkv + 1, dtype=i32, device=device)
+            self.kc_flat = torch.empty((cap, D), dtype=bf, device=device)
+            self.vc_flat = torch.empty((cap, D), dtype=bf, device=device)
         else:
             B = wl.budget
             self.indices = torch.empty((Hkv, B), dtype=i32, device=device)
@@ -80,6 +88,12 @@ class CompressionPlan:
         if wl.pool_kernel:
             kvc.kvc_pool_importance(self.importance, self.pooled, kernel=wl.pool_kernel, mode=wl.pool_mode,
                                     stream=stream)
+        if wl.threshold > 0:
+            kvc.kvc_select_threshold(self.scores[0], self.indices_flat, self.offsets, S=wl.S, w=wl.w,
+                                     recent=wl.recent, threshold=wl.theta, workspace=self.ws_thr, stream=stream)
+            kvc.kvc_compact_ragged(k if k.dim() == 3 else k[0], v if v.dim() == 3 else v[0], self.indices_flat,
+                                   self.offsets, self.kc_flat, self.vc_flat, S=wl.S, stream=stream)
+            return
         if not self.zigzag:
             kvc.kvc_select_topk(self.scores[0], self.indices, S=wl.S, w=wl.w, recent=wl.recent,
                                 budget=wl.budget, workspace=self.ws_select, stream=stream)

@@ -53,6 +53,7 @@ class Workload:
     think_query: bool = False       # query-driven ThinK score (window queries x keys) instead of l_p norms
     pool_kernel: int = 0            # SnapKV 1D pooling of the importance before top-k (0: off)
     pool_mode: int = 0              # 0: average (zero padding, / kernel), 1: max
+    threshold: float = 0.0          # > 0: KVzap threshold selection at threshold * G / (S - w), not top-k
     seed: int = 0
     notes: str = field(default="", compare=False)
 
@@ -72,6 +73,11 @@ class Workload:
     def capacity(self):
         return self.n_candidates + self.recent
 
+    @property
+    def theta(self):
+        """The threshold in importance units (float32), for threshold selection."""
+        return float(np.float32(self.threshold * self.G / self.n))
+
     def with_(self, **kw):
         return replace(self, **kw)
 
@@ -88,6 +94,11 @@ WORKLOADS = {
         name="gqa32x8_s32768_pool7", cfg_id=1, L=1, H=32, Hkv=8, S=32768, w=128, recent=64, budget=2048,
         outliers=4, pool_kernel=7, pool_mode=0,
         notes="the GQA layer above (same inputs) with SnapKV's average pooling (kernel 7) before top-k"),
+    "gqa32x8_s32768_thr2": Workload(
+        name="gqa32x8_s32768_thr2", cfg_id=1, L=1, H=32, Hkv=8, S=32768, w=128, recent=64,
+        outliers=4, threshold=2.0,
+        notes="the GQA layer above (same inputs) with KVzap's threshold rule at twice the uniform share, "
+              "packed per-head output"),
     "zigzag_l32_s16384": Workload(
         name="zigzag_l32_s16384", cfg_id=2, L=32, H=8, Hkv=8, S=16384, w=128, recent=128,
         total_budget=32 * 1024, floor=128, scale_range=(0.5, 3.0),

@@ -180,6 +180,52 @@ def test_channel_prune_validation():
     assert f(FAKE, 8, 100, 128, 10, 0.999, 2, FAKE, None, FAKE, FAKE, ws, None) == E.KVC_E_ARG  # T = 0
 
 
+def _named_call(f, names, ok):
+    def call(**kw):
+        a = dict(zip(names, ok))
+        a.update(kw)
+        return f(*[a[n] for n in names])
+    return call
+
+
+def test_select_threshold_validation():
+    ws = lib.kvc_select_threshold_workspace_size(8, 1000, 32, 32)
+    assert ws >= 8 * 4 and lib.kvc_select_threshold_workspace_size(8, 1000, 1000, 32) == 0
+    names = ["s", "hs", "Hkv", "S", "w", "r", "th", "idx", "off", "ws", "nb", "st"]
+    call = _named_call(lib.kvc_select_threshold, names,
+                       (FAKE, 1000, 8, 1000, 32, 32, 0.5, FAKE, FAKE, FAKE, ws, None))
+    assert call(w=0) == E.KVC_E_ARG
+    assert call(w=1000) == E.KVC_E_ARG
+    assert call(r=1001) == E.KVC_E_ARG
+    assert call(th=float("nan")) == E.KVC_E_ARG
+    assert call(hs=100) == E.KVC_E_SHAPE                                  # stride < S - w
+    assert call(Hkv=70000) == E.KVC_E_SHAPE
+    assert call(Hkv=65535, S=40000, hs=40000) == E.KVC_E_SHAPE             # Hkv * (c + r) >= 2^31
+    assert call(idx=None) == E.KVC_E_ARG
+    assert call(off=None) == E.KVC_E_ARG
+    assert call(s=None) == E.KVC_E_ARG
+    assert call(s=ctypes.c_void_p((1 << 20) + 2)) == E.KVC_E_ARG           # misaligned scores
+    assert call(ws=None) == E.KVC_E_WORKSPACE
+    assert call(nb=8 * 4 - 4) == E.KVC_E_WORKSPACE
+
+
+def test_compact_ragged_validation():
+    names = ["k", "v", "Hkv", "S", "D", "khs", "vhs", "idx", "off", "rows", "ko", "vo", "st"]
+    call = _named_call(lib.kvc_compact_ragged, names,
+                       (FAKE, FAKE, 8, 1000, 128, 1000 * 128, 1000 * 128, FAKE, FAKE, 4000, FAKE, FAKE, None))
+    assert call(D=100) == E.KVC_E_ARG
+    assert call(D=48, khs=1000 * 48, vhs=1000 * 48) == E.KVC_E_UNSUPPORTED    # 256 % (48 / 8) != 0
+    assert call(rows=-1) == E.KVC_E_ARG
+    assert call(off=None) == E.KVC_E_ARG
+    assert call(idx=None) == E.KVC_E_ARG
+    assert call(vo=None) == E.KVC_E_ARG                                    # v without v_out
+    assert call(khs=999 * 128) == E.KVC_E_SHAPE
+    assert call(k=ctypes.c_void_p((1 << 20) + 8)) == E.KVC_E_ARG
+    assert call(off=ctypes.c_void_p((1 << 20) + 2)) == E.KVC_E_ARG
+    assert call(rows=1 << 30) == E.KVC_E_SHAPE                             # max_rows * D / 8 >= 2^31
+    assert call(rows=0) == E.KVC_OK                                        # nothing to gather: no launch
+
+
 def test_channel_prune_query_validation():
     f = lib.kvc_channel_prune_query
     ws = lib.kvc_channel_prune_query_workspace_size(8, 4, 100, 128)

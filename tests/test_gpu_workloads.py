@@ -153,6 +153,37 @@ def test_think_s131072_query():
     assert np.array_equal(plan.mask.cpu().numpy().sum(axis=1), np.full(wl.Hkv, T))
 
 
+def test_gqa32x8_s32768_thr2():
+    wl = wk.WORKLOADS["gqa32x8_s32768_thr2"]
+    plan, (q, k, v), sc = _run(wl)
+    imp = plan.importance[0].cpu().numpy()
+    theta = np.float32(wl.theta)
+    # the threshold selection in isolation on the GPU's own importance: bit-exact
+    gi, go = plan.indices_flat.cpu().numpy(), plan.offsets.cpu().numpy()
+    ri, ro = oracle.threshold.select_threshold_heads(imp, S=wl.S, w=wl.w, recent=wl.recent, theta=theta)
+    assert np.array_equal(go, ro)
+    total = int(go[-1])
+    assert np.array_equal(gi[:total], ri)
+    counts = np.diff(go) - wl.recent
+    print("kept per head:", counts.tolist())
+    assert counts.min() > 0 and len(set(counts.tolist())) > 1, "kept counts should vary by head"
+    # packed compaction, every head: bit-exact against the gather at the GPU's indices
+    assert np.array_equal(bits_of(plan.kc_flat[:total]), oracle.threshold.compact_ragged(k, ri, ro))
+    assert np.array_equal(bits_of(plan.vc_flat[:total]), oracle.threshold.compact_ragged(v, ri, ro))
+    # a sampled head against the oracle's own importance: the keep decision may
+    # differ only for candidates within the importance tolerance of theta
+    g = 2
+    ref = _oracle_imp(wl, q, k, sc[0], [g])[g]
+    check_importance(imp[g][None], ref[None], wl.G, f"head {g}")
+    c = wl.n_candidates
+    mine = set(gi[go[g]:go[g + 1]].tolist())
+    theirs = set(oracle.threshold.select_threshold(ref, S=wl.S, w=wl.w, recent=wl.recent,
+                                                   theta=float(theta)).tolist())
+    for j in mine ^ theirs:
+        assert j < c and abs(ref[j] - float(theta)) <= 1e-3 * ref[j], f"candidate {j} decided away from theta"
+    print("decisions that differ near theta:", len(mine ^ theirs))
+
+
 def test_zigzag_l32_s16384():
     wl = wk.WORKLOADS["zigzag_l32_s16384"]
     plan, (q, k, v), scales = _run(wl)
