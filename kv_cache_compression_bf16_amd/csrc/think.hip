@@ -10,26 +10,31 @@
 // that get pruned); a KV head's query side stacks its G query heads' windows.
 //
 // Design (D = 128):
-//  * think_partial: grid (row chunks of 512, heads); 16 lanes cover one
-//    256-byte row with 16-byte loads, 16 rows in flight per workgroup; per-lane
-//    fp32 sums of |x|^p, folded over the 16 row lanes in a fixed order ->
-//    partial[g, chunk, d].
+//  * think_partial: grid (row chunks of 256, heads); 16 lanes cover one
+//    256-byte row with 16-byte loads and each thread issues its 16 rows'
+//    loads together (addresses clamped, tail masked); per-lane fp32 sums of
+//    |x|^p, folded over the 16 row lanes in a fixed order -> partial[g, chunk, d].
 //  * think_qpartial (query-driven only): grid (G, heads), the same row layout
 //    over one query head's w window rows -> per-channel sums of q^2.
-//  * think_select: one 128-thread workgroup per head folds the chunk partials
-//    in order (times the folded query sums, query-driven: ||Q|| ||K|| and its
-//    square rank alike), ranks channels by (score desc, index asc), writes the
-//    kept channels ascending and the mask.
-//  * think_gather: one wave per row; lane l holds bf16 channels 2l, 2l+1 of the
-//    row, output channel c takes its value with one cross-lane read from lane
-//    channels[c]/2 and the rows are written contiguously.
+//  * think_select: one workgroup per head, 8 groups of 128 threads, group i
+//    folding chunks i, i+8, ... (loads in flight), then the 8 group sums in a
+//    fixed order (times the folded query sums, query-driven: ||Q|| ||K|| and
+//    its square rank alike); channels ranked by (score desc, index asc), kept
+//    channels written ascending, and the mask.
+//  * think_gather: a wave takes 8 rows at a time (8 loads in flight); lane l
+//    holds bf16 channels 2l, 2l+1 of a row and an output channel takes its
+//    value with one cross-lane read from lane channels[c]/2.  With T even and
+//    a 4-byte aligned output, lane c/2 packs output channels c, c+1 into one
+//    4-byte store; otherwise 2-byte stores.
 #include "common.h"
 
 namespace kvc {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kChunkRows = 512;
+constexpr int kChunkRows = 256;
+constexpr int kRowsPerThread = kChunkRows / 16;
+constexpr int kSelGroups = 8;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -43,20 +48,28 @@ __global__ __launch_bounds__(256) void think_partial(const uint16_t* kc, int bud
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   const int r0 = chunk * kChunkRows;
-  const int r1 = min(r0 + kChunkRows, rows);
   const uint16_t* base = kc + (int64_t)g * budget * kD + cg * 8;
-  for (int r = r0 + rl; r < r1; r += 16) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(base + (int64_t)r * kD);
-    const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+  if (rows > 0) {
+    u32x4 x[kRowsPerThread];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = bf16_lo(wv[e]), b = bf16_hi(wv[e]);
-      if (p == 2) {
-        acc[2 * e] = fmaf(a, a, acc[2 * e]);
-        acc[2 * e + 1] = fmaf(b, b, acc[2 * e + 1]);
-      } else {
-        acc[2 * e] += fabsf(a);
-        acc[2 * e + 1] += fabsf(b);
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const int r = r0 + rl + 16 * i;
+      x[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)(r < rows ? r : rows - 1) * kD);
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      if (r0 + rl + 16 * i >= rows) continue;
+      const uint32_t wv[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = bf16_lo(wv[e]), b = bf16_hi(wv[e]);
+        if (p == 2) {
+          acc[2 * e] = fmaf(a, a, acc[2 * e]);
+          acc[2 * e + 1] = fmaf(b, b, acc[2 * e + 1]);
+        } else {
+          acc[2 * e] += fabsf(a);
+          acc[2 * e + 1] += fabsf(b);
+        }
       }
     }
   }
@@ -102,49 +115,103 @@ __global__ __launch_bounds__(256) void think_qpartial(const uint16_t* q, int64_t
 }
 
 // qpart == nullptr: magnitude score; else the query-driven score (squared).
-__global__ __launch_bounds__(kD) void think_select(const float* part, int nchunk, const float* qpart, int G,
-                                                  int T, int32_t* channels, uint8_t* mask) {
+__global__ __launch_bounds__(kD * kSelGroups) void think_select(const float* part, int nchunk, const float* qpart,
+                                                               int G, int T, int32_t* channels, uint8_t* mask) {
+  __shared__ float red[kSelGroups][kD];
   __shared__ float sm[kD];
   __shared__ int ssel[kD];
-  const int g = blockIdx.x, d = threadIdx.x;
+  const int g = blockIdx.x, d = threadIdx.x & (kD - 1), grp = threadIdx.x / kD;
+  const float* pp = part + (int64_t)g * nchunk * kD + d;
+  // chunks grp + 8i go to sum i % 4 (four loads in flight), joined in order
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+  int c = grp;
+  for (; c + 3 * kSelGroups < nchunk; c += 4 * kSelGroups) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] += pp[(int64_t)(c + j * kSelGroups) * kD];
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (c + j * kSelGroups < nchunk) a[j] += pp[(int64_t)(c + j * kSelGroups) * kD];
+  red[grp][d] = (a[0] + a[1]) + (a[2] + a[3]);
+  __syncthreads();
+  // group 0 (threads 0..127) ranks; every thread still meets every barrier
   float M = 0.f;
-  for (int c = 0; c < nchunk; ++c) M += part[((int64_t)g * nchunk + c) * kD + d];
-  if (qpart) {
-    float qn = 0.f;
-    for (int hh = 0; hh < G; ++hh) qn += qpart[((int64_t)g * G + hh) * kD + d];
-    M *= qn;
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < kSelGroups; ++i) M += red[i][d];
+    if (qpart) {
+      float qn = 0.f;
+      for (int hh = 0; hh < G; ++hh) qn += qpart[((int64_t)g * G + hh) * kD + d];
+      M *= qn;
+    }
+    sm[d] = M;
   }
-  sm[d] = M;
   __syncthreads();
-  int rank = 0;
-  for (int e = 0; e < kD; ++e) {
-    const float o = sm[e];
-    rank += (o > M || (o == M && e < d)) ? 1 : 0;
+  bool sel = false;
+  if (grp == 0) {
+    int rank = 0;
+    for (int e = 0; e < kD; ++e) {
+      const float o = sm[e];
+      rank += (o > M || (o == M && e < d)) ? 1 : 0;
+    }
+    sel = rank < T;
+    ssel[d] = sel ? 1 : 0;
   }
-  const bool sel = rank < T;
-  ssel[d] = sel ? 1 : 0;
   __syncthreads();
+  if (grp != 0) return;
   int pos = 0;
   for (int e = 0; e < d; ++e) pos += ssel[e];
   if (sel && pos < T) channels[(int64_t)g * T + pos] = d;   // pos < T unless norms are NaN
   if (mask) mask[(int64_t)g * kD + d] = sel ? 1 : 0;
 }
 
+// kPairs: T even and the output 4-byte aligned (lane l < T/2 stores output
+// channels 2l and 2l+1 as one 4-byte word); else lanes l and l+64 store one
+// bf16 each.
+template <bool kPairs>
 __global__ __launch_bounds__(256) void think_gather(const uint16_t* kc, int budget, int rows, int T,
                                                    const int32_t* channels, uint16_t* out) {
+  constexpr int kRows = 8;   // rows per wave per step, loads in flight
   const int g = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int32_t* ch = channels + (int64_t)g * T;
-  const int c0 = lane, c1 = lane + 64;
-  const int s0 = c0 < T ? ch[c0] : 0;
-  const int s1 = c1 < T ? ch[c1] : 0;
+  int s0, s1;
+  bool w0, w1;
+  if (kPairs) {
+    w0 = 2 * lane < T;
+    w1 = false;
+    s0 = w0 ? ch[2 * lane] : 0;
+    s1 = w0 ? ch[2 * lane + 1] : 0;
+  } else {
+    w0 = lane < T;
+    w1 = lane + 64 < T;
+    s0 = w0 ? ch[lane] : 0;
+    s1 = w1 ? ch[lane + 64] : 0;
+  }
   const uint32_t* src = reinterpret_cast<const uint32_t*>(kc + (int64_t)g * budget * kD);
   uint16_t* dst = out + (int64_t)g * rows * T;
-  for (int r = blockIdx.x * 4 + wave; r < rows; r += gridDim.x * 4) {
-    const uint32_t x = src[(int64_t)r * (kD / 2) + lane];
-    const uint32_t y0 = __shfl(x, s0 >> 1);
-    const uint32_t y1 = __shfl(x, s1 >> 1);
-    if (c0 < T) dst[(int64_t)r * T + c0] = (uint16_t)((s0 & 1) ? (y0 >> 16) : (y0 & 0xFFFFu));
-    if (c1 < T) dst[(int64_t)r * T + c1] = (uint16_t)((s1 & 1) ? (y1 >> 16) : (y1 & 0xFFFFu));
+  const int step = gridDim.x * 4 * kRows;
+  for (int r0 = (blockIdx.x * 4 + wave) * kRows; r0 < rows; r0 += step) {
+    uint32_t x[kRows];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+      const int r = r0 + j < rows ? r0 + j : rows - 1;
+      x[j] = src[(int64_t)r * (kD / 2) + lane];
+    }
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+      const int r = r0 + j;
+      const uint32_t y0 = __shfl(x[j], s0 >> 1);
+      const uint32_t y1 = __shfl(x[j], s1 >> 1);
+      const uint32_t v0 = (s0 & 1) ? (y0 >> 16) : (y0 & 0xFFFFu);
+      const uint32_t v1 = (s1 & 1) ? (y1 >> 16) : (y1 & 0xFFFFu);
+      if (r >= rows) continue;
+      if (kPairs) {
+        if (w0) reinterpret_cast<uint32_t*>(dst + (int64_t)r * T)[lane] = v0 | (v1 << 16);
+      } else {
+        if (w0) dst[(int64_t)r * T + lane] = (uint16_t)v0;
+        if (w1) dst[(int64_t)r * T + lane + 64] = (uint16_t)v1;
+      }
+    }
   }
 }
 
@@ -185,12 +252,18 @@ kvc_status channel_prune(const void* k_c, const void* q, int32_t G, int32_t w, i
   if (q)
     KVC_LAUNCH("think_qpartial", think_qpartial, dim3(G, Hkv), dim3(256), s, static_cast<const uint16_t*>(q),
                q_hs, G, w, qpart);
-  KVC_LAUNCH("think_select", think_select, dim3(Hkv), dim3(kD), s, part, nchunk, qpart, G, T, channels, mask);
+  KVC_LAUNCH("think_select", think_select, dim3(Hkv), dim3(kD * kSelGroups), s, part, nchunk, qpart, G, T,
+             channels, mask);
   if (rows > 0) {
-    int gx = (rows + 3) / 4;
-    if (gx > 2048) gx = 2048;
-    KVC_LAUNCH("think_gather", think_gather, dim3(gx, Hkv), dim3(256), s, kcp, budget, rows, T, channels,
-               static_cast<uint16_t*>(k_pruned));
+    int gx = (rows + 31) / 32;   // 4 waves x 8 rows per workgroup step
+    if (gx > 1024) gx = 1024;
+    uint16_t* kp = static_cast<uint16_t*>(k_pruned);
+    if ((T & 1) == 0 && (reinterpret_cast<uintptr_t>(k_pruned) & 3) == 0)
+      KVC_LAUNCH("think_gather", think_gather<true>, dim3(gx, Hkv), dim3(256), s, kcp, budget, rows, T, channels,
+                 kp);
+    else
+      KVC_LAUNCH("think_gather", think_gather<false>, dim3(gx, Hkv), dim3(256), s, kcp, budget, rows, T, channels,
+                 kp);
   }
   return KVC_OK;
 }
