@@ -14,12 +14,18 @@ Source: ThinK page (papercache summary of arXiv 2407.21018, ICLR 2025):
   (the Frobenius norm of the outer product of the channel's window-query column
   and key column), and the T highest-scoring channels are kept.
 
+* supplementary section on value-cache pruning: channel j of the value cache
+  scores Score_v[j] = ||softmax(Q[-S_obs:] K^T / sqrt(D)) V[:, j]||_F and the
+  T highest-scoring value channels are kept.
+
 Readings: the norm runs over the non-recent kept rows (the rows that get
 pruned), i.e. the first budget - r rows of the compacted cache, whose positions
 all precede the recent window; ties in M go to the lower channel; the kept
-channel list is ascending; V is not touched.  For the query-driven score of a
-KV head shared by G query heads, the window queries of those G heads are
-stacked (G*w rows); the key side is the same non-recent kept rows.
+channel list is ascending.  For the query-driven score of a KV head shared by
+G query heads, the window queries of those G heads are stacked (G*w rows); the
+key side is the same non-recent kept rows.  Value pruning (a separate call)
+takes K and V over those same rows U: the softmax of each stacked query row is
+normalised over U, with the logit scale given (1/sqrt(D) on the page).
 """
 
 import numpy as np
@@ -93,4 +99,48 @@ def think_prune_query(kc, q_obs, *, recent, lam):
         chans[g] = c
         mask[g, c] = 1
         pruned[g] = kc[g, :rows][:, c]
+    return chans, mask, pruned, scores
+
+
+def value_scores(q_group, kc_rows, vc_rows, scale):
+    """Score_v[d] = ||softmax(scale * Q K^T) V[:, d]||_2 over the stacked query rows.
+
+    q_group [R, D], kc_rows / vc_rows [U, D] (float64).  The softmax of each
+    query row runs over the U keys.  Returns float64 [D].
+    """
+    q = np.asarray(q_group, dtype=np.float64)
+    k = np.asarray(kc_rows, dtype=np.float64)
+    v = np.asarray(vc_rows, dtype=np.float64)
+    x = scale * (q @ k.T)                                   # [R, U] logits
+    x -= x.max(axis=1, keepdims=True)
+    e = np.exp(x)
+    P = e / e.sum(axis=1, keepdims=True)                    # row softmax
+    O = P @ v                                               # [R, D] attention output
+    return np.sqrt((O * O).sum(axis=0))                     # Frobenius norm per channel
+
+
+def think_prune_value(kc, vc, q_obs, *, recent, lam, scale):
+    """Value-channel pruning.  kc, vc: [Hkv, B, D] float64 compacted cache
+    (recent rows last); q_obs: [H, w, D] float64, head h in group h // G.
+
+    Returns (channels [Hkv, T] ascending, mask [Hkv, D], pruned values
+    [Hkv, B - recent, T], scores [Hkv, D]).
+    """
+    Hkv, B, D = vc.shape
+    G = q_obs.shape[0] // Hkv
+    T = kept_channels(D, lam)
+    rows = B - recent
+    chans = np.empty((Hkv, T), dtype=np.int64)
+    mask = np.zeros((Hkv, D), dtype=np.uint8)
+    scores = np.zeros((Hkv, D))
+    pruned = np.empty((Hkv, rows, T))
+    for g in range(Hkv):
+        if rows > 0:
+            qg = q_obs[g * G:(g + 1) * G].reshape(-1, D)
+            scores[g] = value_scores(qg, kc[g, :rows], vc[g, :rows], scale)
+        order = np.lexsort((np.arange(D), -scores[g]))
+        c = np.sort(order[:T])
+        chans[g] = c
+        mask[g, c] = 1
+        pruned[g] = vc[g, :rows][:, c]
     return chans, mask, pruned, scores

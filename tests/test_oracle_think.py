@@ -9,9 +9,14 @@
   ThinK page, about 335 GB on the KVzap page).
 * Query-driven score (outer-product Frobenius norm) against the rank-1
   identity ||q k^T||_F = ||q|| ||k||, and a case the query side decides.
+* Value-channel score: one key (output rows = that value row) and zero
+  queries (uniform attention: output rows = the mean value row) in closed
+  form, exact linearity in each value channel, explicit loops on a tiny case,
+  and per-group selection with recent rows not voting.
 """
 
 import json
+import math
 import os
 
 import numpy as np
@@ -108,3 +113,61 @@ def test_query_driven_prefers_channels_the_queries_use():
         assert 5 not in ch[g] and set(loud[g]) <= set(ch[g].tolist())
         assert np.array_equal(pruned[g], kc[g, :B - recent][:, ch[g]])
         assert mask[g].sum() == 8
+
+
+def test_value_score_single_key_and_uniform_attention():
+    rng = np.random.default_rng(21)
+    R, D = 12, 16
+    q = rng.standard_normal((R, D))
+    k1, v1 = rng.standard_normal((1, D)), rng.standard_normal((1, D))
+    # one key: every softmax row is [1], the output rows are V[0]
+    assert np.allclose(think.value_scores(q, k1, v1, 0.3), np.sqrt(R) * np.abs(v1[0]), rtol=1e-13)
+    # zero queries: uniform attention, the output rows are the mean value row
+    k, v = rng.standard_normal((9, D)), rng.standard_normal((9, D))
+    got = think.value_scores(np.zeros((R, D)), k, v, 0.3)
+    assert np.allclose(got, np.sqrt(R) * np.abs(v.mean(axis=0)), rtol=1e-12)
+
+
+def test_value_score_is_linear_in_each_value_channel():
+    rng = np.random.default_rng(22)
+    q, k, v = rng.standard_normal((10, 8)), rng.standard_normal((30, 8)), rng.standard_normal((30, 8))
+    base = think.value_scores(q, k, v, 0.5)
+    v2 = v.copy()
+    v2[:, 3] *= -4.0
+    got = think.value_scores(q, k, v2, 0.5)
+    assert np.isclose(got[3], 4.0 * base[3], rtol=1e-12)
+    assert np.allclose(np.delete(got, 3), np.delete(base, 3), rtol=1e-12)
+
+
+def test_value_score_brute_force():
+    rng = np.random.default_rng(23)
+    R, U, D, a = 3, 4, 5, 0.7
+    q, k, v = rng.standard_normal((R, D)), rng.standard_normal((U, D)), rng.standard_normal((U, D))
+    want = []
+    for d in range(D):
+        tot = 0.0
+        for i in range(R):
+            w = [math.exp(a * sum(q[i, e] * k[j, e] for e in range(D))) for j in range(U)]
+            o = sum(w[j] * v[j, d] for j in range(U)) / sum(w)
+            tot += o * o
+        want.append(math.sqrt(tot))
+    assert np.allclose(think.value_scores(q, k, v, a), want, rtol=1e-12)
+
+
+def test_value_pruning_grouping_and_gather():
+    # uniform attention per group (zero queries): the score is sqrt(G*w) * |mean of
+    # the non-recent V rows|, so each group keeps the channels its own values make loud
+    rng = np.random.default_rng(24)
+    Hkv, G, w, B, D, recent = 2, 3, 2, 24, 16, 4
+    kc = rng.standard_normal((Hkv, B, D))
+    vc = rng.standard_normal((Hkv, B, D)) * 0.01
+    vc[0, :B - recent, [1, 6]] += 5.0
+    vc[1, :B - recent, [2, 11]] += 5.0
+    vc[:, B - recent:, 9] = 100.0                            # recent rows do not vote
+    ch, mask, pruned, sc = think.think_prune_value(kc, vc, np.zeros((Hkv * G, w, D)), recent=recent, lam=0.75,
+                                                   scale=0.25)
+    assert {1, 6} <= set(ch[0].tolist())
+    assert {2, 11} <= set(ch[1].tolist()) and 9 not in ch[0] and 9 not in ch[1]
+    assert np.allclose(sc[1], np.sqrt(G * w) * np.abs(vc[1, :B - recent].mean(axis=0)), rtol=1e-12)
+    for g in range(Hkv):
+        assert np.array_equal(pruned[g], vc[g, :B - recent][:, ch[g]]) and mask[g].sum() == 4
