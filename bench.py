@@ -103,6 +103,15 @@ def algorithmic(wl, kept_rows=None):
         per_kernel["think_gather"] = ("hbm", 0.0, kr * D * 2 + kr * T * 2)
         if wl.think_query:
             per_kernel["think_qpartial"] = ("hbm", 0.0, q_bytes)
+    if wl.think_value_lambda >= 0:
+        Tv = int(math.floor((1 - wl.think_value_lambda) * D))
+        U = wl.budget - wl.recent
+        kr = Hkv * U
+        step_bytes += 2 * kr * D * 2 + q_bytes + kr * D * 2 + kr * Tv * 2
+        # softmax constants over U (pass 1 of the scoring path), then S = K Q^T and O = P V
+        per_kernel["think_rowc_pass1"] = ("mfma", 2.0 * Hkv * R * U * D, q_bytes + kr * D * 2)
+        per_kernel["think_vpartial"] = ("mfma", 4.0 * Hkv * R * U * D, q_bytes + 2 * kr * D * 2)
+        per_kernel["think_gather_v"] = ("hbm", 0.0, kr * D * 2 + kr * Tv * 2)
     return step_bytes, flops_pass, per_kernel
 
 
@@ -158,6 +167,10 @@ def cpu_baseline(wl, data, target_s, tau):
             idx = oracle.select.select(sc, S=wl.S, w=wl.w, recent=wl.recent, budget=B)
         kc = oracle.compact.compact(kraw[g:g + 1], idx[None])
         oracle.compact.compact(vraw[g:g + 1], idx[None])
+        if wl.think_value_lambda >= 0:
+            vcf = oracle.score.bf16_bits_to_f64(oracle.compact.compact(vraw[g:g + 1], idx[None]))
+            oracle.think.think_prune_value(oracle.score.bf16_bits_to_f64(kc), vcf, qf[g * wl.G:(g + 1) * wl.G],
+                                           recent=wl.recent, lam=wl.think_value_lambda, scale=scale)
         if wl.think_lambda >= 0 and wl.think_query:
             oracle.think.think_prune_query(oracle.score.bf16_bits_to_f64(kc), qf[g * wl.G:(g + 1) * wl.G],
                                            recent=wl.recent, lam=wl.think_lambda)
@@ -172,7 +185,8 @@ def cpu_baseline(wl, data, target_s, tau):
     tokens = wl.S * heads / wl.Hkv        # one layer's prompt per Hkv heads of work
     steps = "+".join(["score"] + (["pool"] if wl.pool_kernel else [])
                      + (["threshold", "compact"] if wl.threshold > 0 else ["select", "compact"])
-                     + (["think"] if wl.think_lambda >= 0 else []))
+                     + (["think"] if wl.think_lambda >= 0 else [])
+                     + (["think_value"] if wl.think_value_lambda >= 0 else []))
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{heads} KV-head passes over layer 0 ({wl.Hkv} heads per layer; {steps}, "
                       f"fp64 numpy), {dt:.1f} s"}

@@ -329,6 +329,38 @@ kvc_status kvc_channel_prune_query(const void* k_c, const void* q_obs, int32_t H
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* kvc_channel_prune_value: ThinK value-channel pruning.                     */
+/* ------------------------------------------------------------------------ */
+/*
+ * U = the first budget - recent rows of each head (as for kvc_channel_prune).
+ * Q_g stacks the w window rows of query heads g*G .. g*G + G - 1 (R = G*w
+ * rows).  P = softmax over U of scale * Q_g K_c[g, U]^T (row-wise),
+ * O = P V_c[g, U] ([R, D]), score[g, d] = ||O[:, d]||_2; channels[g] = the
+ * T = floor((1 - lambda) D) channels first in the order (score descending, d
+ * ascending), ascending; mask as for keys; v_pruned[g, t, c] =
+ * v_c[g, t, channels[g, c]] for t in U.  Recent rows keep every channel.
+ * Source: ThinK page, supplementary section on value-cache pruning (the
+ * value-channel score ||softmax(Q[-S_obs:] K^T / sqrt(D)) V[:, j]||_F and
+ * I = Top_T), with the observation window and THINK's implementation
+ * (recent tokens unpruned, binary mask).  The page's scale is 1/sqrt(D).
+ * Layout: k_c, v_c bf16 [Hkv, budget, D] contiguous; q_obs as for
+ *   kvc_channel_prune_query; channels int32 [Hkv, T]; mask uint8 [Hkv, D] or
+ *   NULL; v_pruned bf16 [Hkv, budget - recent, T].
+ * Arithmetic: the softmax constants come from the scoring path's first pass
+ *   (fp32, fixed-order folds); P is split into bf16 hi + lo for the P V MFMA
+ *   (about 2^-17 relative), accumulated in fp32 and folded in a fixed order.
+ * Errors: as kvc_channel_prune_query, plus KVC_E_ARG unless scale is finite
+ *   and > 0 and v_c is 16-byte aligned; KVC_E_SHAPE if G*w > 65536.
+ */
+size_t kvc_channel_prune_value_workspace_size(int32_t Hkv, int32_t G, int32_t w, int32_t budget, int32_t recent,
+                                              int32_t D);
+
+kvc_status kvc_channel_prune_value(const void* k_c, const void* v_c, const void* q_obs, int32_t Hkv, int32_t G,
+                                   int32_t w, int64_t q_head_stride, int32_t budget, int32_t D, int32_t recent,
+                                   double lambda, float scale, int32_t* channels, uint8_t* mask, void* v_pruned,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Kernel timing (measurement support).                                      */
 /* ------------------------------------------------------------------------ */
 /*

@@ -29,6 +29,15 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int device_cu_count();
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Row constants of the scoring path's softmax (score.hip), for callers that
+// need softmax(scale q k^T) over the first n rows of each KV head of k: q is
+// [Hkv*G heads][w][128] bf16 with head stride q_hs, k [Hkv][>= n][128] bf16
+// with head stride k_hs; *rowc receives a pointer into ws, [Hkv][G*w] floats
+// max + log2(sum) in log2 units.  n >= 1.
+size_t score_rowc_workspace_size(int Hkv, int G, int w, int n, int64_t q_hs);
+kvc_status score_rowc(const uint16_t* q, int64_t q_hs, const uint16_t* k, int64_t k_hs, int Hkv, int G, int w,
+                      int n, float scale, void* ws, size_t ws_bytes, const float** rowc, hipStream_t s);
+
 }  // namespace kvc
 
 // Launch `kernel<<<grid, block, shm, stream>>>(args...)` with timing and error

@@ -462,9 +462,10 @@ kvc_status score_grid(K kernel, int threads, size_t lds, int units, int* grid) {
   return KVC_OK;
 }
 
-// Pass 1, combine, pass 2 on one stream.
+// Pass 1, combine and (unless only the row constants are wanted) pass 2 on one
+// stream.
 template <bool kGumbel, int kW, int kT, int kCB>
-kvc_status launch_score(const ScoreParams& p, const Plan& pl, hipStream_t s) {
+kvc_status launch_score(const ScoreParams& p, const Plan& pl, hipStream_t s, bool pass2 = true) {
   constexpr int kThreads = kW * kWave;
   const int units = p.L * p.Hkv * pl.nblk;
   const int heads = p.L * p.Hkv;
@@ -480,6 +481,11 @@ kvc_status launch_score(const ScoreParams& p, const Plan& pl, hipStream_t s) {
   if (st != KVC_OK) return st;
   st = score_grid(k2, kThreads, lds2, units, &g2);
   if (st != KVC_OK) return st;
+  if (!pass2) {   // row constants only (ThinK value scores): named apart from the scoring pass
+    KVC_LAUNCH_SHM("think_rowc_pass1", k1, dim3(g1), dim3(kThreads), lds1, s, p);
+    KVC_LAUNCH("think_rowc_combine", kc, comb_grid, dim3(256), s, p, heads);
+    return KVC_OK;
+  }
   KVC_LAUNCH_SHM(kGumbel ? "score_pass1_gumbel" : "score_pass1", k1, dim3(g1), dim3(kThreads), lds1, s, p);
   KVC_LAUNCH("score_combine", kc, comb_grid, dim3(256), s, p, heads);
   KVC_LAUNCH_SHM(kGumbel ? "score_pass2_gumbel" : "score_pass2", k2, dim3(g2), dim3(kThreads), lds2, s, p);
@@ -535,3 +541,64 @@ extern "C" kvc_status kvc_score(const kvc_score_args* a, const void* q_obs, cons
   if (pl.shape.kw == 8) return launch_score<false, 8, 2, 16>(p, pl, s);
   return launch_score<false, 4, 2, 8>(p, pl, s);
 }
+
+namespace kvc {
+
+// Row constants of softmax(scale * q k^T) over the first n rows of each KV head
+// of k (pass 1 and the combine of the scoring path, no importance): rowc[g*R + r]
+// = max + log2(sum) in log2 units, R = G*w rows per KV head.  k's rows past n
+// are never read, so k may hold fewer than n + w rows.
+static kvc_score_args rowc_args(int Hkv, int G, int w, int n, int64_t q_hs, float scale) {
+  kvc_score_args a{};
+  a.L = 1;
+  a.H = Hkv * G;
+  a.Hkv = Hkv;
+  a.w = w;
+  a.S = n + w;
+  a.D = kD;
+  a.q_head_stride = q_hs;
+  a.k_head_stride = (int64_t)(n + w) * kD;   // validation only: the kernels read rows [0, n)
+  a.scale = scale;
+  return a;
+}
+
+size_t score_rowc_workspace_size(int Hkv, int G, int w, int n, int64_t q_hs) {
+  if (n < 1) return 0;
+  const kvc_score_args a = rowc_args(Hkv, G, w, n, q_hs, 1.0f);
+  Plan pl;
+  return plan(&a, &pl) == KVC_OK ? pl.total : 0;
+}
+
+kvc_status score_rowc(const uint16_t* q, int64_t q_hs, const uint16_t* k, int64_t k_hs, int Hkv, int G, int w,
+                      int n, float scale, void* ws, size_t ws_bytes, const float** rowc, hipStream_t s) {
+  const kvc_score_args a = rowc_args(Hkv, G, w, n, q_hs, scale);
+  Plan pl;
+  kvc_status st = plan(&a, &pl);
+  if (st != KVC_OK) return st;
+  if (k_hs < (int64_t)n * kD || (k_hs & 7)) return KVC_E_SHAPE;
+  if (!ws || ws_bytes < pl.total || !aligned16(ws)) return KVC_E_WORKSPACE;
+  ScoreParams p{};
+  p.q = q;
+  p.k = k;
+  p.q_hs = q_hs;
+  p.k_hs = k_hs;
+  p.imp = nullptr;
+  p.part = reinterpret_cast<float2*>(ws);
+  p.rowc = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.part_bytes);
+  p.scale = scale;
+  p.inv_w = 1.0f / (float)w;
+  p.L = 1;
+  p.Hkv = Hkv;
+  p.G = pl.G;
+  p.w = w;
+  p.S = n + w;
+  p.n = pl.n;
+  p.R = pl.R;
+  p.nblk = pl.nblk;
+  p.chunk_rows = pl.chunk_rows;
+  *rowc = p.rowc;
+  if (pl.shape.kw == 8) return launch_score<false, 8, 2, 16>(p, pl, s, false);
+  return launch_score<false, 4, 2, 8>(p, pl, s, false);
+}
+
+}  // namespace kvc

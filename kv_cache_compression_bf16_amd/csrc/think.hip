@@ -1,4 +1,5 @@
-// kvc_channel_prune / kvc_channel_prune_query: ThinK key-channel pruning.
+// kvc_channel_prune / kvc_channel_prune_query: ThinK key-channel pruning;
+// kvc_channel_prune_value: ThinK value-channel pruning.
 //
 // ThinK page (papercache summary of arXiv 2407.21018): magnitude-based pruning
 // keeps, per head, the T = floor((1 - lambda) D) key channels with the largest
@@ -8,6 +9,10 @@
 // section: recent keys are not pruned and a binary mask records the pruned
 // channels.  The key norms here run over the non-recent kept rows (the rows
 // that get pruned); a KV head's query side stacks its G query heads' windows.
+// The page's supplementary value-pruning section scores value channel j by
+// ||softmax(Q[-S_obs:] K^T / sqrt(D)) V[:, j]||_F; here K and V are the same
+// non-recent kept rows U, each stacked query row's softmax is normalised over
+// U, and the T top-scoring value channels are kept.
 //
 // Design (D = 128):
 //  * think_partial: grid (row chunks of 256, heads); 16 lanes cover one
@@ -21,6 +26,17 @@
 //    fixed order (times the folded query sums, query-driven: ||Q|| ||K|| and
 //    its square rank alike); channels ranked by (score desc, index asc), kept
 //    channels written ascending, and the mask.
+//  * value pruning: the scoring path's pass 1 and combine give each stacked
+//    query row's softmax constant over U (score_rowc); think_vpartial, grid
+//    (key splits of 512, heads, groups of 4 query blocks), stages each 32-key
+//    tile of K (padded rows) and of V transposed (keys contiguous per channel)
+//    in LDS; each wave keeps its 32 query rows' fragments in registers, takes
+//    S = K Q^T with MFMA, P = 2^(S c - rowc) split exactly into bf16 hi + lo,
+//    and accumulates O^T += V^T P^T with MFMA, P used straight from the
+//    accumulator layout as the B operand (the keys of each 16-key step are
+//    permuted the same way in both operands).  think_vnorm folds the splits
+//    in a fixed order and sums O^2 over 8 rows per workgroup; think_select and
+//    think_gather (on V) finish as for keys.
 //  * think_gather: a wave takes 8 rows at a time (8 loads in flight); lane l
 //    holds bf16 channels 2l, 2l+1 of a row and an output channel takes its
 //    value with one cross-lane read from lane channels[c]/2.  With T even and
@@ -215,6 +231,154 @@ __global__ __launch_bounds__(256) void think_gather(const uint16_t* kc, int budg
   }
 }
 
+
+// ---- value pruning
+constexpr int kVWaves = 4;                // query blocks (waves) per workgroup
+constexpr int kVSplit = 512;              // keys per workgroup
+constexpr int kKPitch = kD * 2 + 16;      // bytes per staged key row
+constexpr int kVtPitch = 32 * 2 + 8;      // bytes per staged transposed value row (32 keys)
+constexpr int kVNormRows = 8;             // query rows per think_vnorm workgroup
+
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {   // finite x
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__global__ __launch_bounds__(kVWaves * kWave) void think_vpartial(const uint16_t* q, int64_t q_hs, int G, int w,
+                                                                 const uint16_t* kc, const uint16_t* vc,
+                                                                 int budget, int rows, const float* rowc,
+                                                                 float cc, int nsplit, float* opart) {
+  __shared__ __attribute__((aligned(16))) char ks[32 * kKPitch];
+  __shared__ __attribute__((aligned(16))) char vt[kD * kVtPitch];
+  const int split = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hb = lane >> 5, col = lane & 31;
+  const int R = G * w;
+  const int qb = blockIdx.z * kVWaves + wave;
+  const int row = qb * 32 + col;             // this lane's query row
+  const bool wave_on = qb * 32 < R;
+  // B operand of S = K Q^T: lane holds Q[row][16 s + 8 hb .. +8]
+  bf16x8 qf[8];
+  float rc = INFINITY;                       // rows past R: P = 0
+  if (row < R) {
+    const int hh = row / w, ii = row - hh * w;
+    const uint16_t* qr = q + (int64_t)(g * G + hh) * q_hs + (int64_t)ii * kD + 8 * hb;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qr + 16 * st);
+    rc = rowc[(int64_t)g * R + row];
+  } else {
+#pragma unroll
+    for (int st = 0; st < 8; ++st) qf[st] = bf16x8{};
+  }
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+  const int key_lo = split * kVSplit;
+  const int key_hi = min(key_lo + kVSplit, rows);
+  const uint16_t* kb = kc + (int64_t)g * budget * kD;
+  const uint16_t* vb = vc + (int64_t)g * budget * kD;
+  uint16_t* vt16 = reinterpret_cast<uint16_t*>(vt);
+  for (int t0 = key_lo; t0 < key_hi; t0 += 32) {
+    __syncthreads();   // every wave is done with the previous tile
+    for (int i = tid; i < 32 * 16; i += kVWaves * kWave) {
+      const int kr = i >> 4, ch = i & 15, key = t0 + kr;
+      u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
+      if (key < key_hi) {
+        kv = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * kD + ch * 8);
+        vv = *reinterpret_cast<const u32x4*>(vb + (int64_t)key * kD + ch * 8);
+      }
+      *reinterpret_cast<u32x4*>(ks + kr * kKPitch + ch * 16) = kv;
+      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vt16[(ch * 8 + 2 * j) * (kVtPitch / 2) + kr] = (uint16_t)(vw[j] & 0xFFFFu);
+        vt16[(ch * 8 + 2 * j + 1) * (kVtPitch / 2) + kr] = (uint16_t)(vw[j] >> 16);
+      }
+    }
+    __syncthreads();
+    if (!wave_on) continue;
+    // S[key][row]: lane holds row = col, key = t0 + 8 (e / 4) + 4 hb + e % 4
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + col * kKPitch + (16 * st + 8 * hb) * 2);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], sacc, 0, 0, 0);
+    }
+    // P = 2^(S c - rowc) (0 past the split's keys), as bf16 hi + lo; element
+    // i of operand `half` is e = 8 half + i
+    uint32_t ph[2][4], pl[2][4];
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      uint32_t hbits[2], lbits[2];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int ee = e + k2;
+        const int key = t0 + 8 * (ee >> 2) + 4 * hb + (ee & 3);
+        const float pv = key < key_hi ? __builtin_amdgcn_exp2f(fmaf(sacc[ee], cc, -rc)) : 0.f;
+        hbits[k2] = bf16_rne_bits(pv);
+        lbits[k2] = bf16_rne_bits(pv - __uint_as_float(hbits[k2] << 16));
+      }
+      ph[e >> 3][(e & 7) >> 1] = hbits[0] | (hbits[1] << 16);
+      pl[e >> 3][(e & 7) >> 1] = lbits[0] | (lbits[1] << 16);
+    }
+    // O^T[d][row] += sum over the tile's keys of V^T[d][key] P[row][key]
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, u32x4{ph[half][0], ph[half][1], ph[half][2], ph[half][3]});
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, u32x4{pl[half][0], pl[half][1], pl[half][2], pl[half][3]});
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const char* vr = vt + (32 * db + col) * kVtPitch;
+        const uint2 a0 = *reinterpret_cast<const uint2*>(vr + (16 * half + 4 * hb) * 2);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(vr + (16 * half + 8 + 4 * hb) * 2);
+        const bf16x8 af = __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y});
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bh, oacc[db], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bl, oacc[db], 0, 0, 0);
+      }
+    }
+  }
+  if (!wave_on || row >= R) return;
+  // O^T layout: lane holds row = col and d = 32 db + 8 (e / 4) + 4 hb + e % 4
+  float* op = opart + (((int64_t)g * nsplit + split) * R + row) * kD;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4)
+      *reinterpret_cast<f32x4*>(op + 32 * db + 8 * e4 + 4 * hb) =
+          f32x4{oacc[db][4 * e4], oacc[db][4 * e4 + 1], oacc[db][4 * e4 + 2], oacc[db][4 * e4 + 3]};
+}
+
+// vpart[g, rg, d] = sum over rows r in [8 rg, 8 rg + 8) of (sum over splits of
+// opart[g, split, r, d])^2, every sum in a fixed order.
+__global__ __launch_bounds__(kD * kVNormRows) void think_vnorm(const float* opart, int nsplit, int R,
+                                                              float* vpart) {
+  __shared__ float red[kVNormRows][kD];
+  const int rg = blockIdx.x, g = blockIdx.y, d = threadIdx.x & (kD - 1), rr = threadIdx.x / kD;
+  const int r = rg * kVNormRows + rr;
+  float o2 = 0.f;
+  if (r < R) {
+    const float* pp = opart + ((int64_t)g * nsplit * R + r) * kD + d;
+    const int64_t st = (int64_t)R * kD;
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 3 < nsplit; s += 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] += pp[(s + j) * st];
+    }
+    for (; s < nsplit; ++s) a[0] += pp[s * st];
+    const float o = (a[0] + a[1]) + (a[2] + a[3]);
+    o2 = o * o;
+  }
+  red[rr][d] = o2;
+  __syncthreads();
+  if (rr == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < kVNormRows; ++i) t += red[i][d];
+    vpart[((int64_t)g * gridDim.x + rg) * kD + d] = t;
+  }
+}
+
 }  // namespace
 }  // namespace kvc
 
@@ -300,4 +464,88 @@ extern "C" kvc_status kvc_channel_prune_query(const void* k_c, const void* q_obs
   if (q_head_stride < (int64_t)w * D || (q_head_stride & 7)) return KVC_E_SHAPE;
   return channel_prune(k_c, q_obs, G, w, q_head_stride, Hkv, budget, D, recent, lambda, 2, channels, mask,
                        k_pruned, ws, ws_bytes, kvc_channel_prune_query_workspace_size(Hkv, G, budget, D), stream);
+}
+
+namespace kvc {
+namespace {
+
+struct ValueWs {
+  size_t rowc, opart, vpart, total;
+  int nsplit, nrg;
+};
+
+ValueWs value_ws(int Hkv, int G, int w, int budget, int recent) {
+  ValueWs v{};
+  const int rows = budget - recent, R = G * w;
+  v.nsplit = rows > 0 ? (rows + kVSplit - 1) / kVSplit : 0;
+  v.nrg = (R + kVNormRows - 1) / kVNormRows;
+  const size_t rs = rows > 0 ? score_rowc_workspace_size(Hkv, G, w, rows, (int64_t)w * kD) : 0;
+  v.rowc = 0;
+  v.opart = align_up(rs, 256);
+  v.vpart = v.opart + align_up((size_t)Hkv * v.nsplit * R * kD * sizeof(float), 256);
+  v.total = v.vpart + align_up((size_t)Hkv * v.nrg * kD * sizeof(float), 256);
+  return v;
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" size_t kvc_channel_prune_value_workspace_size(int32_t Hkv, int32_t G, int32_t w, int32_t budget,
+                                                         int32_t recent, int32_t D) {
+  if (Hkv < 1 || G < 1 || w < 1 || budget < 0 || recent < 0 || recent > budget || D != kvc::kD) return 0;
+  if ((int64_t)G * w > 65536) return 0;
+  return kvc::value_ws(Hkv, G, w, budget, recent).total;
+}
+
+extern "C" kvc_status kvc_channel_prune_value(const void* k_c, const void* v_c, const void* q_obs, int32_t Hkv,
+                                              int32_t G, int32_t w, int64_t q_head_stride, int32_t budget,
+                                              int32_t D, int32_t recent, double lambda, float scale,
+                                              int32_t* channels, uint8_t* mask, void* v_pruned, void* ws,
+                                              size_t ws_bytes, void* stream) {
+  using namespace kvc;
+  if (Hkv < 1 || G < 1 || w < 1 || budget < 0 || recent < 0 || recent > budget) return KVC_E_ARG;
+  if (!(lambda >= 0.0 && lambda < 1.0) || !(scale > 0.f && scale < INFINITY)) return KVC_E_ARG;
+  if (D != kD) return KVC_E_UNSUPPORTED;
+  if (Hkv > 65535 || (int64_t)Hkv * G > 65535 || (int64_t)G * w > 65536) return KVC_E_SHAPE;
+  if (q_head_stride < (int64_t)w * D || (q_head_stride & 7)) return KVC_E_SHAPE;
+  const int T = kvc_think_channels(D, lambda);
+  if (T < 1) return KVC_E_ARG;
+  const int rows = budget - recent, R = G * w;
+  if (!k_c || !v_c || !q_obs || !channels || (rows > 0 && !v_pruned)) return KVC_E_ARG;
+  if (!aligned16(k_c) || !aligned16(v_c) || !aligned16(q_obs) || (reinterpret_cast<uintptr_t>(channels) & 3) ||
+      (reinterpret_cast<uintptr_t>(v_pruned) & 1))
+    return KVC_E_ARG;
+  const ValueWs L = value_ws(Hkv, G, w, budget, recent);
+  if (!ws || ws_bytes < L.total || !aligned16(ws)) return KVC_E_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  float* opart = reinterpret_cast<float*>(base + L.opart);
+  float* vpart = reinterpret_cast<float*>(base + L.vpart);
+  const uint16_t* qp = static_cast<const uint16_t*>(q_obs);
+  const uint16_t* kp = static_cast<const uint16_t*>(k_c);
+  const uint16_t* vp = static_cast<const uint16_t*>(v_c);
+  if (rows > 0) {
+    const float* rowc = nullptr;
+    kvc_status st = score_rowc(qp, q_head_stride, kp, (int64_t)budget * kD, Hkv, G, w, rows, scale, base + L.rowc,
+                               L.opart - L.rowc, &rowc, s);
+    if (st != KVC_OK) return st;
+    const int nqg = ((R + 31) / 32 + kVWaves - 1) / kVWaves;
+    KVC_LAUNCH("think_vpartial", think_vpartial, dim3(L.nsplit, Hkv, nqg), dim3(kVWaves * kWave), s, qp,
+               q_head_stride, G, w, kp, vp, budget, rows, rowc, scale * kLog2e, L.nsplit, opart);
+  }
+  KVC_LAUNCH("think_vnorm", think_vnorm, dim3(L.nrg, Hkv), dim3(kD * kVNormRows), s, opart, L.nsplit, R, vpart);
+  KVC_LAUNCH("think_select_v", think_select, dim3(Hkv), dim3(kD * kSelGroups), s, vpart, L.nrg, nullptr, 0, T,
+             channels, mask);
+  if (rows > 0) {
+    int gx = (rows + 31) / 32;
+    if (gx > 1024) gx = 1024;
+    uint16_t* out = static_cast<uint16_t*>(v_pruned);
+    if ((T & 1) == 0 && (reinterpret_cast<uintptr_t>(v_pruned) & 3) == 0)
+      KVC_LAUNCH("think_gather_v", think_gather<true>, dim3(gx, Hkv), dim3(256), s, vp, budget, rows, T, channels,
+                 out);
+    else
+      KVC_LAUNCH("think_gather_v", think_gather<false>, dim3(gx, Hkv), dim3(256), s, vp, budget, rows, T, channels,
+                 out);
+  }
+  return KVC_OK;
 }

@@ -62,6 +62,9 @@ def _load():
         "kvc_channel_prune_workspace_size": (SZ, [I32, I32, I32]),
         "kvc_channel_prune": (ctypes.c_int, [P, I32, I32, I32, I32, F64, I32, P, P, P, P, SZ, P]),
         "kvc_channel_prune_query_workspace_size": (SZ, [I32, I32, I32, I32]),
+        "kvc_channel_prune_value_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32]),
+        "kvc_channel_prune_value": (ctypes.c_int, [P, P, P, I32, I32, I32, I64, I32, I32, I32, F64, ctypes.c_float,
+                                                   P, P, P, P, SZ, P]),
         "kvc_channel_prune_query": (ctypes.c_int, [P, P, I32, I32, I32, I64, I32, I32, I32, F64, P, P, P, P, SZ,
                                                    P]),
         "kvc_timing_enable": (ctypes.c_int, [I32]),
@@ -304,6 +307,28 @@ def kvc_channel_prune_query(k_c, q_obs, channels, k_pruned, *, recent, lam, mask
                                         float(lam), _ptr(channels), _ptr(mask), _ptr(k_pruned), _ptr(ws), nbytes,
                                         _stream(stream, k_c.device)), "kvc_channel_prune_query")
     return channels, k_pruned
+
+
+def kvc_channel_prune_value(k_c, v_c, q_obs, channels, v_pruned, *, recent, lam, scale=None, mask=None,
+                            workspace=None, stream=None):
+    """ThinK value-channel pruning of v_c [Hkv, budget, D], scored with k_c and the window queries q_obs [H, w, D]."""
+    for t, n in ((k_c, "k_c"), (v_c, "v_c"), (q_obs, "q_obs")):
+        _bf16(t, n)
+    Hkv, budget, D = k_c.shape
+    H, w, Dq = q_obs.shape
+    if not (k_c.is_contiguous() and v_c.is_contiguous()) or v_c.shape != k_c.shape:
+        raise ValueError("k_c and v_c must be contiguous [Hkv, budget, D] tensors of one shape")
+    if Dq != D or H % Hkv or q_obs.stride(1) != D or q_obs.stride(2) != 1:
+        raise ValueError(f"shape mismatch: q_obs {tuple(q_obs.shape)}, k_c {tuple(k_c.shape)}")
+    G = H // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    ws, nbytes = _workspace(_lib.kvc_channel_prune_value_workspace_size(Hkv, G, w, budget, recent, D), k_c.device,
+                            workspace)
+    _check(_lib.kvc_channel_prune_value(_ptr(k_c), _ptr(v_c), _ptr(q_obs), Hkv, G, w, q_obs.stride(0), budget, D,
+                                        recent, float(lam), float(scale), _ptr(channels), _ptr(mask),
+                                        _ptr(v_pruned), _ptr(ws), nbytes, _stream(stream, k_c.device)),
+           "kvc_channel_prune_value")
+    return channels, v_pruned
 
 
 # ---------------------------------------------------------------- timing

@@ -2,7 +2,8 @@
 
 Each pass is a fixed sequence of libkvc calls on one stream: score ->
 [SnapKV pooling] -> [ZigZag budgets] -> select (top-k, or KVzap's threshold with packed
-heads) -> compact -> [ThinK, by key norms or by the window queries].  Buffers are allocated once
+heads) -> compact -> [ThinK: key channels by norms or by the window queries; value
+channels].  Buffers are allocated once
 per plan (through torch) so a pass itself allocates nothing on the device.
 No arithmetic happens here.
 """
@@ -74,6 +75,15 @@ class CompressionPlan:
             else:
                 nb = kvc.lib.kvc_channel_prune_workspace_size(Hkv, wl.budget, D)
             self.ws_think = torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
+        self.think_value = wl.think_value_lambda >= 0
+        if self.think_value:
+            Tv = kvc.kvc_think_channels(D, wl.think_value_lambda)
+            rows = wl.budget - wl.recent
+            self.channels_v = torch.empty((Hkv, Tv), dtype=i32, device=device)
+            self.mask_v = torch.empty((Hkv, D), dtype=torch.uint8, device=device)
+            self.vp = torch.empty((Hkv, rows, Tv), dtype=bf, device=device)
+            nb = kvc.lib.kvc_channel_prune_value_workspace_size(Hkv, wl.G, wl.w, wl.budget, wl.recent, D)
+            self.ws_think_v = torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
 
     def score(self, q, k, layer_scales=None, stream=None):
         wl = self.wl
@@ -106,6 +116,10 @@ class CompressionPlan:
             elif self.think:
                 kvc.kvc_channel_prune(self.kc, self.channels, self.kp, recent=wl.recent, lam=wl.think_lambda,
                                       p=wl.think_p, mask=self.mask, workspace=self.ws_think, stream=stream)
+            if self.think_value:
+                kvc.kvc_channel_prune_value(self.kc, self.vc, q if q.dim() == 3 else q[0], self.channels_v, self.vp,
+                                            recent=wl.recent, lam=wl.think_value_lambda, mask=self.mask_v,
+                                            workspace=self.ws_think_v, stream=stream)
             return
         kvc.kvc_lmba_budget(self.importance, self.budgets, total_budget=wl.total_budget,
                             floor_per_layer=wl.floor, capacity=wl.capacity, mass=wl.mass, mba=self.mba,

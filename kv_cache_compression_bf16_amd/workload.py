@@ -51,6 +51,7 @@ class Workload:
     think_lambda: float = -1.0      # < 0: no channel pruning
     think_p: int = 2
     think_query: bool = False       # query-driven ThinK score (window queries x keys) instead of l_p norms
+    think_value_lambda: float = -1.0   # >= 0: ThinK value-channel pruning after the key pruning
     pool_kernel: int = 0            # SnapKV 1D pooling of the importance before top-k (0: off)
     pool_mode: int = 0              # 0: average (zero padding, / kernel), 1: max
     threshold: float = 0.0          # > 0: KVzap threshold selection at threshold * G / (S - w), not top-k
@@ -94,6 +95,11 @@ WORKLOADS = {
         name="gqa32x8_s32768_pool7", cfg_id=1, L=1, H=32, Hkv=8, S=32768, w=128, recent=64, budget=2048,
         outliers=4, pool_kernel=7, pool_mode=0,
         notes="the GQA layer above (same inputs) with SnapKV's average pooling (kernel 7) before top-k"),
+    "think_s131072_kv": Workload(
+        name="think_s131072_kv", cfg_id=4, L=1, H=8, Hkv=8, S=131072, w=64, recent=64,
+        budget=int(0.2 * 131072), outliers=4, think_lambda=0.3, think_query=True, think_value_lambda=0.3,
+        notes="the long-context case above (same inputs) with query-driven key and value channel pruning, "
+              "lambda 0.3 each"),
     "gqa32x8_s32768_thr2": Workload(
         name="gqa32x8_s32768_thr2", cfg_id=1, L=1, H=32, Hkv=8, S=32768, w=128, recent=64,
         outliers=4, threshold=2.0,

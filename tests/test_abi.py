@@ -226,6 +226,31 @@ def test_compact_ragged_validation():
     assert call(rows=0) == E.KVC_OK                                        # nothing to gather: no launch
 
 
+def test_channel_prune_value_validation():
+    ws = lib.kvc_channel_prune_value_workspace_size(8, 4, 16, 100, 10, 128)
+    assert ws > 0
+    assert lib.kvc_channel_prune_value_workspace_size(8, 4, 16, 100, 101, 128) == 0
+    assert lib.kvc_channel_prune_value_workspace_size(8, 4, 16, 100, 10, 64) == 0
+    names = ["k", "v", "q", "Hkv", "G", "w", "qs", "budget", "D", "recent", "lam", "scale", "ch", "mask", "vp",
+             "ws", "nb", "st"]
+    call = _named_call(lib.kvc_channel_prune_value, names,
+                       (FAKE, FAKE, FAKE, 8, 4, 16, 16 * 128, 100, 128, 10, 0.4, 0.088, FAKE, None, FAKE, FAKE, ws,
+                        None))
+    assert call(v=None) == E.KVC_E_ARG
+    assert call(q=None) == E.KVC_E_ARG
+    assert call(v=ctypes.c_void_p((1 << 20) + 8)) == E.KVC_E_ARG           # v not 16-byte aligned
+    assert call(scale=0.0) == E.KVC_E_ARG
+    assert call(scale=float("inf")) == E.KVC_E_ARG
+    assert call(scale=float("nan")) == E.KVC_E_ARG
+    assert call(lam=1.0) == E.KVC_E_ARG
+    assert call(recent=101) == E.KVC_E_ARG
+    assert call(D=64) == E.KVC_E_UNSUPPORTED
+    assert call(G=4, w=20000, qs=20000 * 128) == E.KVC_E_SHAPE             # G * w > 65536
+    assert call(qs=16 * 128 - 8) == E.KVC_E_SHAPE
+    assert call(ws=None) == E.KVC_E_WORKSPACE
+    assert call(nb=ws - 256) == E.KVC_E_WORKSPACE
+
+
 def test_channel_prune_query_validation():
     f = lib.kvc_channel_prune_query
     ws = lib.kvc_channel_prune_query_workspace_size(8, 4, 100, 128)

@@ -289,3 +289,44 @@ def test_channel_prune_query(Hkv, G, w, wpad, B, recent, lam, loud):
         assert np.array_equal(kpb[g], kc[g, :rows][:, gch[g]])
         if loud:
             assert 66 not in gch[g] and {10 + g, 40 + 2 * g} <= set(gch[g].tolist())
+
+
+@pytest.mark.parametrize("Hkv,G,w,B,recent,lam,loud", [
+    (8, 4, 32, 2000, 64, 0.4, False),      # 1936 rows: 4 key splits, ragged last tile
+    (2, 1, 17, 513, 1, 0.3, False),        # a partial query block
+    (3, 2, 8, 100, 100, 0.4, False),       # no prunable rows: every score is 0, lowest channels win
+    (2, 8, 64, 700, 0, 0.0, False),        # R = 512: several query groups; lambda 0 keeps every channel
+    (4, 4, 24, 1500, 32, 0.5, True),       # loud value channels are always kept
+])
+def test_channel_prune_value(Hkv, G, w, B, recent, lam, loud):
+    kvc = _kvc()
+    print(f"[value prune] Hkv={Hkv} G={G} w={w} B={B} r={recent} lam={lam}", flush=True)
+    rng = np.random.default_rng(B + 7 * w)
+    k = rng.standard_normal((Hkv, B, 128), dtype=np.float32)
+    v = rng.standard_normal((Hkv, B, 128), dtype=np.float32)
+    q = rng.standard_normal((Hkv * G, w, 128), dtype=np.float32)
+    loud_ch = [3, 50, 97]
+    if loud:
+        v[:, :, loud_ch] *= 8.0
+    kb, vb, qb = wk.f32_to_bf16_bits(k), wk.f32_to_bf16_bits(v), wk.f32_to_bf16_bits(q)
+    T = oracle.sizes.think_channels(128, lam)
+    rows = B - recent
+    ch = torch.empty((Hkv, T), dtype=torch.int32, device=dev())
+    mask = torch.empty((Hkv, 128), dtype=torch.uint8, device=dev())
+    vp = torch.empty((Hkv, rows, T), dtype=torch.bfloat16, device=dev())
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    kvc.kvc_channel_prune_value(to_dev(kb), to_dev(vb), to_dev(qb), ch, vp, recent=recent, lam=lam, scale=scale,
+                                mask=mask)
+    torch.cuda.synchronize()
+    f64 = oracle.score.bf16_bits_to_f64
+    ref_ch, _, _, scores = oracle.think.think_prune_value(f64(kb), f64(vb), f64(qb), recent=recent, lam=lam,
+                                                          scale=scale)
+    gch, gmask, vpb = ch.cpu().numpy(), mask.cpu().numpy(), bits_of(vp)
+    kinds = []
+    for g in range(Hkv):
+        kinds.append(check_channels(gch[g], scores[g], ref_ch[g], T))
+        assert np.array_equal(gmask[g], np.isin(np.arange(128), gch[g]).astype(np.uint8))
+        assert np.array_equal(vpb[g], vb[g, :rows][:, gch[g]])
+        if loud:
+            assert set(loud_ch) <= set(gch[g].tolist())
+    print("channels:", kinds)

@@ -153,6 +153,34 @@ def test_think_s131072_query():
     assert np.array_equal(plan.mask.cpu().numpy().sum(axis=1), np.full(wl.Hkv, T))
 
 
+def test_think_s131072_kv():
+    wl = wk.WORKLOADS["think_s131072_kv"]
+    plan, (q, k, v), sc = _run(wl)
+    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=[1])
+    print("selection:", kinds)
+    f64 = oracle.score.bf16_bits_to_f64
+    kc, vc = bits_of(plan.kc), bits_of(plan.vc)
+    rows = wl.budget - wl.recent
+    # keys: query-driven, every head
+    T = oracle.sizes.think_channels(wl.D, wl.think_lambda)
+    ref_ch, _, _, ksc = oracle.think.think_prune_query(f64(kc), f64(q), recent=wl.recent, lam=wl.think_lambda)
+    ch, kp = plan.channels.cpu().numpy(), bits_of(plan.kp)
+    # values: every head
+    Tv = oracle.sizes.think_channels(wl.D, wl.think_value_lambda)
+    scale = float(np.float32(1.0 / math.sqrt(wl.D)))
+    ref_vch, _, _, vsc = oracle.think.think_prune_value(f64(kc), f64(vc), f64(q), recent=wl.recent,
+                                                        lam=wl.think_value_lambda, scale=scale)
+    vch, vp = plan.channels_v.cpu().numpy(), bits_of(plan.vp)
+    out = []
+    for g in range(wl.Hkv):
+        out.append(check_channels(ch[g], ksc[g], ref_ch[g], T))
+        assert np.array_equal(kp[g], kc[g, :rows][:, ch[g]])
+        out.append(check_channels(vch[g], vsc[g], ref_vch[g], Tv))
+        assert np.array_equal(vp[g], vc[g, :rows][:, vch[g]])
+    print("channels (key, value per head):", out)
+    assert np.array_equal(plan.mask_v.cpu().numpy().sum(axis=1), np.full(wl.Hkv, Tv))
+
+
 def test_gqa32x8_s32768_thr2():
     wl = wk.WORKLOADS["gqa32x8_s32768_thr2"]
     plan, (q, k, v), sc = _run(wl)
