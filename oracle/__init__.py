@@ -23,6 +23,8 @@ written in the order and notation of the pages it cites:
 * ``threshold`` -- KVzap's threshold rule with a sliding window (variable
                  kept count per head, packed output) and the packed gather.
 * ``compact`` -- gather of the kept K/V rows.
+* ``decode``  -- Keyformer's decode phase: per-step score accumulation over the
+                 compressed cache and eviction of the lowest-scoring old token.
 * ``think``   -- ThinK key-channel pruning, magnitude-based and query-driven.
 * ``sizes``   -- the KV-cache size formula and ThinK's kept-channel count.
 
@@ -30,4 +32,4 @@ Parity status of each function (what pins it) is listed in each module's
 docstring; every function here has at least one pin in ``tests/``.
 """
 
-from . import budget, compact, philox, pool, score, select, sizes, think, threshold  # noqa: F401
+from . import budget, compact, decode, philox, pool, score, select, sizes, think, threshold  # noqa: F401
