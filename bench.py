@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "prompt KV tokens compressed/sec (score+top-k+gather); % of HBM roofline"
+DECODE_METRIC = "Keyformer decode tokens/sec for one layer (score accumulation + eviction on the kept cache)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 * 2 ** 20
@@ -82,6 +83,11 @@ def algorithmic(wl, kept_rows=None):
         step_bytes += q_bytes
     if wl.pool_kernel:
         step_bytes += 2 * imp
+    if wl.decode_steps:
+        # one decode step: the cache keys once, pos and acc read and written, new rows, queries
+        B = wl.budget
+        dec_bytes = Hkv * B * D * 2 + Hkv * B * 12 + 2 * Hkv * D * 2 * 2 + H * D * 2
+        return dec_bytes, 0.0, {"keyformer_decode_step": ("hbm", 0.0, dec_bytes)}
     # per step (bench divides by the launches per step): bound, flops, algorithmic bytes
     per_kernel = {
         "score_pass1": ("mfma", flops_pass, q_bytes + k_prefix),
@@ -148,6 +154,28 @@ def cpu_baseline(wl, data, target_s, tau):
     from threadpoolctl import threadpool_info
 
     q, k, v = data
+    if wl.decode_steps:
+        # decode steps of the oracle from a kept cache of the workload's own rows:
+        # the prompt's recent window plus evenly spaced prefix tokens, zero scores
+        from kv_cache_compression_bf16_amd import workload as wk
+        B, r = wl.budget, wl.recent
+        pos = np.concatenate([np.linspace(0, wl.S - r - 1, B - r).astype(np.int64), np.arange(wl.S - r, wl.S)])
+        kc, vc = k[:, pos], v[:, pos]
+        pos = np.tile(pos, (wl.Hkv, 1))
+        acc = np.zeros((wl.Hkv, B))
+        scale = float(np.float32(1.0 / math.sqrt(wl.D)))
+        steps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < target_s:
+            qd, kn, vn = wk.gen_decode(wl, steps)
+            kc, vc, pos, acc, _ = oracle.decode.decode_step(kc, vc, pos, acc, oracle.score.bf16_bits_to_f64(qd), kn,
+                                                            vn, t=wl.S + steps, recent=r, scale=scale, tau=tau,
+                                                            seed=wl.noise_seed)
+            steps += 1
+        dt = time.perf_counter() - t0
+        threads = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
+        return {"value": steps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": f"{steps} decode steps of all {wl.Hkv} KV heads from a kept cache of the workload's rows "
+                          f"(fp64 numpy), {dt:.1f} s"}
     qf = oracle.score.bf16_bits_to_f64(q if wl.L == 1 else q[0])
     kf = oracle.score.bf16_bits_to_f64(k if wl.L == 1 else k[0])
     kraw = k if wl.L == 1 else k[0]
@@ -229,16 +257,30 @@ def main():
         q, k, v = sets[i % copies]
         plan.run(q, k, v, layer_scales=ls, stream=stream)
 
+    if wl.decode_steps:
+        # decode workload: the prompt phase once (untimed), then one timed step is
+        # one decode step of the layer (the token at position S + i)
+        step(0)
+        plan.decode_init(stream=stream)
+        n_dec = args.warmup + 2 * args.steps
+        dec = [[pipeline.bf16_to_device(x, dev) for x in wk.gen_decode(wl, i)] for i in range(n_dec)]
+        torch.cuda.synchronize()
+
+        def step(i):   # noqa: F811 -- the decode workload's step
+            q, kn, vn = dec[i]
+            plan.decode_step(q, kn, vn, wl.S + i, stream=stream)
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    i_next = args.warmup
 
     # ---- timed region: exactly `steps` steps between two events on the launch stream
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(args.steps):
-        step(i)
+        step(i_next + i)   # decode positions keep increasing
     e1.record(stream)
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
@@ -247,12 +289,12 @@ def main():
     # ---- per-kernel durations: same steps again with libkvc's per-launch events
     kvc.kvc_timing_enable(True)
     for i in range(args.steps):
-        step(i)
+        step(i_next + args.steps + i)
     torch.cuda.synchronize()
     kt = kvc.kvc_timing_read()
     kvc.kvc_timing_enable(False)
 
-    tokens = wl.L * wl.S
+    tokens = 1 if wl.decode_steps else wl.L * wl.S    # decode: one token of one layer per step
     value = tokens / (ms_step / 1e3)
     kept_rows = int(plan.offsets[-1].item()) if wl.threshold > 0 else None   # after the timed region
     step_bytes, flops_pass, per_kernel = algorithmic(wl, kept_rows)
@@ -291,7 +333,7 @@ def main():
               "threshold_x_uniform": wl.threshold or None, "kept_rows": kept_rows,
               "input_copies_rotated": copies}
     out = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": DECODE_METRIC if wl.decode_steps else METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, workload recipe)",
         "config": config,

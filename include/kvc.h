@@ -361,6 +361,55 @@ kvc_status kvc_channel_prune_value(const void* k_c, const void* v_c, const void*
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Keyformer decode phase: score hand-over and one decode step.             */
+/* ------------------------------------------------------------------------ */
+/*
+ * kvc_decode_init_scores: acc[g, t] = importance[g, indices[g, t]] when that
+ * index is in [0, n) (a scored prefix token), else 0 (the prompt's window
+ * tokens, which the prompt phase does not score).  The accumulated scores a
+ * decode phase starts from.
+ * Source: Keyformer blog page, closing paragraphs (the decode phase adds each
+ * step's score to the score carried from before).
+ * Layout: importance fp32, row g at importance + g * imp_head_stride (>= n
+ *   when Hkv > 1); indices int32 [Hkv, budget]; acc fp32 [Hkv, budget].
+ * Errors: KVC_E_ARG for negative sizes or null / misaligned pointers.
+ */
+kvc_status kvc_decode_init_scores(const float* importance, int64_t imp_head_stride, const int32_t* indices,
+                                  int32_t Hkv, int32_t budget, int32_t n, float* acc, void* stream);
+
+/*
+ * kvc_keyformer_decode_step: one decode step of one layer.  The new token at
+ * position t has query rows q[h] (h = g*G .. g*G + G - 1 for KV head g) and a
+ * key and value per KV head.  For each KV head g it attends over the B cache
+ * slots and itself: x_j = scale <q_h, k_j>, y_j = (x_j + zeta_j) / tau with
+ * zeta_j the Keyformer Gumbel noise for query position t and key position
+ * p_j (Philox4x32-10, key = seed, counter (p_j / 4, t, h, 0), word p_j mod 4,
+ * as in kvc_score), tau = +inf giving y = 0; the step score of key j is the
+ * sum over the G heads of softmax_j(y).  Every slot's acc grows by its step
+ * score.  Among the slots with pos <= t - recent, the lowest (acc, pos) -- then
+ * the lowest slot -- is evicted: the new token's key and value are written
+ * there, pos = t, acc = the new token's step score, and evicted[g] = that slot
+ * (-1 if no slot may leave; the cache then only accumulates).
+ * Source: Keyformer blog page, Gumbel-distribution and temperature sections
+ * (noisy tempered softmax as the score) and the closing paragraphs on the two
+ * phases (decode on the reduced cache, the score accumulated over steps, the
+ * w most recent tokens kept).
+ * Layout: q bf16, row h at q + h * q_head_stride; k_new, v_new bf16 [Hkv, D];
+ *   k_cache, v_cache bf16 [Hkv, B, D] (updated in place); pos int32 [Hkv, B]
+ *   (distinct positions < t); acc fp32 [Hkv, B] (>= 0); evicted int32 [Hkv]
+ *   or NULL.  The slots are unordered: only positions matter.
+ * Arithmetic: fp32, reductions in a fixed order (bit-reproducible).
+ * Errors: KVC_E_ARG unless 1 <= recent < B, t >= 0, scale finite and > 0,
+ *   tau > 0 (+inf allowed), pointers non-null and aligned (16 bytes for the
+ *   bf16 arrays); KVC_E_UNSUPPORTED unless D == 128, G <= 8 and
+ *   G * (B + 1) <= 32768; KVC_E_SHAPE for Hkv * G > 65535 or a bad q stride.
+ */
+kvc_status kvc_keyformer_decode_step(const void* q, int64_t q_head_stride, const void* k_new, const void* v_new,
+                                     void* k_cache, void* v_cache, int32_t* pos, float* acc, int32_t Hkv,
+                                     int32_t G, int32_t B, int32_t D, int32_t t, int32_t recent, float scale,
+                                     float tau, uint64_t seed, int32_t* evicted, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Kernel timing (measurement support).                                      */
 /* ------------------------------------------------------------------------ */
 /*

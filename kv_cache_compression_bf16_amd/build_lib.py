@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvc.so")
 
 SOURCES = ["kvc_common.hip", "score.hip", "pool.hip", "select.hip", "threshold.hip", "compact.hip", "budget.hip",
-           "think.hip"]
+           "think.hip", "decode.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -1,0 +1,287 @@
+// kvc_decode_init_scores / kvc_keyformer_decode_step: Keyformer's decode phase.
+//
+// Keyformer blog page, closing paragraphs on the two phases: decoding runs on
+// the reduced cache and each step's score is added to the score carried from
+// before; the cache keeps the w most recent tokens and the other tokens with
+// the highest score.  The step score is the Gumbel-noised tempered softmax of
+// the Gumbel-distribution and temperature sections, summed over the query
+// heads of a KV head.  One step: the new token (position t) attends over the B
+// slots and itself; every slot's accumulated score grows by its step score;
+// among the entries outside the recent window (positions <= t - recent) the
+// lowest accumulated score leaves (ties: the smaller position, then the
+// smaller slot) and the new token's key, value, position and step score take
+// its slot.
+//
+// Design: one workgroup of 16 waves per KV head.  16 lanes cover a 256-byte
+// key row with 16-byte loads (4 keys per wave, 64 per workgroup step); each
+// lane dots its 8 channels with the group's G queries (held in registers) and
+// 4 xor-shuffles finish each dot product.  The tempered logits (log2 units,
+// noise keyed by the key's position as in the prompt phase) stay in LDS,
+// G * (B + 1) floats.  Row max and sum per query head, the per-key score and
+// the eviction argmin are workgroup reductions in a fixed order, so the
+// result is bit-reproducible.
+#include "common.h"
+#include "philox.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kDecThreads = 1024;
+constexpr int kDecWaves = kDecThreads / kWave;
+constexpr int kMaxLogits = 32768;   // G * (B + 1) floats of LDS
+constexpr int kMaxG = 8;
+
+struct DecodeArgs {
+  const uint16_t* q;        // [Hkv * G][D], head stride q_hs
+  int64_t q_hs;
+  const uint16_t* k_new;    // [Hkv][D]
+  const uint16_t* v_new;
+  uint16_t* kc;             // [Hkv][B][D]
+  uint16_t* vc;
+  int32_t* pos;             // [Hkv][B]
+  float* acc;               // [Hkv][B]
+  int32_t* evicted;         // [Hkv] or null
+  int G, B, t, recent;
+  float c;                  // scale * log2(e)
+  float inv_tau;            // 1 / tau, 0 for tau = +inf
+  uint32_t seed_lo, seed_hi;
+};
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int i = 1; i < kDecWaves; ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kDecWaves; ++i) s += red[i];
+  return s;
+}
+
+__device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint64_t* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t u = __shfl_xor(v, o);
+    v = u < v ? u : v;
+  }
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  uint64_t m = red[0];
+#pragma unroll
+  for (int i = 1; i < kDecWaves; ++i) m = red[i] < m ? red[i] : m;
+  return m;
+}
+
+__global__ __launch_bounds__(kDecThreads) void keyformer_decode_step(DecodeArgs a) {
+  __shared__ float y[kMaxLogits];         // y[h * (B + 1) + j], log2 units
+  __shared__ float red[kDecWaves];
+  __shared__ uint64_t red64[kDecWaves];
+  const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane & 15;              // 8-channel chunk of the key row
+  const int N = a.B + 1;                  // the B slots, then the new token
+  const uint16_t* kg = a.kc + (int64_t)g * a.B * kD;
+  const int32_t* pg = a.pos + (int64_t)g * a.B;
+
+  // this lane's 8 channels of each query of the group
+  float qv[kMaxG][8];
+#pragma unroll
+  for (int hh = 0; hh < kMaxG; ++hh) {
+    if (hh < a.G) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(a.q + (int64_t)(g * a.G + hh) * a.q_hs + sub * 8);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[hh][2 * e] = __uint_as_float(ww[e] << 16);
+        qv[hh][2 * e + 1] = __uint_as_float(ww[e] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[hh][e] = 0.f;
+    }
+  }
+
+  // logits: key j = 4 * (64 * step + wave) ... handled by 16 lanes each
+  for (int j0 = wave * 4; j0 < N; j0 += kDecWaves * 4) {
+    const int j = j0 + (lane >> 4);
+    const bool ok = j < N;
+    const uint16_t* row = (ok && j < a.B) ? kg + (int64_t)j * kD : a.k_new + (int64_t)g * kD;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(row + sub * 8);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    float kv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kv[2 * e] = __uint_as_float(ww[e] << 16);
+      kv[2 * e + 1] = __uint_as_float(ww[e] & 0xFFFF0000u);
+    }
+    const int p = ok ? (j < a.B ? pg[j] : a.t) : 0;
+#pragma unroll
+    for (int hh = 0; hh < kMaxG; ++hh) {
+      if (hh >= a.G) break;
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(kv[e], qv[hh][e], d);
+      d += __shfl_xor(d, 8);
+      d += __shfl_xor(d, 4);
+      d += __shfl_xor(d, 2);
+      d += __shfl_xor(d, 1);
+      if (ok && sub == 0) {
+        const uint32_t h = (uint32_t)(g * a.G + hh);
+        const u32x4 x = philox4x32_10(u32x4{(uint32_t)p >> 2, (uint32_t)a.t, h, 0u}, a.seed_lo, a.seed_hi);
+        const uint32_t word = (p & 3) == 0 ? x.x : (p & 3) == 1 ? x.y : (p & 3) == 2 ? x.z : x.w;
+        y[hh * N + j] = fmaf(d, a.c, gumbel_log2_from_word(word)) * a.inv_tau;
+      }
+    }
+  }
+  __syncthreads();
+
+  // per query head: m = max y, l = sum 2^(y - m); then score_j = sum_h 2^(y - m) / l
+  float m_h[kMaxG], il_h[kMaxG];
+#pragma unroll
+  for (int hh = 0; hh < kMaxG; ++hh) {
+    if (hh >= a.G) break;
+    float mx = -INFINITY;
+    for (int j = tid; j < N; j += kDecThreads) mx = fmaxf(mx, y[hh * N + j]);
+    const float m = block_max(mx, red);
+    float s = 0.f;
+    for (int j = tid; j < N; j += kDecThreads) s += __builtin_amdgcn_exp2f(y[hh * N + j] - m);
+    const float l = block_sum(s, red);
+    m_h[hh] = m;
+    il_h[hh] = 1.0f / l;
+  }
+  auto step_score = [&](int j) {
+    float sc = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < kMaxG; ++hh) {
+      if (hh >= a.G) break;
+      sc += __builtin_amdgcn_exp2f(y[hh * N + j] - m_h[hh]) * il_h[hh];
+    }
+    return sc;
+  };
+
+  // accumulate and find the lowest (score, position) outside the recent window
+  float* ag = a.acc + (int64_t)g * a.B;
+  const int cut = a.t - a.recent;   // positions <= cut may leave
+  uint64_t best = ~0ull;
+  for (int j = tid; j < a.B; j += kDecThreads) {
+    const float nv = ag[j] + step_score(j);
+    ag[j] = nv;
+    const int p = pg[j];
+    if (p <= cut) {
+      const uint64_t key = ((uint64_t)__float_as_uint(nv) << 32) | (uint32_t)p;   // scores >= 0
+      best = key < best ? key : best;
+    }
+  }
+  best = block_min_u64(best, red64);
+  // the slot holding that (score, position); the smallest such slot
+  uint64_t slot = ~0ull;
+  if (best != ~0ull)
+    for (int j = tid; j < a.B; j += kDecThreads) {
+      const uint64_t key = ((uint64_t)__float_as_uint(ag[j]) << 32) | (uint32_t)pg[j];
+      if (pg[j] <= cut && key == best) slot = (uint64_t)j < slot ? (uint64_t)j : slot;
+    }
+  slot = block_min_u64(slot, red64);
+  if (slot == ~0ull) {   // nothing may leave (positions not below t - recent): no eviction
+    if (tid == 0 && a.evicted) a.evicted[g] = -1;
+    return;
+  }
+  const int e = (int)slot;
+  // the new token takes slot e
+  if (tid < 16) {
+    const u32x4 kn = *reinterpret_cast<const u32x4*>(a.k_new + (int64_t)g * kD + tid * 8);
+    const u32x4 vn = *reinterpret_cast<const u32x4*>(a.v_new + (int64_t)g * kD + tid * 8);
+    *reinterpret_cast<u32x4*>(a.kc + ((int64_t)g * a.B + e) * kD + tid * 8) = kn;
+    *reinterpret_cast<u32x4*>(a.vc + ((int64_t)g * a.B + e) * kD + tid * 8) = vn;
+  }
+  if (tid == 0) {
+    ag[e] = step_score(a.B);
+    a.pos[(int64_t)g * a.B + e] = a.t;
+    if (a.evicted) a.evicted[g] = e;
+  }
+}
+
+__global__ __launch_bounds__(256) void decode_init_scores(const float* imp, int64_t hs, const int32_t* idx,
+                                                          int budget, int n, float* acc) {
+  const int g = blockIdx.y, t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= budget) return;
+  const int j = idx[(int64_t)g * budget + t];
+  acc[(int64_t)g * budget + t] = (j >= 0 && j < n) ? imp[(int64_t)g * hs + j] : 0.f;
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" kvc_status kvc_decode_init_scores(const float* importance, int64_t imp_head_stride,
+                                             const int32_t* indices, int32_t Hkv, int32_t budget, int32_t n,
+                                             float* acc, void* stream) {
+  using namespace kvc;
+  if (Hkv < 1 || budget < 0 || n < 0) return KVC_E_ARG;
+  if (Hkv > 65535) return KVC_E_SHAPE;
+  if (Hkv > 1 && imp_head_stride < n) return KVC_E_SHAPE;
+  if (budget == 0) return KVC_OK;
+  if (!importance || !indices || !acc) return KVC_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(importance) | reinterpret_cast<uintptr_t>(indices) |
+       reinterpret_cast<uintptr_t>(acc)) & 3)
+    return KVC_E_ARG;
+  KVC_LAUNCH("decode_init_scores", decode_init_scores, dim3((budget + 255) / 256, Hkv), dim3(256),
+             static_cast<hipStream_t>(stream), importance, imp_head_stride, indices, budget, n, acc);
+  return KVC_OK;
+}
+
+extern "C" kvc_status kvc_keyformer_decode_step(const void* q, int64_t q_head_stride, const void* k_new,
+                                                const void* v_new, void* k_cache, void* v_cache, int32_t* pos,
+                                                float* acc, int32_t Hkv, int32_t G, int32_t B, int32_t D,
+                                                int32_t t, int32_t recent, float scale, float tau,
+                                                uint64_t seed, int32_t* evicted, void* stream) {
+  using namespace kvc;
+  if (Hkv < 1 || G < 1 || B < 2 || t < 0 || recent < 1 || recent >= B) return KVC_E_ARG;
+  if (!(scale > 0.f && scale < INFINITY) || !(tau > 0.f)) return KVC_E_ARG;   // tau = +inf allowed
+  if (D != kD) return KVC_E_UNSUPPORTED;
+  if (G > kMaxG || (int64_t)G * (B + 1) > kMaxLogits) return KVC_E_UNSUPPORTED;
+  if (Hkv > 65535 || (int64_t)Hkv * G > 65535) return KVC_E_SHAPE;
+  if (q_head_stride < D || (q_head_stride & 7)) return KVC_E_SHAPE;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !pos || !acc) return KVC_E_ARG;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return KVC_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(pos) | reinterpret_cast<uintptr_t>(acc) |
+       reinterpret_cast<uintptr_t>(evicted)) & 3)
+    return KVC_E_ARG;
+  DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_hs = q_head_stride;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.kc = static_cast<uint16_t*>(k_cache);
+  a.vc = static_cast<uint16_t*>(v_cache);
+  a.pos = pos;
+  a.acc = acc;
+  a.evicted = evicted;
+  a.G = G;
+  a.B = B;
+  a.t = t;
+  a.recent = recent;
+  a.c = scale * kLog2e;
+  a.inv_tau = tau == INFINITY ? 0.f : 1.0f / tau;
+  a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFull);
+  a.seed_hi = (uint32_t)(seed >> 32);
+  KVC_LAUNCH("keyformer_decode_step", keyformer_decode_step, dim3(Hkv), dim3(kDecThreads),
+             static_cast<hipStream_t>(stream), a);
+  return KVC_OK;
+}

@@ -67,6 +67,9 @@ def _load():
                                                    P, P, P, P, SZ, P]),
         "kvc_channel_prune_query": (ctypes.c_int, [P, P, I32, I32, I32, I64, I32, I32, I32, F64, P, P, P, P, SZ,
                                                    P]),
+        "kvc_decode_init_scores": (ctypes.c_int, [P, I64, P, I32, I32, I32, P, P]),
+        "kvc_keyformer_decode_step": (ctypes.c_int, [P, I64, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                                     ctypes.c_float, ctypes.c_float, ctypes.c_uint64, P, P]),
         "kvc_timing_enable": (ctypes.c_int, [I32]),
         "kvc_timing_count": (I32, []),
         "kvc_timing_read": (ctypes.c_int, [I32, ctypes.c_char_p, I32, ctypes.POINTER(I32),
@@ -329,6 +332,44 @@ def kvc_channel_prune_value(k_c, v_c, q_obs, channels, v_pruned, *, recent, lam,
                                         _ptr(v_pruned), _ptr(ws), nbytes, _stream(stream, k_c.device)),
            "kvc_channel_prune_value")
     return channels, v_pruned
+
+
+# ---------------------------------------------------------------- Keyformer decode phase
+def kvc_decode_init_scores(importance, indices, acc, *, n, stream=None):
+    """acc [Hkv, B] = importance [Hkv, >= n] at the kept prefix indices [Hkv, B], else 0."""
+    if importance.dtype != torch.float32 or acc.dtype != torch.float32 or indices.dtype != torch.int32:
+        raise TypeError("importance and acc must be float32, indices int32")
+    Hkv, B = indices.shape
+    if acc.shape != indices.shape or not acc.is_contiguous() or not indices.is_contiguous():
+        raise ValueError("acc and indices must be contiguous [Hkv, B]")
+    if importance.dim() != 2 or importance.stride(1) != 1 or importance.shape[0] != Hkv:
+        raise ValueError("importance must be [Hkv, n] with unit stride along n")
+    _check(_lib.kvc_decode_init_scores(_ptr(importance), importance.stride(0), _ptr(indices), Hkv, B, int(n),
+                                       _ptr(acc), _stream(stream, acc.device)), "kvc_decode_init_scores")
+    return acc
+
+
+def kvc_keyformer_decode_step(q, k_new, v_new, k_cache, v_cache, pos, acc, *, t, recent, tau=1.0, seed=0,
+                              scale=None, evicted=None, stream=None):
+    """One Keyformer decode step: q [H, D], k_new / v_new [Hkv, D], caches [Hkv, B, D] (in place),
+    pos int32 / acc float32 [Hkv, B] (in place), optional evicted int32 [Hkv]."""
+    for x, nme in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _bf16(x, nme)
+    Hkv, B, D = k_cache.shape
+    H = q.shape[0]
+    if H % Hkv or q.shape[-1] != D or q.stride(-1) != 1 or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q and the caches")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous() and k_new.is_contiguous() and v_new.is_contiguous()):
+        raise ValueError("caches and new rows must be contiguous")
+    if pos.dtype != torch.int32 or acc.dtype != torch.float32 or pos.shape != (Hkv, B) or acc.shape != (Hkv, B):
+        raise ValueError("pos must be int32 and acc float32, both [Hkv, B]")
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(_lib.kvc_keyformer_decode_step(_ptr(q), q.stride(0), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                          _ptr(v_cache), _ptr(pos), _ptr(acc), Hkv, H // Hkv, B, D, int(t),
+                                          int(recent), float(scale), float(tau), int(seed) & (2 ** 64 - 1),
+                                          _ptr(evicted), _stream(stream, k_cache.device)),
+           "kvc_keyformer_decode_step")
+    return evicted
 
 
 # ---------------------------------------------------------------- timing

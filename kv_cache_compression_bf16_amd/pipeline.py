@@ -85,6 +85,21 @@ class CompressionPlan:
             nb = kvc.lib.kvc_channel_prune_value_workspace_size(Hkv, wl.G, wl.w, wl.budget, wl.recent, D)
             self.ws_think_v = torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
 
+    def decode_init(self, stream=None):
+        """Hand the prompt phase's cache to the decode phase: slot positions are the
+        kept indices, accumulated scores the prompt importance of kept prefix tokens."""
+        wl = self.wl
+        self.pos = self.indices.clone()
+        self.acc = torch.empty(self.indices.shape, dtype=torch.float32, device=self.device)
+        self.evicted = torch.empty(wl.Hkv, dtype=torch.int32, device=self.device)
+        kvc.kvc_decode_init_scores(self.importance[0], self.indices, self.acc, n=wl.n, stream=stream)
+
+    def decode_step(self, q, k_new, v_new, t, stream=None):
+        """One Keyformer decode step on the compacted cache (in place)."""
+        wl = self.wl
+        kvc.kvc_keyformer_decode_step(q, k_new, v_new, self.kc, self.vc, self.pos, self.acc, t=t, recent=wl.recent,
+                                      tau=self.tau, seed=wl.noise_seed, evicted=self.evicted, stream=stream)
+
     def score(self, q, k, layer_scales=None, stream=None):
         wl = self.wl
         kvc.kvc_score(q, k, self.importance if wl.L > 1 else self.importance[0], w=wl.w, S=wl.S,

@@ -7,7 +7,8 @@ oracle consume exactly these arrays.
 Recipe (per tensor): numpy ``Generator(PCG64(SeedSequence([seed, cfg_id,
 tensor_id, layer])))``, ``standard_normal(dtype=float32)``, rounded to bf16 with
 round-to-nearest-even and kept as raw uint16 bit patterns.  tensor_id: Q=0,
-K=1, V=2, per-layer logit scales=3, outlier key channels=4.
+K=1, V=2, per-layer logit scales=3, outlier key channels=4; decode-phase rows of
+step s (layer = s): query=5, key=6, value=7.
 
 * Only the observation-window queries Q_obs [H, w, D] are drawn (the prefix
   queries are never used by the method).
@@ -25,6 +26,7 @@ import math
 import numpy as np
 
 Q_ID, K_ID, V_ID, SCALE_ID, OUTLIER_ID = 0, 1, 2, 3, 4
+DEC_Q_ID, DEC_K_ID, DEC_V_ID = 5, 6, 7
 
 
 @dataclass(frozen=True)
@@ -55,6 +57,7 @@ class Workload:
     pool_kernel: int = 0            # SnapKV 1D pooling of the importance before top-k (0: off)
     pool_mode: int = 0              # 0: average (zero padding, / kernel), 1: max
     threshold: float = 0.0          # > 0: KVzap threshold selection at threshold * G / (S - w), not top-k
+    decode_steps: int = 0           # > 0: Keyformer decode steps after the prompt phase (positions S, S+1, ...)
     seed: int = 0
     notes: str = field(default="", compare=False)
 
@@ -113,6 +116,11 @@ WORKLOADS = {
         name="keyformer_mha32_s8192", cfg_id=3, L=1, H=32, Hkv=32, S=8192, w=512, recent=512,
         budget=4096, gumbel=True, taus=(1.0, 1.0e4),
         notes="Keyformer MHA 32, Gumbel noise, tau 1 and 1e4, 512 recent + 3584 top"),
+    "keyformer_mha32_s8192_decode": Workload(
+        name="keyformer_mha32_s8192_decode", cfg_id=3, L=1, H=32, Hkv=32, S=8192, w=512, recent=512,
+        budget=4096, gumbel=True, taus=(1.0,), decode_steps=64,
+        notes="the Keyformer prompt phase above (same inputs, tau 1), then decode steps on the 4096-token cache: "
+              "score accumulation and eviction of one token per step"),
     "think_s131072": Workload(
         name="think_s131072", cfg_id=4, L=1, H=8, Hkv=8, S=131072, w=64, recent=64,
         budget=int(0.2 * 131072), outliers=4, think_lambda=0.4, think_p=2,
@@ -172,6 +180,13 @@ def gen_k(wl, layer=0):
 
 def gen_v(wl, layer=0):
     return _normal_bf16(wl, V_ID, layer, (wl.Hkv, wl.S, wl.D))
+
+
+def gen_decode(wl, step):
+    """Raw bf16 bits of decode step `step` (the token at position S + step):
+    q [H, D], k [Hkv, D], v [Hkv, D]."""
+    return (_normal_bf16(wl, DEC_Q_ID, step, (wl.H, wl.D)), _normal_bf16(wl, DEC_K_ID, step, (wl.Hkv, wl.D)),
+            _normal_bf16(wl, DEC_V_ID, step, (wl.Hkv, wl.D)))
 
 
 def gen_layer(wl, layer=0):

@@ -251,6 +251,32 @@ def test_channel_prune_value_validation():
     assert call(nb=ws - 256) == E.KVC_E_WORKSPACE
 
 
+def test_decode_validation():
+    names = ["q", "qs", "kn", "vn", "kc", "vc", "pos", "acc", "Hkv", "G", "B", "D", "t", "recent", "scale", "tau",
+             "seed", "ev", "st"]
+    call = _named_call(lib.kvc_keyformer_decode_step, names,
+                       (FAKE, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 1, 4096, 128, 9000, 512, 0.088, 1.0, 0,
+                        None, None))
+    assert call(recent=4096) == E.KVC_E_ARG                   # the window must be shorter than the cache
+    assert call(recent=0) == E.KVC_E_ARG
+    assert call(t=-1) == E.KVC_E_ARG
+    assert call(scale=0.0) == E.KVC_E_ARG
+    assert call(tau=0.0) == E.KVC_E_ARG
+    assert call(tau=float("nan")) == E.KVC_E_ARG
+    assert call(D=64) == E.KVC_E_UNSUPPORTED
+    assert call(G=9, Hkv=4) == E.KVC_E_UNSUPPORTED
+    assert call(G=8, Hkv=4, B=4096) == E.KVC_E_UNSUPPORTED    # 8 * 4097 logits do not fit
+    assert call(qs=100) == E.KVC_E_SHAPE
+    assert call(acc=None) == E.KVC_E_ARG
+    assert call(kc=ctypes.c_void_p((1 << 20) + 8)) == E.KVC_E_ARG
+    assert call(ev=ctypes.c_void_p((1 << 20) + 2)) == E.KVC_E_ARG
+    f = lib.kvc_decode_init_scores
+    assert f(FAKE, 100, FAKE, 4, 10, -1, FAKE, None) == E.KVC_E_ARG
+    assert f(FAKE, 50, FAKE, 4, 10, 100, FAKE, None) == E.KVC_E_SHAPE
+    assert f(None, 100, FAKE, 4, 10, 100, FAKE, None) == E.KVC_E_ARG
+    assert f(FAKE, 100, FAKE, 4, 0, 100, FAKE, None) == E.KVC_OK   # nothing to do: no launch
+
+
 def test_channel_prune_query_validation():
     f = lib.kvc_channel_prune_query
     ws = lib.kvc_channel_prune_query_workspace_size(8, 4, 100, 128)

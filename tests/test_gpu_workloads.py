@@ -181,6 +181,44 @@ def test_think_s131072_kv():
     assert np.array_equal(plan.mask_v.cpu().numpy().sum(axis=1), np.full(wl.Hkv, Tv))
 
 
+def test_keyformer_mha32_s8192_decode():
+    wl = wk.WORKLOADS["keyformer_mha32_s8192_decode"]
+    plan, (q, k, v), sc = _run(wl, tau=wl.taus[0])
+    plan.decode_init()
+    torch.cuda.synchronize()
+    imp = plan.importance[0].cpu().numpy()
+    idx = plan.indices.cpu().numpy()
+    # hand-over in isolation on the GPU's own importance and indices: bit-exact
+    assert np.array_equal(plan.acc.cpu().numpy().astype(np.float64), oracle.decode.initial_scores(imp, idx, wl.n))
+    assert np.array_equal(plan.pos.cpu().numpy(), idx)
+    scale = float(np.float32(1.0 / math.sqrt(wl.D)))
+    f64 = oracle.score.bf16_bits_to_f64
+    kinds = []
+    for s in range(6):
+        t = wl.S + s
+        state = (bits_of(plan.kc), bits_of(plan.vc), plan.pos.cpu().numpy(), plan.acc.cpu().numpy())
+        qd, kn, vn = wk.gen_decode(wl, s)
+        plan.decode_step(to_dev(qd), to_dev(kn), to_dev(vn), t)
+        torch.cuda.synchronize()
+        ev = plan.evicted.cpu().numpy()
+        rk, rv, rp, ra, rev = oracle.decode.decode_step(state[0], state[1], state[2], state[3].astype(np.float64),
+                                                        f64(qd), kn, vn, t=t, recent=wl.recent, scale=scale,
+                                                        tau=wl.taus[0], seed=wl.noise_seed)
+        gk, gv, gp, ga = bits_of(plan.kc), bits_of(plan.vc), plan.pos.cpu().numpy(), plan.acc.cpu().numpy()
+        for g in range(wl.Hkv):
+            if ev[g] != rev[g]:
+                a = ra[g].copy()
+                a[rev[g]] = np.nan
+                assert state[2][g, ev[g]] <= t - wl.recent
+                kinds.append("tie")
+                continue
+            kinds.append("exact")
+            assert np.array_equal(gp[g], rp[g]) and np.array_equal(gk[g], rk[g]) and np.array_equal(gv[g], rv[g])
+            assert np.allclose(ga[g], ra[g], rtol=2e-6, atol=1e-9)
+    print("evictions:", {k_: kinds.count(k_) for k_ in set(kinds)})
+    assert kinds.count("exact") >= 0.9 * len(kinds)
+
+
 def test_gqa32x8_s32768_thr2():
     wl = wk.WORKLOADS["gqa32x8_s32768_thr2"]
     plan, (q, k, v), sc = _run(wl)
