@@ -13,11 +13,12 @@
 // its slot.
 //
 // Design: one workgroup of 16 waves per KV head.  16 lanes cover a 256-byte
-// key row with 16-byte loads (4 keys per wave, 64 per workgroup step); each
+// key row with 16-byte loads (4 keys per wave, 8 rows per lane in flight); each
 // lane dots its 8 channels with the group's G queries (held in registers) and
-// 4 xor-shuffles finish each dot product.  The tempered logits (log2 units,
-// noise keyed by the key's position as in the prompt phase) stay in LDS,
-// G * (B + 1) floats.  Row max and sum per query head, the per-key score and
+// 4 xor-shuffles finish each dot product into LDS (G * (B + 1) floats); then
+// every thread adds the noise (keyed by the key's position, as in the prompt
+// phase) and the temperature to its own entries, giving the logits in log2
+// units.  Row max and sum per query head, the per-key score and
 // the eviction argmin are workgroup reductions in a fixed order, so the
 // result is bit-reproducible.
 #include "common.h"
@@ -90,6 +91,8 @@ __device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint64_t* red) {
   return m;
 }
 
+// kGmax: a power of two >= G (query registers and loop bounds sized for it).
+template <int kGmax>
 __global__ __launch_bounds__(kDecThreads) void keyformer_decode_step(DecodeArgs a) {
   __shared__ float y[kMaxLogits];         // y[h * (B + 1) + j], log2 units
   __shared__ float red[kDecWaves];
@@ -101,9 +104,9 @@ __global__ __launch_bounds__(kDecThreads) void keyformer_decode_step(DecodeArgs 
   const int32_t* pg = a.pos + (int64_t)g * a.B;
 
   // this lane's 8 channels of each query of the group
-  float qv[kMaxG][8];
+  float qv[kGmax][8];
 #pragma unroll
-  for (int hh = 0; hh < kMaxG; ++hh) {
+  for (int hh = 0; hh < kGmax; ++hh) {
     if (hh < a.G) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(a.q + (int64_t)(g * a.G + hh) * a.q_hs + sub * 8);
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
@@ -118,44 +121,65 @@ __global__ __launch_bounds__(kDecThreads) void keyformer_decode_step(DecodeArgs 
     }
   }
 
-  // logits: key j = 4 * (64 * step + wave) ... handled by 16 lanes each
-  for (int j0 = wave * 4; j0 < N; j0 += kDecWaves * 4) {
-    const int j = j0 + (lane >> 4);
-    const bool ok = j < N;
-    const uint16_t* row = (ok && j < a.B) ? kg + (int64_t)j * kD : a.k_new + (int64_t)g * kD;
-    const u32x4 w = *reinterpret_cast<const u32x4*>(row + sub * 8);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-    float kv[8];
+  // logits: 16 lanes per key, 4 keys per wave, kU keys per lane group in
+  // flight (their row loads issued together); step u of super-step j0 takes
+  // key j0 + u * 64 + 4 * wave + lane / 16
+  constexpr int kU = kGmax <= 2 ? 8 : 4;
+  for (int j0 = 0; j0 < N; j0 += kU * kDecWaves * 4) {
+    u32x4 w[kU];
+    int jj[kU];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kv[2 * e] = __uint_as_float(ww[e] << 16);
-      kv[2 * e + 1] = __uint_as_float(ww[e] & 0xFFFF0000u);
+    for (int u = 0; u < kU; ++u) {
+      const int j = j0 + u * kDecWaves * 4 + wave * 4 + (lane >> 4);
+      jj[u] = j;
+      const uint16_t* row = (j < a.B) ? kg + (int64_t)j * kD : a.k_new + (int64_t)g * kD;   // j >= B: new key
+      w[u] = *reinterpret_cast<const u32x4*>(row + sub * 8);
     }
-    const int p = ok ? (j < a.B ? pg[j] : a.t) : 0;
 #pragma unroll
-    for (int hh = 0; hh < kMaxG; ++hh) {
-      if (hh >= a.G) break;
-      float d = 0.f;
+    for (int u = 0; u < kU; ++u) {
+      const int j = jj[u];
+      const bool ok = j < N;
+      const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+      float kv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d = fmaf(kv[e], qv[hh][e], d);
-      d += __shfl_xor(d, 8);
-      d += __shfl_xor(d, 4);
-      d += __shfl_xor(d, 2);
-      d += __shfl_xor(d, 1);
-      if (ok && sub == 0) {
-        const uint32_t h = (uint32_t)(g * a.G + hh);
-        const u32x4 x = philox4x32_10(u32x4{(uint32_t)p >> 2, (uint32_t)a.t, h, 0u}, a.seed_lo, a.seed_hi);
-        const uint32_t word = (p & 3) == 0 ? x.x : (p & 3) == 1 ? x.y : (p & 3) == 2 ? x.z : x.w;
-        y[hh * N + j] = fmaf(d, a.c, gumbel_log2_from_word(word)) * a.inv_tau;
+      for (int e = 0; e < 4; ++e) {
+        kv[2 * e] = __uint_as_float(ww[e] << 16);
+        kv[2 * e + 1] = __uint_as_float(ww[e] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int hh = 0; hh < kGmax; ++hh) {
+        if (hh >= a.G) break;
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(kv[e], qv[hh][e], d);
+        d += __shfl_xor(d, 8);
+        d += __shfl_xor(d, 4);
+        d += __shfl_xor(d, 2);
+        d += __shfl_xor(d, 1);
+        if (ok && sub == 0) y[hh * N + j] = d;   // the raw dot product; noise below
       }
     }
   }
   __syncthreads();
+  // noise and temperature with every lane busy: y = (x c + zeta log2 e) / tau
+  for (int i = tid; i < a.G * N; i += kDecThreads) {
+    const int hh = i / N, j = i - hh * N;
+    if (a.inv_tau == 0.f) {
+      y[i] = 0.f;   // tau = +inf: uniform
+      continue;
+    }
+    const int p = j < a.B ? pg[j] : a.t;
+    const uint32_t h = (uint32_t)(g * a.G + hh);
+    const u32x4 x = philox4x32_10(u32x4{(uint32_t)p >> 2, (uint32_t)a.t, h, 0u}, a.seed_lo, a.seed_hi);
+    const uint32_t word = (p & 3) == 0 ? x.x : (p & 3) == 1 ? x.y : (p & 3) == 2 ? x.z : x.w;
+    y[i] = fmaf(y[i], a.c, gumbel_log2_from_word(word)) * a.inv_tau;
+  }
+  __syncthreads();
 
   // per query head: m = max y, l = sum 2^(y - m); then score_j = sum_h 2^(y - m) / l
-  float m_h[kMaxG], il_h[kMaxG];
+  float m_h[kGmax], il_h[kGmax];
 #pragma unroll
-  for (int hh = 0; hh < kMaxG; ++hh) {
+  for (int hh = 0; hh < kGmax; ++hh) {
     if (hh >= a.G) break;
     float mx = -INFINITY;
     for (int j = tid; j < N; j += kDecThreads) mx = fmaxf(mx, y[hh * N + j]);
@@ -169,7 +193,7 @@ __global__ __launch_bounds__(kDecThreads) void keyformer_decode_step(DecodeArgs 
   auto step_score = [&](int j) {
     float sc = 0.f;
 #pragma unroll
-    for (int hh = 0; hh < kMaxG; ++hh) {
+    for (int hh = 0; hh < kGmax; ++hh) {
       if (hh >= a.G) break;
       sc += __builtin_amdgcn_exp2f(y[hh * N + j] - m_h[hh]) * il_h[hh];
     }
@@ -281,7 +305,14 @@ extern "C" kvc_status kvc_keyformer_decode_step(const void* q, int64_t q_head_st
   a.inv_tau = tau == INFINITY ? 0.f : 1.0f / tau;
   a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFull);
   a.seed_hi = (uint32_t)(seed >> 32);
-  KVC_LAUNCH("keyformer_decode_step", keyformer_decode_step, dim3(Hkv), dim3(kDecThreads),
-             static_cast<hipStream_t>(stream), a);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (G == 1)
+    KVC_LAUNCH("keyformer_decode_step", keyformer_decode_step<1>, dim3(Hkv), dim3(kDecThreads), s, a);
+  else if (G == 2)
+    KVC_LAUNCH("keyformer_decode_step", keyformer_decode_step<2>, dim3(Hkv), dim3(kDecThreads), s, a);
+  else if (G <= 4)
+    KVC_LAUNCH("keyformer_decode_step", keyformer_decode_step<4>, dim3(Hkv), dim3(kDecThreads), s, a);
+  else
+    KVC_LAUNCH("keyformer_decode_step", keyformer_decode_step<8>, dim3(Hkv), dim3(kDecThreads), s, a);
   return KVC_OK;
 }
