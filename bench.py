@@ -122,20 +122,22 @@ def algorithmic(wl, kept_rows=None):
 
 
 KERNEL_SOURCE = {"score": "score.hip", "select": "select.hip", "compact": "compact.hip", "lmba": "budget.hip",
-                 "pool": "pool.hip", "threshold": "threshold.hip",
+                 "pool": "pool.hip", "threshold": "threshold.hip", "keyformer": "decode.hip", "decode": "decode.hip",
                  "think": "think.hip"}
 
 
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
     (profiles/hbm_traffic_<workload>.md), or None if there is none or the kernel's
-    source has changed since the counters were taken."""
+    source (common.h, philox.h for the scoring and decode kernels, its .hip file)
+    has changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     csrc = os.path.join(ROOT, "kv_cache_compression_bf16_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("common.h", KERNEL_SOURCE[kernel.split("_")[0]]):
+    src = KERNEL_SOURCE[kernel.split("_")[0]]
+    for f in ("common.h",) + (("philox.h",) if src in ("score.hip", "decode.hip") else ()) + (src,):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     for line in open(path):
