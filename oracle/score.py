@@ -27,6 +27,10 @@ Readings where the pages are silent (each also listed in the design notes):
   window means (so a row sums to G);
 * noise is added before dividing by tau; tau = +inf gives y = 0 (uniform);
 * the Gumbel generator is the one in ``oracle.philox``.
+
+``importance_causal`` is the other reading of Keyformer's prompt phase (full,
+causal attention); its pins are a harmonic-sum closed form at tau = inf, the
+row and group sums, and explicit loops on a tiny case.
 """
 
 import numpy as np
@@ -97,5 +101,44 @@ def importance(q_obs, k, *, S, w, scale, gumbel=False, tau=1.0, seed=0, kv_heads
         for h in range(g * G, (g + 1) * G):
             acc += head_window_mean(q_obs[h], k[g], n=n, scale=scale, gumbel=gumbel, seed=seed,
                                     head=h, S=S, w=w, tau=tau)
+        out[g] = acc
+    return out
+
+
+# ---- Keyformer's other reading: causal scoring over the whole prompt
+#
+# Keyformer blog page, closing paragraphs: the prompt phase is a full attention
+# pass with the Gumbel noise added, from which the key tokens are picked.  Read
+# as causal attention: window query i sits at position P = S - w + i and sees
+# the keys j <= P (with w = S every prompt position is a query).  Its noisy
+# tempered softmax runs over those P + 1 keys; the importance of key j is the
+# mean over the w query rows (0 for the rows that cannot see it), summed over
+# the G query heads of the KV head, for every j in [0, S).
+
+def head_causal_mean(q_h, k_g, *, S, w, scale, gumbel=False, seed=0, head=0, tau=1.0, rows=None):
+    """a[j] = (1/w) * sum over the given window rows i (default: all) of p[i, j],
+    p the causal softmax of row i.  Returns [S] float64."""
+    out = np.zeros(S)
+    for i in (range(w) if rows is None else rows):
+        P = S - w + i
+        x = scale * (k_g[:P + 1] @ q_h[i])
+        if gumbel:
+            x = np.zeros_like(x) if np.isinf(tau) else (x + philox.keyformer_noise(seed, head, P, np.arange(P + 1))) / tau
+        e = np.exp(x - x.max())
+        out[:P + 1] += e / e.sum()
+    return out / w
+
+
+def importance_causal(q_obs, k, *, S, w, scale, gumbel=False, tau=1.0, seed=0, kv_heads=None):
+    """Causal importance I[g, j], j in [0, S).  q_obs: [H, w, D] float64 (the
+    last w prompt queries), k: [Hkv, >= S, D] float64.  Returns [Hkv, S]."""
+    H, Hkv = q_obs.shape[0], k.shape[0]
+    G = H // Hkv
+    out = np.full((Hkv, S), np.nan)
+    for g in (range(Hkv) if kv_heads is None else kv_heads):
+        acc = np.zeros(S)
+        for h in range(g * G, (g + 1) * G):
+            acc += head_causal_mean(q_obs[h], k[g], S=S, w=w, scale=scale, gumbel=gumbel, seed=seed, head=h,
+                                    tau=tau)
         out[g] = acc
     return out
