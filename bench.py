@@ -74,6 +74,12 @@ def algorithmic(wl, kept_rows=None):
         B_total = wl.total_budget * Hkv if wl.total_budget else L * Hkv * wl.budget
     rows = B_total * D * 2
     flops_pass = 2.0 * L * Hkv * R * n * D
+    if wl.causal:
+        # every key up to the row's position: w (S - w) + w (w + 1) / 2 (row, key) pairs per query head
+        n = S
+        k_prefix = L * Hkv * n * D * 2
+        imp = L * Hkv * n * 4
+        flops_pass = 2.0 * D * L * H * (w * (S - w) + w * (w + 1) / 2)
     step_bytes = q_bytes + k_prefix + 2 * imp + B_total * 4 + 2 * rows * 2
     if wl.think_lambda >= 0:
         T = int(math.floor((1 - wl.think_lambda) * D))
@@ -94,6 +100,10 @@ def algorithmic(wl, kept_rows=None):
         "score_pass2": ("mfma", flops_pass, q_bytes + k_prefix + imp),
         "score_pass1_gumbel": ("mfma", flops_pass, q_bytes + k_prefix),
         "score_pass2_gumbel": ("mfma", flops_pass, q_bytes + k_prefix + imp),
+        "score_causal_pass1_gumbel": ("mfma", flops_pass, q_bytes + k_prefix),
+        "score_causal_pass2_gumbel": ("mfma", flops_pass, q_bytes + k_prefix + imp),
+        "score_causal_pass1": ("mfma", flops_pass, q_bytes + k_prefix),
+        "score_causal_pass2": ("mfma", flops_pass, q_bytes + k_prefix + imp),
         "select_topk": ("hbm", 0.0, imp + B_total * 4),
         "threshold_count": ("hbm", 0.0, imp),
         "threshold_emit": ("hbm", 0.0, imp + B_total * 4),
@@ -178,6 +188,24 @@ def cpu_baseline(wl, data, target_s, tau):
         return {"value": steps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                 "sample": f"{steps} decode steps of all {wl.Hkv} KV heads from a kept cache of the workload's rows "
                           f"(fp64 numpy), {dt:.1f} s"}
+    if wl.causal:
+        # whole query rows of the causal oracle (head 0, from position 0 on) until the
+        # time target; the rate is scaled by the share of the layer's (row, key) pairs done
+        qh = oracle.score.bf16_bits_to_f64(q[0])
+        kg = oracle.score.bf16_bits_to_f64(k[0])
+        scale = float(np.float32(1.0 / math.sqrt(wl.D)))
+        total_pairs = wl.H * (wl.w * (wl.S - wl.w) + wl.w * (wl.w + 1) / 2)
+        pairs, i, t0 = 0, 0, time.perf_counter()
+        while i < wl.w and time.perf_counter() - t0 < target_s:
+            oracle.score.head_causal_mean(qh, kg, S=wl.S, w=wl.w, scale=scale, gumbel=wl.gumbel, seed=wl.noise_seed,
+                                          head=0, tau=tau, rows=[i])
+            pairs += wl.S - wl.w + i + 1
+            i += 1
+        dt = time.perf_counter() - t0
+        threads = max([1] + [t.get("num_threads", 1) for t in threadpool_info()])
+        return {"value": wl.S * (pairs / total_pairs) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": f"{i} causal query rows of head 0 ({pairs} of the layer's {int(total_pairs)} (row, key) "
+                          f"pairs; scoring only, fp64 numpy), {dt:.1f} s"}
     qf = oracle.score.bf16_bits_to_f64(q if wl.L == 1 else q[0])
     kf = oracle.score.bf16_bits_to_f64(k if wl.L == 1 else k[0])
     kraw = k if wl.L == 1 else k[0]

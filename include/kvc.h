@@ -126,6 +126,24 @@ size_t kvc_score_workspace_size(const kvc_score_args* args /* host */);
 kvc_status kvc_score(const kvc_score_args* args /* host */, const void* q_obs, const void* k,
                      float* importance, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * kvc_score_causal: Keyformer's other reading of its prompt phase, a full
+ * (causal) attention pass.  Window row i of query head h sits at position
+ * P = S - w + i and sees the keys j <= P: x = alpha <q, k_j> (+ noise,
+ * / tau, exactly as kvc_score, the noise counter using P), softmax over those
+ * P + 1 keys, and I[l, g, j] = (1/w) sum over the rows of g's query heads of
+ * p[row, j] for every j in [0, S) (0 from rows that cannot see j).  With
+ * w = S every prompt position is a query.
+ * Source: Keyformer blog page, closing paragraphs (the prompt phase is a full
+ * attention pass, with the Gumbel noise, from which key tokens are picked).
+ * Layout: as kvc_score, except importance fp32 [L, Hkv, S] and w <= S.
+ * Errors: as kvc_score, plus KVC_E_SHAPE unless w <= S and w % 32 == 0.
+ */
+size_t kvc_score_causal_workspace_size(const kvc_score_args* args /* host */);
+
+kvc_status kvc_score_causal(const kvc_score_args* args /* host */, const void* q_obs, const void* k,
+                            float* importance, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* kvc_lmba_budget: ZigZag per-layer budgets from importance.                */
 /* ------------------------------------------------------------------------ */

@@ -86,11 +86,14 @@ struct ScoreParams {
   float inv_w;
   uint32_t seed_lo, seed_hi;
   int L, Hkv, G, w, S, n, R, nblk, chunk_rows;
+  int causal_unit;   // causal scoring: keys per unit (row r sees units b <= pos(r) / causal_unit); else 0
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <bool kPass2, bool kGumbel, int kW, int kT, int kCB>
+// kCausal: keys [0, S) and window row i (position S - w + i) sees the keys at
+// positions <= its own; w % 32 == 0, so no 32-row query block spans two heads.
+template <bool kPass2, bool kGumbel, bool kCausal, int kW, int kT, int kCB>
 __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreParams p) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int kThreads = kW * kWave;
@@ -114,12 +117,29 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
     if (ii < 0) { --hh; ii += p.w; }
     if (ii >= p.w) { ++hh; ii -= p.w; }
   };
+  // prompt position of window row r (row past R: past every key)
+  auto row_pos = [&](int r) {
+    if (r >= p.R) return p.S;
+    int hh, ii;
+    split_row(r, hh, ii);
+    return p.S - p.w + ii;
+  };
 
-  // This workgroup's contiguous range of units u = (layer*Hkv + g)*nblk + blk.
-  const int total = p.L * p.Hkv * p.nblk;
+  // This workgroup's units u = (layer*Hkv + g)*nblk + blk: a contiguous range,
+  // or (causal: a unit's work shrinks with blk) every gridDim.x-th unit of the
+  // order (blk, head), so each workgroup gets a mix and the costly ones first.
+  const int heads = p.L * p.Hkv;
+  const int total = heads * p.nblk;
   const int per = total / (int)gridDim.x, extra = total % (int)gridDim.x;
-  const int u0 = (int)blockIdx.x * per + min((int)blockIdx.x, extra);
-  const int u1 = u0 + per + ((int)blockIdx.x < extra ? 1 : 0);
+  const int u_first = (int)blockIdx.x * per + min((int)blockIdx.x, extra);
+  const int n_units = kCausal ? (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x
+                              : per + ((int)blockIdx.x < extra ? 1 : 0);
+  auto unit_at = [&](int it) {
+    if (!kCausal) return u_first + it;
+    const int v = (int)blockIdx.x + it * (int)gridDim.x;
+    const int blk = v / heads, head = v - blk * heads;
+    return head * p.nblk + blk;
+  };
 
   // K fragments of unit u: lane holds key (32t + col) of its wave's tiles,
   // 16-byte chunk (2s + hb), already in the MFMA A-operand layout.
@@ -137,12 +157,13 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
   };
 
   bf16x8 kf[kT][8];
-  if (u0 < u1) load_k(u0, kf);
+  if (n_units > 0) load_k(unit_at(0), kf);
   int staged = -1;   // head whose query rows are in LDS (single-chunk case)
-  for (int u = u0; u < u1; ++u) {
+  for (int it = 0; it < n_units; ++it) {
+    const int u = unit_at(it);
     const int head = u / p.nblk, blk = u - head * p.nblk;
     const int layer = head / p.Hkv, g = head - layer * p.Hkv;
-    if (u != u0) load_k(u, kf);   // issued before this unit's staging, if any
+    if (it != 0) load_k(u, kf);   // issued before this unit's staging, if any
     const int key0 = blk * kKeysPerUnit + wave * kKeysPerWave;
     const bool wave_full = key0 + kKeysPerWave <= p.n;   // no key of this wave past the prefix
     const float alpha = p.layer_scales ? p.layer_scales[layer] : p.scale;
@@ -220,12 +241,13 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
     auto row_stats = [&](auto clean_c, f32x16 (&acc)[kT], int r) -> float {
       constexpr bool kClean = decltype(clean_c)::value;
       if (!kClean) {
+        const int rpos = kCausal ? row_pos(r) : 0;
 #pragma unroll
         for (int t = 0; t < kT; ++t)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = key0 + 32 * t + 8 * (e >> 2) + 4 * hb + (e & 3);
-            if (key >= p.n || r >= p.R) acc[t][e] = -INFINITY;
+            if (key >= p.n || r >= p.R || (kCausal && key > rpos)) acc[t][e] = -INFINITY;
           }
       }
       float mx = acc[0][0];
@@ -255,6 +277,19 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
       const int nrows = min(rows_alloc, (p.R - c0 + 31) / 32 * 32);
       const int nb = nrows / 32;
       const bool rows_full = c0 + nrows <= p.R;
+      // causal: positions of the chunk's rows; skip a chunk no row of which
+      // sees this unit (uniform over the workgroup), and take the unmasked
+      // path only where every key of this wave is visible to every row
+      bool causal_clean = true;
+      if (kCausal) {
+        int h0, i0, h1, i1;
+        split_row(c0, h0, i0);
+        split_row(min(c0 + nrows, p.R) - 1, h1, i1);
+        const int pmin = h0 == h1 ? p.S - p.w + i0 : p.S - p.w;
+        const int pmax = h0 == h1 ? p.S - p.w + i1 : p.S - 1;
+        if (pmax < blk * kKeysPerUnit) continue;
+        causal_clean = pmin >= key0 + kKeysPerWave - 1;
+      }
       if (p.R > rows_alloc || head != staged) {
         __syncthreads();   // every wave is done with the previous rows
         stage(c0, nrows);
@@ -276,7 +311,7 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
             }
           }
         };
-        if (wave_full && rows_full)
+        if (wave_full && rows_full && causal_clean)
           blocks(std::true_type{});
         else
           blocks(std::false_type{});
@@ -310,6 +345,14 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
           f32x16 acc[kT];
           mfma_block(qb, acc);
           if (kGumbel) noisy(acc, c0 + qb * 32 + col);
+          if (kCausal && !causal_clean) {
+            const int rpos = row_pos(c0 + qb * 32 + col);
+#pragma unroll
+            for (int t = 0; t < kT; ++t)
+#pragma unroll
+              for (int e = 0; e < 16; ++e)
+                if (key0 + 32 * t + 8 * (e >> 2) + 4 * hb + (e & 3) > rpos) acc[t][e] = -INFINITY;
+          }
           const float rc = rcs[qb * 32 + col];   // +inf for rows past R: adds 0
 #pragma unroll
           for (int t = 0; t < kT; ++t)
@@ -360,8 +403,10 @@ __global__ __launch_bounds__(256) void score_combine(ScoreParams p, int heads) {
   float m = -INFINITY, l = 0.f;
   if (head < heads && r < p.R) {
     const float2* pp = p.part + (int64_t)head * p.nblk * p.R + r;
+    // causal: only the units this row's position can see were scored for it
+    const int nb_row = p.causal_unit ? min(p.nblk, (p.S - p.w + r % p.w) / p.causal_unit + 1) : p.nblk;
 #pragma unroll 4
-    for (int b = q; b < p.nblk; b += kGroups) {
+    for (int b = q; b < nb_row; b += kGroups) {
       const float2 a = pp[(int64_t)b * p.R];
       const float mn = fmaxf(m, a.x);
       const float ms = (mn == -INFINITY) ? 0.f : mn;
@@ -389,11 +434,11 @@ struct Plan {
   size_t part_bytes, rowc_bytes, total;
 };
 
-kvc_status plan(const kvc_score_args* a, Plan* pl) {
+kvc_status plan(const kvc_score_args* a, Plan* pl, bool causal = false) {
   if (!a) return KVC_E_ARG;
   if (a->L < 1 || a->H < 1 || a->Hkv < 1 || a->w < 1 || a->S < 2 || a->D < 1) return KVC_E_ARG;
   if (a->H % a->Hkv) return KVC_E_SHAPE;
-  if (a->w >= a->S) return KVC_E_SHAPE;
+  if (causal ? (a->w > a->S || (a->w & 31)) : a->w >= a->S) return KVC_E_SHAPE;
   if (a->D != kD) return KVC_E_UNSUPPORTED;
   if (a->L > 65535 || a->Hkv > 65535) return KVC_E_SHAPE;
   const int64_t G = a->H / a->Hkv;
@@ -405,7 +450,7 @@ kvc_status plan(const kvc_score_args* a, Plan* pl) {
   if ((a->q_head_stride | a->k_head_stride | a->q_layer_stride | a->k_layer_stride) & 7) return KVC_E_ARG;
   if (!a->layer_scales && !(a->scale > 0.f && isfinite(a->scale))) return KVC_E_ARG;
   if (a->gumbel && !(a->tau > 0.f)) return KVC_E_ARG;   // rejects NaN; +inf allowed
-  pl->n = a->S - a->w;
+  pl->n = causal ? a->S : a->S - a->w;
   pl->G = (int)G;
   pl->R = (int)(G * a->w);
   pl->shape = score_shape(pl->R, a->gumbel != 0);
@@ -434,8 +479,9 @@ kvc_status score_grid(K kernel, int threads, size_t lds, int units, int* grid) {
 
 // Pass 1, combine and (unless only the row constants are wanted) pass 2 on one
 // stream.
-template <bool kGumbel, int kW, int kT, int kCB>
-kvc_status launch_score(const ScoreParams& p, const Plan& pl, hipStream_t s, bool pass2 = true) {
+template <bool kGumbel, bool kCausal, int kW, int kT, int kCB>
+kvc_status launch_score(ScoreParams p, const Plan& pl, hipStream_t s, bool pass2 = true) {
+  p.causal_unit = kCausal ? 32 * kW * kT : 0;
   constexpr int kThreads = kW * kWave;
   const int units = p.L * p.Hkv * pl.nblk;
   const int heads = p.L * p.Hkv;
@@ -444,8 +490,8 @@ kvc_status launch_score(const ScoreParams& p, const Plan& pl, hipStream_t s, boo
   const dim3 comb_grid(heads * ((pl.R + comb_rows - 1) / comb_rows));
   auto kc = wide ? score_combine<8> : score_combine<32>;
   const size_t lds1 = score_lds_bytes(pl.chunk_rows, kW, false), lds2 = score_lds_bytes(pl.chunk_rows, kW, true);
-  auto k1 = score_pass<false, kGumbel, kW, kT, kCB>;
-  auto k2 = score_pass<true, kGumbel, kW, kT, kCB>;
+  auto k1 = score_pass<false, kGumbel, kCausal, kW, kT, kCB>;
+  auto k2 = score_pass<true, kGumbel, kCausal, kW, kT, kCB>;
   int g1 = 0, g2 = 0;
   kvc_status st = score_grid(k1, kThreads, lds1, units, &g1);
   if (st != KVC_OK) return st;
@@ -456,9 +502,13 @@ kvc_status launch_score(const ScoreParams& p, const Plan& pl, hipStream_t s, boo
     KVC_LAUNCH("think_rowc_combine", kc, comb_grid, dim3(256), s, p, heads);
     return KVC_OK;
   }
-  KVC_LAUNCH_SHM(kGumbel ? "score_pass1_gumbel" : "score_pass1", k1, dim3(g1), dim3(kThreads), lds1, s, p);
+  KVC_LAUNCH_SHM(kCausal ? (kGumbel ? "score_causal_pass1_gumbel" : "score_causal_pass1")
+                         : (kGumbel ? "score_pass1_gumbel" : "score_pass1"),
+                 k1, dim3(g1), dim3(kThreads), lds1, s, p);
   KVC_LAUNCH("score_combine", kc, comb_grid, dim3(256), s, p, heads);
-  KVC_LAUNCH_SHM(kGumbel ? "score_pass2_gumbel" : "score_pass2", k2, dim3(g2), dim3(kThreads), lds2, s, p);
+  KVC_LAUNCH_SHM(kCausal ? (kGumbel ? "score_causal_pass2_gumbel" : "score_causal_pass2")
+                         : (kGumbel ? "score_pass2_gumbel" : "score_pass2"),
+                 k2, dim3(g2), dim3(kThreads), lds2, s, p);
   return KVC_OK;
 }
 
@@ -470,17 +520,19 @@ extern "C" size_t kvc_score_workspace_size(const kvc_score_args* args) {
   return kvc::plan(args, &pl) == KVC_OK ? pl.total : 0;
 }
 
-extern "C" kvc_status kvc_score(const kvc_score_args* a, const void* q_obs, const void* k,
-                                float* importance, void* ws, size_t ws_bytes, void* stream) {
-  using namespace kvc;
+namespace kvc {
+namespace {
+
+kvc_status score_entry(const kvc_score_args* a, const void* q_obs, const void* k, float* importance, void* ws,
+                       size_t ws_bytes, void* stream, bool causal) {
   Plan pl;
-  kvc_status st = plan(a, &pl);
+  kvc_status st = plan(a, &pl, causal);
   if (st != KVC_OK) return st;
   if (!q_obs || !k || !importance) return KVC_E_ARG;
   if (!aligned16(q_obs) || !aligned16(k) || (reinterpret_cast<uintptr_t>(importance) & 3)) return KVC_E_ARG;
   if (!ws || ws_bytes < pl.total || !aligned16(ws)) return KVC_E_WORKSPACE;
 
-  ScoreParams p;
+  ScoreParams p{};
   p.q = static_cast<const uint16_t*>(q_obs);
   p.k = static_cast<const uint16_t*>(k);
   p.q_hs = a->q_head_stride;
@@ -507,9 +559,32 @@ extern "C" kvc_status kvc_score(const kvc_score_args* a, const void* q_obs, cons
   p.chunk_rows = pl.chunk_rows;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a->gumbel) return launch_score<true, 4, 1, 4>(p, pl, s);
-  if (pl.shape.kw == 8) return launch_score<false, 8, 2, 16>(p, pl, s);
-  return launch_score<false, 4, 2, 8>(p, pl, s);
+  if (causal) {
+    if (a->gumbel) return launch_score<true, true, 4, 1, 4>(p, pl, s);
+    if (pl.shape.kw == 8) return launch_score<false, true, 8, 2, 16>(p, pl, s);
+    return launch_score<false, true, 4, 2, 8>(p, pl, s);
+  }
+  if (a->gumbel) return launch_score<true, false, 4, 1, 4>(p, pl, s);
+  if (pl.shape.kw == 8) return launch_score<false, false, 8, 2, 16>(p, pl, s);
+  return launch_score<false, false, 4, 2, 8>(p, pl, s);
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" kvc_status kvc_score(const kvc_score_args* a, const void* q_obs, const void* k, float* importance,
+                                void* ws, size_t ws_bytes, void* stream) {
+  return kvc::score_entry(a, q_obs, k, importance, ws, ws_bytes, stream, false);
+}
+
+extern "C" size_t kvc_score_causal_workspace_size(const kvc_score_args* args) {
+  kvc::Plan pl;
+  return kvc::plan(args, &pl, true) == KVC_OK ? pl.total : 0;
+}
+
+extern "C" kvc_status kvc_score_causal(const kvc_score_args* a, const void* q_obs, const void* k,
+                                       float* importance, void* ws, size_t ws_bytes, void* stream) {
+  return kvc::score_entry(a, q_obs, k, importance, ws, ws_bytes, stream, true);
 }
 
 namespace kvc {
@@ -567,8 +642,8 @@ kvc_status score_rowc(const uint16_t* q, int64_t q_hs, const uint16_t* k, int64_
   p.nblk = pl.nblk;
   p.chunk_rows = pl.chunk_rows;
   *rowc = p.rowc;
-  if (pl.shape.kw == 8) return launch_score<false, 8, 2, 16>(p, pl, s, false);
-  return launch_score<false, 4, 2, 8>(p, pl, s, false);
+  if (pl.shape.kw == 8) return launch_score<false, false, 8, 2, 16>(p, pl, s, false);
+  return launch_score<false, false, 4, 2, 8>(p, pl, s, false);
 }
 
 }  // namespace kvc

@@ -50,6 +50,8 @@ def _load():
         "kvc_think_channels": (ctypes.c_int, [ctypes.c_int, F64]),
         "kvc_score_workspace_size": (SZ, [ctypes.POINTER(ScoreArgs)]),
         "kvc_score": (ctypes.c_int, [ctypes.POINTER(ScoreArgs), P, P, P, P, SZ, P]),
+        "kvc_score_causal_workspace_size": (SZ, [ctypes.POINTER(ScoreArgs)]),
+        "kvc_score_causal": (ctypes.c_int, [ctypes.POINTER(ScoreArgs), P, P, P, P, SZ, P]),
         "kvc_lmba_budget_workspace_size": (SZ, [I32, I32, I32]),
         "kvc_lmba_budget": (ctypes.c_int, [P, I32, I32, I32, F64, I64, I32, I32, P, P, P, SZ, P]),
         "kvc_pool_importance": (ctypes.c_int, [P, I64, P, I64, I32, I32, I32, I32, P]),
@@ -171,6 +173,25 @@ def kvc_score(q_obs, k, importance, *, w, S, scale=None, layer_scales=None, gumb
     ws, nbytes = _workspace(_lib.kvc_score_workspace_size(ctypes.byref(a)), k.device, workspace)
     _check(_lib.kvc_score(ctypes.byref(a), _ptr(q_obs), _ptr(k), _ptr(importance), _ptr(ws), nbytes,
                           _stream(stream, k.device)), "kvc_score")
+    return importance
+
+
+def kvc_score_causal(q_obs, k, importance, *, w, S, scale=None, layer_scales=None, gumbel=False, tau=1.0, seed=0,
+                     workspace=None, stream=None):
+    """Causal importance into ``importance`` (fp32 [L?, Hkv, S]): window row i sits at
+    position S - w + i and sees the keys at positions <= its own (w <= S, w % 32 == 0)."""
+    _bf16(q_obs, "q_obs")
+    _bf16(k, "k")
+    if layer_scales is not None and (layer_scales.dtype != torch.float32 or not layer_scales.is_cuda):
+        raise TypeError("layer_scales must be a float32 GPU tensor")
+    a = score_args(q_obs, k, w=w, S=S, scale=scale, layer_scales=layer_scales, gumbel=gumbel, tau=tau,
+                   seed=seed)
+    if importance.dtype != torch.float32 or not importance.is_contiguous() \
+            or importance.numel() != a.L * a.Hkv * S:
+        raise ValueError("importance must be contiguous float32 with L*Hkv*S elements")
+    ws, nbytes = _workspace(_lib.kvc_score_causal_workspace_size(ctypes.byref(a)), k.device, workspace)
+    _check(_lib.kvc_score_causal(ctypes.byref(a), _ptr(q_obs), _ptr(k), _ptr(importance), _ptr(ws), nbytes,
+                                 _stream(stream, k.device)), "kvc_score_causal")
     return importance
 
 

@@ -29,7 +29,7 @@ class CompressionPlan:
         self.tau = tau
         f32, i32, bf = torch.float32, torch.int32, torch.bfloat16
         L, Hkv, n, D = wl.L, wl.Hkv, wl.n, wl.D
-        self.importance = torch.empty((L, Hkv, n), dtype=f32, device=device)
+        self.importance = torch.empty((L, Hkv, wl.imp_len), dtype=f32, device=device)
         # scores the selection ranks: the importance, or its SnapKV pooling
         self.pooled = torch.empty_like(self.importance) if wl.pool_kernel else None
         self.scores = self.pooled if wl.pool_kernel else self.importance
@@ -40,8 +40,9 @@ class CompressionPlan:
         a.q_head_stride, a.q_layer_stride = wl.w * D, wl.H * wl.w * D
         a.k_head_stride, a.k_layer_stride = wl.S * D, Hkv * wl.S * D
         a.scale, a.gumbel, a.tau = 1.0, 1 if wl.gumbel else 0, 1.0
-        self.ws_score = torch.empty(max(kvc.kvc_score_workspace_size(a), 256), dtype=torch.uint8, device=device)
-        sel_ws = kvc.lib.kvc_select_topk_workspace_size(Hkv, n)
+        nb = kvc.lib.kvc_score_causal_workspace_size(a) if wl.causal else kvc.kvc_score_workspace_size(a)
+        self.ws_score = torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
+        sel_ws = kvc.lib.kvc_select_topk_workspace_size(Hkv, wl.S - wl.select_w)
         self.ws_select = torch.empty(max(sel_ws, 256), dtype=torch.uint8, device=device)
         if self.zigzag:
             self.budgets = torch.empty(L, dtype=i32, device=device)
@@ -102,7 +103,7 @@ class CompressionPlan:
 
     def score(self, q, k, layer_scales=None, stream=None):
         wl = self.wl
-        kvc.kvc_score(q, k, self.importance if wl.L > 1 else self.importance[0], w=wl.w, S=wl.S,
+        (kvc.kvc_score_causal if wl.causal else kvc.kvc_score)(q, k, self.importance if wl.L > 1 else self.importance[0], w=wl.w, S=wl.S,
                       layer_scales=layer_scales, gumbel=wl.gumbel, tau=self.tau, seed=wl.noise_seed,
                       workspace=self.ws_score, stream=stream)
 
@@ -120,7 +121,7 @@ class CompressionPlan:
                                    self.offsets, self.kc_flat, self.vc_flat, S=wl.S, stream=stream)
             return
         if not self.zigzag:
-            kvc.kvc_select_topk(self.scores[0], self.indices, S=wl.S, w=wl.w, recent=wl.recent,
+            kvc.kvc_select_topk(self.scores[0], self.indices, S=wl.S, w=wl.select_w, recent=wl.recent,
                                 budget=wl.budget, workspace=self.ws_select, stream=stream)
             kvc.kvc_compact(k if k.dim() == 3 else k[0], v if v.dim() == 3 else v[0], self.indices, self.kc,
                             self.vc, S=wl.S, stream=stream)

@@ -58,6 +58,7 @@ class Workload:
     pool_mode: int = 0              # 0: average (zero padding, / kernel), 1: max
     threshold: float = 0.0          # > 0: KVzap threshold selection at threshold * G / (S - w), not top-k
     decode_steps: int = 0           # > 0: Keyformer decode steps after the prompt phase (positions S, S+1, ...)
+    causal: bool = False            # causal scoring: window row i (position S - w + i) over keys [0, S)
     seed: int = 0
     notes: str = field(default="", compare=False)
 
@@ -70,8 +71,18 @@ class Workload:
         return self.S - self.w
 
     @property
+    def imp_len(self):
+        """Keys an importance row covers: the prefix, or (causal) the whole prompt."""
+        return self.S if self.causal else self.S - self.w
+
+    @property
+    def select_w(self):
+        """The window argument of the selection: candidates [0, min(S - select_w, S - recent))."""
+        return self.recent if self.causal else self.w
+
+    @property
     def n_candidates(self):
-        return min(self.S - self.w, self.S - self.recent)
+        return min(self.S - self.select_w, self.S - self.recent)
 
     @property
     def capacity(self):
@@ -116,6 +127,11 @@ WORKLOADS = {
         name="keyformer_mha32_s8192", cfg_id=3, L=1, H=32, Hkv=32, S=8192, w=512, recent=512,
         budget=4096, gumbel=True, taus=(1.0, 1.0e4),
         notes="Keyformer MHA 32, Gumbel noise, tau 1 and 1e4, 512 recent + 3584 top"),
+    "keyformer_mha32_s8192_causal": Workload(
+        name="keyformer_mha32_s8192_causal", cfg_id=3, L=1, H=32, Hkv=32, S=8192, w=8192, recent=512,
+        budget=4096, gumbel=True, taus=(1.0,), causal=True,
+        notes="Keyformer's full-attention reading of the prompt phase: all 8192 positions are queries, causal, "
+              "Gumbel noise tau 1; 512 recent + 3584 top of the other 7680 (same keys as the MHA 32 case)"),
     "keyformer_mha32_s8192_decode": Workload(
         name="keyformer_mha32_s8192_decode", cfg_id=3, L=1, H=32, Hkv=32, S=8192, w=512, recent=512,
         budget=4096, gumbel=True, taus=(1.0,), decode_steps=64,

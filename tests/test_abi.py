@@ -277,6 +277,25 @@ def test_decode_validation():
     assert f(FAKE, 100, FAKE, 4, 0, 100, FAKE, None) == E.KVC_OK   # nothing to do: no launch
 
 
+def test_score_causal_validation():
+    a = kvc.ScoreArgs()
+    a.L, a.H, a.Hkv, a.w, a.S, a.D = 1, 32, 32, 8192, 8192, 128
+    a.q_head_stride, a.q_layer_stride = 8192 * 128, 32 * 8192 * 128
+    a.k_head_stride, a.k_layer_stride = 8192 * 128, 32 * 8192 * 128
+    a.scale, a.gumbel, a.tau = 0.088, 1, 1.0
+    ws = lib.kvc_score_causal_workspace_size(ctypes.byref(a))
+    assert ws > 0                                                # w == S is allowed here
+    assert lib.kvc_score_workspace_size(ctypes.byref(a)) == 0    # but not for the window scoring
+    f = lib.kvc_score_causal
+    assert f(ctypes.byref(a), FAKE, FAKE, FAKE, None, ws, None) == E.KVC_E_WORKSPACE
+    a.w = 8191
+    assert f(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, ws, None) == E.KVC_E_SHAPE   # w % 32 != 0
+    a.w = 8224
+    assert f(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, ws, None) == E.KVC_E_SHAPE   # w > S
+    a.w, a.tau = 8192, 0.0
+    assert f(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, ws, None) == E.KVC_E_ARG
+
+
 def test_channel_prune_query_validation():
     f = lib.kvc_channel_prune_query
     ws = lib.kvc_channel_prune_query_workspace_size(8, 4, 100, 128)

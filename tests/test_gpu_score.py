@@ -119,3 +119,27 @@ def test_deterministic_bytes():
     a = _gpu_importance(qb, kb, w=128, S=5000)
     b = _gpu_importance(qb, kb, w=128, S=5000)
     assert a.tobytes() == b.tobytes()
+
+
+# ---------------------------------------------------------------- causal (whole-prompt) scoring
+@pytest.mark.parametrize("H,Hkv,S,w,gumbel,tau", [
+    (4, 4, 640, 640, True, 1.0),       # every position a query; 5 row chunks x 5 key units, Gumbel shape
+    (8, 2, 1000, 512, False, 1.0),     # GQA, window shorter than the prompt: keys past it still seen causally
+    (2, 2, 300, 256, False, 1.0),      # R = 256: the 4-wave shape, a ragged last unit
+    (2, 2, 384, 384, True, float("inf")),
+    (2, 1, 320, 320, True, 1.0e4),
+])
+def test_score_causal_matches_oracle(H, Hkv, S, w, gumbel, tau):
+    from kv_cache_compression_bf16_amd import kvc
+    print(f"[causal] H={H} Hkv={Hkv} S={S} w={w} gumbel={gumbel} tau={tau}", flush=True)
+    rng = np.random.default_rng(S + w + H)
+    q = wk.f32_to_bf16_bits(rng.standard_normal((H, w, 128), dtype=np.float32))
+    k = wk.f32_to_bf16_bits(rng.standard_normal((Hkv, S, 128), dtype=np.float32) * 1.5)
+    imp = torch.empty((Hkv, S), dtype=torch.float32, device=dev())
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    kvc.kvc_score_causal(to_dev(q), to_dev(k), imp, w=w, S=S, scale=scale, gumbel=gumbel, tau=tau, seed=77)
+    torch.cuda.synchronize()
+    ref = oracle.score.importance_causal(oracle.score.bf16_bits_to_f64(q), oracle.score.bf16_bits_to_f64(k), S=S,
+                                         w=w, scale=scale, gumbel=gumbel, tau=tau, seed=77)
+    worst = check_importance(imp.cpu().numpy(), ref, H // Hkv, "causal")
+    print("worst relative error:", worst)

@@ -181,6 +181,31 @@ def test_think_s131072_kv():
     assert np.array_equal(plan.mask_v.cpu().numpy().sum(axis=1), np.full(wl.Hkv, Tv))
 
 
+def test_keyformer_mha32_s8192_causal():
+    wl = wk.WORKLOADS["keyformer_mha32_s8192_causal"]
+    tau = wl.taus[0]
+    plan, (q, k, v), sc = _run(wl, tau=tau)
+    imp = plan.importance[0].cpu().numpy()
+    # any size: every row of every query head sums to 1, so each KV head's importance sums to G
+    assert np.allclose(imp.astype(np.float64).sum(axis=1), wl.G, rtol=1e-5, atol=0)
+    # sampled, element-wise: the last 512 keys of two heads, from the 512 rows that can see them
+    f64 = oracle.score.bf16_bits_to_f64
+    scale = float(np.float32(1.0 / math.sqrt(wl.D)))
+    for g in (0, 21):
+        ref = oracle.score.head_causal_mean(f64(q[g]), f64(k[g]), S=wl.S, w=wl.w, scale=scale, gumbel=True,
+                                            seed=wl.noise_seed, head=g, tau=tau,
+                                            rows=range(wl.w - 512, wl.w))[wl.S - 512:]
+        gpu = imp[g, wl.S - 512:].astype(np.float64)
+        assert np.all(np.abs(gpu - ref) <= 1e-3 * ref + 1e-30), f"head {g}"
+    # selection (candidates [0, S - r)) in isolation on the GPU's importance, and the compaction
+    idx = plan.indices.cpu().numpy()
+    ref_idx = oracle.select.select_heads(imp.astype(np.float64), S=wl.S, w=wl.select_w, recent=wl.recent,
+                                         budget=wl.budget)
+    assert np.array_equal(idx, ref_idx)
+    assert np.array_equal(bits_of(plan.kc), oracle.compact.compact(k, idx))
+    assert np.array_equal(bits_of(plan.vc), oracle.compact.compact(v, idx))
+
+
 def test_keyformer_mha32_s8192_decode():
     wl = wk.WORKLOADS["keyformer_mha32_s8192_decode"]
     plan, (q, k, v), sc = _run(wl, tau=wl.taus[0])
