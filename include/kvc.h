@@ -221,6 +221,27 @@ kvc_status kvc_select_topk(const float* importance, int64_t imp_head_stride, int
                            int32_t w, int32_t recent, int32_t budget, int32_t* indices,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * kvc_select_topk_layers: kvc_select_topk for L layers in one launch, with
+ * per-layer budgets read on the device (the budgets kvc_lmba_budget writes),
+ * so no host round trip sits between budgeting and selection.  Layer l keeps
+ * budgets[l] tokens per KV head; its block of `indices` starts at
+ * Hkv * (budgets[0] + ... + budgets[l-1]) and holds [Hkv, budgets[l]] (the
+ * layout of per-layer calls on one flat buffer).
+ * Source: as kvc_select_topk; ZigZagKV blog page, token-selection section
+ * (each layer selects with its own quota).
+ * Layout: importance fp32, row (l, g) at importance + l*imp_layer_stride +
+ *   g*imp_head_stride; budgets int32 [L] on the device, each in
+ *   [recent, c + recent] and summing to at most total_budget; indices int32
+ *   with Hkv * total_budget entries.  A layer whose budget is out of range or
+ *   whose block would pass Hkv * total_budget entries writes nothing.
+ * Errors: as kvc_select_topk; KVC_E_UNSUPPORTED when c > 32768 (use one
+ *   kvc_select_topk call per layer there).
+ */
+kvc_status kvc_select_topk_layers(const float* importance, int64_t imp_head_stride, int64_t imp_layer_stride,
+                                  int32_t L, int32_t Hkv, int32_t S, int32_t w, int32_t recent,
+                                  const int32_t* budgets, int32_t total_budget, int32_t* indices, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* kvc_select_threshold: keep every candidate scoring >= threshold.          */
 /* ------------------------------------------------------------------------ */
@@ -265,6 +286,25 @@ kvc_status kvc_select_threshold(const float* scores, int64_t score_head_stride, 
 kvc_status kvc_compact(const void* k, const void* v, int32_t Hkv, int32_t S, int32_t D,
                        int64_t k_head_stride, int64_t v_head_stride, const int32_t* indices,
                        int32_t budget, void* k_out, void* v_out, void* stream);
+
+/*
+ * kvc_compact_layers: kvc_compact for L layers in one launch with per-layer
+ * budgets read on the device: layer l's block of `indices` and of the outputs
+ * starts at row Hkv * (budgets[0] + ... + budgets[l-1]) and holds
+ * [Hkv, budgets[l]] rows, k_out[row] = k[l, g, indices[row]] (v likewise).
+ * Source: as kvc_compact, per layer (ZigZagKV's per-layer quotas).
+ * Layout: k, v bf16, row j of head g of layer l at base + l*layer_stride +
+ *   g*head_stride + j*D; budgets int32 [L] (device); indices int32 and
+ *   k_out, v_out bf16 with Hkv * total_budget rows.  A layer whose block would
+ *   pass Hkv * total_budget rows writes nothing; an index outside [0, S)
+ *   yields a row of 0xFFFF.
+ * Errors: as kvc_compact; KVC_E_UNSUPPORTED unless D / 8 divides 256;
+ *   KVC_E_SHAPE if Hkv * L > 65535 or a layer stride is too small.
+ */
+kvc_status kvc_compact_layers(const void* k, const void* v, int32_t L, int32_t Hkv, int32_t S, int32_t D,
+                              int64_t k_head_stride, int64_t k_layer_stride, int64_t v_head_stride,
+                              int64_t v_layer_stride, const int32_t* budgets, int32_t total_budget,
+                              const int32_t* indices, void* k_out, void* v_out, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* kvc_compact_ragged: gather kept rows of packed heads.                     */

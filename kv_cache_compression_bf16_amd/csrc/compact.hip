@@ -1,6 +1,7 @@
 // kvc_compact: gather the kept K and V rows into a dense per-head cache.
 // kvc_compact_ragged: the same for per-head kept counts that vary (packed
-// heads, as the threshold selection writes them).
+// heads, as the threshold selection writes them).  kvc_compact_layers: every
+// layer in one launch, each with its own budget read on the device.
 //
 // Keyformer blog page, prompt-phase paragraph: the kept tokens form the new,
 // smaller cache; KVzap news page: the cache is (2, L, H, T, D).  The copy is of
@@ -110,6 +111,50 @@ __global__ __launch_bounds__(256) void compact_ragged_rows(const uint16_t* k, co
   }
 }
 
+// Layers in one launch: grid (row blocks, Hkv * L, planes).  Layer l's block
+// of indices and outputs starts at row Hkv * (budgets[0] + ... + budgets[l-1]),
+// head g's rows at g * budgets[l] within it; a workgroup strides over its
+// head's rows.  A layer whose block would pass out_rows rows writes nothing.
+template <int kRPT>
+__global__ __launch_bounds__(256) void compact_layers_rows(const uint16_t* k, const uint16_t* v, int S, int D,
+                                                            int Hkv, int64_t khs, int64_t kls, int64_t vhs,
+                                                            int64_t vls, const int32_t* budgets, int64_t out_rows,
+                                                            const int32_t* idx, uint16_t* ko, uint16_t* vo) {
+  const int hl = blockIdx.y, layer = hl / Hkv, g = hl - layer * Hkv;
+  const bool isv = blockIdx.z != 0;
+  int64_t before = 0;
+  for (int i = 0; i < layer; ++i) before += budgets[i];
+  const int B = budgets[layer];
+  const int64_t base = (int64_t)Hkv * before + (int64_t)g * B;
+  if (B <= 0 || before < 0 || base + B > out_rows) return;
+  const uint16_t* src = isv ? v + layer * vls + g * vhs : k + layer * kls + g * khs;
+  uint16_t* dst = (isv ? vo : ko) + base * D;
+  const int32_t* ix = idx + base;
+  const int chunks = D >> 3, rpp = 256 / chunks;
+  const int ch = threadIdx.x % chunks;
+  const int step = gridDim.x * rpp * kRPT;
+  for (int r0 = blockIdx.x * rpp * kRPT + threadIdx.x / chunks; r0 - (int)(threadIdx.x / chunks) < B; r0 += step) {
+    int j[kRPT];
+#pragma unroll
+    for (int q = 0; q < kRPT; ++q) {
+      const int t = r0 + q * rpp;
+      j[q] = t < B ? ix[t] : -1;
+    }
+    u32x4 val[kRPT];
+#pragma unroll
+    for (int q = 0; q < kRPT; ++q) {
+      const bool ok = j[q] >= 0 && j[q] < S;
+      val[q] = *reinterpret_cast<const u32x4*>(src + (int64_t)(ok ? j[q] : 0) * D + ch * 8);
+      if (!ok) val[q] = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    }
+#pragma unroll
+    for (int q = 0; q < kRPT; ++q) {
+      const int t = r0 + q * rpp;
+      if (t < B) *reinterpret_cast<u32x4*>(dst + (int64_t)t * D + ch * 8) = val[q];
+    }
+  }
+}
+
 }  // namespace
 }  // namespace kvc
 
@@ -174,5 +219,38 @@ extern "C" kvc_status kvc_compact_ragged(const void* k, const void* v, int32_t H
              static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), S, D, k_head_stride,
              v_head_stride, indices, offsets, max_rows, static_cast<uint16_t*>(k_out),
              static_cast<uint16_t*>(v_out));
+  return KVC_OK;
+}
+
+extern "C" kvc_status kvc_compact_layers(const void* k, const void* v, int32_t L, int32_t Hkv, int32_t S, int32_t D,
+                                         int64_t k_head_stride, int64_t k_layer_stride, int64_t v_head_stride,
+                                         int64_t v_layer_stride, const int32_t* budgets, int32_t total_budget,
+                                         const int32_t* indices, void* k_out, void* v_out, void* stream) {
+  using namespace kvc;
+  if (L < 1 || Hkv < 1 || S < 1 || total_budget < 0 || D < 8 || D > 1024 || (D & 7)) return KVC_E_ARG;
+  if (256 % (D / 8)) return KVC_E_UNSUPPORTED;
+  if ((int64_t)Hkv * L > 65535) return KVC_E_SHAPE;
+  if (!k || !k_out || !budgets || !indices) return KVC_E_ARG;
+  if ((v == nullptr) != (v_out == nullptr)) return KVC_E_ARG;
+  if (k_head_stride < (int64_t)S * D || (v && v_head_stride < (int64_t)S * D)) return KVC_E_SHAPE;
+  if (L > 1 && (k_layer_stride < Hkv * k_head_stride || (v && v_layer_stride < Hkv * v_head_stride)))
+    return KVC_E_SHAPE;
+  if ((k_head_stride | k_layer_stride) & 7 || (v && ((v_head_stride | v_layer_stride) & 7))) return KVC_E_ARG;
+  if (!aligned16(k) || !aligned16(k_out) || (v && (!aligned16(v) || !aligned16(v_out)))) return KVC_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(indices) | reinterpret_cast<uintptr_t>(budgets)) & 3) return KVC_E_ARG;
+  const int64_t rows = (int64_t)Hkv * total_budget;
+  if (rows == 0) return KVC_OK;
+  if (rows * (D / 8) > 0x7FFFFFFF - 256) return KVC_E_SHAPE;
+  constexpr int kRPT = 4;
+  const int rows_per_wg = 256 / (D / 8) * kRPT;
+  // a layer's budget is known only on the device: enough workgroups for 4x the
+  // mean per-layer budget, striding beyond that
+  int64_t mean = ((int64_t)total_budget + L - 1) / L;
+  int gx = (int)((4 * mean + rows_per_wg - 1) / rows_per_wg);
+  gx = gx < 1 ? 1 : (gx > 64 ? 64 : gx);
+  KVC_LAUNCH("compact_layers", compact_layers_rows<kRPT>, dim3(gx, Hkv * L, v ? 2 : 1), dim3(256),
+             static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), S,
+             D, Hkv, k_head_stride, k_layer_stride, v_head_stride, v_layer_stride, budgets, rows, indices,
+             static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out));
   return KVC_OK;
 }

@@ -117,17 +117,32 @@ __device__ __forceinline__ void load_round(const uint32_t* v, int c, int r, uint
   for (int i = 0; i < kVPL; ++i) key[i] = (base + 64 * i < c) ? order_key(raw[i]) : 0u;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* imp, int64_t hs, int c,
+// Layers in one launch (budgets != null): grid (Hkv, L); layer l keeps
+// budgets[l] tokens per head and its block of the output starts at
+// Hkv * (budgets[0] + ... + budgets[l-1]) (head g's rows at g * budgets[l]), the
+// layout of per-layer calls on one flat buffer.  A layer whose budget is out
+// of range, or whose block would pass out_cap entries, writes nothing.
+__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* imp, int64_t hs, int64_t ls, int c,
                                                                  int k_top, int S, int recent, int budget,
+                                                                 const int32_t* budgets, int64_t out_cap,
                                                                  int32_t* out) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t wsum[kSelWaves], wsum2[kSelWaves];
   __shared__ uint32_t s_digit, s_above;
   __shared__ uint32_t tr[kRound + kRound / 64];   // 130 KB: transposed keys, then kept positions
 
-  const int g = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
-  const uint32_t* v = reinterpret_cast<const uint32_t*>(imp + (int64_t)g * hs);
-  int32_t* o = out + (int64_t)g * budget;
+  const int g = blockIdx.x, layer = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
+  int64_t obase = (int64_t)g * budget;
+  if (budgets) {
+    int64_t before = 0;
+    for (int i = 0; i < layer; ++i) before += budgets[i];
+    budget = budgets[layer];
+    k_top = budget - recent;
+    obase = (int64_t)gridDim.x * before + (int64_t)g * budget;
+    if (k_top < 0 || k_top > c || before < 0 || obase < 0 || obase + budget > out_cap) return;
+  }
+  const uint32_t* v = reinterpret_cast<const uint32_t*>(imp + layer * ls + (int64_t)g * hs);
+  int32_t* o = out + obase;
 
   for (int t = tid; t < recent; t += kSelThreads) o[k_top + t] = S - recent + t;
   if (k_top == 0) return;
@@ -499,7 +514,8 @@ extern "C" kvc_status kvc_select_topk(const float* importance, int64_t imp_head_
   const int k_top = budget - recent;
   if (use_one_workgroup(c) || k_top == 0 || k_top >= c) {
     KVC_LAUNCH("select_topk", one::select_topk_kernel, dim3(Hkv), dim3(one::kSelThreads), s, importance,
-               imp_head_stride, c, k_top, S, recent, budget, indices);
+               imp_head_stride, (int64_t)0, c, k_top, S, recent, budget, (const int32_t*)nullptr,
+               (int64_t)Hkv * budget, indices);
     return KVC_OK;
   }
 
@@ -526,5 +542,29 @@ extern "C" kvc_status kvc_select_topk(const float* importance, int64_t imp_head_
   KVC_LAUNCH("select_level1", many::select_level<1>, grid, dim3(many::kThreads), s, a);
   KVC_LAUNCH("select_level2", many::select_level<2>, grid, dim3(many::kThreads), s, a);
   KVC_LAUNCH("select_emit", many::select_emit, grid, dim3(many::kThreads), s, a);
+  return KVC_OK;
+}
+
+extern "C" kvc_status kvc_select_topk_layers(const float* importance, int64_t imp_head_stride,
+                                             int64_t imp_layer_stride, int32_t L, int32_t Hkv, int32_t S,
+                                             int32_t w, int32_t recent, const int32_t* budgets,
+                                             int32_t total_budget, int32_t* indices, void* stream) {
+  using namespace kvc;
+  if (L < 1 || Hkv < 1 || S < 2 || w < 1 || w >= S || recent < 0 || recent > S || total_budget < 0)
+    return KVC_E_ARG;
+  const int32_t n = S - w;
+  const int32_t c = n < S - recent ? n : S - recent;
+  if (!use_one_workgroup(c)) return KVC_E_UNSUPPORTED;
+  if (Hkv > 65535 || L > 65535) return KVC_E_SHAPE;
+  if ((imp_head_stride < n && Hkv > 1) || (imp_layer_stride < (int64_t)Hkv * imp_head_stride && L > 1))
+    return KVC_E_SHAPE;
+  if (!importance || !budgets || !indices) return KVC_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(importance) | reinterpret_cast<uintptr_t>(budgets) |
+       reinterpret_cast<uintptr_t>(indices)) & 3)
+    return KVC_E_ARG;
+  if (total_budget == 0) return KVC_OK;
+  KVC_LAUNCH("select_topk_layers", one::select_topk_kernel, dim3(Hkv, L), dim3(one::kSelThreads),
+             static_cast<hipStream_t>(stream), importance, imp_head_stride, imp_layer_stride, c, 0, S, recent, 0,
+             budgets, (int64_t)Hkv * total_budget, indices);
   return KVC_OK;
 }

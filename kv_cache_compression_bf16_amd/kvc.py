@@ -58,6 +58,8 @@ def _load():
         "kvc_select_topk_workspace_size": (SZ, [I32, I32]),
         "kvc_select_topk": (ctypes.c_int, [P, I64, I32, I32, I32, I32, I32, P, P, SZ, P]),
         "kvc_compact": (ctypes.c_int, [P, P, I32, I32, I32, I64, I64, P, I32, P, P, P]),
+        "kvc_select_topk_layers": (ctypes.c_int, [P, I64, I64, I32, I32, I32, I32, I32, P, I32, P, P]),
+        "kvc_compact_layers": (ctypes.c_int, [P, P, I32, I32, I32, I32, I64, I64, I64, I64, P, I32, P, P, P, P]),
         "kvc_select_threshold_workspace_size": (SZ, [I32, I32, I32, I32]),
         "kvc_select_threshold": (ctypes.c_int, [P, I64, I32, I32, I32, I32, ctypes.c_float, P, P, P, SZ, P]),
         "kvc_compact_ragged": (ctypes.c_int, [P, P, I32, I32, I32, I64, I64, P, P, I32, P, P, P]),
@@ -245,6 +247,25 @@ def kvc_select_topk(importance, indices, *, S, w, recent, budget, workspace=None
     return indices
 
 
+SELECT_ONE_WORKGROUP_MAX = 32768   # candidates per row up to which kvc_select_topk_layers applies
+
+
+def kvc_select_topk_layers(importance, budgets, indices, *, S, w, recent, total_budget, stream=None):
+    """All layers at once: importance [L, Hkv, n] fp32, budgets int32 [L] (device),
+    indices int32 with Hkv * total_budget entries (layer blocks packed in order)."""
+    if importance.dtype != torch.float32 or importance.dim() != 3 or importance.stride(2) != 1:
+        raise ValueError("importance must be float32 [L, Hkv, n] with unit stride along n")
+    if budgets.dtype != torch.int32 or indices.dtype != torch.int32 or not indices.is_contiguous():
+        raise TypeError("budgets and indices must be int32 (indices contiguous)")
+    L, Hkv, _ = importance.shape
+    if budgets.numel() != L or indices.numel() < Hkv * total_budget:
+        raise ValueError("budgets needs L entries and indices Hkv * total_budget")
+    _check(_lib.kvc_select_topk_layers(_ptr(importance), importance.stride(1), importance.stride(0), L, Hkv, S, w,
+                                       recent, _ptr(budgets), int(total_budget), _ptr(indices),
+                                       _stream(stream, importance.device)), "kvc_select_topk_layers")
+    return indices
+
+
 # ---------------------------------------------------------------- kvc_compact
 def kvc_compact(k, v, indices, k_out, v_out, *, S, stream=None):
     """k_out[g, t] = k[g, indices[g, t]] (and v likewise); k, v [Hkv, S_alloc, D]."""
@@ -258,6 +279,25 @@ def kvc_compact(k, v, indices, k_out, v_out, *, S, stream=None):
     _check(_lib.kvc_compact(_ptr(k), _ptr(v), Hkv, S, D, k.stride(0), 0 if v is None else v.stride(0),
                             _ptr(indices), budget, _ptr(k_out), _ptr(v_out), _stream(stream, k.device)),
            "kvc_compact")
+    return k_out, v_out
+
+
+def kvc_compact_layers(k, v, budgets, indices, k_out, v_out, *, S, total_budget, stream=None):
+    """All layers at once: k, v [L, Hkv, S_alloc, D]; outputs [Hkv * total_budget, D] rows, layer blocks packed."""
+    _bf16(k, "k")
+    L, Hkv, _, D = k.shape
+    if k.stride(2) != D or k.stride(3) != 1 or not k_out.is_contiguous() or k_out.shape[-1] != D:
+        raise ValueError("k rows must be contiguous with stride D and k_out contiguous [rows, D]")
+    if k_out.numel() < Hkv * total_budget * D or indices.numel() < Hkv * total_budget or budgets.numel() != L:
+        raise ValueError("outputs and indices need Hkv * total_budget rows and budgets L entries")
+    if v is not None:
+        _bf16(v, "v")
+        if v.shape != k.shape or v.stride(2) != D or v_out.shape != k_out.shape or not v_out.is_contiguous():
+            raise ValueError("v / v_out must match k / k_out")
+    _check(_lib.kvc_compact_layers(_ptr(k), _ptr(v), L, Hkv, S, D, k.stride(1), k.stride(0),
+                                   0 if v is None else v.stride(1), 0 if v is None else v.stride(0),
+                                   _ptr(budgets), int(total_budget), _ptr(indices), _ptr(k_out), _ptr(v_out),
+                                   _stream(stream, k.device)), "kvc_compact_layers")
     return k_out, v_out
 
 

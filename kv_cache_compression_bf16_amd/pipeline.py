@@ -140,17 +140,30 @@ class CompressionPlan:
         kvc.kvc_lmba_budget(self.importance, self.budgets, total_budget=wl.total_budget,
                             floor_per_layer=wl.floor, capacity=wl.capacity, mass=wl.mass, mba=self.mba,
                             stream=stream)
-        budgets = self.budgets.cpu().tolist()      # sizes the per-layer outputs (one small D2H copy)
-        self.layer_budgets = budgets
-        off = 0
-        Hkv, D = wl.Hkv, wl.D
-        self.layer_views = []
-        for l, B in enumerate(budgets):
-            idx = self.indices_flat[off * Hkv:(off + B) * Hkv].view(Hkv, B)
-            kc = self.kc_flat[off * Hkv * D:(off + B) * Hkv * D].view(Hkv, B, D)
-            vc = self.vc_flat[off * Hkv * D:(off + B) * Hkv * D].view(Hkv, B, D)
+        if wl.n_candidates <= kvc.SELECT_ONE_WORKGROUP_MAX:
+            # every layer in one launch each, budgets read on the device: no host round trip
+            kvc.kvc_select_topk_layers(self.scores, self.budgets, self.indices_flat, S=wl.S, w=wl.w,
+                                       recent=wl.recent, total_budget=wl.total_budget, stream=stream)
+            kvc.kvc_compact_layers(k, v, self.budgets, self.indices_flat, self.kc_flat.view(-1, wl.D),
+                                   self.vc_flat.view(-1, wl.D), S=wl.S, total_budget=wl.total_budget,
+                                   stream=stream)
+            return
+        # long prompts: one call per layer, sized from the budgets on the host
+        for l, (B, idx, kc, vc) in enumerate(self.zigzag_layers()):
             kvc.kvc_select_topk(self.scores[l], idx, S=wl.S, w=wl.w, recent=wl.recent, budget=B,
                                 workspace=self.ws_select, stream=stream)
             kvc.kvc_compact(k[l], v[l], idx, kc, vc, S=wl.S, stream=stream)
-            self.layer_views.append((idx, kc, vc))
+
+    def zigzag_layers(self):
+        """Per-layer (budget, indices, K, V) views of the ZigZag outputs; reads the
+        budgets back to the host (a synchronising copy)."""
+        wl = self.wl
+        Hkv, D = wl.Hkv, wl.D
+        out, off = [], 0
+        for B in self.budgets.cpu().tolist():
+            idx = self.indices_flat[off * Hkv:(off + B) * Hkv].view(Hkv, B)
+            kc = self.kc_flat[off * Hkv * D:(off + B) * Hkv * D].view(Hkv, B, D)
+            vc = self.vc_flat[off * Hkv * D:(off + B) * Hkv * D].view(Hkv, B, D)
+            out.append((B, idx, kc, vc))
             off += B
+        return out

@@ -296,6 +296,30 @@ def test_score_causal_validation():
     assert f(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, ws, None) == E.KVC_E_ARG
 
 
+def test_layers_batched_validation():
+    f = lib.kvc_select_topk_layers
+    #         imp   hs     ls          L   Hkv  S      w    r    budgets tot   idx   stream
+    ok = [FAKE, 16256, 8 * 16256, 32, 8, 16384, 128, 128, FAKE, 32768, FAKE, None]
+    call = _named_call(f, list("abcdefghijkl"), ok)
+    assert call(f=70000, g=128) == E.KVC_E_UNSUPPORTED        # c > 32768: not the one-workgroup path
+    assert call(g=16384) == E.KVC_E_ARG                        # w >= S
+    assert call(c=16256 * 7) == E.KVC_E_SHAPE                  # layer stride < Hkv * head stride
+    assert call(i=None) == E.KVC_E_ARG
+    assert call(k=None) == E.KVC_E_ARG
+    assert call(j=-1) == E.KVC_E_ARG
+    assert call(j=0) == E.KVC_OK                               # nothing to select: no launch
+    g = lib.kvc_compact_layers
+    okc = [FAKE, FAKE, 32, 8, 16384, 128, 16384 * 128, 8 * 16384 * 128, 16384 * 128, 8 * 16384 * 128, FAKE, 32768,
+           FAKE, FAKE, FAKE, None]
+    callc = _named_call(g, list("abcdefghijklmnop"), okc)
+    assert callc(f=48, g=16384 * 48, h=8 * 16384 * 48, i=16384 * 48, j=8 * 16384 * 48) == E.KVC_E_UNSUPPORTED
+    assert callc(h=16384 * 128) == E.KVC_E_SHAPE               # k layer stride too small
+    assert callc(c=10000) == E.KVC_E_SHAPE                     # Hkv * L > 65535
+    assert callc(k=None) == E.KVC_E_ARG
+    assert callc(o=None) == E.KVC_E_ARG                        # v without v_out
+    assert callc(l=0) == E.KVC_OK                              # nothing to gather: no launch
+
+
 def test_channel_prune_query_validation():
     f = lib.kvc_channel_prune_query
     ws = lib.kvc_channel_prune_query_workspace_size(8, 4, 100, 128)

@@ -330,3 +330,38 @@ def test_channel_prune_value(Hkv, G, w, B, recent, lam, loud):
         if loud:
             assert set(loud_ch) <= set(gch[g].tolist())
     print("channels:", kinds)
+
+
+def test_select_and_compact_layers_batched():
+    # all layers in one launch each, budgets on the device: identical to per-layer calls
+    kvc = _kvc()
+    rng = np.random.default_rng(61)
+    L, Hkv, S, w, recent, D = 5, 3, 3000, 64, 64, 128
+    n = S - w
+    imp = rng.exponential(size=(L, Hkv, n)).astype(np.float32)
+    imp[1, 1, :500] = 1.0                                    # ties across the cut in one row
+    budgets = np.array([64, 500, 1, 2936 + 64, 130], dtype=np.int32)   # incl. k_top = 0 and k_top = c
+    budgets[2] = 64                                          # (k_top = 0)
+    tot = int(budgets.sum())
+    k = wk.f32_to_bf16_bits(rng.standard_normal((L, Hkv, S, D), dtype=np.float32))
+    v = wk.f32_to_bf16_bits(rng.standard_normal((L, Hkv, S, D), dtype=np.float32))
+    imp_t = torch.from_numpy(imp).to(dev())
+    b_t = torch.from_numpy(budgets).to(dev())
+    idx = torch.full((Hkv * tot + 7,), -9, dtype=torch.int32, device=dev())
+    ko = torch.zeros((Hkv * tot + 7, D), dtype=torch.int16, device=dev())
+    vo = torch.zeros((Hkv * tot + 7, D), dtype=torch.int16, device=dev())
+    kvc.kvc_select_topk_layers(imp_t, b_t, idx, S=S, w=w, recent=recent, total_budget=tot)
+    kvc.kvc_compact_layers(to_dev(k), to_dev(v), b_t, idx, ko, vo, S=S, total_budget=tot)
+    torch.cuda.synchronize()
+    gi, gk, gv = idx.cpu().numpy(), bits_of(ko), bits_of(vo)
+    off = 0
+    for l in range(L):
+        B = int(budgets[l])
+        ref = _ref_select(imp[l], S=S, w=w, recent=recent, budget=B)
+        got = gi[off * Hkv:(off + B) * Hkv].reshape(Hkv, B)
+        assert np.array_equal(got, ref), f"layer {l}"
+        assert np.array_equal(gk[off * Hkv:(off + B) * Hkv].reshape(Hkv, B, D), oracle.compact.compact(k[l], ref))
+        assert np.array_equal(gv[off * Hkv:(off + B) * Hkv].reshape(Hkv, B, D), oracle.compact.compact(v[l], ref))
+        off += B
+    assert np.all(gi[Hkv * tot:] == -9)                     # nothing past the blocks
+    assert np.all(gk[Hkv * tot:] == 0)

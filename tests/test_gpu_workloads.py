@@ -281,7 +281,8 @@ def test_zigzag_l32_s16384():
     imp = plan.importance.cpu().numpy()
     assert np.allclose(imp.astype(np.float64).sum(axis=-1), 1.0, rtol=1e-5, atol=0)
     mba = plan.mba.cpu().numpy()
-    budgets = plan.layer_budgets
+    layers = plan.zigzag_layers()            # the batched launches' per-layer blocks
+    budgets = [B for B, _, _, _ in layers]
     # budgets in isolation on the GPU's importance: bit-exact
     ref_mba, ref_b = oracle.budget.zigzag_budgets(imp.astype(np.float64), total_budget=wl.total_budget,
                                                   floor=wl.floor, capacity=wl.capacity, mass=wl.mass)
@@ -290,8 +291,7 @@ def test_zigzag_l32_s16384():
     assert sum(budgets) == wl.total_budget and min(budgets) >= wl.floor
     assert len(set(budgets)) > 1, "budgets should vary by layer"
     # every layer: selection in isolation bit-exact, compaction bit-exact
-    for l, (idx_t, kc_t, vc_t) in enumerate(plan.layer_views):
-        B = budgets[l]
+    for l, (B, idx_t, kc_t, vc_t) in enumerate(layers):
         idx = idx_t.cpu().numpy()
         ref_idx = oracle.select.select_heads(imp[l].astype(np.float64), S=wl.S, w=wl.w, recent=wl.recent,
                                              budget=B)
@@ -311,5 +311,5 @@ def test_zigzag_l32_s16384():
             band = c[lo - 1:hi] / c[-1]
             assert np.all(np.abs(band - wl.mass) <= 1e-3), f"MBA {mba[l, g]} vs {m_ref}"
         ref_idx = oracle.select.select(ref, S=wl.S, w=wl.w, recent=wl.recent, budget=budgets[l])
-        check_selection(plan.layer_views[l][0].cpu().numpy()[g], ref, ref_idx, S=wl.S, w=wl.w,
+        check_selection(layers[l][1].cpu().numpy()[g], ref, ref_idx, S=wl.S, w=wl.w,
                         recent=wl.recent, budget=budgets[l])
