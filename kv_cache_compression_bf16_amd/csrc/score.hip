@@ -93,7 +93,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // kCausal: keys [0, S) and window row i (position S - w + i) sees the keys at
 // positions <= its own; w % 32 == 0, so no 32-row query block spans two heads.
-template <bool kPass2, bool kGumbel, bool kCausal, int kW, int kT, int kCB>
+// kPF: tiles of the next unit's keys prefetched during this unit (0..kT).
+template <bool kPass2, bool kGumbel, bool kCausal, int kW, int kT, int kCB, int kPF>
 __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreParams p) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int kThreads = kW * kWave;
@@ -142,7 +143,22 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
   };
 
   // K fragments of unit u: lane holds key (32t + col) of its wave's tiles,
-  // 16-byte chunk (2s + hb), already in the MFMA A-operand layout.
+  // 16-byte chunk (2s + hb), already in the MFMA A-operand layout; tiles
+  // [t0, t0 + kN) into dst[0 .. kN).
+  auto load_tiles = [&](int u, int t0, auto n_c, bf16x8 (*dst)[8]) {
+    constexpr int kN = decltype(n_c)::value;
+    const int head = u / p.nblk, blk = u - head * p.nblk;
+    const int layer = head / p.Hkv, g = head - layer * p.Hkv;
+    const uint16_t* kb = p.k + layer * p.k_ls + g * p.k_hs;
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int t = t0 + i;
+      const int j = min(blk * kKeysPerUnit + wave * kKeysPerWave + t * 32 + col, p.n - 1);   // clamp; masked
+      const bf16x8* row = reinterpret_cast<const bf16x8*>(kb + (int64_t)j * kD);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) dst[i][s] = row[2 * s + hb];
+    }
+  };
   auto load_k = [&](int u, bf16x8 (&dst)[kT][8]) {
     const int head = u / p.nblk, blk = u - head * p.nblk;
     const int layer = head / p.Hkv, g = head - layer * p.Hkv;
@@ -156,14 +172,28 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
     }
   };
 
+  // The first kPF tiles of the next unit are loaded during this one (after any
+  // staging, unconditionally -- the last unit reloads itself -- so the count
+  // of outstanding loads is the same on every path and the block loop never
+  // waits for them).
   bf16x8 kf[kT][8];
+  bf16x8 kn[kPF > 0 ? kPF : 1][8];
   if (n_units > 0) load_k(unit_at(0), kf);
   int staged = -1;   // head whose query rows are in LDS (single-chunk case)
   for (int it = 0; it < n_units; ++it) {
     const int u = unit_at(it);
     const int head = u / p.nblk, blk = u - head * p.nblk;
     const int layer = head / p.Hkv, g = head - layer * p.Hkv;
-    if (it != 0) load_k(u, kf);   // issued before this unit's staging, if any
+    if (it != 0) {
+      if (kPF > 0) {
+#pragma unroll
+        for (int t = 0; t < kPF; ++t)
+#pragma unroll
+          for (int s2 = 0; s2 < 8; ++s2) kf[t][s2] = kn[t][s2];
+      }
+      if (kPF < kT) load_tiles(u, kPF, std::integral_constant<int, kT - kPF>{}, kf + kPF);
+    }
+
     const int key0 = blk * kKeysPerUnit + wave * kKeysPerWave;
     const bool wave_full = key0 + kKeysPerWave <= p.n;   // no key of this wave past the prefix
     const float alpha = p.layer_scales ? p.layer_scales[layer] : p.scale;
@@ -295,6 +325,13 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
         stage(c0, nrows);
         __syncthreads();
         staged = head;
+      }
+      if (kPF > 0) {
+        // this unit's K tiles and staged rows are in (the first MFMA needs
+        // them anyway); then the next unit's first kPF tiles, which nothing
+        // in the block loop waits for
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        load_tiles(unit_at(min(it + 1, n_units - 1)), 0, std::integral_constant<int, (kPF > 0 ? kPF : 1)>{}, kn);
       }
       if (!kPass2) {
         float st[kCB];   // per-block partials stay in registers until the chunk is done
@@ -479,7 +516,12 @@ kvc_status score_grid(K kernel, int threads, size_t lds, int units, int* grid) {
 
 // Pass 1, combine and (unless only the row constants are wanted) pass 2 on one
 // stream.
-template <bool kGumbel, bool kCausal, int kW, int kT, int kCB>
+// Prefetch depth: every tile where the registers allow it (the 8-wave pass 2)
+// and for the 4-wave shape when a workgroup walks many units of >= 4 query
+// blocks (R >= 128; there it beats a second workgroup per CU, which a deeper
+// prefetch costs); one tile otherwise; none for the Keyformer shape (3 waves
+// per SIMD, no registers to spare).
+template <bool kGumbel, bool kCausal, int kW, int kT, int kCB, int kPF1, int kPF2>
 kvc_status launch_score(ScoreParams p, const Plan& pl, hipStream_t s, bool pass2 = true) {
   p.causal_unit = kCausal ? 32 * kW * kT : 0;
   constexpr int kThreads = kW * kWave;
@@ -490,8 +532,8 @@ kvc_status launch_score(ScoreParams p, const Plan& pl, hipStream_t s, bool pass2
   const dim3 comb_grid(heads * ((pl.R + comb_rows - 1) / comb_rows));
   auto kc = wide ? score_combine<8> : score_combine<32>;
   const size_t lds1 = score_lds_bytes(pl.chunk_rows, kW, false), lds2 = score_lds_bytes(pl.chunk_rows, kW, true);
-  auto k1 = score_pass<false, kGumbel, kCausal, kW, kT, kCB>;
-  auto k2 = score_pass<true, kGumbel, kCausal, kW, kT, kCB>;
+  auto k1 = score_pass<false, kGumbel, kCausal, kW, kT, kCB, kPF1>;
+  auto k2 = score_pass<true, kGumbel, kCausal, kW, kT, kCB, kPF2>;
   int g1 = 0, g2 = 0;
   kvc_status st = score_grid(k1, kThreads, lds1, units, &g1);
   if (st != KVC_OK) return st;
@@ -560,13 +602,14 @@ kvc_status score_entry(const kvc_score_args* a, const void* q_obs, const void* k
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (causal) {
-    if (a->gumbel) return launch_score<true, true, 4, 1, 4>(p, pl, s);
-    if (pl.shape.kw == 8) return launch_score<false, true, 8, 2, 16>(p, pl, s);
-    return launch_score<false, true, 4, 2, 8>(p, pl, s);
+    if (a->gumbel) return launch_score<true, true, 4, 1, 4, 0, 0>(p, pl, s);
+    if (pl.shape.kw == 8) return launch_score<false, true, 8, 2, 16, 1, 1>(p, pl, s);
+    return launch_score<false, true, 4, 2, 8, 1, 1>(p, pl, s);
   }
-  if (a->gumbel) return launch_score<true, false, 4, 1, 4>(p, pl, s);
-  if (pl.shape.kw == 8) return launch_score<false, false, 8, 2, 16>(p, pl, s);
-  return launch_score<false, false, 4, 2, 8>(p, pl, s);
+  if (a->gumbel) return launch_score<true, false, 4, 1, 4, 0, 0>(p, pl, s);
+  if (pl.shape.kw == 8) return launch_score<false, false, 8, 2, 16, 1, 2>(p, pl, s);
+  if (pl.R >= 128) return launch_score<false, false, 4, 2, 8, 2, 2>(p, pl, s);
+  return launch_score<false, false, 4, 2, 8, 1, 1>(p, pl, s);
 }
 
 }  // namespace
@@ -642,8 +685,9 @@ kvc_status score_rowc(const uint16_t* q, int64_t q_hs, const uint16_t* k, int64_
   p.nblk = pl.nblk;
   p.chunk_rows = pl.chunk_rows;
   *rowc = p.rowc;
-  if (pl.shape.kw == 8) return launch_score<false, false, 8, 2, 16>(p, pl, s, false);
-  return launch_score<false, false, 4, 2, 8>(p, pl, s, false);
+  if (pl.shape.kw == 8) return launch_score<false, false, 8, 2, 16, 1, 2>(p, pl, s, false);
+  if (pl.R >= 128) return launch_score<false, false, 4, 2, 8, 2, 2>(p, pl, s, false);
+  return launch_score<false, false, 4, 2, 8, 1, 1>(p, pl, s, false);
 }
 
 }  // namespace kvc
