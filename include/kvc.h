@@ -456,16 +456,22 @@ kvc_status kvc_decode_init_scores(const float* importance, int64_t imp_head_stri
  *   k_cache, v_cache bf16 [Hkv, B, D] (updated in place); pos int32 [Hkv, B]
  *   (distinct positions < t); acc fp32 [Hkv, B] (>= 0); evicted int32 [Hkv]
  *   or NULL.  The slots are unordered: only positions matter.
- * Arithmetic: fp32, reductions in a fixed order (bit-reproducible).
+ * Arithmetic: fp32, reductions in a fixed order (bit-reproducible).  The
+ *   workspace holds the step's logits and per-chunk softmax statistics
+ *   (kvc_keyformer_decode_step_workspace_size bytes).
  * Errors: KVC_E_ARG unless 1 <= recent < B, t >= 0, scale finite and > 0,
  *   tau > 0 (+inf allowed), pointers non-null and aligned (16 bytes for the
- *   bf16 arrays); KVC_E_UNSUPPORTED unless D == 128, G <= 8 and
- *   G * (B + 1) <= 32768; KVC_E_SHAPE for Hkv * G > 65535 or a bad q stride.
+ *   bf16 arrays and the workspace); KVC_E_UNSUPPORTED unless D == 128 and
+ *   G <= 8; KVC_E_SHAPE for Hkv * G > 65535, B > 2^28 or a bad q stride;
+ *   KVC_E_WORKSPACE for a missing or short workspace.
  */
+size_t kvc_keyformer_decode_step_workspace_size(int32_t Hkv, int32_t G, int32_t B);
+
 kvc_status kvc_keyformer_decode_step(const void* q, int64_t q_head_stride, const void* k_new, const void* v_new,
                                      void* k_cache, void* v_cache, int32_t* pos, float* acc, int32_t Hkv,
                                      int32_t G, int32_t B, int32_t D, int32_t t, int32_t recent, float scale,
-                                     float tau, uint64_t seed, int32_t* evicted, void* stream);
+                                     float tau, uint64_t seed, int32_t* evicted, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Kernel timing (measurement support).                                      */

@@ -12,15 +12,18 @@
 // smaller slot) and the new token's key, value, position and step score take
 // its slot.
 //
-// Design: one workgroup of 16 waves per KV head.  16 lanes cover a 256-byte
-// key row with 16-byte loads (4 keys per wave, 8 rows per lane in flight); each
-// lane dots its 8 channels with the group's G queries (held in registers) and
-// 4 xor-shuffles finish each dot product into LDS (G * (B + 1) floats); then
-// every thread adds the noise (keyed by the key's position, as in the prompt
-// phase) and the temperature to its own entries, giving the logits in log2
-// units.  Row max and sum per query head, the per-key score and
-// the eviction argmin are workgroup reductions in a fixed order, so the
-// result is bit-reproducible.
+// Design: two launches.  decode_logits, grid (chunks of 256 keys, KV heads):
+// 16 lanes cover a 256-byte key row with 16-byte loads (8 rows per lane in
+// flight) and dot it with the group's G queries (registers, kernel templated
+// on G <= 8), 4 xor-shuffles finishing each product; then every thread adds
+// the noise (keyed by the key's position, as in the prompt phase) and the
+// temperature to its own entries, giving logits in log2 units, written to the
+// workspace with the chunk's (max, sum of 2^(y - max)) per query head.
+// decode_update, one workgroup of 16 waves per KV head: folds the chunk
+// statistics in a fixed order into each head's softmax constants, then
+// accumulates the step scores, finds the lowest (score, position, slot)
+// outside the recent window with a two-stage 64-bit argmin and writes the new
+// token there.  Every reduction runs in a fixed order: bit-reproducible.
 #include "common.h"
 #include "philox.h"
 
@@ -30,7 +33,6 @@ namespace {
 constexpr int kD = 128;
 constexpr int kDecThreads = 1024;
 constexpr int kDecWaves = kDecThreads / kWave;
-constexpr int kMaxLogits = 32768;   // G * (B + 1) floats of LDS
 constexpr int kMaxG = 8;
 
 struct DecodeArgs {
@@ -49,32 +51,6 @@ struct DecodeArgs {
   uint32_t seed_lo, seed_hi;
 };
 
-__device__ __forceinline__ float block_max(float v, float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float m = red[0];
-#pragma unroll
-  for (int i = 1; i < kDecWaves; ++i) m = fmaxf(m, red[i]);
-  return m;
-}
-
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < kDecWaves; ++i) s += red[i];
-  return s;
-}
-
 __device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint64_t* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -91,19 +67,50 @@ __device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint64_t* red) {
   return m;
 }
 
+constexpr int kChunkKeys = 256;            // keys per decode_logits workgroup
+constexpr int kLogitThreads = 256;
+
+template <int kWaves>
+__device__ __forceinline__ float wg_max(float v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+
+template <int kWaves>
+__device__ __forceinline__ float wg_sum(float v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) s += red[i];
+  return s;
+}
+
 // kGmax: a power of two >= G (query registers and loop bounds sized for it).
+// y[(g * G + hh) * N + j] in log2 units; stats[(g * nchunk + chunk) * G + hh].
 template <int kGmax>
-__global__ __launch_bounds__(kDecThreads) void keyformer_decode_step(DecodeArgs a) {
-  __shared__ float y[kMaxLogits];         // y[h * (B + 1) + j], log2 units
-  __shared__ float red[kDecWaves];
-  __shared__ uint64_t red64[kDecWaves];
-  const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sub = lane & 15;              // 8-channel chunk of the key row
-  const int N = a.B + 1;                  // the B slots, then the new token
+__global__ __launch_bounds__(kLogitThreads) void decode_logits(DecodeArgs a, float* y, float2* stats, int nchunk) {
+  constexpr int kWaves = kLogitThreads / kWave;
+  __shared__ float ys[kGmax][kChunkKeys];
+  __shared__ float red[kWaves];
+  const int chunk = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane & 15;
+  const int N = a.B + 1, j_lo = chunk * kChunkKeys, nk = min(kChunkKeys, N - j_lo);
   const uint16_t* kg = a.kc + (int64_t)g * a.B * kD;
   const int32_t* pg = a.pos + (int64_t)g * a.B;
 
-  // this lane's 8 channels of each query of the group
   float qv[kGmax][8];
 #pragma unroll
   for (int hh = 0; hh < kGmax; ++hh) {
@@ -121,24 +128,19 @@ __global__ __launch_bounds__(kDecThreads) void keyformer_decode_step(DecodeArgs 
     }
   }
 
-  // logits: 16 lanes per key, 4 keys per wave, kU keys per lane group in
-  // flight (their row loads issued together); step u of super-step j0 takes
-  // key j0 + u * 64 + 4 * wave + lane / 16
-  constexpr int kU = kGmax <= 2 ? 8 : 4;
-  for (int j0 = 0; j0 < N; j0 += kU * kDecWaves * 4) {
+  // dot products: local key jl = 16 u + 4 wave + lane / 16, 8 rows in flight
+  constexpr int kU = 8;
+  for (int u0 = 0; u0 < kChunkKeys / 16; u0 += kU) {
     u32x4 w[kU];
-    int jj[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int j = j0 + u * kDecWaves * 4 + wave * 4 + (lane >> 4);
-      jj[u] = j;
-      const uint16_t* row = (j < a.B) ? kg + (int64_t)j * kD : a.k_new + (int64_t)g * kD;   // j >= B: new key
+      const int j = j_lo + 16 * (u0 + u) + 4 * wave + (lane >> 4);
+      const uint16_t* row = j < a.B ? kg + (int64_t)j * kD : a.k_new + (int64_t)g * kD;   // j >= B: new key
       w[u] = *reinterpret_cast<const u32x4*>(row + sub * 8);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int j = jj[u];
-      const bool ok = j < N;
+      const int jl = 16 * (u0 + u) + 4 * wave + (lane >> 4);
       const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
       float kv[8];
 #pragma unroll
@@ -156,37 +158,58 @@ __global__ __launch_bounds__(kDecThreads) void keyformer_decode_step(DecodeArgs 
         d += __shfl_xor(d, 4);
         d += __shfl_xor(d, 2);
         d += __shfl_xor(d, 1);
-        if (ok && sub == 0) y[hh * N + j] = d;   // the raw dot product; noise below
+        if (sub == 0) ys[hh][jl] = d;
       }
     }
   }
   __syncthreads();
   // noise and temperature with every lane busy: y = (x c + zeta log2 e) / tau
-  for (int i = tid; i < a.G * N; i += kDecThreads) {
-    const int hh = i / N, j = i - hh * N;
-    if (a.inv_tau == 0.f) {
-      y[i] = 0.f;   // tau = +inf: uniform
-      continue;
+  for (int i = tid; i < a.G * nk; i += kLogitThreads) {
+    const int hh = i / nk, jl = i - hh * nk, j = j_lo + jl;
+    float v = 0.f;   // tau = +inf: uniform
+    if (a.inv_tau != 0.f) {
+      const int p = j < a.B ? pg[j] : a.t;
+      const uint32_t h = (uint32_t)(g * a.G + hh);
+      const u32x4 x = philox4x32_10(u32x4{(uint32_t)p >> 2, (uint32_t)a.t, h, 0u}, a.seed_lo, a.seed_hi);
+      const uint32_t word = (p & 3) == 0 ? x.x : (p & 3) == 1 ? x.y : (p & 3) == 2 ? x.z : x.w;
+      v = fmaf(ys[hh][jl], a.c, gumbel_log2_from_word(word)) * a.inv_tau;
     }
-    const int p = j < a.B ? pg[j] : a.t;
-    const uint32_t h = (uint32_t)(g * a.G + hh);
-    const u32x4 x = philox4x32_10(u32x4{(uint32_t)p >> 2, (uint32_t)a.t, h, 0u}, a.seed_lo, a.seed_hi);
-    const uint32_t word = (p & 3) == 0 ? x.x : (p & 3) == 1 ? x.y : (p & 3) == 2 ? x.z : x.w;
-    y[i] = fmaf(y[i], a.c, gumbel_log2_from_word(word)) * a.inv_tau;
+    ys[hh][jl] = v;
+    y[((int64_t)g * a.G + hh) * N + j] = v;
   }
   __syncthreads();
+  for (int hh = 0; hh < a.G; ++hh) {
+    const float m = wg_max<kWaves>(tid < nk ? ys[hh][tid] : -INFINITY, red);
+    const float l = wg_sum<kWaves>(tid < nk ? __builtin_amdgcn_exp2f(ys[hh][tid] - m) : 0.f, red);
+    if (tid == 0) stats[((int64_t)g * nchunk + chunk) * a.G + hh] = float2{m, l};
+  }
+}
 
-  // per query head: m = max y, l = sum 2^(y - m); then score_j = sum_h 2^(y - m) / l
+template <int kGmax>
+__global__ __launch_bounds__(kDecThreads) void decode_update(DecodeArgs a, const float* y, const float2* stats,
+                                                             int nchunk) {
+  __shared__ float red[kDecWaves];
+  __shared__ uint64_t red64[kDecWaves];
+  const int g = blockIdx.x, tid = threadIdx.x;
+  const int N = a.B + 1;
+  const int32_t* pg = a.pos + (int64_t)g * a.B;
+  const float* yg = y + (int64_t)g * a.G * N;
+
+  // each query head's softmax constants from the chunk statistics (fixed order)
   float m_h[kGmax], il_h[kGmax];
 #pragma unroll
   for (int hh = 0; hh < kGmax; ++hh) {
     if (hh >= a.G) break;
+    const float2* sh = stats + (int64_t)g * nchunk * a.G + hh;
     float mx = -INFINITY;
-    for (int j = tid; j < N; j += kDecThreads) mx = fmaxf(mx, y[hh * N + j]);
-    const float m = block_max(mx, red);
-    float s = 0.f;
-    for (int j = tid; j < N; j += kDecThreads) s += __builtin_amdgcn_exp2f(y[hh * N + j] - m);
-    const float l = block_sum(s, red);
+    for (int c = tid; c < nchunk; c += kDecThreads) mx = fmaxf(mx, sh[(int64_t)c * a.G].x);
+    const float m = wg_max<kDecWaves>(mx, red);
+    float sm = 0.f;
+    for (int c = tid; c < nchunk; c += kDecThreads) {
+      const float2 st = sh[(int64_t)c * a.G];
+      sm += st.y * __builtin_amdgcn_exp2f(st.x - m);
+    }
+    const float l = wg_sum<kDecWaves>(sm, red);
     m_h[hh] = m;
     il_h[hh] = 1.0f / l;
   }
@@ -195,7 +218,7 @@ __global__ __launch_bounds__(kDecThreads) void keyformer_decode_step(DecodeArgs 
 #pragma unroll
     for (int hh = 0; hh < kGmax; ++hh) {
       if (hh >= a.G) break;
-      sc += __builtin_amdgcn_exp2f(y[hh * N + j] - m_h[hh]) * il_h[hh];
+      sc += __builtin_amdgcn_exp2f(yg[(int64_t)hh * N + j] - m_h[hh]) * il_h[hh];
     }
     return sc;
   };
@@ -269,17 +292,43 @@ extern "C" kvc_status kvc_decode_init_scores(const float* importance, int64_t im
   return KVC_OK;
 }
 
+namespace kvc {
+namespace {
+
+struct DecodeWs {
+  size_t y, stats, total;
+  int nchunk;
+};
+
+DecodeWs decode_ws(int Hkv, int G, int B) {
+  DecodeWs w{};
+  w.nchunk = (B + 1 + kChunkKeys - 1) / kChunkKeys;
+  w.y = 0;
+  w.stats = align_up((size_t)Hkv * G * (B + 1) * sizeof(float), 256);
+  w.total = w.stats + align_up((size_t)Hkv * w.nchunk * G * sizeof(float2), 256);
+  return w;
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" size_t kvc_keyformer_decode_step_workspace_size(int32_t Hkv, int32_t G, int32_t B) {
+  if (Hkv < 1 || G < 1 || G > kvc::kMaxG || B < 2) return 0;
+  return kvc::decode_ws(Hkv, G, B).total;
+}
+
 extern "C" kvc_status kvc_keyformer_decode_step(const void* q, int64_t q_head_stride, const void* k_new,
                                                 const void* v_new, void* k_cache, void* v_cache, int32_t* pos,
                                                 float* acc, int32_t Hkv, int32_t G, int32_t B, int32_t D,
                                                 int32_t t, int32_t recent, float scale, float tau,
-                                                uint64_t seed, int32_t* evicted, void* stream) {
+                                                uint64_t seed, int32_t* evicted, void* workspace,
+                                                size_t workspace_bytes, void* stream) {
   using namespace kvc;
   if (Hkv < 1 || G < 1 || B < 2 || t < 0 || recent < 1 || recent >= B) return KVC_E_ARG;
   if (!(scale > 0.f && scale < INFINITY) || !(tau > 0.f)) return KVC_E_ARG;   // tau = +inf allowed
   if (D != kD) return KVC_E_UNSUPPORTED;
-  if (G > kMaxG || (int64_t)G * (B + 1) > kMaxLogits) return KVC_E_UNSUPPORTED;
-  if (Hkv > 65535 || (int64_t)Hkv * G > 65535) return KVC_E_SHAPE;
+  if (G > kMaxG) return KVC_E_UNSUPPORTED;
+  if (Hkv > 65535 || (int64_t)Hkv * G > 65535 || B > (1 << 28)) return KVC_E_SHAPE;
   if (q_head_stride < D || (q_head_stride & 7)) return KVC_E_SHAPE;
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !pos || !acc) return KVC_E_ARG;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -287,6 +336,10 @@ extern "C" kvc_status kvc_keyformer_decode_step(const void* q, int64_t q_head_st
   if ((reinterpret_cast<uintptr_t>(pos) | reinterpret_cast<uintptr_t>(acc) |
        reinterpret_cast<uintptr_t>(evicted)) & 3)
     return KVC_E_ARG;
+  const DecodeWs W = decode_ws(Hkv, G, B);
+  if (!workspace || workspace_bytes < W.total || !aligned16(workspace)) return KVC_E_WORKSPACE;
+  float* y = reinterpret_cast<float*>(static_cast<char*>(workspace) + W.y);
+  float2* stats = reinterpret_cast<float2*>(static_cast<char*>(workspace) + W.stats);
   DecodeArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.q_hs = q_head_stride;
@@ -306,13 +359,21 @@ extern "C" kvc_status kvc_keyformer_decode_step(const void* q, int64_t q_head_st
   a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFull);
   a.seed_hi = (uint32_t)(seed >> 32);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 lg(W.nchunk, Hkv);
+#define KVC_DECODE(GM)                                                                                        \
+  do {                                                                                                        \
+    KVC_LAUNCH("keyformer_decode_logits", decode_logits<GM>, lg, dim3(kLogitThreads), s, a, y, stats, W.nchunk); \
+    KVC_LAUNCH("keyformer_decode_update", decode_update<GM>, dim3(Hkv), dim3(kDecThreads), s, a,               \
+               static_cast<const float*>(y), static_cast<const float2*>(stats), W.nchunk);                     \
+  } while (0)
   if (G == 1)
-    KVC_LAUNCH("keyformer_decode_step", keyformer_decode_step<1>, dim3(Hkv), dim3(kDecThreads), s, a);
+    KVC_DECODE(1);
   else if (G == 2)
-    KVC_LAUNCH("keyformer_decode_step", keyformer_decode_step<2>, dim3(Hkv), dim3(kDecThreads), s, a);
+    KVC_DECODE(2);
   else if (G <= 4)
-    KVC_LAUNCH("keyformer_decode_step", keyformer_decode_step<4>, dim3(Hkv), dim3(kDecThreads), s, a);
+    KVC_DECODE(4);
   else
-    KVC_LAUNCH("keyformer_decode_step", keyformer_decode_step<8>, dim3(Hkv), dim3(kDecThreads), s, a);
+    KVC_DECODE(8);
+#undef KVC_DECODE
   return KVC_OK;
 }

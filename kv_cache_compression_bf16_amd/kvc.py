@@ -72,8 +72,10 @@ def _load():
         "kvc_channel_prune_query": (ctypes.c_int, [P, P, I32, I32, I32, I64, I32, I32, I32, F64, P, P, P, P, SZ,
                                                    P]),
         "kvc_decode_init_scores": (ctypes.c_int, [P, I64, P, I32, I32, I32, P, P]),
+        "kvc_keyformer_decode_step_workspace_size": (SZ, [I32, I32, I32]),
         "kvc_keyformer_decode_step": (ctypes.c_int, [P, I64, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
-                                                     ctypes.c_float, ctypes.c_float, ctypes.c_uint64, P, P]),
+                                                     ctypes.c_float, ctypes.c_float, ctypes.c_uint64, P, P, SZ,
+                                                     P]),
         "kvc_timing_enable": (ctypes.c_int, [I32]),
         "kvc_timing_count": (I32, []),
         "kvc_timing_read": (ctypes.c_int, [I32, ctypes.c_char_p, I32, ctypes.POINTER(I32),
@@ -411,7 +413,7 @@ def kvc_decode_init_scores(importance, indices, acc, *, n, stream=None):
 
 
 def kvc_keyformer_decode_step(q, k_new, v_new, k_cache, v_cache, pos, acc, *, t, recent, tau=1.0, seed=0,
-                              scale=None, evicted=None, stream=None):
+                              scale=None, evicted=None, workspace=None, stream=None):
     """One Keyformer decode step: q [H, D], k_new / v_new [Hkv, D], caches [Hkv, B, D] (in place),
     pos int32 / acc float32 [Hkv, B] (in place), optional evicted int32 [Hkv]."""
     for x, nme in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
@@ -425,10 +427,12 @@ def kvc_keyformer_decode_step(q, k_new, v_new, k_cache, v_cache, pos, acc, *, t,
     if pos.dtype != torch.int32 or acc.dtype != torch.float32 or pos.shape != (Hkv, B) or acc.shape != (Hkv, B):
         raise ValueError("pos must be int32 and acc float32, both [Hkv, B]")
     scale = 1.0 / math.sqrt(D) if scale is None else scale
+    ws, nbytes = _workspace(_lib.kvc_keyformer_decode_step_workspace_size(Hkv, H // Hkv, B), k_cache.device,
+                            workspace)
     _check(_lib.kvc_keyformer_decode_step(_ptr(q), q.stride(0), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                                           _ptr(v_cache), _ptr(pos), _ptr(acc), Hkv, H // Hkv, B, D, int(t),
                                           int(recent), float(scale), float(tau), int(seed) & (2 ** 64 - 1),
-                                          _ptr(evicted), _stream(stream, k_cache.device)),
+                                          _ptr(evicted), _ptr(ws), nbytes, _stream(stream, k_cache.device)),
            "kvc_keyformer_decode_step")
     return evicted
 

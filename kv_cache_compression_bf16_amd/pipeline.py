@@ -93,13 +93,16 @@ class CompressionPlan:
         self.pos = self.indices.clone()
         self.acc = torch.empty(self.indices.shape, dtype=torch.float32, device=self.device)
         self.evicted = torch.empty(wl.Hkv, dtype=torch.int32, device=self.device)
+        nb = kvc.lib.kvc_keyformer_decode_step_workspace_size(wl.Hkv, wl.G, wl.budget)
+        self.ws_decode = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.device)
         kvc.kvc_decode_init_scores(self.importance[0], self.indices, self.acc, n=wl.n, stream=stream)
 
     def decode_step(self, q, k_new, v_new, t, stream=None):
         """One Keyformer decode step on the compacted cache (in place)."""
         wl = self.wl
         kvc.kvc_keyformer_decode_step(q, k_new, v_new, self.kc, self.vc, self.pos, self.acc, t=t, recent=wl.recent,
-                                      tau=self.tau, seed=wl.noise_seed, evicted=self.evicted, stream=stream)
+                                      tau=self.tau, seed=wl.noise_seed, evicted=self.evicted,
+                                      workspace=self.ws_decode, stream=stream)
 
     def score(self, q, k, layer_scales=None, stream=None):
         wl = self.wl

@@ -253,10 +253,12 @@ def test_channel_prune_value_validation():
 
 def test_decode_validation():
     names = ["q", "qs", "kn", "vn", "kc", "vc", "pos", "acc", "Hkv", "G", "B", "D", "t", "recent", "scale", "tau",
-             "seed", "ev", "st"]
+             "seed", "ev", "ws", "nb", "st"]
+    ws = lib.kvc_keyformer_decode_step_workspace_size(32, 1, 4096)
+    assert ws >= 32 * 4097 * 4 and lib.kvc_keyformer_decode_step_workspace_size(32, 9, 4096) == 0
     call = _named_call(lib.kvc_keyformer_decode_step, names,
                        (FAKE, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 1, 4096, 128, 9000, 512, 0.088, 1.0, 0,
-                        None, None))
+                        None, FAKE, ws, None))
     assert call(recent=4096) == E.KVC_E_ARG                   # the window must be shorter than the cache
     assert call(recent=0) == E.KVC_E_ARG
     assert call(t=-1) == E.KVC_E_ARG
@@ -265,7 +267,9 @@ def test_decode_validation():
     assert call(tau=float("nan")) == E.KVC_E_ARG
     assert call(D=64) == E.KVC_E_UNSUPPORTED
     assert call(G=9, Hkv=4) == E.KVC_E_UNSUPPORTED
-    assert call(G=8, Hkv=4, B=4096) == E.KVC_E_UNSUPPORTED    # 8 * 4097 logits do not fit
+    assert call(B=(1 << 28) + 1) == E.KVC_E_SHAPE
+    assert call(ws=None) == E.KVC_E_WORKSPACE
+    assert call(nb=ws - 256) == E.KVC_E_WORKSPACE
     assert call(qs=100) == E.KVC_E_SHAPE
     assert call(acc=None) == E.KVC_E_ARG
     assert call(kc=ctypes.c_void_p((1 << 20) + 8)) == E.KVC_E_ARG

@@ -86,7 +86,8 @@ def _run_steps(rng, *, Hkv, G, B, recent, steps, tau, acc0, seed=11):
 @pytest.mark.parametrize("Hkv,G,B,recent,steps,tau", [
     (4, 2, 600, 32, 12, 1.0),
     (2, 1, 4096, 512, 4, 1.0e4),       # Keyformer's cache and window sizes, the other temperature
-    (3, 8, 4095, 100, 2, 1.0),         # G * (B + 1) = 32768: the logits fill the LDS
+    (3, 8, 4095, 100, 2, 1.0),         # G = 8, the widest query group
+    (2, 8, 6000, 64, 2, 1.0),          # G * (B + 1) = 48008 logits per head, 24 key chunks
     (2, 4, 257, 1, 6, 0.5),            # window of one token
 ])
 def test_decode_steps_match_oracle(Hkv, G, B, recent, steps, tau):
