@@ -236,7 +236,6 @@ __global__ __launch_bounds__(256) void think_gather(const uint16_t* kc, int budg
 constexpr int kVWaves = 4;                // query blocks (waves) per workgroup
 constexpr int kVSplit = 512;              // keys per workgroup
 constexpr int kKPitch = kD * 2 + 16;      // bytes per staged key row
-constexpr int kVtPitch = 32 * 2 + 8;      // bytes per staged transposed value row (32 keys)
 constexpr int kVNormRows = 8;             // query rows per think_vnorm workgroup
 
 
@@ -245,18 +244,31 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {   // finite x
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Query blocks per workgroup for R rows (1, 2 or 4); the other waves take
+// further 32-key tiles of each staging step ("key phases").
+__host__ __device__ inline int vq_per_wg(int R) {
+  const int nqb = (R + 31) / 32;
+  return nqb >= 4 ? 4 : (nqb >= 2 ? 2 : 1);
+}
+
 __global__ __launch_bounds__(kVWaves * kWave) void think_vpartial(const uint16_t* q, int64_t q_hs, int G, int w,
                                                                  const uint16_t* kc, const uint16_t* vc,
                                                                  int budget, int rows, const float* rowc,
                                                                  float cc, int nsplit, float* opart) {
-  __shared__ __attribute__((aligned(16))) char ks[32 * kKPitch];
-  __shared__ __attribute__((aligned(16))) char vt[kD * kVtPitch];
+  // staging: K rows (kVWaves*32 x 272 B) then V^T (128 x (64 kp + 8) B); after
+  // the key loop the same bytes hold the key phases' partial O for the fold
+  __shared__ __attribute__((aligned(16))) char smem[kVWaves * 32 * kKPitch + kD * (kVWaves * 64 + 8)];
   const int split = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hb = lane >> 5, col = lane & 31;
   const int R = G * w;
-  const int qb = blockIdx.z * kVWaves + wave;
+  const int qpw = vq_per_wg(R), kp = kVWaves / qpw;
+  const int phase = wave / qpw;              // which 32-key tile of a staging step
+  const int qb = blockIdx.z * qpw + wave % qpw;
   const int row = qb * 32 + col;             // this lane's query row
   const bool wave_on = qb * 32 < R;
+  const int vt_pitch = 64 * kp + 8;          // bytes per staged V^T row (32 kp keys + padding)
+  char* ks = smem;
+  char* vt = smem + kVWaves * 32 * kKPitch;
   // B operand of S = K Q^T: lane holds Q[row][16 s + 8 hb .. +8]
   bf16x8 qf[8];
   float rc = INFINITY;                       // rows past R: P = 0
@@ -277,31 +289,46 @@ __global__ __launch_bounds__(kVWaves * kWave) void think_vpartial(const uint16_t
   const int key_hi = min(key_lo + kVSplit, rows);
   const uint16_t* kb = kc + (int64_t)g * budget * kD;
   const uint16_t* vb = vc + (int64_t)g * budget * kD;
-  uint16_t* vt16 = reinterpret_cast<uint16_t*>(vt);
-  for (int t0 = key_lo; t0 < key_hi; t0 += 32) {
-    __syncthreads();   // every wave is done with the previous tile
-    for (int i = tid; i < 32 * 16; i += kVWaves * kWave) {
-      const int kr = i >> 4, ch = i & 15, key = t0 + kr;
-      u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
-      if (key < key_hi) {
-        kv = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * kD + ch * 8);
-        vv = *reinterpret_cast<const u32x4*>(vb + (int64_t)key * kD + ch * 8);
-      }
-      *reinterpret_cast<u32x4*>(ks + kr * kKPitch + ch * 16) = kv;
-      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+  const int nkeys = 32 * kp;                 // keys per staging step
+  for (int t0 = key_lo; t0 < key_hi; t0 += nkeys) {
+    __syncthreads();   // every wave is done with the previous step
+    // a thread stages 4 consecutive keys of one 8-channel chunk: 4 K rows as
+    // 16-byte writes, and per channel the 4 keys' values as one 8-byte V^T write
+    for (int i = tid; i < nkeys * 4; i += kVWaves * kWave) {
+      const int kr0 = (i >> 4) * 4, ch = i & 15;
+      uint32_t vwd[4][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vt16[(ch * 8 + 2 * j) * (kVtPitch / 2) + kr] = (uint16_t)(vw[j] & 0xFFFFu);
-        vt16[(ch * 8 + 2 * j + 1) * (kVtPitch / 2) + kr] = (uint16_t)(vw[j] >> 16);
+      for (int r = 0; r < 4; ++r) {
+        const int key = t0 + kr0 + r;
+        u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
+        if (key < key_hi) {
+          kv = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * kD + ch * 8);
+          vv = *reinterpret_cast<const u32x4*>(vb + (int64_t)key * kD + ch * 8);
+        }
+        *reinterpret_cast<u32x4*>(ks + (kr0 + r) * kKPitch + ch * 16) = kv;
+        vwd[r][0] = vv.x;
+        vwd[r][1] = vv.y;
+        vwd[r][2] = vv.z;
+        vwd[r][3] = vv.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {   // channels ch*8 + 2j (low halves) and ch*8 + 2j + 1 (high halves)
+        const uint2 lo = uint2{(vwd[0][j] & 0xFFFFu) | (vwd[1][j] << 16), (vwd[2][j] & 0xFFFFu) | (vwd[3][j] << 16)};
+        const uint2 hi = uint2{(vwd[0][j] >> 16) | (vwd[1][j] & 0xFFFF0000u),
+                               (vwd[2][j] >> 16) | (vwd[3][j] & 0xFFFF0000u)};
+        *reinterpret_cast<uint2*>(vt + (ch * 8 + 2 * j) * vt_pitch + kr0 * 2) = lo;
+        *reinterpret_cast<uint2*>(vt + (ch * 8 + 2 * j + 1) * vt_pitch + kr0 * 2) = hi;
       }
     }
     __syncthreads();
-    if (!wave_on) continue;
-    // S[key][row]: lane holds row = col, key = t0 + 8 (e / 4) + 4 hb + e % 4
+    const int tb = t0 + 32 * phase;          // this wave's 32-key tile
+    if (!wave_on || tb >= key_hi) continue;
+    // S[key][row]: lane holds row = col, key = tb + 8 (e / 4) + 4 hb + e % 4
     f32x16 sacc = f32x16{};
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + col * kKPitch + (16 * st + 8 * hb) * 2);
+      const bf16x8 kf =
+          *reinterpret_cast<const bf16x8*>(ks + (32 * phase + col) * kKPitch + (16 * st + 8 * hb) * 2);
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], sacc, 0, 0, 0);
     }
     // P = 2^(S c - rowc) (0 past the split's keys), as bf16 hi + lo; element
@@ -313,7 +340,7 @@ __global__ __launch_bounds__(kVWaves * kWave) void think_vpartial(const uint16_t
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         const int ee = e + k2;
-        const int key = t0 + 8 * (ee >> 2) + 4 * hb + (ee & 3);
+        const int key = tb + 8 * (ee >> 2) + 4 * hb + (ee & 3);
         const float pv = key < key_hi ? __builtin_amdgcn_exp2f(fmaf(sacc[ee], cc, -rc)) : 0.f;
         hbits[k2] = bf16_rne_bits(pv);
         lbits[k2] = bf16_rne_bits(pv - __uint_as_float(hbits[k2] << 16));
@@ -328,7 +355,7 @@ __global__ __launch_bounds__(kVWaves * kWave) void think_vpartial(const uint16_t
       const bf16x8 bl = __builtin_bit_cast(bf16x8, u32x4{pl[half][0], pl[half][1], pl[half][2], pl[half][3]});
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const char* vr = vt + (32 * db + col) * kVtPitch;
+        const char* vr = vt + (32 * db + col) * vt_pitch + 64 * phase;
         const uint2 a0 = *reinterpret_cast<const uint2*>(vr + (16 * half + 4 * hb) * 2);
         const uint2 a1 = *reinterpret_cast<const uint2*>(vr + (16 * half + 8 + 4 * hb) * 2);
         const bf16x8 af = __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y});
@@ -337,7 +364,25 @@ __global__ __launch_bounds__(kVWaves * kWave) void think_vpartial(const uint16_t
       }
     }
   }
-  if (!wave_on || row >= R) return;
+  // fold the key phases of each query block in phase order through LDS
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);   // [(phase - 1) * qpw + block][64 lanes][64]
+  if (phase > 0) {
+    float* dst = red + ((int64_t)((phase - 1) * qpw + wave % qpw) * 64 + lane) * 64;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dst[db * 16 + e] = oacc[db][e];
+  }
+  __syncthreads();
+  if (phase != 0 || !wave_on || row >= R) return;
+  for (int ph2 = 1; ph2 < kp; ++ph2) {
+    const float* src = red + ((int64_t)((ph2 - 1) * qpw + wave % qpw) * 64 + lane) * 64;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] += src[db * 16 + e];
+  }
   // O^T layout: lane holds row = col and d = 32 db + 8 (e / 4) + 4 hb + e % 4
   float* op = opart + (((int64_t)g * nsplit + split) * R + row) * kD;
 #pragma unroll
@@ -529,7 +574,8 @@ extern "C" kvc_status kvc_channel_prune_value(const void* k_c, const void* v_c, 
     kvc_status st = score_rowc(qp, q_head_stride, kp, (int64_t)budget * kD, Hkv, G, w, rows, scale, base + L.rowc,
                                L.opart - L.rowc, &rowc, s);
     if (st != KVC_OK) return st;
-    const int nqg = ((R + 31) / 32 + kVWaves - 1) / kVWaves;
+    const int qpw = vq_per_wg(R);
+    const int nqg = ((R + 31) / 32 + qpw - 1) / qpw;
     KVC_LAUNCH("think_vpartial", think_vpartial, dim3(L.nsplit, Hkv, nqg), dim3(kVWaves * kWave), s, qp,
                q_head_stride, G, w, kp, vp, budget, rows, rowc, scale * kLog2e, L.nsplit, opart);
   }
