@@ -93,7 +93,11 @@ def algorithmic(wl, kept_rows=None):
         # one decode step: the cache keys once, pos and acc read and written, new rows, queries
         B = wl.budget
         dec_bytes = Hkv * B * D * 2 + Hkv * B * 12 + 2 * Hkv * D * 2 * 2 + H * D * 2
-        return dec_bytes, 0.0, {"keyformer_decode_step": ("hbm", 0.0, dec_bytes)}
+        logits = H * (B + 1) * 4        # the step's tempered logits, written then read once
+        return dec_bytes, 0.0, {
+            "keyformer_decode_logits": ("hbm", 0.0, Hkv * (B + 1) * D * 2 + Hkv * B * 4 + H * D * 2 + logits),
+            "keyformer_decode_update": ("hbm", 0.0, logits + Hkv * B * 12 + 2 * Hkv * D * 2 * 2),
+        }
     # per step (bench divides by the launches per step): bound, flops, algorithmic bytes
     per_kernel = {
         "score_pass1": ("mfma", flops_pass, q_bytes + k_prefix),
