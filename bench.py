@@ -337,6 +337,11 @@ def main():
     avg_s = kernels[dom]["avg_us"] / 1e6
     per_launch = args.steps / kernels[dom]["launches"]     # one step's figure -> one launch's
     bound, flops, nbytes = per_kernel.get(dom, ("hbm", 0.0, 0))
+    # the roofline that binds this kernel: the larger of its MFMA time and its
+    # HBM time at peak (a scoring pass over few query rows moves more bytes
+    # per flop than the chip's ratio and is HBM-bound)
+    if bound == "mfma" and nbytes / (HBM_PEAK_GBS * 1e9) > flops / (MFMA_BF16_PEAK_TFLOPS * 1e12):
+        bound = "hbm"
     traffic = measured_traffic(dom, wl.name)
     if bound == "mfma":
         achieved = flops * per_launch / avg_s / 1e12
