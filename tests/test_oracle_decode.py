@@ -8,7 +8,8 @@
   (Gumbel-max), here a key made to dominate.
 * Permuting the cache slots permutes the result and evicts the same token
   (the noise is keyed by position, not slot).
-* Tokens in the recent window are never evicted, whatever their score.
+* Tokens in the recent window are never evicted, whatever their score; a
+  token at exactly t - recent is outside it and may leave.
 * Brute force on a tiny cache: the evicted slot has the smallest (score,
   position) among the non-recent entries.
 * initial_scores reads the prompt importance at kept prefix positions.
@@ -109,3 +110,16 @@ def test_initial_scores():
     imp = np.array([[0.1, 0.2, 0.3, 0.4], [1.0, 2.0, 3.0, 4.0]])
     idx = np.array([[0, 3, 5], [2, 4, 6]])
     assert np.allclose(decode.initial_scores(imp, idx, 4), [[0.1, 0.4, 0.0], [3.0, 0.0, 0.0]])
+
+
+def test_token_at_the_window_edge_may_leave():
+    # the recent window is the positions > t - recent: a token at exactly
+    # t - recent is outside it and, with the lowest score, is the one evicted
+    rng = np.random.default_rng(35)
+    Hkv, G, B, D, recent, t = 1, 1, 8, 4, 3, 100
+    kc, vc, _ = _state(rng, Hkv, G, B, D, t)
+    pos = np.array([[10, 20, 30, 40, 50, t - recent, t - 2, t - 1]])
+    acc = np.array([[5.0, 5.0, 5.0, 5.0, 5.0, 0.0, 0.0, 0.0]])
+    q, kn, vn = _new(rng, Hkv, G, D)
+    new = decode.decode_step(kc, vc, pos, acc, q, kn, vn, t=t, recent=recent, scale=0.5, tau=1.0, seed=2)
+    assert new[4][0] == 5 and new[2][0, 5] == t

@@ -8,7 +8,9 @@
 * KV-cache size formula against the two sizes the pages print (13 GB on the
   ThinK page, about 335 GB on the KVzap page).
 * Query-driven score (outer-product Frobenius norm) against the rank-1
-  identity ||q k^T||_F = ||q|| ||k||, and a case the query side decides.
+  identity ||q k^T||_F = ||q|| ||k||, a case the query side decides, the
+  contiguous query-head grouping (one group's loud channels do not reach the
+  other) and recent rows not voting.
 * Value-channel score: one key (output rows = that value row) and zero
   queries (uniform attention: output rows = the mean value row) in closed
   form, exact linearity in each value channel, explicit loops on a tiny case,
@@ -171,3 +173,24 @@ def test_value_pruning_grouping_and_gather():
     assert np.allclose(sc[1], np.sqrt(G * w) * np.abs(vc[1, :B - recent].mean(axis=0)), rtol=1e-12)
     for g in range(Hkv):
         assert np.array_equal(pruned[g], vc[g, :B - recent][:, ch[g]]) and mask[g].sum() == 4
+
+
+def test_query_driven_group_is_contiguous_and_recent_rows_do_not_vote():
+    # each group's own loud query channels dominate its scores; the other
+    # group's loud channels (other query heads) do not reach it
+    rng = np.random.default_rng(25)
+    Hkv, G, w, B, D, recent = 2, 2, 3, 20, 16, 4
+    kc = np.sign(rng.standard_normal((Hkv, B, D)))
+    q = rng.standard_normal((Hkv * G, w, D)) * 0.1
+    loud = {0: [2, 9], 1: [4, 7]}
+    for g, cols in loud.items():
+        q[g * G:(g + 1) * G][:, :, cols] *= 100.0
+    _, _, _, sc = think.think_prune_query(kc, q, recent=recent, lam=0.5)
+    for g in range(Hkv):
+        assert sc[g][loud[g]].min() > 10.0 * sc[g][loud[1 - g]].max()
+    # equal key and query energy in every channel except a huge value in the
+    # recent rows of channel 7: the recent rows do not vote, so ties -> 0..T-1
+    kc2 = np.ones((1, 12, 16))
+    kc2[0, 8:, 7] = 1000.0
+    ch, _, _, _ = think.think_prune_query(kc2, np.ones((1, 2, 16)), recent=4, lam=0.75)
+    assert ch[0].tolist() == [0, 1, 2, 3]
