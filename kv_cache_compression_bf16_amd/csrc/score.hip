@@ -26,7 +26,7 @@
 //    accumulate in registers across all query blocks; the 32-lane reduction
 //    happens once per unit.  Every key column has a single owner, so no
 //    atomics are used and results are bit-reproducible.
-//  * Pass 1 keeps each wave's per-row (max, sum of exp2) in registers and
+//  * Pass 1 keeps each half-wave's per-row (max, sum of exp2) in registers and
 //    folds the waves in a fixed order, 4 query blocks at a time through a
 //    small LDS strip, into per-(row, unit) partials in log2 units; a combine
 //    kernel folds those per row into rowc = m + log2(l); pass 2 recomputes
@@ -70,7 +70,7 @@ inline Shape score_shape(int R, bool gumbel) {
 inline int score_chunk_rows(int R, const Shape& sh) { return min((R + 31) / 32 * 32, 32 * sh.cb); }
 inline size_t score_lds_bytes(int rows, int kw, bool pass2) {
   // staged rows, then the row constants (pass 2) or the 4-block fold strip (pass 1)
-  return (size_t)rows * kRowPitch + (pass2 ? (size_t)rows * sizeof(float) : (size_t)4 * 32 * kw * 2 * sizeof(float));
+  return (size_t)rows * kRowPitch + (pass2 ? (size_t)rows * sizeof(float) : (size_t)4 * 32 * kw * 2 * sizeof(float2));
 }
 
 struct ScoreParams {
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
   const int hb = lane >> 5, col = lane & 31;
   const int rows_alloc = p.chunk_rows;
   float* rcs = reinterpret_cast<float*>(lds + (size_t)rows_alloc * kRowPitch);    // pass 2: [rows]
-  float* fold = reinterpret_cast<float*>(lds + (size_t)rows_alloc * kRowPitch);   // pass 1: [kW][128][2]
+  float2* fold = reinterpret_cast<float2*>(lds + (size_t)rows_alloc * kRowPitch); // pass 1: [kW][128][2]
 
   // row r -> (query head r / w, window offset r % w): a float estimate of the
   // quotient, then one exact integer correction (r < 2^16 + 32, so the
@@ -266,9 +266,10 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
           acc[t][4 * r4 + 3] = fmaf(acc[t][4 * r4 + 3], c, gumbel_log2_from_word(x.w)) * p.inv_tau;
         }
     };
-    // Pass 1, one query block: this wave's (max, sum of exp2) of the lane's row
-    // over its keys; lanes of half-wave 0 return the max, half-wave 1 the sum.
-    auto row_stats = [&](auto clean_c, f32x16 (&acc)[kT], int r) -> float {
+    // Pass 1, one query block: (max, sum of exp2) of the lane's row over the
+    // lane's own keys; the two half-waves (the same rows, other keys) are
+    // folded later with the other waves.
+    auto row_stats = [&](auto clean_c, f32x16 (&acc)[kT], int r) -> float2 {
       constexpr bool kClean = decltype(clean_c)::value;
       if (!kClean) {
         const int rpos = kCausal ? row_pos(r) : 0;
@@ -292,12 +293,7 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
       for (int t = 0; t < kT; ++t)
 #pragma unroll
         for (int e = 0; e < 16; ++e) l += fast_exp2(fmaf(acc[t][e], cc, -mts));
-      // fold with the other half-wave (same query row, the other keys of each group)
-      const float mo = __shfl_xor(mt, 32), lo = __shfl_xor(l, 32);
-      const float m2 = fmaxf(mt, mo);
-      const float m2s = (m2 == -INFINITY) ? 0.f : m2;
-      const float l2 = l * fast_exp2(mt - m2s) + lo * fast_exp2(mo - m2s);
-      return hb ? l2 : m2;
+      return float2{mt, l};
     };
 
     f32x16 colacc[kT];
@@ -334,11 +330,11 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
         load_tiles(unit_at(min(it + 1, n_units - 1)), 0, std::integral_constant<int, (kPF > 0 ? kPF : 1)>{}, kn);
       }
       if (!kPass2) {
-        float st[kCB];   // per-block partials stay in registers until the chunk is done
+        float2 st[kCB];   // per-block partials stay in registers until the chunk is done
         auto blocks = [&](auto clean_c) {
 #pragma unroll
           for (int qb = 0; qb < kCB; ++qb) {
-            st[qb] = 0.f;
+            st[qb] = float2{-INFINITY, 0.f};
             if (qb < nb) {
               f32x16 acc[kT];
               mfma_block(qb, acc);
@@ -365,12 +361,14 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
               if (rr < nrows && r < p.R) {
                 float m = -INFINITY;
 #pragma unroll
-                for (int v = 0; v < kW; ++v) m = fmaxf(m, fold[(v * kFoldBlocks * 32 + i) * 2]);
+                for (int v = 0; v < 2 * kW; ++v) m = fmaxf(m, fold[(v >> 1) * kFoldBlocks * 64 + i * 2 + (v & 1)].x);
                 const float ms = (m == -INFINITY) ? 0.f : m;
                 float l = 0.f;
 #pragma unroll
-                for (int v = 0; v < kW; ++v)
-                  l += fold[(v * kFoldBlocks * 32 + i) * 2 + 1] * fast_exp2(fold[(v * kFoldBlocks * 32 + i) * 2] - ms);
+                for (int v = 0; v < 2 * kW; ++v) {
+                  const float2 e = fold[(v >> 1) * kFoldBlocks * 64 + i * 2 + (v & 1)];
+                  l += e.y * fast_exp2(e.x - ms);
+                }
                 p.part[head_row0 * p.nblk + (int64_t)blk * p.R + r] = float2{m, l};
               }
             }
@@ -520,7 +518,8 @@ kvc_status score_grid(K kernel, int threads, size_t lds, int units, int* grid) {
 // and for the 4-wave shape when a workgroup walks many units of >= 4 query
 // blocks (R >= 128; there it beats a second workgroup per CU, which a deeper
 // prefetch costs); one tile otherwise; none for the Keyformer shape (3 waves
-// per SIMD, no registers to spare).
+// per SIMD, no registers to spare) nor for the causal 8-wave pass 1 (its
+// masking path leaves no registers for it).
 template <bool kGumbel, bool kCausal, int kW, int kT, int kCB, int kPF1, int kPF2>
 kvc_status launch_score(ScoreParams p, const Plan& pl, hipStream_t s, bool pass2 = true) {
   p.causal_unit = kCausal ? 32 * kW * kT : 0;
@@ -603,7 +602,7 @@ kvc_status score_entry(const kvc_score_args* a, const void* q_obs, const void* k
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (causal) {
     if (a->gumbel) return launch_score<true, true, 4, 1, 4, 0, 0>(p, pl, s);
-    if (pl.shape.kw == 8) return launch_score<false, true, 8, 2, 16, 1, 1>(p, pl, s);
+    if (pl.shape.kw == 8) return launch_score<false, true, 8, 2, 16, 0, 1>(p, pl, s);
     return launch_score<false, true, 4, 2, 8, 1, 1>(p, pl, s);
   }
   if (a->gumbel) return launch_score<true, false, 4, 1, 4, 0, 0>(p, pl, s);

@@ -8,14 +8,17 @@
 //
 // Both designs below run an exact MSB-first radix select on order-preserving
 // 32-bit keys of the fp32 scores with LDS histograms and integer atomics
-// (exact and order-independent), then write the kept positions in order
-// (each thread owns consecutive candidates; workgroup scans give the output
-// offsets), so the output is ascending without a sort and bit-reproducible.
+// (exact and order-independent), then write the kept positions in order, so
+// the output is ascending without a sort and bit-reproducible.
 //
 //  * Up to 32768 candidates per head (one launch): one 1024-thread workgroup
 //    per head keeps all keys in registers; its levels work on key - min, each
 //    taking the next (up to) 11 bits below the top set bit of max - min, so
-//    scores of similar magnitude still spread over the bins.
+//    scores of similar magnitude still spread over the bins.  As soon as the
+//    bin holding the k_top-th key has at most 256 keys, those are gathered in
+//    LDS and ranked directly (usually after the first level).  Emission: each
+//    wave owns a contiguous span of candidates, so ballots and mbcnt within
+//    the wave plus per-wave counts give every kept candidate its slot.
 //  * More candidates (four launches, each ordered after the previous one on
 //    the stream): every head is cut into chunks of at most 4096 and each
 //    (chunk, head) gets a 256-thread workgroup.  Levels of 11, 11 and 10 bits;
@@ -93,12 +96,11 @@ __device__ __forceinline__ void block_min_max(uint32_t& lo, uint32_t& hi, uint32
   __syncthreads();
 }
 
-// Candidates are handled in rounds of kRound = 32768: in round r, wave w owns
-// the contiguous range [r*kRound + w*kSpan, +kSpan) and lane l holds
-// candidates base + 64*i + l (i < kVPL), so every load instruction reads 256
-// contiguous bytes and a lane keeps kVPL loads in flight.  With one round (up
-// to 32768 candidates) the keys are loaded once and stay in registers for all
-// radix levels and both emission passes.
+// Up to kRound = 32768 candidates: wave w owns the contiguous range
+// [w*kSpan, (w+1)*kSpan) and lane l holds candidates w*kSpan + 64*i + l
+// (i < kVPL), so every load instruction reads 256 contiguous bytes and a lane
+// keeps kVPL loads in flight.  The keys are loaded once and stay in registers
+// for every radix level and the emission.
 constexpr int kVPL = 32768 / kSelThreads;          // candidates per lane per round
 constexpr int kSpan = kVPL * kWave;                 // candidates per wave per round
 constexpr int kRound = kSelWaves * kSpan;
@@ -117,21 +119,26 @@ __device__ __forceinline__ void load_round(const uint32_t* v, int c, int r, uint
   for (int i = 0; i < kVPL; ++i) key[i] = (base + 64 * i < c) ? order_key(raw[i]) : 0u;
 }
 
+// Keys of the threshold bin are ranked directly once a level leaves at most
+// this many of them.
+constexpr int kLiveMax = 256;
+
 // Layers in one launch (budgets != null): grid (Hkv, L); layer l keeps
 // budgets[l] tokens per head and its block of the output starts at
 // Hkv * (budgets[0] + ... + budgets[l-1]) (head g's rows at g * budgets[l]), the
 // layout of per-layer calls on one flat buffer.  A layer whose budget is out
 // of range, or whose block would pass out_cap entries, writes nothing.
+// Candidate counts above kRound are never launched here with 0 < k_top < c.
 __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* imp, int64_t hs, int64_t ls, int c,
                                                                  int k_top, int S, int recent, int budget,
                                                                  const int32_t* budgets, int64_t out_cap,
                                                                  int32_t* out) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t wsum[kSelWaves], wsum2[kSelWaves];
-  __shared__ uint32_t s_digit, s_above;
-  __shared__ uint32_t tr[kRound + kRound / 64];   // 130 KB: transposed keys, then kept positions
+  __shared__ uint32_t s_digit, s_above, s_count, s_live, s_T, s_krem;
+  __shared__ __attribute__((aligned(16))) uint32_t live[kLiveMax];
 
-  const int g = blockIdx.x, layer = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
+  const int g = blockIdx.x, layer = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int64_t obase = (int64_t)g * budget;
   if (budgets) {
     int64_t before = 0;
@@ -150,31 +157,58 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
     for (int j = tid; j < c; j += kSelThreads) o[j] = j;
     return;
   }
+  if (c > kRound) return;
 
-  const int rounds = (c + kRound - 1) / kRound;
   uint32_t key[kVPL];
-  if (rounds == 1) load_round(v, c, 0, key);
-  const int lbase = wave * kSpan + (tid & 63);   // candidate of key[0] in round 0
+  load_round(v, c, 0, key);
+  const int lbase = wave * kSpan + lane;   // candidate of key[0]
 
-  // ---- key range of the candidates
+  // Waves are full (every slot a candidate), partial (the one holding c - 1)
+  // or empty (uniform per wave); empty waves skip every per-key loop.
+  const bool wave_full = wave * kSpan + kSpan <= c, wave_empty = wave * kSpan >= c;
+
+  // ---- key range of the candidates (slots past them hold key 0: no effect
+  // on the max; the min skips them)
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int r = 0; r < rounds; ++r) {
-    if (rounds > 1) load_round(v, c, r, key);
-    const int j0 = r * kRound + lbase;
+  if (wave_full) {
+#pragma unroll
+    for (int i = 0; i < kVPL; i += 2) {
+      kmin = min(kmin, min(key[i], key[i + 1]));
+      kmax = max(kmax, max(key[i], key[i + 1]));
+    }
+  } else if (!wave_empty) {
 #pragma unroll
     for (int i = 0; i < kVPL; ++i) {
-      const bool in = j0 + 64 * i < c;
-      kmin = min(kmin, in ? key[i] : 0xFFFFFFFFu);
-      kmax = max(kmax, in ? key[i] : 0u);
+      kmin = min(kmin, lbase + 64 * i < c ? key[i] : 0xFFFFFFFFu);
+      kmax = max(kmax, key[i]);
     }
   }
   block_min_max(kmin, kmax, wsum, wsum2);
+  // From here on key[i] holds d = key - kmin.  The partial wave's slots past
+  // the candidates take d = 0: they follow every candidate in position order
+  // and no candidate is smaller, so they are never kept (ties are taken in
+  // position order and the candidates alone hold k_top keys >= T) and need
+  // no range test.
+  if (wave_full) {
+#pragma unroll
+    for (int i = 0; i < kVPL; ++i) key[i] -= kmin;
+  } else {
+#pragma unroll
+    for (int i = 0; i < kVPL; ++i) key[i] = lbase + 64 * i < c ? key[i] - kmin : 0u;
+  }
 
-  // ---- radix select on d = key - kmin, MSB first.  Bits [top, 32) of the
-  // k_top-th largest d are known (= hi); each level resolves up to 11 more.
+  // ---- radix select on d, MSB first.  Bits [top, 32) of the k_top-th
+  // largest d are known (= hi); each level resolves up to 11 more.
+  // Once the keys sharing the resolved bits are few, they are ranked directly.
   int top = 32 - __clz(kmax - kmin);   // 0 when every candidate has the same key
   uint32_t hi = 0, krem = (uint32_t)k_top;
-  while (top > 0) {
+  uint32_t T;
+  bool first = true;   // the first level counts every key: all d < 2^top
+  while (true) {
+    if (top == 0) {
+      T = hi;   // every bit resolved: take krem of the keys equal to T
+      break;
+    }
     const int width = top < 11 ? top : 11;
     const int sh = top - width;
     const uint32_t dmask = (1u << width) - 1u;
@@ -184,18 +218,22 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
     if (tid == 0) {
       s_digit = 0;
       s_above = 0;
+      s_count = 0;
+      s_live = 0;
     }
     __syncthreads();
-    for (int r = 0; r < rounds; ++r) {
-      if (rounds > 1) load_round(v, c, r, key);
-      const int j0 = r * kRound + lbase;
+    if (wave_empty) {
+    } else if (first) {
+#pragma unroll
+      for (int i = 0; i < kVPL; ++i) atomicAdd(&hist[(key[i] >> sh) & dmask], 1u);
+    } else {
 #pragma unroll
       for (int i = 0; i < kVPL; ++i) {
-        const uint32_t d = key[i] - kmin;
-        const bool live = j0 + 64 * i < c && (d & hmask) == hval;
-        if (live) atomicAdd(&hist[(d >> sh) & dmask], 1u);
+        const uint32_t d = key[i];
+        if ((d & hmask) == hval) atomicAdd(&hist[(d >> sh) & dmask], 1u);
       }
     }
+    first = false;
     __syncthreads();
     // suffix counts: thread tid owns bins [kBPT*rt, kBPT*rt + kBPT), rt = last - tid
     const int rt = kSelThreads - 1 - tid;
@@ -214,6 +252,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
       if (suf >= krem && suf - hb[i] < krem) {
         s_digit = kBPT * rt + i;
         s_above = suf - hb[i];
+        s_count = hb[i];
       }
       below += hb[i];
     }
@@ -221,60 +260,111 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
     hi = (hi << width) | s_digit;
     krem -= s_above;
     top = sh;
+    const uint32_t count = s_count;   // keys whose bits [top, 32) of d equal hi
+    if (top > 0 && count <= (uint32_t)kLiveMax) {
+      // gather those keys (any order; count of them, so the slots stay below kLiveMax) ...
+      if (!wave_empty) {
+#pragma unroll
+        for (int i = 0; i < kVPL; ++i) {
+          const uint32_t d = key[i];
+          if ((d >> top) == hi) {
+            const uint32_t slot = atomicAdd(&s_live, 1u);
+            if (slot < (uint32_t)kLiveMax) live[slot] = d;
+          }
+        }
+      }
+      __syncthreads();
+      // ... and the one whose rank (keys greater, keys equal) covers krem is T
+      // (16-byte broadcast reads, 8 in flight; slots past count hold no key)
+      if (tid < (int)count) {
+        const uint32_t x = live[tid];
+        uint32_t gt = 0, eq = 0;
+        const uint4* l4 = reinterpret_cast<const uint4*>(live);
+        for (int j0 = 0; j0 < (int)count; j0 += 32) {
+          uint4 y[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) y[u] = l4[j0 / 4 + u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const uint32_t yy[4] = {y[u].x, y[u].y, y[u].z, y[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool ok = j0 + 4 * u + e < (int)count;
+              gt += ok && yy[e] > x ? 1u : 0u;
+              eq += ok && yy[e] == x ? 1u : 0u;
+            }
+          }
+        }
+        if (gt < krem && krem <= gt + eq) {   // every such thread holds the same x
+          s_T = x;
+          s_krem = krem - gt;
+        }
+      }
+      __syncthreads();
+      T = s_T;
+      krem = s_krem;
+      break;
+    }
     __syncthreads();
   }
-  const uint32_t T = kmin + hi;   // k_top-th largest key; take krem of the keys equal to T
 
-  // ---- ordered emission, round by round.  The round's keys are transposed
-  // through LDS (word j at j + j/64: conflict-free both ways) so that thread t
-  // owns the 64 consecutive candidates [64t, 64t + 64); per-thread counts and
-  // two workgroup scans give each thread its output offset; the kept
-  // positions go to LDS in order and then out with coalesced stores, so the
-  // output is ascending without a sort.
-  uint32_t eq_carry = 0, out_carry = 0;
-  for (int r = 0; r < rounds; ++r) {
-    if (rounds > 1) {
-      __syncthreads();   // the previous round's copy-out is done with `tr`
-      load_round(v, c, r, key);
-    }
-    const int j0 = r * kRound + lbase;
+  // ---- ordered emission.  Wave w owns candidates [w*kSpan, (w+1)*kSpan) and
+  // its lane l holds the one at offset 64i + l, so (wave, i, lane) is position
+  // order.  A kept candidate's output slot is (keys > T before it) +
+  // min(keys == T before it, krem): per-wave counts give the earlier waves'
+  // share, ballots and mbcnt the rest.  Output is ascending without a sort.
+  // When every key equal to T is kept (the usual case), the kept keys are
+  // exactly those >= T and one ballot per step suffices.
+  uint32_t n_ge = 0, n_eq = 0;
+  if (!wave_empty) {
 #pragma unroll
     for (int i = 0; i < kVPL; ++i) {
-      const int jl = j0 - r * kRound + 64 * i;      // position within the round
-      tr[jl + (jl >> 6)] = key[i];
+      n_ge += (uint32_t)__popcll(__ballot(key[i] >= T));
+      n_eq += (uint32_t)__popcll(__ballot(key[i] == T));
+      __builtin_amdgcn_sched_barrier(0);   // one step's compares at a time (they would spill)
     }
-    __syncthreads();
-    const int seg = tid * kVPL;                      // this thread's first position in the round
-    const int valid = min(kVPL, max(0, c - r * kRound - seg));
-    uint32_t mine[kVPL];
-    uint32_t n_gt = 0, n_eq = 0;
+  }
+  if (lane == 0) {
+    wsum[wave] = n_ge;
+    wsum2[wave] = n_eq;
+  }
+  __syncthreads();
+  // positions are recomputed here from an opaque copy of lbase: otherwise the
+  // compiler keeps the 32 positions of the range test alive (in scratch)
+  int pos0 = lbase;
+  asm volatile("" : "+v"(pos0));
+  uint32_t ge_run = 0, eq_run = 0, eq_all = 0;
+  for (int u = 0; u < kSelWaves; ++u) {
+    ge_run += u < wave ? wsum[u] : 0u;
+    eq_run += u < wave ? wsum2[u] : 0u;
+    eq_all += wsum2[u];
+  }
+  if (wave_empty) return;
+  if (eq_all <= krem) {   // then the keys >= T number exactly k_top
 #pragma unroll
-    for (int e = 0; e < kVPL; ++e) {
-      mine[e] = tr[seg + e + ((seg + e) >> 6)];      // = position seg + e, padded
-      n_gt += (e < valid && mine[e] > T) ? 1u : 0u;
-      n_eq += (e < valid && mine[e] == T) ? 1u : 0u;
+    for (int i = 0; i < kVPL; ++i) {
+      const bool ge = key[i] >= T;
+      const uint64_t b = __ballot(ge);
+      const uint32_t slot = ge_run + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+      if (ge && slot < (uint32_t)k_top) o[slot] = pos0 + 64 * i;   // < k_top by construction; checked anyway
+      ge_run += (uint32_t)__popcll(b);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    uint32_t eq_tot, take_tot;
-    const uint32_t eq_b = block_excl_scan<kSelThreads>(n_eq, wsum, &eq_tot) + eq_carry;   // also orders tr reads before writes
-    const uint32_t room = krem > eq_b ? krem - eq_b : 0u;
-    const uint32_t n_take = n_gt + (n_eq < room ? n_eq : room);
-    uint32_t pos = block_excl_scan<kSelThreads>(n_take, wsum, &take_tot);   // offset within this round's output
-    uint32_t eq_left = n_eq < room ? n_eq : room;    // T-valued candidates this thread keeps
-    const uint32_t jb = (uint32_t)(r * kRound + seg);
+    return;
+  }
+  uint32_t gt_run = ge_run - eq_run;
 #pragma unroll
-    for (int e = 0; e < kVPL; ++e) {
-      const bool in = e < valid;
-      const bool eq = in && mine[e] == T;
-      const bool take = (in && mine[e] > T) || (eq && eq_left > 0);
-      eq_left -= (eq && eq_left > 0) ? 1u : 0u;
-      if (take) tr[pos] = jb + e;                    // pos < take_tot <= kRound
-      pos += take ? 1u : 0u;
-    }
-    __syncthreads();
-    const uint32_t n_out = min(take_tot, (uint32_t)k_top - min(out_carry, (uint32_t)k_top));
-    for (uint32_t t = tid; t < n_out; t += kSelThreads) o[out_carry + t] = (int32_t)tr[t];
-    eq_carry += eq_tot;
-    out_carry += take_tot;
+  for (int i = 0; i < kVPL; ++i) {
+    const bool gt = key[i] > T, eq = key[i] == T;
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    const uint32_t below_g = __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
+    const uint32_t below_e = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+    const uint32_t er = eq_run + below_e;
+    const uint32_t slot = gt_run + below_g + min(er, krem);   // < k_top by construction; checked anyway
+    if ((gt || (eq && er < krem)) && slot < (uint32_t)k_top) o[slot] = pos0 + 64 * i;
+    gt_run += (uint32_t)__popcll(bg);
+    eq_run += (uint32_t)__popcll(be);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

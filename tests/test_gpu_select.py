@@ -52,6 +52,12 @@ def _ref_select(imp32, **kw):
     (3, 40016, 16, 16, 9000, "equal"),          # chunked path: one key everywhere -> lowest positions
     (2, 50064, 64, 64, 7000, "wide"),           # chunked path: full key range, +-inf
     (2, 45000, 10, 5, 20000, "zeros_denorm"),   # chunked path: zeros and denormals
+    (8, 32768, 128, 64, 2048, "exp"),           # 32K-token GQA shape: the bin of T is ranked directly
+    (4, 32768, 128, 64, 2048, "dups"),          # ~6 copies of each value: ties inside the ranked bin
+    (2, 32768, 128, 64, 2048, "ties3"),         # the bin of T holds ~11K keys: every radix level
+    (2, 32768, 128, 64, 2048, "narrow"),        # a tiny key range in one workgroup
+    (2, 32768, 128, 0, 30000, "exp"),           # k_top close to the candidate count
+    (3, 32767 + 128, 128, 0, 5, "dups"),        # 32767 candidates: the last wave part-filled
 ])
 def test_select_bit_exact(Hkv, S, w, recent, budget, kind):
     rng = np.random.default_rng(S + budget)
@@ -60,6 +66,8 @@ def test_select_bit_exact(Hkv, S, w, recent, budget, kind):
         imp = rng.exponential(size=(Hkv, n)).astype(np.float32)
     elif kind == "ties3":
         imp = (rng.integers(0, 3, size=(Hkv, n)) / 7.0).astype(np.float32)
+    elif kind == "dups":
+        imp = (rng.integers(0, 5000, size=(Hkv, n)) / 5000.0).astype(np.float32)
     elif kind == "equal":
         imp = np.full((Hkv, n), 1.0 / n, dtype=np.float32)
     elif kind == "narrow":
