@@ -73,6 +73,11 @@ inline size_t score_lds_bytes(int rows, int kw, bool pass2) {
   return (size_t)rows * kRowPitch + (pass2 ? (size_t)rows * sizeof(float) : (size_t)4 * 32 * kw * 2 * sizeof(float2));
 }
 
+// Most units per head for which pass 2 folds the row constants itself: one
+// step of loads per row.  Beyond it the fold's chain of round trips to
+// memory, which pass 2 must wait for, costs more than the combine launch.
+constexpr int kFuseRowcUnits = 32;
+
 struct ScoreParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -87,6 +92,7 @@ struct ScoreParams {
   uint32_t seed_lo, seed_hi;
   int L, Hkv, G, w, S, n, R, nblk, chunk_rows;
   int causal_unit;   // causal scoring: keys per unit (row r sees units b <= pos(r) / causal_unit); else 0
+  int fuse_rowc;     // pass 2 folds the partials into the row constants itself (no combine launch)
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -226,10 +232,36 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
           }
         }
       }
-      if (kPass2)
+      constexpr bool kCanFuse = kPass2 && !kGumbel && !kCausal;   // the Keyformer shape has no registers to spare
+      if (kPass2 && !(kCanFuse && p.fuse_rowc))
         for (int i = tid; i < nrows; i += kThreads) {
           const int r = c0 + i;
           rcs[i] = r < p.R ? p.rowc[head_row0 + r] : INFINITY;
+        }
+      if (kCanFuse && p.fuse_rowc)
+        // rowc = m + log2(sum_b l_b 2^(m_b - m)) over the head's units, one
+        // thread per row, kFuseStep units per step in order (loads from a
+        // clamped unit index, so none waits on a branch)
+        for (int i = tid; i < nrows; i += kThreads) {
+          constexpr int kFuseStep = kFuseRowcUnits;   // one step: every unit's load in flight at once
+          const int r = min(c0 + i, p.R - 1);
+          const float2* pp = p.part + head_row0 * p.nblk + r;
+          float m = -INFINITY, l = 0.f;
+          for (int b0 = 0; b0 < p.nblk; b0 += kFuseStep) {
+            float2 a[kFuseStep];
+#pragma unroll
+            for (int e = 0; e < kFuseStep; ++e) a[e] = pp[(int64_t)min(b0 + e, p.nblk - 1) * p.R];
+            float mn = m;
+#pragma unroll
+            for (int e = 0; e < kFuseStep; ++e) mn = fmaxf(mn, b0 + e < p.nblk ? a[e].x : -INFINITY);
+            const float ms = (mn == -INFINITY) ? 0.f : mn;
+            float acc = l * fast_exp2(m - ms);
+#pragma unroll
+            for (int e = 0; e < kFuseStep; ++e) acc += b0 + e < p.nblk ? a[e].y * fast_exp2(a[e].x - ms) : 0.f;
+            m = mn;
+            l = acc;
+          }
+          rcs[i] = (c0 + i < p.R && l > 0.f) ? m + log2f(l) : INFINITY;
         }
     };
     // A operands from registers, B operand (32 query rows) from LDS:
@@ -356,21 +388,37 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
             for (int qq = 0; qq < kFoldBlocks; ++qq)
               if (f0 + qq < kCB && f0 + qq < nb) fold[((wave * kFoldBlocks + qq) * 32 + col) * 2 + hb] = st[f0 + qq];
             __syncthreads();
-            for (int i = tid; i < kFoldBlocks * 32; i += kThreads) {
+            {
+              // kTPR adjacent threads per row, each folding kPer of its 2*kW
+              // entries, then an xor tree over the kTPR (a fixed order; every
+              // thread of the row ends with the same value)
+              constexpr int kTPR = kThreads / (kFoldBlocks * 32);
+              constexpr int kPer = 2 * kW / kTPR;
+              static_assert(kTPR * kFoldBlocks * 32 == kThreads && kPer * kTPR == 2 * kW, "fold split");
+              const int i = tid / kTPR, j = tid % kTPR;
               const int rr = f0 * 32 + i, r = c0 + rr;
-              if (rr < nrows && r < p.R) {
-                float m = -INFINITY;
+              float2 e[kPer];
 #pragma unroll
-                for (int v = 0; v < 2 * kW; ++v) m = fmaxf(m, fold[(v >> 1) * kFoldBlocks * 64 + i * 2 + (v & 1)].x);
-                const float ms = (m == -INFINITY) ? 0.f : m;
-                float l = 0.f;
-#pragma unroll
-                for (int v = 0; v < 2 * kW; ++v) {
-                  const float2 e = fold[(v >> 1) * kFoldBlocks * 64 + i * 2 + (v & 1)];
-                  l += e.y * fast_exp2(e.x - ms);
-                }
-                p.part[head_row0 * p.nblk + (int64_t)blk * p.R + r] = float2{m, l};
+              for (int k = 0; k < kPer; ++k) {
+                const int v = j * kPer + k;
+                e[k] = fold[(v >> 1) * kFoldBlocks * 64 + i * 2 + (v & 1)];
               }
+              float m = e[0].x;
+#pragma unroll
+              for (int k = 1; k < kPer; ++k) m = fmaxf(m, e[k].x);
+              const float ms = (m == -INFINITY) ? 0.f : m;
+              float l = 0.f;
+#pragma unroll
+              for (int k = 0; k < kPer; ++k) l += e[k].y * fast_exp2(e[k].x - ms);
+#pragma unroll
+              for (int o = 1; o < kTPR; o <<= 1) {
+                const float mo = __shfl_xor(m, o), lo = __shfl_xor(l, o);
+                const float m2 = fmaxf(m, mo);
+                const float m2s = (m2 == -INFINITY) ? 0.f : m2;
+                l = l * fast_exp2(m - m2s) + lo * fast_exp2(mo - m2s);
+                m = m2;
+              }
+              if (j == 0 && rr < nrows && r < p.R) p.part[head_row0 * p.nblk + (int64_t)blk * p.R + r] = float2{m, l};
             }
             __syncthreads();
           }
@@ -546,7 +594,7 @@ kvc_status launch_score(ScoreParams p, const Plan& pl, hipStream_t s, bool pass2
   KVC_LAUNCH_SHM(kCausal ? (kGumbel ? "score_causal_pass1_gumbel" : "score_causal_pass1")
                          : (kGumbel ? "score_pass1_gumbel" : "score_pass1"),
                  k1, dim3(g1), dim3(kThreads), lds1, s, p);
-  KVC_LAUNCH("score_combine", kc, comb_grid, dim3(256), s, p, heads);
+  if (!p.fuse_rowc) KVC_LAUNCH("score_combine", kc, comb_grid, dim3(256), s, p, heads);
   KVC_LAUNCH_SHM(kCausal ? (kGumbel ? "score_causal_pass2_gumbel" : "score_causal_pass2")
                          : (kGumbel ? "score_pass2_gumbel" : "score_pass2"),
                  k2, dim3(g2), dim3(kThreads), lds2, s, p);
@@ -598,6 +646,9 @@ kvc_status score_entry(const kvc_score_args* a, const void* q_obs, const void* k
   p.R = pl.R;
   p.nblk = pl.nblk;
   p.chunk_rows = pl.chunk_rows;
+  // A workgroup stages a head's rows once when they fit one chunk; with few
+  // units per row, folding them there is cheaper than a combine launch.
+  p.fuse_rowc = (!causal && !a->gumbel && pl.R <= pl.chunk_rows && pl.nblk <= kFuseRowcUnits) ? 1 : 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (causal) {
