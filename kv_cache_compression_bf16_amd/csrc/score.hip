@@ -142,7 +142,9 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
   const int n_units = kCausal ? (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x
                               : per + ((int)blockIdx.x < extra ? 1 : 0);
   auto unit_at = [&](int it) {
-    if (!kCausal) return u_first + it;
+    // pass 2 walks its range backwards: it starts on the keys pass 1 read
+    // last, which the same workgroup index may still find in its XCD's L2
+    if (!kCausal) return kPass2 ? u_first + n_units - 1 - it : u_first + it;
     const int v = (int)blockIdx.x + it * (int)gridDim.x;
     const int blk = v / heads, head = v - blk * heads;
     return head * p.nblk + blk;
