@@ -128,8 +128,9 @@ __global__ __launch_bounds__(kLogitThreads) void decode_logits(DecodeArgs a, flo
     }
   }
 
-  // dot products: local key jl = 16 u + 4 wave + lane / 16, 8 rows in flight
-  constexpr int kU = 8;
+  // dot products: local key jl = 16 u + 4 wave + lane / 16, all 16 rows of a
+  // lane in flight at once
+  constexpr int kU = kChunkKeys / 16;
   for (int u0 = 0; u0 < kChunkKeys / 16; u0 += kU) {
     u32x4 w[kU];
 #pragma unroll
@@ -185,7 +186,13 @@ __global__ __launch_bounds__(kLogitThreads) void decode_logits(DecodeArgs a, flo
   }
 }
 
-template <int kGmax>
+// kSlots > 0: the head's slots are held in registers, kSlots per thread
+// (B <= kSlots * kDecThreads), and every independent load (chunk statistics,
+// the thread's logits, scores and positions, the new token's logits and rows)
+// is issued at the start, so the step pays one round trip to memory; the
+// scores are written once, after the evicted slot is known.  kSlots = 0:
+// strided loops over the slots, for any B.
+template <int kGmax, int kSlots>
 __global__ __launch_bounds__(kDecThreads) void decode_update(DecodeArgs a, const float* y, const float2* stats,
                                                              int nchunk) {
   __shared__ float red[kDecWaves];
@@ -194,38 +201,156 @@ __global__ __launch_bounds__(kDecThreads) void decode_update(DecodeArgs a, const
   const int N = a.B + 1;
   const int32_t* pg = a.pos + (int64_t)g * a.B;
   const float* yg = y + (int64_t)g * a.G * N;
+  float* ag = a.acc + (int64_t)g * a.B;
+  const int cut = a.t - a.recent;   // positions <= cut may leave
 
-  // each query head's softmax constants from the chunk statistics (fixed order)
+  // register path: this thread's slots j = tid + kDecThreads * s (clamped
+  // addresses; slots past B are never used), the new token's logits and rows
+  constexpr int kS = kSlots > 0 ? kSlots : 1;
+  float yv[kS][kGmax], av[kS], ynew[kGmax];
+  int pv[kS];
+  u32x4 kn{}, vn{};
+  if constexpr (kSlots > 0) {
+#pragma unroll
+    for (int s2 = 0; s2 < kSlots; ++s2) {
+      const int j = min(tid + kDecThreads * s2, a.B - 1);
+      av[s2] = ag[j];
+      pv[s2] = pg[j];
+#pragma unroll
+      for (int hh = 0; hh < kGmax; ++hh) yv[s2][hh] = hh < a.G ? yg[(int64_t)hh * N + j] : 0.f;
+    }
+#pragma unroll
+    for (int hh = 0; hh < kGmax; ++hh) ynew[hh] = hh < a.G ? yg[(int64_t)hh * N + a.B] : 0.f;
+    if (tid < 16) {
+      kn = *reinterpret_cast<const u32x4*>(a.k_new + (int64_t)g * kD + tid * 8);
+      vn = *reinterpret_cast<const u32x4*>(a.v_new + (int64_t)g * kD + tid * 8);
+    }
+  }
+
+  // each query head's softmax constants from the chunk statistics (fixed
+  // order; with nchunk <= kDecThreads a thread holds at most one chunk)
   float m_h[kGmax], il_h[kGmax];
+  float2 st[kGmax];
+#pragma unroll
+  for (int hh = 0; hh < kGmax; ++hh)
+    st[hh] = (hh < a.G && tid < nchunk) ? stats[((int64_t)g * nchunk + tid) * a.G + hh] : float2{-INFINITY, 0.f};
+  // Up to 64 chunks: wave 0 folds them alone and hands the constants over
+  // through LDS (one barrier).  Its xor trees are those of the workgroup-wide
+  // fold below, whose other waves would only add -inf to the max and +0 to
+  // the sum, so both give the same bits.
+  __shared__ float s_m[kGmax], s_il[kGmax];
+  const bool one_wave = nchunk <= kWave;
+  if (one_wave) {
+    if (tid < kWave) {
+#pragma unroll
+      for (int hh = 0; hh < kGmax; ++hh) {
+        if (hh >= a.G) break;
+        float m = st[hh].x;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        float l = tid < nchunk ? st[hh].y * __builtin_amdgcn_exp2f(st[hh].x - m) : 0.f;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+        if (tid == 0) {
+          s_m[hh] = m;
+          s_il[hh] = 1.0f / l;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < kGmax; ++hh) {
+      m_h[hh] = hh < a.G ? s_m[hh] : 0.f;
+      il_h[hh] = hh < a.G ? s_il[hh] : 0.f;
+    }
+  }
 #pragma unroll
   for (int hh = 0; hh < kGmax; ++hh) {
-    if (hh >= a.G) break;
+    if (one_wave || hh >= a.G) break;
     const float2* sh = stats + (int64_t)g * nchunk * a.G + hh;
-    float mx = -INFINITY;
-    for (int c = tid; c < nchunk; c += kDecThreads) mx = fmaxf(mx, sh[(int64_t)c * a.G].x);
+    float mx = st[hh].x;
+    for (int c = tid + kDecThreads; c < nchunk; c += kDecThreads) mx = fmaxf(mx, sh[(int64_t)c * a.G].x);
     const float m = wg_max<kDecWaves>(mx, red);
-    float sm = 0.f;
-    for (int c = tid; c < nchunk; c += kDecThreads) {
-      const float2 st = sh[(int64_t)c * a.G];
-      sm += st.y * __builtin_amdgcn_exp2f(st.x - m);
+    float sm = tid < nchunk ? st[hh].y * __builtin_amdgcn_exp2f(st[hh].x - m) : 0.f;
+    for (int c = tid + kDecThreads; c < nchunk; c += kDecThreads) {
+      const float2 s1 = sh[(int64_t)c * a.G];
+      sm += s1.y * __builtin_amdgcn_exp2f(s1.x - m);
     }
     const float l = wg_sum<kDecWaves>(sm, red);
     m_h[hh] = m;
     il_h[hh] = 1.0f / l;
   }
-  auto step_score = [&](int j) {
+  // step score of an entry from its G logits (query heads in order)
+  auto score_of = [&](const float* yy) {
     float sc = 0.f;
 #pragma unroll
     for (int hh = 0; hh < kGmax; ++hh) {
       if (hh >= a.G) break;
-      sc += __builtin_amdgcn_exp2f(yg[(int64_t)hh * N + j] - m_h[hh]) * il_h[hh];
+      sc += __builtin_amdgcn_exp2f(yy[hh] - m_h[hh]) * il_h[hh];
     }
     return sc;
   };
+  auto step_score = [&](int j) {
+    float yy[kGmax];
+#pragma unroll
+    for (int hh = 0; hh < kGmax; ++hh) yy[hh] = hh < a.G ? yg[(int64_t)hh * N + j] : 0.f;
+    return score_of(yy);
+  };
 
-  // accumulate and find the lowest (score, position) outside the recent window
-  float* ag = a.acc + (int64_t)g * a.B;
-  const int cut = a.t - a.recent;   // positions <= cut may leave
+  if constexpr (kSlots > 0) {
+    // accumulate and find the lowest (score, position, slot) outside the
+    // recent window: one workgroup reduction of (key, slot) pairs
+    __shared__ uint32_t red_slot[kDecWaves];
+    float nv[kSlots];
+    uint64_t best = ~0ull;
+    uint32_t bslot = ~0u;
+#pragma unroll
+    for (int s2 = 0; s2 < kSlots; ++s2) {
+      nv[s2] = av[s2] + score_of(yv[s2]);
+      if (tid + kDecThreads * s2 < a.B && pv[s2] <= cut) {
+        const uint64_t key = ((uint64_t)__float_as_uint(nv[s2]) << 32) | (uint32_t)pv[s2];   // scores >= 0
+        if (key < best) {   // slots ascend with s2: an equal key keeps the smaller slot
+          best = key;
+          bslot = (uint32_t)(tid + kDecThreads * s2);
+        }
+      }
+    }
+    auto take = [&](uint64_t k2, uint32_t s3) {
+      if (k2 < best || (k2 == best && s3 < bslot)) {
+        best = k2;
+        bslot = s3;
+      }
+    };
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t k2 = __shfl_xor(best, o);
+      const uint32_t s3 = (uint32_t)__shfl_xor((int)bslot, o);
+      take(k2, s3);
+    }
+    if ((tid & (kWave - 1)) == 0) {
+      red64[tid >> 6] = best;
+      red_slot[tid >> 6] = bslot;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kDecWaves; ++i) take(red64[i], red_slot[i]);
+    const int e = best == ~0ull ? -1 : (int)bslot;   // -1: nothing may leave, no eviction
+    const float snew = score_of(ynew);
+#pragma unroll
+    for (int s2 = 0; s2 < kSlots; ++s2) {
+      const int j = tid + kDecThreads * s2;
+      if (j < a.B) ag[j] = j == e ? snew : nv[s2];
+      if (j == e) a.pos[(int64_t)g * a.B + e] = a.t;
+    }
+    if (tid == 0 && a.evicted) a.evicted[g] = e;
+    if (e >= 0 && tid < 16) {
+      *reinterpret_cast<u32x4*>(a.kc + ((int64_t)g * a.B + e) * kD + tid * 8) = kn;
+      *reinterpret_cast<u32x4*>(a.vc + ((int64_t)g * a.B + e) * kD + tid * 8) = vn;
+    }
+    return;
+  }
+
+  // any B: strided loops
   uint64_t best = ~0ull;
   for (int j = tid; j < a.B; j += kDecThreads) {
     const float nv = ag[j] + step_score(j);
@@ -237,7 +362,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_update(DecodeArgs a, const
     }
   }
   best = block_min_u64(best, red64);
-  // the slot holding that (score, position); the smallest such slot
   uint64_t slot = ~0ull;
   if (best != ~0ull)
     for (int j = tid; j < a.B; j += kDecThreads) {
@@ -252,10 +376,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_update(DecodeArgs a, const
   const int e = (int)slot;
   // the new token takes slot e
   if (tid < 16) {
-    const u32x4 kn = *reinterpret_cast<const u32x4*>(a.k_new + (int64_t)g * kD + tid * 8);
-    const u32x4 vn = *reinterpret_cast<const u32x4*>(a.v_new + (int64_t)g * kD + tid * 8);
-    *reinterpret_cast<u32x4*>(a.kc + ((int64_t)g * a.B + e) * kD + tid * 8) = kn;
-    *reinterpret_cast<u32x4*>(a.vc + ((int64_t)g * a.B + e) * kD + tid * 8) = vn;
+    const u32x4 k1 = *reinterpret_cast<const u32x4*>(a.k_new + (int64_t)g * kD + tid * 8);
+    const u32x4 v1 = *reinterpret_cast<const u32x4*>(a.v_new + (int64_t)g * kD + tid * 8);
+    *reinterpret_cast<u32x4*>(a.kc + ((int64_t)g * a.B + e) * kD + tid * 8) = k1;
+    *reinterpret_cast<u32x4*>(a.vc + ((int64_t)g * a.B + e) * kD + tid * 8) = v1;
   }
   if (tid == 0) {
     ag[e] = step_score(a.B);
@@ -360,11 +484,21 @@ extern "C" kvc_status kvc_keyformer_decode_step(const void* q, int64_t q_head_st
   a.seed_hi = (uint32_t)(seed >> 32);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 lg(W.nchunk, Hkv);
+  // slots per thread of the update's register path (0: strided loops); 8 only
+  // for G <= 4 (with 8 query heads the 64 logits of 8 slots would spill)
+  const int slots = B <= 4 * kDecThreads ? 4 : (B <= 8 * kDecThreads && G <= 4 ? 8 : 0);
+#define KVC_UPDATE(GM, NS)                                                                                    \
+  KVC_LAUNCH("keyformer_decode_update", (decode_update<GM, NS>), dim3(Hkv), dim3(kDecThreads), s, a,         \
+             static_cast<const float*>(y), static_cast<const float2*>(stats), W.nchunk)
 #define KVC_DECODE(GM)                                                                                        \
   do {                                                                                                        \
     KVC_LAUNCH("keyformer_decode_logits", decode_logits<GM>, lg, dim3(kLogitThreads), s, a, y, stats, W.nchunk); \
-    KVC_LAUNCH("keyformer_decode_update", decode_update<GM>, dim3(Hkv), dim3(kDecThreads), s, a,               \
-               static_cast<const float*>(y), static_cast<const float2*>(stats), W.nchunk);                     \
+    if (slots == 4)                                                                                           \
+      KVC_UPDATE(GM, 4);                                                                                      \
+    else if (slots == 8)                                                                                      \
+      KVC_UPDATE(GM, (GM <= 4 ? 8 : 0));                                                                      \
+    else                                                                                                      \
+      KVC_UPDATE(GM, 0);                                                                                      \
   } while (0)
   if (G == 1)
     KVC_DECODE(1);
@@ -375,5 +509,6 @@ extern "C" kvc_status kvc_keyformer_decode_step(const void* q, int64_t q_head_st
   else
     KVC_DECODE(8);
 #undef KVC_DECODE
+#undef KVC_UPDATE
   return KVC_OK;
 }

@@ -89,6 +89,8 @@ def _run_steps(rng, *, Hkv, G, B, recent, steps, tau, acc0, seed=11):
     (3, 8, 4095, 100, 2, 1.0),         # G = 8, the widest query group
     (2, 8, 6000, 64, 2, 1.0),          # G * (B + 1) = 48008 logits per head, 24 key chunks
     (2, 4, 257, 1, 6, 0.5),            # window of one token
+    (2, 2, 5000, 128, 3, 1.0),         # 4096 < B <= 8192 with G <= 4: eight slots per update thread
+    (1, 1, 9000, 64, 2, 1.0),          # B > 8192: the update's strided loops
 ])
 def test_decode_steps_match_oracle(Hkv, G, B, recent, steps, tau):
     rng = np.random.default_rng(B + G)
