@@ -189,38 +189,50 @@ __global__ __launch_bounds__(kMbaThreads) void mba_kernel(const float* imp, int 
   }
 }
 
-// Fixed-order workgroup sum of int64 (all threads get it).
+// Workgroup sum of int64 over kThreads threads (all threads get it).
+template <int kThreads>
 __device__ int64_t block_sum_i64(int64_t x, int64_t* scratch) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  if (kThreads == kWave) return x;   // one wave: no exchange needed
   if (lane == 0) scratch[wid] = x;
   __syncthreads();
   int64_t t = 0;
-  for (int i = 0; i < kAllocThreads / kWave; ++i) t += scratch[i];
+  for (int i = 0; i < kThreads / kWave; ++i) t += scratch[i];
   __syncthreads();
   return t;
 }
 
-__global__ __launch_bounds__(kAllocThreads) void allocate_kernel(const int32_t* mba, int L, int Hkv,
-                                                                int64_t total, int floor_l, int cap,
-                                                                int32_t* budgets) {
-  __shared__ int64_t s_rem[kMaxLayers];
-  __shared__ int s_free[kMaxLayers];
-  __shared__ int64_t scratch[kAllocThreads / kWave];
+// One thread per layer: kThreads = 64 (a single wave, no workgroup barriers
+// in the sums) up to 64 layers, kAllocThreads beyond.
+template <int kThreads>
+__global__ __launch_bounds__(kThreads) void allocate_kernel(const int32_t* mba, int L, int Hkv, int64_t total,
+                                                            int floor_l, int cap, int32_t* budgets) {
+  __shared__ int64_t s_rem[kThreads];
+  __shared__ int s_free[kThreads];
+  __shared__ int64_t scratch[kThreads / kWave];
+  auto block_sum = [&](int64_t x) { return block_sum_i64<kThreads>(x, scratch); };
 
   const int l = threadIdx.x;
   const bool has = l < L;
+  // M_l = sum of the layer's MBA over its KV heads, 8 loads in flight at a time
   int64_t M = 0;
   if (has)
-    for (int g = 0; g < Hkv; ++g) M += mba[(int64_t)l * Hkv + g];
+    for (int g0 = 0; g0 < Hkv; g0 += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = g0 + e < Hkv ? mba[(int64_t)l * Hkv + g0 + e] : 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) M += v[e];
+    }
   bool clamped = false;
   for (int iter = 0; iter <= L; ++iter) {
-    const int64_t nclamped = block_sum_i64(has && clamped ? 1 : 0, scratch);
+    const int64_t nclamped = block_sum(has && clamped ? 1 : 0);
     const int64_t R = total - (int64_t)L * floor_l - nclamped * (int64_t)(cap - floor_l);
     const bool fr = has && !clamped;
-    const int64_t Wsum = block_sum_i64(fr ? M : 0, scratch);
-    const int64_t nfree = block_sum_i64(fr ? 1 : 0, scratch);
+    const int64_t Wsum = block_sum(fr ? M : 0);
+    const int64_t nfree = block_sum(fr ? 1 : 0);
     const int64_t w = fr ? (Wsum > 0 ? M : 1) : 0;
     const int64_t W = Wsum > 0 ? Wsum : nfree;
     int64_t q = 0, rem = 0;
@@ -228,7 +240,7 @@ __global__ __launch_bounds__(kAllocThreads) void allocate_kernel(const int32_t* 
       q = (R * w) / W;
       rem = (R * w) % W;
     }
-    const int64_t left = R - block_sum_i64(q, scratch);
+    const int64_t left = R - block_sum(q);
     if (has) {
       s_rem[l] = rem;
       s_free[l] = fr ? 1 : 0;
@@ -245,7 +257,7 @@ __global__ __launch_bounds__(kAllocThreads) void allocate_kernel(const int32_t* 
     }
     __syncthreads();
     const bool over = fr && (int64_t)floor_l + q > (int64_t)cap;
-    const int64_t nover = block_sum_i64(over ? 1 : 0, scratch);
+    const int64_t nover = block_sum(over ? 1 : 0);
     if (nover == 0) {
       if (has) budgets[l] = clamped ? cap : (int32_t)(floor_l + q);
       return;
@@ -285,7 +297,11 @@ extern "C" kvc_status kvc_lmba_budget(const float* importance, int32_t L, int32_
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   KVC_LAUNCH("lmba_mba", mba_kernel, dim3(L * Hkv), dim3(kMbaThreads), s, importance, n, mass, mba_buf);
-  KVC_LAUNCH("lmba_allocate", allocate_kernel, dim3(1), dim3(kAllocThreads), s, mba_buf, L, Hkv,
-             total_budget, floor_per_layer, capacity, budgets);
+  if (L <= kWave)
+    KVC_LAUNCH("lmba_allocate", allocate_kernel<kWave>, dim3(1), dim3(kWave), s, mba_buf, L, Hkv, total_budget,
+               floor_per_layer, capacity, budgets);
+  else
+    KVC_LAUNCH("lmba_allocate", allocate_kernel<kAllocThreads>, dim3(1), dim3(kAllocThreads), s, mba_buf, L, Hkv,
+               total_budget, floor_per_layer, capacity, budgets);
   return KVC_OK;
 }
