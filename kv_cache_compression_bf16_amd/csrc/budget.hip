@@ -57,6 +57,11 @@ __device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t x, uint64_t* ws
 constexpr int kMbaBins = 2048;
 constexpr int kMbaBPT = kMbaBins / kMbaThreads;   // bins per thread in the suffix scans
 
+// kKPT > 0: the row is read once, kKPT keys per thread held in registers
+// together with their fixed-point masses (n <= kKPT * kMbaThreads), and
+// every later pass works on those; kKPT = 0: every pass reads the row again.
+// Both walk the same keys and add the same integers, so they agree exactly.
+template <int kKPT>
 __global__ __launch_bounds__(kMbaThreads) void mba_kernel(const float* imp, int n, double mass,
                                                          int32_t* mba_out) {
   __shared__ uint32_t hc[kMbaBins];   // count per bin
@@ -70,14 +75,34 @@ __global__ __launch_bounds__(kMbaThreads) void mba_kernel(const float* imp, int 
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const uint32_t* v = reinterpret_cast<const uint32_t*>(imp + (int64_t)row * n);
 
+  constexpr int kR = kKPT > 0 ? kKPT : 1;
+  uint32_t kr[kR];
+  uint64_t fr[kR];
+  if constexpr (kKPT > 0) {
+#pragma unroll
+    for (int i = 0; i < kKPT; ++i) {
+      const int j = tid + i * kMbaThreads;
+      kr[i] = v[j < n ? j : n - 1];   // clamped address; entries past n are never used
+    }
+  }
+  // f(key) over this thread's keys: j = tid + i * kMbaThreads, in order
+  auto for_keys = [&](auto&& f) {
+    if constexpr (kKPT > 0) {
+#pragma unroll
+      for (int i = 0; i < kKPT; ++i)
+        if (tid + i * kMbaThreads < n) f(kr[i], i);
+    } else {
+#pragma unroll 4
+      for (int j = tid; j < n; j += kMbaThreads) f(v[j], 0);
+    }
+  };
+
   // key range (scores are >= 0, so the raw bits are order-preserving keys)
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll 4
-  for (int j = tid; j < n; j += kMbaThreads) {
-    const uint32_t k = v[j];
+  for_keys([&](uint32_t k, int) {
     kmin = min(kmin, k);
     kmax = max(kmax, k);
-  }
+  });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor(kmin, o));
@@ -106,8 +131,16 @@ __global__ __launch_bounds__(kMbaThreads) void mba_kernel(const float* imp, int 
   auto fix = [&](uint32_t key) -> uint64_t { return (uint64_t)ldexp((double)__uint_as_float(key), shift); };
 
   uint64_t part = 0;
-#pragma unroll 4
-  for (int j = tid; j < n; j += kMbaThreads) part += fix(v[j]);
+  for_keys([&](uint32_t k, int i) {
+    const uint64_t f = fix(k);
+    if constexpr (kKPT > 0) fr[i] = f;
+    part += f;
+  });
+  // fixed-point mass of a key: cached in the register path
+  auto fixed = [&](uint32_t k, int i) -> uint64_t {
+    if constexpr (kKPT > 0) return fr[i];
+    return fix(k);
+  };
   uint64_t total;
   (void)block_excl_scan_u64(part, wsum, &total);
   const uint64_t target = (uint64_t)ceil((double)total * mass);   // keep at least this much
@@ -133,16 +166,14 @@ __global__ __launch_bounds__(kMbaThreads) void mba_kernel(const float* imp, int 
     }
     if (tid == 0) s_bin = 0u;
     __syncthreads();
-#pragma unroll 4
-    for (int j = tid; j < n; j += kMbaThreads) {
-      const uint32_t k = v[j];
+    for_keys([&](uint32_t k, int i) {
       const uint32_t d = k - kmin;
       if ((d & hmask) == hval) {
         const uint32_t b = (d >> sh) & dmask;
         atomicAdd(&hc[b], 1u);
-        atomicAdd(reinterpret_cast<unsigned long long*>(&hm[b]), (unsigned long long)fix(k));
+        atomicAdd(reinterpret_cast<unsigned long long*>(&hm[b]), (unsigned long long)fixed(k, i));
       }
-    }
+    });
     __syncthreads();
     // suffix sums of mass and count: the thread owns kMbaBPT bins from base
     const int base = kMbaBPT * (kMbaThreads - 1 - tid);
@@ -296,7 +327,10 @@ extern "C" kvc_status kvc_lmba_budget(const float* importance, int32_t L, int32_
     mba_buf = static_cast<int32_t*>(ws);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  KVC_LAUNCH("lmba_mba", mba_kernel, dim3(L * Hkv), dim3(kMbaThreads), s, importance, n, mass, mba_buf);
+  if (n <= 16 * kMbaThreads)
+    KVC_LAUNCH("lmba_mba", mba_kernel<16>, dim3(L * Hkv), dim3(kMbaThreads), s, importance, n, mass, mba_buf);
+  else
+    KVC_LAUNCH("lmba_mba", mba_kernel<0>, dim3(L * Hkv), dim3(kMbaThreads), s, importance, n, mass, mba_buf);
   if (L <= kWave)
     KVC_LAUNCH("lmba_allocate", allocate_kernel<kWave>, dim3(1), dim3(kWave), s, mba_buf, L, Hkv, total_budget,
                floor_per_layer, capacity, budgets);

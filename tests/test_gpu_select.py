@@ -179,6 +179,7 @@ def _gpu_budget(imp, **kw):
     (7, 4, 4096, 7 * 3000, 100, 3500, 3),     # forces capacity clamping
     (3, 9, 500, 3 * 200, 50, 500, 5),         # nine KV heads: two steps of MBA loads per layer
     (70, 9, 300, 70 * 100, 20, 300, 4),       # more layers than one wave allocates
+    (2, 3, 20000, 2 * 6000, 100, 20000, 6),   # rows longer than the MBA kernel keeps in registers
 ])
 def test_budgets_bit_exact(L, Hkv, n, total, floor, cap, seed):
     imp = _rows(L, Hkv, n, seed)
