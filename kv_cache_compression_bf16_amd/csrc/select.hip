@@ -403,29 +403,65 @@ __device__ __forceinline__ const uint32_t* chunk_suffix(const SelArgs& a, int L,
   return a.suf + (((int64_t)L * gridDim.y + g) * a.nchunk + q) * kBins;
 }
 
-// Sum over the head's chunks of level L's suffix count at bin b (all threads).
-__device__ __forceinline__ uint32_t suffix_total(const SelArgs& a, int L, int g, int b, uint32_t* wsum) {
-  uint32_t x = 0;
-  for (int q = threadIdx.x; q < a.nchunk; q += kThreads) x += chunk_suffix(a, L, g, q)[b];
-  uint32_t tot;
-  (void)block_excl_scan<kThreads>(x, wsum, &tot);
-  return tot;
-}
-
 // Level L's digit: the largest d with total suffix count >= krem (the count
-// at bin 0, all live keys, is >= krem), and the count above it.
+// at bin 0, all live keys, is >= krem), and the count above it.  The totals
+// are non-increasing in d, so two rounds find it: the 32 coarse bins 64c,
+// then the 64 bins of the chosen coarse interval.  Each round sums its bins
+// over the chunks with every load in flight at once (integer sums: the order
+// does not matter).  Both rounds end in barriers, which also publish LDS
+// writes made before the call.
+constexpr int kCoarse = kBins / 64;                                // 32 coarse bins
+static_assert(kThreads % kCoarse == 0 && kThreads % 64 == 0, "resolve_digit thread split");
 __device__ __forceinline__ void resolve_digit(const SelArgs& a, int L, int g, uint32_t krem, uint32_t* wsum,
                                               uint32_t& digit, uint32_t& above) {
-  int lo = 0, hi = kBins - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (suffix_total(a, L, g, mid, wsum) >= krem)
-      lo = mid;
-    else
-      hi = mid - 1;
+  (void)wsum;
+  __shared__ uint32_t rs_part[kThreads];
+  __shared__ uint32_t rs_tot[64];
+  const int tid = threadIdx.x;
+  const uint32_t* base = chunk_suffix(a, L, g, 0);
+  // round 1: totals at bins 64c; thread tid sums chunks q = tid / 32 (mod 8) of bin 64 (tid % 32)
+  {
+    constexpr int kGroups = kThreads / kCoarse;
+    const int c = tid % kCoarse;
+    uint32_t x = 0;
+    for (int q = tid / kCoarse; q < a.nchunk; q += kGroups) x += base[(int64_t)q * kBins + 64 * c];
+    rs_part[tid] = x;
+    __syncthreads();
+    if (tid < kCoarse) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int i = 0; i < kGroups; ++i) t += rs_part[i * kCoarse + tid];
+      rs_tot[tid] = t;
+    }
+    __syncthreads();
   }
-  digit = (uint32_t)lo;
-  above = lo + 1 < kBins ? suffix_total(a, L, g, lo + 1, wsum) : 0u;
+  int cstar = 0;
+  for (int c = 1; c < kCoarse; ++c)
+    if (rs_tot[c] >= krem) cstar = c;
+  const uint32_t next_coarse = cstar + 1 < kCoarse ? rs_tot[cstar + 1] : 0u;
+  __syncthreads();   // every thread has read rs_tot before round 2 reuses it
+  // round 2: totals at bins 64 cstar + i, i < 64
+  {
+    constexpr int kGroups = kThreads / 64;
+    const int i = tid % 64;
+    uint32_t x = 0;
+    for (int q = tid / 64; q < a.nchunk; q += kGroups) x += base[(int64_t)q * kBins + 64 * cstar + i];
+    rs_part[tid] = x;
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int k = 0; k < kGroups; ++k) t += rs_part[k * 64 + tid];
+      rs_tot[tid] = t;
+    }
+    __syncthreads();
+  }
+  int istar = 0;
+  for (int i = 1; i < 64; ++i)
+    if (rs_tot[i] >= krem) istar = i;
+  digit = (uint32_t)(64 * cstar + istar);
+  above = istar + 1 < 64 ? rs_tot[istar + 1] : next_coarse;
+  __syncthreads();   // rs_tot is read by every thread before any later reuse
 }
 
 template <int kLevel>
@@ -434,6 +470,16 @@ __global__ __launch_bounds__(kThreads) void select_level(SelArgs a) {
   __shared__ uint32_t wsum[kWaves];
   const int p = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   uint32_t* st = a.state + g * kStateWords;
+
+  // the chunk (<= kMaxChunk candidates) with every load in flight at once,
+  // from clamped addresses (entries past j1 are not counted); issued before
+  // the digit resolution, whose round trips they overlap
+  const int j0 = p * a.chunk, j1 = min(a.c, j0 + a.chunk);
+  const uint32_t* v = a.imp + (int64_t)g * a.hs;
+  uint32_t raw[kSegment];
+#pragma unroll
+  for (int e = 0; e < kSegment; ++e) raw[e] = v[min(j0 + tid + e * kThreads, j1 - 1)];
+  for (int b = tid; b < kBins; b += kThreads) h[b] = 0u;
 
   // digits resolved so far: (key & pmask) == prefix marks the keys still live
   uint32_t prefix = 0, pmask = 0;
@@ -452,15 +498,12 @@ __global__ __launch_bounds__(kThreads) void select_level(SelArgs a) {
       st[kLevel == 1 ? kKrem1 : kKrem2] = krem - above;
     }
   }
-
-  for (int b = tid; b < kBins; b += kThreads) h[b] = 0u;
-  __syncthreads();
-  const int j0 = p * a.chunk, j1 = min(a.c, j0 + a.chunk);
-  const uint32_t* v = a.imp + (int64_t)g * a.hs;
-#pragma unroll 4
-  for (int j = j0 + tid; j < j1; j += kThreads) {
-    const uint32_t key = order_key(v[j]);
-    if ((key & pmask) == prefix) atomicAdd(&h[(key >> level_shift(kLevel)) & level_mask(kLevel)], 1u);
+  __syncthreads();   // the cleared histogram
+#pragma unroll
+  for (int e = 0; e < kSegment; ++e) {
+    const uint32_t key = order_key(raw[e]);
+    if (j0 + tid + e * kThreads < j1 && (key & pmask) == prefix)
+      atomicAdd(&h[(key >> level_shift(kLevel)) & level_mask(kLevel)], 1u);
   }
   __syncthreads();
 
@@ -492,7 +535,16 @@ __global__ __launch_bounds__(kThreads) void select_emit(SelArgs a) {
     for (int t = tid; t < a.recent; t += kThreads) o[a.k_top + t] = a.S - a.recent + t;
   const int j0 = p * a.chunk, cnt = min(a.c, j0 + a.chunk) - j0;
   const uint32_t* v = a.imp + (int64_t)g * a.hs + j0;
-  for (int j = tid; j < cnt; j += kThreads) keys[j + (j >> 6)] = order_key(v[j]);
+  {
+    uint32_t raw[kSegment];   // every load in flight at once, clamped addresses
+#pragma unroll
+    for (int e = 0; e < kSegment; ++e) raw[e] = v[min(tid + e * kThreads, cnt - 1)];
+#pragma unroll
+    for (int e = 0; e < kSegment; ++e) {
+      const int j = tid + e * kThreads;
+      if (j < cnt) keys[j + (j >> 6)] = order_key(raw[e]);
+    }
+  }
 
   // T = the k_top-th key; krem of the T-valued candidates are taken
   const uint32_t d0 = st[kD0], d1 = st[kD1], krem2 = st[kKrem2];
