@@ -167,6 +167,16 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
   // or empty (uniform per wave); empty waves skip every per-key loop.
   const bool wave_full = wave * kSpan + kSpan <= c, wave_empty = wave * kSpan >= c;
 
+  // the first level's histogram and flags are cleared here, while the loads
+  // are in flight; the range reduction's barriers publish them
+  for (int b = tid; b < kBins; b += kSelThreads) hist[b] = 0;
+  if (tid == 0) {
+    s_digit = 0;
+    s_above = 0;
+    s_count = 0;
+    s_live = 0;
+  }
+
   // ---- key range of the candidates (slots past them hold key 0: no effect
   // on the max; the min skips them)
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -214,14 +224,16 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
     const uint32_t dmask = (1u << width) - 1u;
     const uint32_t hmask = top >= 32 ? 0u : (0xFFFFFFFFu << top);   // bits already resolved
     const uint32_t hval = top >= 32 ? 0u : (hi << top);
-    for (int b = tid; b < kBins; b += kSelThreads) hist[b] = 0;
-    if (tid == 0) {
-      s_digit = 0;
-      s_above = 0;
-      s_count = 0;
-      s_live = 0;
+    if (!first) {   // the first level's were cleared before the range reduction
+      for (int b = tid; b < kBins; b += kSelThreads) hist[b] = 0;
+      if (tid == 0) {
+        s_digit = 0;
+        s_above = 0;
+        s_count = 0;
+        s_live = 0;
+      }
+      __syncthreads();
     }
-    __syncthreads();
     if (wave_empty) {
     } else if (first) {
 #pragma unroll
@@ -315,13 +327,19 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
   // share, ballots and mbcnt the rest.  Output is ascending without a sort.
   // When every key equal to T is kept (the usual case), the kept keys are
   // exactly those >= T and one ballot per step suffices.
+  // per-wave counts of keys >= T and == T: per-lane counts summed over the
+  // wave (vector adds and one xor tree, no ballot-to-scalar round trips)
   uint32_t n_ge = 0, n_eq = 0;
   if (!wave_empty) {
 #pragma unroll
     for (int i = 0; i < kVPL; ++i) {
-      n_ge += (uint32_t)__popcll(__ballot(key[i] >= T));
-      n_eq += (uint32_t)__popcll(__ballot(key[i] == T));
-      __builtin_amdgcn_sched_barrier(0);   // one step's compares at a time (they would spill)
+      n_ge += key[i] >= T ? 1u : 0u;
+      n_eq += key[i] == T ? 1u : 0u;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      n_ge += (uint32_t)__shfl_xor((int)n_ge, o);
+      n_eq += (uint32_t)__shfl_xor((int)n_eq, o);
     }
   }
   if (lane == 0) {
