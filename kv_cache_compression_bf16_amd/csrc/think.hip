@@ -138,16 +138,31 @@ __global__ __launch_bounds__(kD * kSelGroups) void think_select(const float* par
   __shared__ int ssel[kD];
   const int g = blockIdx.x, d = threadIdx.x & (kD - 1), grp = threadIdx.x / kD;
   const float* pp = part + (int64_t)g * nchunk * kD + d;
-  // chunks grp + 8i go to sum i % 4 (four loads in flight), joined in order
+  // chunks grp + 8i go to sum i % 4, joined in order.  Up to 16 chunks per
+  // group every load is in flight at once (missing chunks add +0, which
+  // leaves the non-negative sums unchanged); beyond, four at a time.
   float a[4] = {0.f, 0.f, 0.f, 0.f};
-  int c = grp;
-  for (; c + 3 * kSelGroups < nchunk; c += 4 * kSelGroups) {
+  constexpr int kOnce = 16;
+  if (nchunk <= kOnce * kSelGroups) {
+    float v[kOnce];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] += pp[(int64_t)(c + j * kSelGroups) * kD];
+    for (int i = 0; i < kOnce; ++i) {
+      const int c1 = grp + i * kSelGroups;
+      v[i] = pp[(int64_t)min(c1, nchunk - 1) * kD];
+      if (c1 >= nchunk) v[i] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kOnce; ++i) a[i % 4] += v[i];
+  } else {
+    int c = grp;
+    for (; c + 3 * kSelGroups < nchunk; c += 4 * kSelGroups) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] += pp[(int64_t)(c + j * kSelGroups) * kD];
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (c + j * kSelGroups < nchunk) a[j] += pp[(int64_t)(c + j * kSelGroups) * kD];
   }
-#pragma unroll
-  for (int j = 0; j < 3; ++j)
-    if (c + j * kSelGroups < nchunk) a[j] += pp[(int64_t)(c + j * kSelGroups) * kD];
   red[grp][d] = (a[0] + a[1]) + (a[2] + a[3]);
   __syncthreads();
   // group 0 (threads 0..127) ranks; every thread still meets every barrier
