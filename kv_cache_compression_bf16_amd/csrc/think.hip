@@ -305,21 +305,38 @@ __global__ __launch_bounds__(kVWaves * kWave) void think_vpartial(const uint16_t
   const uint16_t* kb = kc + (int64_t)g * budget * kD;
   const uint16_t* vb = vc + (int64_t)g * budget * kD;
   const int nkeys = 32 * kp;                 // keys per staging step
-  for (int t0 = key_lo; t0 < key_hi; t0 += nkeys) {
-    __syncthreads();   // every wave is done with the previous step
-    // a thread stages 4 consecutive keys of one 8-channel chunk: 4 K rows as
-    // 16-byte writes, and per channel the 4 keys' values as one 8-byte V^T write
-    for (int i = tid; i < nkeys * 4; i += kVWaves * kWave) {
+  // a thread stages 4 consecutive keys of one 8-channel chunk per item (at
+  // most two items): 4 K rows as 16-byte writes, and per channel the 4 keys'
+  // values as one 8-byte V^T write.  The next step's items are loaded into
+  // registers while this step computes.
+  constexpr int kItems = (32 * kVWaves * 4) / (kVWaves * kWave);
+  u32x4 pk[kItems][4], pv[kItems][4];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+      const int i = tid + it * kVWaves * kWave;
+      const int kr0 = (i >> 4) * 4, ch = i & 15;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // clamped address; keys past key_hi are zeroed when staged
+        const int kk = min(t0 + kr0 + r, key_hi - 1);
+        pk[it][r] = *reinterpret_cast<const u32x4*>(kb + (int64_t)kk * kD + ch * 8);
+        pv[it][r] = *reinterpret_cast<const u32x4*>(vb + (int64_t)kk * kD + ch * 8);
+      }
+    }
+  };
+  auto put = [&](int t0) {
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+      const int i = tid + it * kVWaves * kWave;
+      if (i >= nkeys * 4) continue;
       const int kr0 = (i >> 4) * 4, ch = i & 15;
       uint32_t vwd[4][4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = t0 + kr0 + r;
-        u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
-        if (key < key_hi) {
-          kv = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * kD + ch * 8);
-          vv = *reinterpret_cast<const u32x4*>(vb + (int64_t)key * kD + ch * 8);
-        }
+        const bool ok = t0 + kr0 + r < key_hi;
+        const u32x4 kv = ok ? pk[it][r] : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 vv = ok ? pv[it][r] : u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(ks + (kr0 + r) * kKPitch + ch * 16) = kv;
         vwd[r][0] = vv.x;
         vwd[r][1] = vv.y;
@@ -335,6 +352,12 @@ __global__ __launch_bounds__(kVWaves * kWave) void think_vpartial(const uint16_t
         *reinterpret_cast<uint2*>(vt + (ch * 8 + 2 * j + 1) * vt_pitch + kr0 * 2) = hi;
       }
     }
+  };
+  if (key_lo < key_hi) fetch(key_lo);
+  for (int t0 = key_lo; t0 < key_hi; t0 += nkeys) {
+    __syncthreads();   // every wave is done with the previous step
+    put(t0);
+    if (t0 + nkeys < key_hi) fetch(t0 + nkeys);   // uniform over the workgroup
     __syncthreads();
     const int tb = t0 + 32 * phase;          // this wave's 32-key tile
     if (!wave_on || tb >= key_hi) continue;
