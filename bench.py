@@ -29,6 +29,17 @@ METRIC = "prompt KV tokens compressed/sec (score+top-k+gather); % of HBM rooflin
 DECODE_METRIC = "Keyformer decode tokens/sec for one layer (score accumulation + eviction on the kept cache)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+# vector ALU: 256 CUs x 4 SIMDs x 32 lane-operations per clock x 2.4 GHz (the
+# published unpacked fp32 / fp64 vector rate, 78.6 T FMA/s)
+VALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
+# vector operations per noisy tempered logit that the Gumbel path itself needs:
+# Philox4x32-10 (10 rounds of 2 wide products and 2 three-input xors per 4
+# samples: 10), the uniform from a word (3), -ln(-ln u) (2 logs, 2 scalings:
+# 4), (x c + g) / tau (2); then pass 1's max, shift, exp2, add (4) or pass 2's
+# shift, exp2, add (3).  Transcendentals count as one operation although the
+# hardware issues them at a lower rate, so the fraction is a lower bound.
+GUMBEL_OPS_PASS1 = 10 + 3 + 4 + 2 + 4
+GUMBEL_OPS_PASS2 = 10 + 3 + 4 + 2 + 3
 MALL_BYTES = 256 * 2 ** 20
 
 
@@ -98,14 +109,16 @@ def algorithmic(wl, kept_rows=None):
             "keyformer_decode_logits": ("hbm", 0.0, Hkv * (B + 1) * D * 2 + Hkv * B * 4 + H * D * 2 + logits),
             "keyformer_decode_update": ("hbm", 0.0, logits + Hkv * B * 12 + 2 * Hkv * D * 2 * 2),
         }
-    # per step (bench divides by the launches per step): bound, flops, algorithmic bytes
+    # per step (bench divides by the launches per step): bound, flops, algorithmic
+    # bytes[, vector operations]
+    logits = flops_pass / (2.0 * D)
     per_kernel = {
         "score_pass1": ("mfma", flops_pass, q_bytes + k_prefix),
         "score_pass2": ("mfma", flops_pass, q_bytes + k_prefix + imp),
-        "score_pass1_gumbel": ("mfma", flops_pass, q_bytes + k_prefix),
-        "score_pass2_gumbel": ("mfma", flops_pass, q_bytes + k_prefix + imp),
-        "score_causal_pass1_gumbel": ("mfma", flops_pass, q_bytes + k_prefix),
-        "score_causal_pass2_gumbel": ("mfma", flops_pass, q_bytes + k_prefix + imp),
+        "score_pass1_gumbel": ("mfma", flops_pass, q_bytes + k_prefix, GUMBEL_OPS_PASS1 * logits),
+        "score_pass2_gumbel": ("mfma", flops_pass, q_bytes + k_prefix + imp, GUMBEL_OPS_PASS2 * logits),
+        "score_causal_pass1_gumbel": ("mfma", flops_pass, q_bytes + k_prefix, GUMBEL_OPS_PASS1 * logits),
+        "score_causal_pass2_gumbel": ("mfma", flops_pass, q_bytes + k_prefix + imp, GUMBEL_OPS_PASS2 * logits),
         "score_causal_pass1": ("mfma", flops_pass, q_bytes + k_prefix),
         "score_causal_pass2": ("mfma", flops_pass, q_bytes + k_prefix + imp),
         "select_topk": ("hbm", 0.0, imp + B_total * 4),
@@ -336,14 +349,21 @@ def main():
     dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
     avg_s = kernels[dom]["avg_us"] / 1e6
     per_launch = args.steps / kernels[dom]["launches"]     # one step's figure -> one launch's
-    bound, flops, nbytes = per_kernel.get(dom, ("hbm", 0.0, 0))
-    # the roofline that binds this kernel: the larger of its MFMA time and its
-    # HBM time at peak (a scoring pass over few query rows moves more bytes
-    # per flop than the chip's ratio and is HBM-bound)
-    if bound == "mfma" and nbytes / (HBM_PEAK_GBS * 1e9) > flops / (MFMA_BF16_PEAK_TFLOPS * 1e12):
-        bound = "hbm"
-    traffic = measured_traffic(dom, wl.name)
+    bound, flops, nbytes, ops = (per_kernel.get(dom, ("hbm", 0.0, 0)) + (0.0,))[:4]
+    # the roofline that binds this kernel: the longest of its MFMA, HBM and
+    # vector-ALU times at peak (a scoring pass over few query rows moves more
+    # bytes per flop than the chip's ratio and is HBM-bound; the Gumbel passes
+    # spend more on Philox and logs than on their MFMA work)
+    t_roof = {"mfma": flops / (MFMA_BF16_PEAK_TFLOPS * 1e12), "hbm": nbytes / (HBM_PEAK_GBS * 1e9),
+              "alu": ops / (VALU_PEAK_TOPS * 1e12)}
     if bound == "mfma":
+        bound = max(t_roof, key=t_roof.get)
+    traffic = measured_traffic(dom, wl.name)
+    if bound == "alu":
+        achieved = ops * per_launch / avg_s / 1e12
+        roof = {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS, "unit": "Tops/s",
+                "frac": achieved / VALU_PEAK_TOPS, "traffic": traffic}
+    elif bound == "mfma":
         achieved = flops * per_launch / avg_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
@@ -354,10 +374,12 @@ def main():
     roof["kernel"] = dom
     roof["alg_bytes_per_launch"] = nbytes * per_launch
     for name, kk in kernels.items():
-        b, f, nb = per_kernel.get(name, ("", 0.0, 0))
+        b, f, nb, op = (per_kernel.get(name, ("", 0.0, 0)) + (0.0,))[:4]
         pl = args.steps / kk["launches"]
         kk["alg_TFLOPs"] = round(f * pl / (kk["avg_us"] / 1e6) / 1e12, 2) if f else None
         kk["alg_GBs"] = round(nb * pl / (kk["avg_us"] / 1e6) / 1e9, 1) if nb else None
+        if op:
+            kk["alg_Tops"] = round(op * pl / (kk["avg_us"] / 1e6) / 1e12, 2)
         kk["avg_us"] = round(kk["avg_us"], 2)
 
     cpu = None
