@@ -313,3 +313,30 @@ def test_zigzag_l32_s16384():
         ref_idx = oracle.select.select(ref, S=wl.S, w=wl.w, recent=wl.recent, budget=budgets[l])
         check_selection(layers[l][1].cpu().numpy()[g], ref, ref_idx, S=wl.S, w=wl.w,
                         recent=wl.recent, budget=budgets[l])
+
+
+# ---------------------------------------------------------------- determinism
+_OUTPUTS = ("importance", "pooled", "indices", "kc", "vc", "budgets", "mba", "indices_flat", "kc_flat", "vc_flat",
+            "channels", "mask", "kp", "channels_v", "mask_v", "vp")
+
+
+def _output_bytes(plan):
+    out = {}
+    for name in _OUTPUTS:
+        t = getattr(plan, name, None)
+        if isinstance(t, torch.Tensor):
+            out[name] = t.detach().contiguous().view(-1).view(torch.uint8).cpu().numpy().tobytes()
+    return out
+
+
+@pytest.mark.parametrize("name", ["gqa32x8_s32768", "think_s131072_kv", "keyformer_mha32_s8192"])
+def test_pipeline_outputs_identical_across_runs(name):
+    # every reduction has a fixed order and no float atomics are used, so two
+    # passes over the same inputs (separate plans and buffers) give the same bytes
+    wl = wk.WORKLOADS[name]
+    a, _, _ = _run(wl)
+    b, _, _ = _run(wl)
+    ba, bb = _output_bytes(a), _output_bytes(b)
+    assert ba.keys() == bb.keys() and "importance" in ba
+    for key in ba:
+        assert ba[key] == bb[key], f"{name}: {key} differs between runs"
