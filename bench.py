@@ -270,8 +270,9 @@ def cpu_baseline(wl, data, target_s, tau):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); rerun with --gpus 1", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(heads, layers and sequence blocks would shard over GPUs, but no collective is built); "
+              "rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     if args.calibrate_copy:
