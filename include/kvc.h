@@ -45,7 +45,7 @@ typedef enum kvc_status {
   KVC_E_SHAPE = 2,        /* inconsistent sizes                                */
   KVC_E_WORKSPACE = 3,    /* workspace missing or smaller than required        */
   KVC_E_DEVICE = 4,       /* a HIP call or kernel launch failed                */
-  KVC_E_UNSUPPORTED = 5   /* valid request this build does not implement       */
+  KVC_E_UNSUPPORTED = 5   /* valid request the library does not implement      */
 } kvc_status;
 
 /* Static description of a status code; never NULL. */
