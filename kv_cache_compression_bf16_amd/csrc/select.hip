@@ -423,10 +423,10 @@ __device__ __forceinline__ const uint32_t* chunk_suffix(const SelArgs& a, int L,
 
 // Level L's digit: the largest d with total suffix count >= krem (the count
 // at bin 0, all live keys, is >= krem), and the count above it.  The totals
-// are non-increasing in d, so two rounds find it: the 32 coarse bins 64c,
-// then the 64 bins of the chosen coarse interval.  Each round sums its bins
+// are non-increasing in d, so two steps find it: the 32 coarse bins 64c,
+// then the 64 bins of the chosen coarse interval.  Each step sums its bins
 // over the chunks with every load in flight at once (integer sums: the order
-// does not matter).  Both rounds end in barriers, which also publish LDS
+// does not matter).  Both steps end in barriers, which also publish LDS
 // writes made before the call.
 constexpr int kCoarse = kBins / 64;                                // 32 coarse bins
 static_assert(kThreads % kCoarse == 0 && kThreads % 64 == 0, "resolve_digit thread split");
@@ -437,7 +437,7 @@ __device__ __forceinline__ void resolve_digit(const SelArgs& a, int L, int g, ui
   __shared__ uint32_t rs_tot[64];
   const int tid = threadIdx.x;
   const uint32_t* base = chunk_suffix(a, L, g, 0);
-  // round 1: totals at bins 64c; thread tid sums chunks q = tid / 32 (mod 8) of bin 64 (tid % 32)
+  // coarse step: totals at bins 64c; thread tid sums chunks q = tid / 32 (mod 8) of bin 64 (tid % 32)
   {
     constexpr int kGroups = kThreads / kCoarse;
     const int c = tid % kCoarse;
@@ -457,8 +457,8 @@ __device__ __forceinline__ void resolve_digit(const SelArgs& a, int L, int g, ui
   for (int c = 1; c < kCoarse; ++c)
     if (rs_tot[c] >= krem) cstar = c;
   const uint32_t next_coarse = cstar + 1 < kCoarse ? rs_tot[cstar + 1] : 0u;
-  __syncthreads();   // every thread has read rs_tot before round 2 reuses it
-  // round 2: totals at bins 64 cstar + i, i < 64
+  __syncthreads();   // every thread has read rs_tot before the fine step reuses it
+  // fine step: totals at bins 64 cstar + i, i < 64
   {
     constexpr int kGroups = kThreads / 64;
     const int i = tid % 64;
