@@ -19,10 +19,11 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 x, uint32_t k0, uint32_t k1
     }
     const uint64_t p0 = (uint64_t)0xD2511F53u * x.x;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * x.z;
+    // each three-way xor is one v_bitop3_b32 (truth table 0x96 = a ^ b ^ c)
     u32x4 y;
-    y.x = (uint32_t)(p1 >> 32) ^ x.y ^ k0;
+    y.x = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), x.y, k0, 0x96);
     y.y = (uint32_t)p1;
-    y.z = (uint32_t)(p0 >> 32) ^ x.w ^ k1;
+    y.z = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), x.w, k1, 0x96);
     y.w = (uint32_t)p0;
     x = y;
   }
