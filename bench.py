@@ -176,17 +176,98 @@ def measured_traffic(kernel, workload):
     return None
 
 
-def cpu_baseline(wl, data, target_s, tau):
-    """The oracle, as it stands, on a bounded sample of the same workload (whole KV heads)."""
+# ---- CPU oracle baseline ----------------------------------------------------
+# Workers are forked before anything touches the GPU and hold the host inputs
+# copy-on-write; each runs the oracle with BLAS pinned to one thread.
+_CPU = {}
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+
+    _CPU["limits"] = threadpool_limits(1)
+
+
+def _causal_row(wl, u):
+    """The query row of causal unit u: rows visited with an odd stride, so a short
+    sample spreads over short and long rows alike."""
+    return ((u // wl.H) * 4099) % wl.w
+
+
+def _cpu_unit(u):
+    """One unit of oracle work: a whole KV head of layer 0 (score [+ pool] + select
+    + compact [+ ThinK]), or one causal query row.  Returns the unit index."""
     import numpy as np
     import oracle
-    from threadpoolctl import threadpool_info
 
-    q, k, v = data
+    wl, (q, k, v), tau = _CPU["wl"], _CPU["data"], _CPU["tau"]
+    scale = float(np.float32(1.0 / math.sqrt(wl.D)))
+    if wl.causal:
+        h, i = u % wl.H, _causal_row(wl, u)
+        oracle.score.head_causal_mean(oracle.score.bf16_bits_to_f64(q[h]),
+                                      oracle.score.bf16_bits_to_f64(k[h // wl.G]), S=wl.S, w=wl.w, scale=scale,
+                                      gumbel=wl.gumbel, seed=wl.noise_seed, head=h, tau=tau, rows=[i])
+        return u
+    q0 = q if wl.L == 1 else q[0]
+    kraw = k if wl.L == 1 else k[0]
+    vraw = v if wl.L == 1 else v[0]
+    g = u % wl.Hkv
+    qf = oracle.score.bf16_bits_to_f64(q0[g * wl.G:(g + 1) * wl.G])
+    kf = oracle.score.bf16_bits_to_f64(kraw[g])
+    B = wl.budget if wl.budget else wl.total_budget // wl.L
+    # KV head g's importance: the sum of its query heads' window means (the noise keyed
+    # by the true query-head index)
+    imp = sum(oracle.score.head_window_mean(qf[i], kf, n=wl.n, scale=scale, gumbel=wl.gumbel, seed=wl.noise_seed,
+                                            head=g * wl.G + i, S=wl.S, w=wl.w, tau=tau) for i in range(wl.G))
+    sc = oracle.pool.pool(imp[None], wl.pool_kernel, wl.pool_mode)[0] if wl.pool_kernel else imp
+    if wl.threshold > 0:
+        idx = oracle.threshold.select_threshold(sc, S=wl.S, w=wl.w, recent=wl.recent, theta=wl.theta)
+    else:
+        idx = oracle.select.select(sc, S=wl.S, w=wl.w, recent=wl.recent, budget=B)
+    kc = oracle.compact.compact(kraw[g:g + 1], idx[None])
+    vc = oracle.compact.compact(vraw[g:g + 1], idx[None])
+    if wl.think_value_lambda >= 0:
+        oracle.think.think_prune_value(oracle.score.bf16_bits_to_f64(kc), oracle.score.bf16_bits_to_f64(vc), qf,
+                                       recent=wl.recent, lam=wl.think_value_lambda, scale=scale)
+    if wl.think_lambda >= 0 and wl.think_query:
+        oracle.think.think_prune_query(oracle.score.bf16_bits_to_f64(kc), qf, recent=wl.recent,
+                                       lam=wl.think_lambda)
+    elif wl.think_lambda >= 0:
+        oracle.think.think_prune(oracle.score.bf16_bits_to_f64(kc), recent=wl.recent, lam=wl.think_lambda,
+                                 p=wl.think_p)
+    return u
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(wl, data, target_s, tau, max_workers=16):
+    """The oracle, as it stands, on a bounded sample of the same workload, spread
+    over a process pool of one worker per available host core (at most
+    ``max_workers``, the host share of one GPU), BLAS pinned to one thread each."""
+    import multiprocessing as mp
+
+    import numpy as np
+    import oracle
+
+    cores = max(1, min(len(os.sched_getaffinity(0)), max_workers))
     if wl.decode_steps:
-        # decode steps of the oracle from a kept cache of the workload's own rows:
-        # the prompt's recent window plus evenly spaced prefix tokens, zero scores
+        # decode steps depend on each other: one process, BLAS pinned to one thread,
+        # from a kept cache of the workload's own rows (the prompt's recent window
+        # plus evenly spaced prefix tokens, zero scores)
+        from threadpoolctl import threadpool_limits
+
         from kv_cache_compression_bf16_amd import workload as wk
+        q, k, v = data
         B, r = wl.budget, wl.recent
         pos = np.concatenate([np.linspace(0, wl.S - r - 1, B - r).astype(np.int64), np.arange(wl.S - r, wl.S)])
         kc, vc = k[:, pos], v[:, pos]
@@ -194,77 +275,41 @@ def cpu_baseline(wl, data, target_s, tau):
         acc = np.zeros((wl.Hkv, B))
         scale = float(np.float32(1.0 / math.sqrt(wl.D)))
         steps, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < target_s:
-            qd, kn, vn = wk.gen_decode(wl, steps)
-            kc, vc, pos, acc, _ = oracle.decode.decode_step(kc, vc, pos, acc, oracle.score.bf16_bits_to_f64(qd), kn,
-                                                            vn, t=wl.S + steps, recent=r, scale=scale, tau=tau,
-                                                            seed=wl.noise_seed)
-            steps += 1
+        with threadpool_limits(1):
+            while time.perf_counter() - t0 < target_s:
+                qd, kn, vn = wk.gen_decode(wl, steps)
+                kc, vc, pos, acc, _ = oracle.decode.decode_step(kc, vc, pos, acc, oracle.score.bf16_bits_to_f64(qd),
+                                                                kn, vn, t=wl.S + steps, recent=r, scale=scale,
+                                                                tau=tau, seed=wl.noise_seed)
+                steps += 1
         dt = time.perf_counter() - t0
-        threads = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
-        return {"value": steps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        return {"value": steps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle", "cpu_model": _cpu_model(),
                 "sample": f"{steps} decode steps of all {wl.Hkv} KV heads from a kept cache of the workload's rows "
-                          f"(fp64 numpy), {dt:.1f} s"}
-    if wl.causal:
-        # whole query rows of the causal oracle (head 0, from position 0 on) until the
-        # time target; the rate is scaled by the share of the layer's (row, key) pairs done
-        qh = oracle.score.bf16_bits_to_f64(q[0])
-        kg = oracle.score.bf16_bits_to_f64(k[0])
-        scale = float(np.float32(1.0 / math.sqrt(wl.D)))
-        total_pairs = wl.H * (wl.w * (wl.S - wl.w) + wl.w * (wl.w + 1) / 2)
-        pairs, i, t0 = 0, 0, time.perf_counter()
-        while i < wl.w and time.perf_counter() - t0 < target_s:
-            oracle.score.head_causal_mean(qh, kg, S=wl.S, w=wl.w, scale=scale, gumbel=wl.gumbel, seed=wl.noise_seed,
-                                          head=0, tau=tau, rows=[i])
-            pairs += wl.S - wl.w + i + 1
-            i += 1
+                          f"(fp64 numpy, one process: the steps are sequential), {dt:.1f} s"}
+    _CPU.update(wl=wl, data=data, tau=tau)
+    done, t0 = 0, time.perf_counter()
+    with mp.get_context("fork").Pool(cores, initializer=_cpu_worker_init) as pool:
+        # rounds of one unit per worker until the time target; whole rounds only
+        while time.perf_counter() - t0 < target_s:
+            done += len(pool.map(_cpu_unit, range(done, done + cores), chunksize=1))
         dt = time.perf_counter() - t0
-        threads = max([1] + [t.get("num_threads", 1) for t in threadpool_info()])
-        return {"value": wl.S * (pairs / total_pairs) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                "sample": f"{i} causal query rows of head 0 ({pairs} of the layer's {int(total_pairs)} (row, key) "
-                          f"pairs; scoring only, fp64 numpy), {dt:.1f} s"}
-    qf = oracle.score.bf16_bits_to_f64(q if wl.L == 1 else q[0])
-    kf = oracle.score.bf16_bits_to_f64(k if wl.L == 1 else k[0])
-    kraw = k if wl.L == 1 else k[0]
-    vraw = v if wl.L == 1 else v[0]
-    scale = float(np.float32(1.0 / math.sqrt(wl.D)))
-    B = wl.budget if wl.budget else wl.total_budget // wl.L
-    # whole KV heads of layer 0, cycling over the heads until the time target
-    heads, t0 = 0, time.perf_counter()
-    while True:
-        g = heads % wl.Hkv
-        imp = oracle.score.importance(qf, kf, S=wl.S, w=wl.w, scale=scale, gumbel=wl.gumbel, tau=tau,
-                                      seed=wl.noise_seed, kv_heads=[g])
-        sc = oracle.pool.pool(imp[g:g + 1], wl.pool_kernel, wl.pool_mode)[0] if wl.pool_kernel else imp[g]
-        if wl.threshold > 0:
-            idx = oracle.threshold.select_threshold(sc, S=wl.S, w=wl.w, recent=wl.recent, theta=wl.theta)
-        else:
-            idx = oracle.select.select(sc, S=wl.S, w=wl.w, recent=wl.recent, budget=B)
-        kc = oracle.compact.compact(kraw[g:g + 1], idx[None])
-        oracle.compact.compact(vraw[g:g + 1], idx[None])
-        if wl.think_value_lambda >= 0:
-            vcf = oracle.score.bf16_bits_to_f64(oracle.compact.compact(vraw[g:g + 1], idx[None]))
-            oracle.think.think_prune_value(oracle.score.bf16_bits_to_f64(kc), vcf, qf[g * wl.G:(g + 1) * wl.G],
-                                           recent=wl.recent, lam=wl.think_value_lambda, scale=scale)
-        if wl.think_lambda >= 0 and wl.think_query:
-            oracle.think.think_prune_query(oracle.score.bf16_bits_to_f64(kc), qf[g * wl.G:(g + 1) * wl.G],
-                                           recent=wl.recent, lam=wl.think_lambda)
-        elif wl.think_lambda >= 0:
-            oracle.think.think_prune(oracle.score.bf16_bits_to_f64(kc), recent=wl.recent, lam=wl.think_lambda,
-                                     p=wl.think_p)
-        heads += 1
-        if time.perf_counter() - t0 >= target_s:
-            break
-    dt = time.perf_counter() - t0
-    threads = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
-    tokens = wl.S * heads / wl.Hkv        # one layer's prompt per Hkv heads of work
+    if wl.causal:
+        # whole causal query rows (row i of every head in turn); scaled by the share of
+        # the layer's (row, key) pairs done
+        total_pairs = wl.H * (wl.w * (wl.S - wl.w) + wl.w * (wl.w + 1) / 2)
+        pairs = sum(wl.S - wl.w + _causal_row(wl, u) + 1 for u in range(done))
+        return {"value": wl.S * (pairs / total_pairs) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                "cpu_model": _cpu_model(),
+                "sample": f"{done} causal query rows ({pairs} of the layer's {int(total_pairs)} (row, key) pairs; "
+                          f"scoring only, fp64 numpy), {cores} worker processes x 1 BLAS thread, {dt:.1f} s"}
     steps = "+".join(["score"] + (["pool"] if wl.pool_kernel else [])
                      + (["threshold", "compact"] if wl.threshold > 0 else ["select", "compact"])
                      + (["think"] if wl.think_lambda >= 0 else [])
                      + (["think_value"] if wl.think_value_lambda >= 0 else []))
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{heads} KV-head passes over layer 0 ({wl.Hkv} heads per layer; {steps}, "
-                      f"fp64 numpy), {dt:.1f} s"}
+    return {"value": wl.S * done / wl.Hkv / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"{done} KV-head passes over layer 0 ({wl.Hkv} heads per layer; {steps}, fp64 numpy), "
+                      f"{cores} worker processes x 1 BLAS thread, {dt:.1f} s"}
 
 
 def main():
@@ -293,6 +338,11 @@ def main():
     else:
         qs, ks, vs = zip(*(wk.gen_layer(wl, l) for l in range(wl.L)))
         host = (np.stack(qs), np.stack(ks), np.stack(vs))
+    cpu = None
+    if not args.no_cpu:
+        # before anything touches the GPU: the oracle's worker processes are forked here
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, host, args.cpu_seconds, args.tau)
     set_bytes = sum(x.nbytes for x in host)
     copies = max(1, min(8, math.ceil(2 * MALL_BYTES / set_bytes)))
     base = [pipeline.bf16_to_device(x, dev) for x in host]
@@ -382,11 +432,6 @@ def main():
         if op:
             kk["alg_Tops"] = round(op * pl / (kk["avg_us"] / 1e6) / 1e12, 2)
         kk["avg_us"] = round(kk["avg_us"], 2)
-
-    cpu = None
-    if not args.no_cpu:
-        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, host, args.cpu_seconds, args.tau)
 
     config = {"workload": wl.name, "layers": wl.L, "q_heads": wl.H, "kv_heads": wl.Hkv, "seq_len": wl.S,
               "head_dim": wl.D, "window": wl.w, "recent": wl.recent,

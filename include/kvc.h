@@ -96,9 +96,17 @@ int kvc_think_channels(int D, double lambda);
  *              rows j in [0, S) must be readable (only j < n are used)
  *   importance fp32 [L, Hkv, n] contiguous (written in full)
  *   layer_scales: NULL, or device fp32 [L] of alpha_l (then `scale` is ignored)
- * Limits: D == 128 (else KVC_E_UNSUPPORTED); 1 <= w < S; H % Hkv == 0;
- *   G * w <= 4096; scale > 0 and finite (or every layer_scales entry, which
- *   the library cannot check); tau > 0 (may be +inf) when gumbel != 0.
+ * Errors: KVC_E_UNSUPPORTED unless D == 128; KVC_E_ARG unless L, H, Hkv,
+ *   w >= 1, S >= 2, the four strides are multiples of 8, scale > 0 and finite
+ *   (when layer_scales is NULL; the library cannot check a device array),
+ *   tau > 0 (+inf allowed, NaN rejected) when gumbel != 0, and q_obs / k are
+ *   16-byte aligned, importance 4-byte aligned; KVC_E_SHAPE unless
+ *   H % Hkv == 0, 1 <= w < S, G * w <= 65536 (G = H / Hkv), L <= 65535,
+ *   Hkv <= 65535, q_head_stride >= w*D, k_head_stride >= S*D and, for L > 1,
+ *   q_layer_stride >= H*q_head_stride and k_layer_stride >= Hkv*k_head_stride;
+ *   KVC_E_WORKSPACE if the workspace is missing, short or not 16-byte aligned.
+ *   Up to 512 (Keyformer noise: 128) of a KV head's G*w query rows are staged
+ *   on chip at a time; more rows are processed in chunks of that size.
  * Precision: bf16 products, fp32 accumulation and softmax statistics, fixed
  *   reduction order; relative error of I well under 1e-3.
  */
@@ -160,12 +168,26 @@ kvc_status kvc_score_causal(const kvc_score_args* args /* host */, const void* q
  * fewest KV entries keeping 90% of a head's attention; LMBA: mean over the
  * layer's heads) and section on ZigZag's space allocation (share of the total
  * budget proportional to LMBA, with a minimum reserved per layer).
- * Layout: importance fp32 [L, Hkv, n] contiguous, entries >= 0.  mba int32
+ * Layout: importance fp32 [L, Hkv, n] contiguous, entries >= 0 (-0.0 counts
+ *   as 0; NaN and negative entries are outside the contract).  mba int32
  *   [L, Hkv] or NULL; budgets int32 [L] (tokens per KV head, recent window
- *   included).
- * Errors: KVC_E_ARG unless 0 < mass <= 1, 0 <= floor <= capacity and
- *   L*floor <= total_budget <= L*capacity.  L <= 65536.
- * Mass sums are fp64, in a fixed order.
+ *   included).  workspace: kvc_lmba_budget_workspace_size bytes when mba is
+ *   NULL (it then holds the MBA), else unused.
+ * Errors: KVC_E_ARG unless 1 <= L <= 1024, Hkv >= 1, n >= 1, 0 < mass <= 1,
+ *   0 <= floor <= capacity, L*floor <= total_budget <= L*capacity and the
+ *   pointers are non-null and 4-byte aligned; KVC_E_SHAPE if L*Hkv > 65535,
+ *   total_budget >= 2^31 or Hkv*n >= 2^31; KVC_E_WORKSPACE if mba is NULL and
+ *   the workspace is missing or short.
+ * Arithmetic: each score x enters the MBA search as the 64-bit fixed-point
+ *   integer floor(x * 2^s), s chosen per row so that n copies of the row's
+ *   largest score fit in 62 bits; sums of these integers are exact and
+ *   order-independent (bit-reproducible).  The truncation loses less than
+ *   n * 2^-s of a row's total (about 1e-10 of its largest score at n = 16K),
+ *   so only a crossing within that margin of mass * total can resolve
+ *   differently from exact real arithmetic.  The target is ceil of the fp64
+ *   product total * mass, clamped to the total (with mass = 1 the MBA is
+ *   the number of scores whose fixed-point mass is nonzero).  The
+ *   allocation is exact int64 arithmetic.
  */
 size_t kvc_lmba_budget_workspace_size(int32_t L, int32_t Hkv, int32_t n);
 

@@ -54,6 +54,19 @@ __device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t x, uint64_t* ws
   return before + v - x;
 }
 
+// The mass a head's kept scores must reach: ceil of the fp64 product
+// total * mass (the rounding the threshold test of the MBA definition uses in
+// fp64), never more than total, and exactly total for mass = 1.  Without the
+// clamp, the rounding of total to fp64 can put the target above the total,
+// and then no bin of the radix search below reaches it.
+__device__ __forceinline__ uint64_t mass_target(uint64_t total, double mass) {
+  if (mass >= 1.0) return total;
+  const double t = ceil((double)total * mass);
+  if (!(t < 18446744073709551616.0)) return total;   // 2^64: out of range (cannot happen for mass < 1)
+  const uint64_t u = (uint64_t)t;
+  return u < total ? u : total;
+}
+
 constexpr int kMbaBins = 2048;
 constexpr int kMbaBPT = kMbaBins / kMbaThreads;   // bins per thread in the suffix scans
 
@@ -85,15 +98,18 @@ __global__ __launch_bounds__(kMbaThreads) void mba_kernel(const float* imp, int 
       kr[i] = v[j < n ? j : n - 1];   // clamped address; entries past n are never used
     }
   }
+  // -0.0 (bits 0x80000000) is a valid zero score: fold it onto +0.0 so that
+  // the raw bits of every score >= 0 are order-preserving keys
+  auto key_of = [](uint32_t b) -> uint32_t { return b == 0x80000000u ? 0u : b; };
   // f(key) over this thread's keys: j = tid + i * kMbaThreads, in order
   auto for_keys = [&](auto&& f) {
     if constexpr (kKPT > 0) {
 #pragma unroll
       for (int i = 0; i < kKPT; ++i)
-        if (tid + i * kMbaThreads < n) f(kr[i], i);
+        if (tid + i * kMbaThreads < n) f(key_of(kr[i]), i);
     } else {
 #pragma unroll 4
-      for (int j = tid; j < n; j += kMbaThreads) f(v[j], 0);
+      for (int j = tid; j < n; j += kMbaThreads) f(key_of(v[j]), 0);
     }
   };
 
@@ -143,7 +159,7 @@ __global__ __launch_bounds__(kMbaThreads) void mba_kernel(const float* imp, int 
   };
   uint64_t total;
   (void)block_excl_scan_u64(part, wsum, &total);
-  const uint64_t target = (uint64_t)ceil((double)total * mass);   // keep at least this much
+  const uint64_t target = mass_target(total, mass);   // keep at least this much (<= total)
   if (target == 0) {
     if (tid == 0) mba_out[row] = 0;
     return;
@@ -164,7 +180,11 @@ __global__ __launch_bounds__(kMbaThreads) void mba_kernel(const float* imp, int 
       hc[b] = 0u;
       hm[b] = 0ull;
     }
-    if (tid == 0) s_bin = 0u;
+    if (tid == 0) {
+      s_bin = 0u;
+      s_above_m = 0ull;
+      s_above_c = 0u;
+    }
     __syncthreads();
     for_keys([&](uint32_t k, int i) {
       const uint32_t d = k - kmin;

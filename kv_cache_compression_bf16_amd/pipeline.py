@@ -152,16 +152,18 @@ class CompressionPlan:
                                    stream=stream)
             return
         # long prompts: one call per layer, sized from the budgets on the host
-        for l, (B, idx, kc, vc) in enumerate(self.zigzag_layers()):
+        for l, (B, idx, kc, vc) in enumerate(self.zigzag_layers(stream)):
             kvc.kvc_select_topk(self.scores[l], idx, S=wl.S, w=wl.w, recent=wl.recent, budget=B,
                                 workspace=self.ws_select, stream=stream)
             kvc.kvc_compact(k[l], v[l], idx, kc, vc, S=wl.S, stream=stream)
 
-    def zigzag_layers(self):
-        """Per-layer (budget, indices, K, V) views of the ZigZag outputs; reads the
-        budgets back to the host (a synchronising copy)."""
+    def zigzag_layers(self, stream=None):
+        """Per-layer (budget, indices, K, V) views of the ZigZag outputs.  Reads the
+        budgets back to the host after synchronising ``stream`` (the one the budget
+        kernel was enqueued on; None: torch's current stream of the device)."""
         wl = self.wl
         Hkv, D = wl.Hkv, wl.D
+        (stream if stream is not None else torch.cuda.current_stream(self.device)).synchronize()
         out, off = [], 0
         for B in self.budgets.cpu().tolist():
             idx = self.indices_flat[off * Hkv:(off + B) * Hkv].view(Hkv, B)

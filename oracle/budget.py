@@ -54,11 +54,6 @@ def mba(scores, mass=0.9):
     return lo
 
 
-def layer_mba_sum(importance_layer, mass=0.9):
-    """M_l = sum over the layer's KV heads of MBA (LMBA_l = M_l / Hkv)."""
-    return int(sum(mba(row, mass) for row in importance_layer))
-
-
 def _largest_remainder(R, weights):
     """Split R integer units in proportion to integer ``weights``:
     q_l = floor(R*w_l/W) plus one unit each for the R - sum(q) layers with the
@@ -101,7 +96,15 @@ def allocate(layer_sums, total_budget, floor, capacity):
 
 
 def zigzag_budgets(importance_model, *, total_budget, floor, capacity, mass=0.9):
-    """importance_model: [L, Hkv, n].  Returns (mba [L, Hkv] ints, budgets [L] ints)."""
-    mbas = [[mba(row, mass) for row in layer] for layer in importance_model]
-    sums = [sum(r) for r in mbas]
+    """importance_model: [L, Hkv, n] (layer, KV head, prefix token).
+
+    MBA per (layer, head); M_l = sum over the layer's heads of MBA (LMBA_l =
+    M_l / Hkv; the 1/Hkv cancels in the proportional share, so the exact
+    integer sum is what the allocation weighs).  Returns (mba [L][Hkv] ints,
+    budgets [L] ints)."""
+    imp = np.asarray(importance_model, dtype=np.float64)
+    if imp.ndim != 3:
+        raise ValueError("importance must be [L, Hkv, n]")
+    mbas = [[mba(imp[l, g], mass) for g in range(imp.shape[1])] for l in range(imp.shape[0])]
+    sums = [sum(mbas[l]) for l in range(imp.shape[0])]
     return mbas, allocate(sums, total_budget, floor, capacity)

@@ -57,6 +57,9 @@ F32_ALPHA = float(np.float32(1 / math.sqrt(128)))
     (4, 4, 1, 300),        # single query row
     (2, 1, 33, 290),       # G=2, 66 rows, n=257: one key past a block
     (32, 8, 128, 4096 + 77),
+    (64, 8, 128, 2048 + 300),   # G*w = 1024: two 512-row chunks re-staged for every unit
+    (32, 4, 80, 1500),          # G*w = 640: a 512-row chunk plus a ragged 128-row one
+    (16, 1, 130, 1200),         # G*w = 2080: four full chunks and a 32-row tail, 2 rows past a block
 ])
 def test_importance_matches_oracle(H, Hkv, w, S):
     qb, kb = _draw(H, Hkv, w, S, seed=H * 1000 + S)

@@ -224,6 +224,43 @@ def test_budget_mixed_magnitudes():
     assert bud.tolist() == ref_b
 
 
+@pytest.mark.parametrize("mass", [1.0, 0.5])
+def test_budgets_other_mass_fractions(mass):
+    # mass = 1 needs every score whose fixed-point mass is nonzero (the target is the exact
+    # total); mass = 0.5 crosses well inside the row
+    if mass == 1.0:
+        # well-conditioned rows: every nonzero score is far above both the fixed-point
+        # resolution and the fp64 rounding of the oracle's total, and some scores are 0
+        rng = np.random.default_rng(11)
+        imp = rng.uniform(0.1, 1.0, size=(4, 3, 3000))
+        imp[rng.random(imp.shape) < 0.2] = 0.0
+        imp = (imp / imp.sum(axis=-1, keepdims=True)).astype(np.float32)
+    else:
+        imp = _rows(4, 3, 3000, 12)
+    mba, bud = _gpu_budget(imp, total_budget=4 * 1200, floor_per_layer=64, capacity=3000, mass=mass)
+    ref_mba, ref_b = oracle.budget.zigzag_budgets(imp.astype(np.float64), total_budget=4 * 1200, floor=64,
+                                                  capacity=3000, mass=mass)
+    assert np.array_equal(mba, np.array(ref_mba))
+    assert bud.tolist() == ref_b
+    if mass == 1.0:
+        assert np.array_equal(mba, (imp > 0).sum(axis=-1))
+
+
+def test_budget_negative_zero_is_zero():
+    # -0.0 is a zero score, not the largest key
+    n = 500
+    imp = _rows(2, 2, n, 13)
+    imp[:, :, ::7] = np.float32(-0.0)
+    imp[1, 1, :] = np.float32(-0.0)
+    imp[1, 1, 42] = 1.0
+    mba, bud = _gpu_budget(imp, total_budget=2 * 200, floor_per_layer=10, capacity=n)
+    ref_mba, ref_b = oracle.budget.zigzag_budgets(imp.astype(np.float64), total_budget=2 * 200, floor=10,
+                                                  capacity=n)
+    assert np.array_equal(mba, np.array(ref_mba))
+    assert mba[1, 1] == 1
+    assert bud.tolist() == ref_b
+
+
 def test_budget_equal_lmba_is_uniform():
     imp = np.tile(_rows(1, 4, 2048, 9), (6, 1, 1))
     _, bud = _gpu_budget(imp, total_budget=6 * 500, floor_per_layer=64, capacity=2048)

@@ -230,18 +230,25 @@ def test_keyformer_mha32_s8192_decode():
                                                         f64(qd), kn, vn, t=t, recent=wl.recent, scale=scale,
                                                         tau=wl.taus[0], seed=wl.noise_seed)
         gk, gv, gp, ga = bits_of(plan.kc), bits_of(plan.vc), plan.pos.cpu().numpy(), plan.acc.cpu().numpy()
+        G = wl.G
         for g in range(wl.Hkv):
             if ev[g] != rev[g]:
-                a = ra[g].copy()
-                a[rev[g]] = np.nan
-                assert state[2][g, ev[g]] <= t - wl.recent
+                # a tie: the oracle's accumulated scores (prior score + this step's score,
+                # fp64) of the GPU's evicted slot and of the oracle's are within 1e-5
+                keys = np.concatenate([f64(state[0][g]), f64(kn[g])[None]])
+                stp = oracle.decode.step_scores(keys, np.concatenate([state[2][g], [t]]),
+                                                f64(qd[g * G:(g + 1) * G]), t=t, heads=range(g * G, (g + 1) * G),
+                                                scale=scale, tau=wl.taus[0], seed=wl.noise_seed)
+                a = state[3][g].astype(np.float64) + stp[:wl.budget]
+                assert state[2][g, ev[g]] <= t - wl.recent, "a recent token was evicted"
+                assert abs(a[ev[g]] - a[rev[g]]) <= 1e-5 * max(a[rev[g]], 1e-30), \
+                    f"step {s} head {g}: evicted slot {ev[g]} vs {rev[g]} outside a tie"
                 kinds.append("tie")
                 continue
             kinds.append("exact")
             assert np.array_equal(gp[g], rp[g]) and np.array_equal(gk[g], rk[g]) and np.array_equal(gv[g], rv[g])
             assert np.allclose(ga[g], ra[g], rtol=2e-6, atol=1e-9)
     print("evictions:", {k_: kinds.count(k_) for k_ in set(kinds)})
-    assert kinds.count("exact") >= 0.9 * len(kinds)
 
 
 def test_gqa32x8_s32768_thr2():
@@ -313,6 +320,42 @@ def test_zigzag_l32_s16384():
         ref_idx = oracle.select.select(ref, S=wl.S, w=wl.w, recent=wl.recent, budget=budgets[l])
         check_selection(layers[l][1].cpu().numpy()[g], ref, ref_idx, S=wl.S, w=wl.w,
                         recent=wl.recent, budget=budgets[l])
+
+
+def test_zigzag_long_prompt_per_layer_path_on_a_side_stream():
+    # more than 32768 candidates per head: the pipeline selects and compacts one layer
+    # at a time, sized from the budgets read back on the host; everything runs on a
+    # non-default stream, which the host read must wait for
+    wl = wk.WORKLOADS["zigzag_l32_s16384"].with_(name="zigzag_l2_s33000", L=2, H=2, Hkv=2, S=33000, w=64,
+                                                 recent=64, total_budget=2 * 4000, floor=128)
+    assert wl.n_candidates > 32768
+    qs, ks, vs = zip(*(wk.gen_layer(wl, l) for l in range(wl.L)))
+    q, k, v = np.stack(qs), np.stack(ks), np.stack(vs)
+    scales = wk.layer_scales(wl)
+    side = torch.cuda.Stream(device=dev())
+    with torch.cuda.stream(side):
+        qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+        ls = torch.from_numpy(scales).to(dev())
+    side.synchronize()
+    plan = pipeline.CompressionPlan(wl, dev())
+    plan.run(qd, kd, vd, layer_scales=ls, stream=side)
+    side.synchronize()
+    imp = plan.importance.cpu().numpy()
+    assert np.allclose(imp.astype(np.float64).sum(axis=-1), 1.0, rtol=1e-5, atol=0)
+    ref_mba, ref_b = oracle.budget.zigzag_budgets(imp.astype(np.float64), total_budget=wl.total_budget,
+                                                  floor=wl.floor, capacity=wl.capacity, mass=wl.mass)
+    assert np.array_equal(plan.mba.cpu().numpy(), np.array(ref_mba))
+    layers = plan.zigzag_layers(side)
+    assert [B for B, _, _, _ in layers] == ref_b
+    for l, (B, idx_t, kc_t, vc_t) in enumerate(layers):
+        idx = idx_t.cpu().numpy()
+        ref_idx = oracle.select.select_heads(imp[l].astype(np.float64), S=wl.S, w=wl.w, recent=wl.recent,
+                                             budget=B)
+        assert np.array_equal(idx, ref_idx), f"layer {l}"
+        assert np.array_equal(bits_of(kc_t), oracle.compact.compact(k[l], idx))
+        assert np.array_equal(bits_of(vc_t), oracle.compact.compact(v[l], idx))
+    ref = _oracle_imp(wl, q[1], k[1], scales[1], [1])[1]
+    check_importance(imp[1, 1][None], ref[None], 1, "layer 1 head 1")
 
 
 # ---------------------------------------------------------------- determinism

@@ -119,3 +119,61 @@ def test_infeasible_budget_raises():
         budget.allocate([1, 1], total_budget=5, floor=3, capacity=10)
     with pytest.raises(ValueError):
         budget.allocate([1, 1], total_budget=30, floor=3, capacity=10)
+
+
+# ---- the composition the GPU budgets are compared against -----------------
+def _hand_model():
+    """[L=3, Hkv=2, n=7] with MBA fixed by construction (ZigZagKV page, new
+    observations section: MBA is the fewest entries holding 90% of a head's
+    attention): one-hot -> 1, two equal spikes -> 2 (one spike holds only 50%),
+    uniform over 7 -> ceil(0.9 * 7) = 7."""
+    n = 7
+    one_hot = np.zeros(n); one_hot[4] = 1.0
+    two_hot = np.zeros(n); two_hot[[1, 5]] = 0.5
+    uniform = np.full(n, 1.0 / n)
+    model = np.stack([
+        np.stack([one_hot, two_hot]),     # layer 0: MBA (1, 2) -> M_0 = 3
+        np.stack([uniform, one_hot]),     # layer 1: MBA (7, 1) -> M_1 = 8
+        np.stack([uniform, two_hot]),     # layer 2: MBA (7, 2) -> M_2 = 9
+    ])
+    return model
+
+
+def test_zigzag_budgets_hand_worked_exact_shares():
+    # F = 2, R = 26 - 3*2 = 20, sum M = 20: shares are exactly M_l -> B = F + (3, 8, 9)
+    mbas, B = budget.zigzag_budgets(_hand_model(), total_budget=26, floor=2, capacity=100, mass=MASS)
+    assert mbas == [[1, 2], [7, 1], [7, 2]]
+    assert B == [5, 10, 11]
+
+
+def test_zigzag_budgets_hand_worked_largest_remainder():
+    # F = 2, R = 19 - 6 = 13, sum M = 20: 13*M_l = 39, 104, 117 -> q = (1, 5, 5),
+    # remainders (19, 4, 17) mod 20, two units left -> layers 0 and 2: q = (2, 5, 6)
+    mbas, B = budget.zigzag_budgets(_hand_model(), total_budget=19, floor=2, capacity=100, mass=MASS)
+    assert B == [4, 7, 8]
+    # a per-layer MEAN truncated to an integer (1, 4, 4) would give (2, 9, 9) + F = (4, 11, 11)
+    # at R = 20; a transposed [Hkv, L] reading would weigh the two heads, not the three layers
+    _, B20 = budget.zigzag_budgets(_hand_model(), total_budget=26, floor=2, capacity=100, mass=MASS)
+    assert B20 != [4, 11, 11]
+
+
+def test_zigzag_budgets_layer_order_and_head_grouping():
+    # permuting the layers permutes the budgets; permuting heads inside a layer changes nothing
+    model = _hand_model()
+    perm = [2, 0, 1]
+    _, B = budget.zigzag_budgets(model, total_budget=26, floor=2, capacity=100, mass=MASS)
+    _, Bp = budget.zigzag_budgets(model[perm], total_budget=26, floor=2, capacity=100, mass=MASS)
+    assert Bp == [B[l] for l in perm]
+    _, Bh = budget.zigzag_budgets(model[:, ::-1], total_budget=26, floor=2, capacity=100, mass=MASS)
+    assert Bh == B
+    # moving a uniform head from layer 2 into layer 0 moves budget with it
+    swapped = model.copy()
+    swapped[0, 1], swapped[2, 0] = model[2, 0], model[0, 1]   # layer 0: MBA (1, 7); layer 2: (2, 2)
+    mbas, Bs = budget.zigzag_budgets(swapped, total_budget=26, floor=2, capacity=100, mass=MASS)
+    assert mbas == [[1, 7], [7, 1], [2, 2]]
+    assert Bs == [10, 10, 6]
+
+
+def test_zigzag_budgets_rejects_wrong_rank():
+    with pytest.raises(ValueError):
+        budget.zigzag_budgets(np.ones((4, 5)), total_budget=8, floor=1, capacity=5)

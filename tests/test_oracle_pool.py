@@ -45,3 +45,33 @@ def test_closed_forms():
 def test_rejects_even_kernel():
     with pytest.raises(ValueError):
         oracle.pool.pool_row(np.zeros(4), 4, AVG)
+
+
+@pytest.mark.parametrize("mode", [AVG, MAX])
+def test_pool_multi_row_keeps_each_row_apart(mode):
+    # importance [2, 3, n]: row (a, b) holds one spike of height (a+1)(b+1) at its own
+    # position p = 5a + 7b + 3, so each pooled row must show that row's plateau
+    # [p - h, p + h] at that row's height (ZigZagKV page, SnapKV section: pooling runs
+    # along the keys of each head separately), nothing else, and the shape is kept.
+    n, k = 40, 5
+    h = k // 2
+    x = np.zeros((2, 3, n))
+    for a in range(2):
+        for b in range(3):
+            x[a, b, 5 * a + 7 * b + 3] = (a + 1) * (b + 1)
+    out = oracle.pool.pool(x, k, mode)
+    assert out.shape == x.shape
+    for a in range(2):
+        for b in range(3):
+            p, v = 5 * a + 7 * b + 3, (a + 1) * (b + 1)
+            want = np.zeros(n)
+            want[p - h:p + h + 1] = v / k if mode == AVG else v
+            assert np.allclose(out[a, b], want, rtol=0, atol=1e-15), (a, b)
+
+
+def test_pool_single_row_input_stays_one_dimensional():
+    x = np.arange(9, dtype=np.float64)
+    out = oracle.pool.pool(x, 3, AVG)
+    assert out.shape == (9,)
+    assert np.allclose(out[1:-1], x[1:-1])          # a linear ramp is kept by a centred box
+    assert np.isclose(out[0], (0 + 1) / 3) and np.isclose(out[-1], (7 + 8) / 3)

@@ -87,3 +87,30 @@ def test_compact_gathers_rows():
     for g in range(Hkv):
         assert np.all(out[g, :, 0] == g * 1000 + idx[g])
         assert np.all(out[g] == out[g, :, :1])
+
+
+def test_select_heads_per_row():
+    # head g scores its own candidates (4g + 1, 4g + 2) highest, so with k_top = 2 each
+    # row of the result must be exactly those two plus the recent window, in that head's
+    # row (ZigZagKV page, SnapKV section: per-head top-K plus the last window).
+    Hkv, S, w, r = 5, 40, 6, 3
+    c = min(S - w, S - r)
+    imp = np.full((Hkv, S - w), 0.01)
+    for g in range(Hkv):
+        imp[g, 4 * g + 1] = 1.0 + g
+        imp[g, 4 * g + 2] = 0.5 + g
+    out = select.select_heads(imp, S=S, w=w, recent=r, budget=2 + r)
+    assert out.shape == (Hkv, 2 + r)
+    for g in range(Hkv):
+        assert out[g].tolist() == [4 * g + 1, 4 * g + 2, S - 3, S - 2, S - 1], g
+    assert c == S - w
+
+
+def test_select_heads_rows_are_independent():
+    # reversing the heads reverses the rows of the result
+    rng = np.random.default_rng(5)
+    imp = rng.exponential(size=(4, 300))
+    a = select.select_heads(imp, S=340, w=40, recent=16, budget=80)
+    b = select.select_heads(imp[::-1], S=340, w=40, recent=16, budget=80)
+    assert np.array_equal(a[::-1], b)
+    assert not np.array_equal(a[0], a[1])
