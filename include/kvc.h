@@ -135,6 +135,27 @@ kvc_status kvc_score(const kvc_score_args* args /* host */, const void* q_obs, c
                      float* importance, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kvc_score_noalloc: kvc_score for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, kernels and results as kvc_score (bit-identical
+ * importance), but the workspace is the library's static per-device scratch:
+ * kvc_score_noalloc_max_workspace() bytes (16 MiB), held by every device the
+ * library runs on until the process ends.  Neither this call nor its kernels
+ * allocate or free memory.
+ * Errors: as kvc_score; KVC_E_WORKSPACE, before any device call, when
+ *   kvc_score_workspace_size(args) exceeds the scratch; KVC_E_DEVICE if the
+ *   scratch address of the current device cannot be obtained.
+ * Concurrency: all calls on one device share its scratch, which keeps the last
+ *   call's contents (every byte a call reads it has written first).  Calls
+ *   that overlap in time on one device -- other streams, other host threads --
+ *   race and corrupt each other's results; serialise them.
+ */
+size_t kvc_score_noalloc_max_workspace(void);
+
+kvc_status kvc_score_noalloc(const kvc_score_args* args /* host */, const void* q_obs, const void* k,
+                             float* importance, void* stream);
+
+/*
  * kvc_score_causal: Keyformer's other reading of its prompt phase, a full
  * (causal) attention pass.  Window row i of query head h sits at position
  * P = S - w + i and sees the keys j <= P: x = alpha <q, k_j> (+ noise,

@@ -36,10 +36,19 @@
 //    fully used.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
 #include "philox.h"
+
+// Scratch of kvc_score_noalloc: the scoring workspace (row-statistics partials
+// and row constants) for callers that cannot allocate.  Every device the
+// library runs on holds one copy, at its own address, until the process ends.
+// Host code never passes this name to a kernel: it is a host-side stand-in;
+// the device address comes from hipGetSymbolAddress (score_scratch_ptr).
+static constexpr size_t kScoreScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kScoreScratchBytes];
 
 
 namespace kvc {
@@ -743,3 +752,42 @@ kvc_status score_rowc(const uint16_t* q, int64_t q_hs, const uint16_t* k, int64_
 }
 
 }  // namespace kvc
+
+namespace kvc {
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up once per
+// device (with that device current) and kept.
+kvc_status score_scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return KVC_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVC_E_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVC_OK;
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" size_t kvc_score_noalloc_max_workspace(void) { return kScoreScratchBytes; }
+
+extern "C" kvc_status kvc_score_noalloc(const kvc_score_args* a, const void* q_obs, const void* k, float* importance,
+                                        void* stream) {
+  kvc::Plan pl;
+  kvc_status st = kvc::plan(a, &pl);
+  if (st != KVC_OK) return st;
+  if (pl.total > kScoreScratchBytes) return KVC_E_WORKSPACE;   // checked before any device call
+  void* ws = nullptr;
+  st = kvc::score_scratch_ptr(&ws);
+  if (st != KVC_OK) return st;
+  return kvc::score_entry(a, q_obs, k, importance, ws, kScoreScratchBytes, stream, false);
+}

@@ -50,6 +50,8 @@ def _load():
         "kvc_think_channels": (ctypes.c_int, [ctypes.c_int, F64]),
         "kvc_score_workspace_size": (SZ, [ctypes.POINTER(ScoreArgs)]),
         "kvc_score": (ctypes.c_int, [ctypes.POINTER(ScoreArgs), P, P, P, P, SZ, P]),
+        "kvc_score_noalloc_max_workspace": (SZ, []),
+        "kvc_score_noalloc": (ctypes.c_int, [ctypes.POINTER(ScoreArgs), P, P, P, P]),
         "kvc_score_causal_workspace_size": (SZ, [ctypes.POINTER(ScoreArgs)]),
         "kvc_score_causal": (ctypes.c_int, [ctypes.POINTER(ScoreArgs), P, P, P, P, SZ, P]),
         "kvc_lmba_budget_workspace_size": (SZ, [I32, I32, I32]),
@@ -177,6 +179,24 @@ def kvc_score(q_obs, k, importance, *, w, S, scale=None, layer_scales=None, gumb
     ws, nbytes = _workspace(_lib.kvc_score_workspace_size(ctypes.byref(a)), k.device, workspace)
     _check(_lib.kvc_score(ctypes.byref(a), _ptr(q_obs), _ptr(k), _ptr(importance), _ptr(ws), nbytes,
                           _stream(stream, k.device)), "kvc_score")
+    return importance
+
+
+def kvc_score_noalloc(q_obs, k, importance, *, w, S, scale=None, layer_scales=None, gumbel=False, tau=1.0,
+                      seed=0, stream=None):
+    """kvc_score with the library's per-device static scratch as its workspace (no
+    device allocation by the library or here); calls that overlap on one device race."""
+    _bf16(q_obs, "q_obs")
+    _bf16(k, "k")
+    if layer_scales is not None and (layer_scales.dtype != torch.float32 or not layer_scales.is_cuda):
+        raise TypeError("layer_scales must be a float32 GPU tensor")
+    a = score_args(q_obs, k, w=w, S=S, scale=scale, layer_scales=layer_scales, gumbel=gumbel, tau=tau,
+                   seed=seed)
+    if importance.dtype != torch.float32 or not importance.is_contiguous() \
+            or importance.numel() != a.L * a.Hkv * (S - w):
+        raise ValueError("importance must be contiguous float32 with L*Hkv*(S-w) elements")
+    _check(_lib.kvc_score_noalloc(ctypes.byref(a), _ptr(q_obs), _ptr(k), _ptr(importance),
+                                  _stream(stream, k.device)), "kvc_score_noalloc")
     return importance
 
 
