@@ -34,6 +34,7 @@
 //  * Keyformer noise: lane values come in groups of 4 consecutive, 4-aligned
 //    keys, which is exactly one Philox4x32-10 block, so every Philox call is
 //    fully used.
+#include <limits.h>
 #include <math.h>
 
 #include <mutex>
@@ -102,7 +103,22 @@ struct ScoreParams {
   int L, Hkv, G, w, S, n, R, nblk, chunk_rows;
   int causal_unit;   // causal scoring: keys per unit (row r sees units b <= pos(r) / causal_unit); else 0
   int fuse_rowc;     // pass 2 folds the partials into the row constants itself (no combine launch)
+  int seg_grid;      // > 0: pass 1 wrote one partial per (head, workgroup segment) and ran on
+                     // this many workgroups (score_pass_seg); 0: one partial per (head, unit)
 };
+
+// Contiguous unit ranges over a grid of `grid` workgroups: the workgroup that
+// owns unit u (every workgroup owns per or per + 1 consecutive units).
+__host__ __device__ inline int unit_owner(int u, int total, int grid) {
+  const int per = total / grid, extra = total % grid;
+  const int big = extra * (per + 1);
+  return u < big ? u / (per + 1) : extra + (u - big) / per;
+}
+// Partials of head h in segment mode: one per workgroup whose range meets the
+// head's units [h*nblk, (h+1)*nblk), indexed from the first of them.
+__host__ __device__ inline int head_segments(int h, int nblk, int total, int grid) {
+  return unit_owner((h + 1) * nblk - 1, total, grid) - unit_owner(h * nblk, total, grid) + 1;
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -481,6 +497,338 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
   }
 }
 
+// ---- window passes for 256 < G*w <= 512: statistics kept per segment -------
+//
+// The same tiling as score_pass's 8-wave shape (8 waves x 2 tiles of 32 keys,
+// K in registers, the head's rows staged once in LDS), with three changes:
+//  * Pass 1 keeps each lane's (max, sum) per query block across all of the
+//    workgroup's units of a head and folds them once per head segment (not
+//    once per unit), with a lazy reference: a block's exponentials are taken
+//    against the row's running maximum; only when no maximum exists yet, or
+//    the block would overflow it (a key far above it), is the block's own
+//    maximum taken and the sum rescaled.  Partials are indexed by workgroup
+//    segment (seg_grid mode), so a head has as many as workgroups meet it.
+//  * Pass 2 folds those few partials into the row constants while staging
+//    the rows, so no combine kernel runs between the passes.
+//  * The next unit's key tiles that do not fit a prefetch register set are
+//    loaded straight into the key registers once the last block's MFMAs have
+//    read them, and the query fragments of the next block are read during
+//    the current block's exponentials.
+// (A barrier-synchronised ping-pong of the two waves of each SIMD -- one in
+// its MFMAs while the other does exponentials -- measured slower than
+// leaving the waves free.)
+
+// f(integral_constant<int, Q>) for Q = I .. N-1, unrolled at compile time
+// (register arrays indexed by Q stay in registers whatever the body's size).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <bool kPass2, int kPF>
+__global__ __launch_bounds__(512, 1) void score_pass_seg(ScoreParams p) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int kW = 8, kT = 2, kCB = 16, kThreads = kW * kWave;
+  constexpr int kKeysPerWave = 32 * kT, kKeysPerUnit = kKeysPerWave * kW, kFoldBlocks = 4;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hb = lane >> 5, col = lane & 31;
+  const int rows_alloc = p.chunk_rows;   // >= R: one chunk
+  const int nb = (p.R + 31) / 32;
+  float* rcs = reinterpret_cast<float*>(lds + (size_t)rows_alloc * kRowPitch);
+  float2* fold = reinterpret_cast<float2*>(lds + (size_t)rows_alloc * kRowPitch);
+
+  const float inv_w = 1.0f / (float)p.w;
+  auto split_row = [&](int r, int& hh, int& ii) {
+    hh = (int)((float)r * inv_w);
+    ii = r - hh * p.w;
+    if (ii < 0) { --hh; ii += p.w; }
+    if (ii >= p.w) { ++hh; ii -= p.w; }
+  };
+  const int heads = p.L * p.Hkv;
+  const int total = heads * p.nblk;
+  const int per = total / (int)gridDim.x, extra = total % (int)gridDim.x;
+  const int u_first = (int)blockIdx.x * per + min((int)blockIdx.x, extra);
+  const int n_units = per + ((int)blockIdx.x < extra ? 1 : 0);
+  // pass 2 walks its range backwards: its first keys are the ones pass 1 read last
+  auto unit_at = [&](int it) { return kPass2 ? u_first + n_units - 1 - it : u_first + it; };
+
+  auto load_tiles = [&](int u, int t0, auto n_c, bf16x8 (*dst)[8]) {
+    constexpr int kN = decltype(n_c)::value;
+    const int head = u / p.nblk, blk = u - head * p.nblk;
+    const int layer = head / p.Hkv, g = head - layer * p.Hkv;
+    const uint16_t* kb = p.k + layer * p.k_ls + g * p.k_hs;
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int j = min(blk * kKeysPerUnit + wave * kKeysPerWave + (t0 + i) * 32 + col, p.n - 1);   // clamp; masked
+      const bf16x8* row = reinterpret_cast<const bf16x8*>(kb + (int64_t)j * kD);
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) dst[i][s2] = row[2 * s2 + hb];
+    }
+  };
+  bf16x8 kf[kT][8];
+  bf16x8 kn[kPF > 0 ? kPF : 1][8];
+  bf16x8 qf[8];
+  auto read_q = [&](int qb) {
+    const char* qsb = lds + (qb * 32 + col) * kRowPitch + hb * 16;
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) qf[s2] = *reinterpret_cast<const bf16x8*>(qsb + 32 * s2);
+  };
+  auto mfma_block = [&](f32x16 (&acc)[kT]) {
+#pragma unroll
+    for (int t = 0; t < kT; ++t) acc[t] = f32x16{};
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+#pragma unroll
+      for (int t = 0; t < kT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s2], qf[s2], acc[t], 0, 0, 0);
+  };
+
+  // stage the head's rows (zero rows past R) and, in pass 2, its row constants
+  auto stage = [&](int head) {
+    const int layer = head / p.Hkv, g = head - layer * p.Hkv;
+    const uint16_t* qg = p.q + layer * p.q_ls + (int64_t)g * p.G * p.q_hs;
+    const int nrows = nb * 32, tot = nrows * 16;
+    for (int base = 0; base < tot; base += 8 * kThreads) {
+      u32x4 v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = base + e * kThreads + tid;
+        const int r = min(i >> 4, p.R - 1);
+        int hh, ii;
+        split_row(r, hh, ii);
+        v[e] = *reinterpret_cast<const u32x4*>(qg + hh * p.q_hs + (int64_t)ii * kD + (i & 15) * 8);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = base + e * kThreads + tid;
+        if (i < tot) *reinterpret_cast<u32x4*>(lds + (i >> 4) * kRowPitch + (i & 15) * 16) =
+            (i >> 4) < p.R ? v[e] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (kPass2) {
+      const int64_t head_row0 = (int64_t)head * p.R;
+      if (!p.fuse_rowc) {
+        for (int i = tid; i < nrows; i += kThreads) rcs[i] = i < p.R ? p.rowc[head_row0 + i] : INFINITY;
+      } else {
+        // rowc = m + log2(sum_s l_s 2^(m_s - m)) over the head's segments, one
+        // thread per row, every segment's load in flight at once (<= 32)
+        const int nseg = head_segments(head, p.nblk, total, p.seg_grid);
+        for (int i = tid; i < nrows; i += kThreads) {
+          const int r = min(i, p.R - 1);
+          const float2* pp = p.part + head_row0 * p.nblk + r;
+          float2 a[kFuseRowcUnits];
+#pragma unroll
+          for (int e = 0; e < kFuseRowcUnits; ++e) a[e] = pp[(int64_t)min(e, nseg - 1) * p.R];
+          float m = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < kFuseRowcUnits; ++e) m = fmaxf(m, e < nseg ? a[e].x : -INFINITY);
+          const float ms = (m == -INFINITY) ? 0.f : m;
+          float l = 0.f;
+#pragma unroll
+          for (int e = 0; e < kFuseRowcUnits; ++e) l += e < nseg ? a[e].y * fast_exp2(a[e].x - ms) : 0.f;
+          rcs[i] = (i < p.R && l > 0.f) ? m + log2f(l) : INFINITY;
+        }
+      }
+    }
+  };
+
+  float2 st[kCB];
+  f32x16 colacc[kT];
+  int cur = -1;
+  float cc = 0.f;
+  // pass 1: fold each lane's per-block (max, sum) over the 2*kW half-waves of
+  // every row, kFoldBlocks query blocks at a time through LDS, in a fixed order
+  auto flush = [&](int head) {
+    const int seg = (int)blockIdx.x - unit_owner(head * p.nblk, total, (int)gridDim.x);
+    const int64_t base = ((int64_t)head * p.nblk + seg) * p.R;
+#pragma unroll
+    for (int f0 = 0; f0 < kCB; f0 += kFoldBlocks) {
+      if (f0 < nb) {
+#pragma unroll
+        for (int qq = 0; qq < kFoldBlocks; ++qq) fold[((wave * kFoldBlocks + qq) * 32 + col) * 2 + hb] = st[f0 + qq];
+        __syncthreads();
+        {
+          constexpr int kTPR = kThreads / (kFoldBlocks * 32);
+          constexpr int kPer = 2 * kW / kTPR;
+          const int i = tid / kTPR, j = tid % kTPR;
+          const int r = f0 * 32 + i;
+          float2 e[kPer];
+#pragma unroll
+          for (int k = 0; k < kPer; ++k) {
+            const int v = j * kPer + k;
+            e[k] = fold[(v >> 1) * kFoldBlocks * 64 + i * 2 + (v & 1)];
+          }
+          float m = e[0].x;
+#pragma unroll
+          for (int k = 1; k < kPer; ++k) m = fmaxf(m, e[k].x);
+          const float ms = (m == -INFINITY) ? 0.f : m;
+          float l = 0.f;
+#pragma unroll
+          for (int k = 0; k < kPer; ++k) l += e[k].y * fast_exp2(e[k].x - ms);
+#pragma unroll
+          for (int o = 1; o < kTPR; o <<= 1) {
+            const float mo = __shfl_xor(m, o), lo = __shfl_xor(l, o);
+            const float m2 = fmaxf(m, mo);
+            const float m2s = (m2 == -INFINITY) ? 0.f : m2;
+            l = l * fast_exp2(m - m2s) + lo * fast_exp2(mo - m2s);
+            m = m2;
+          }
+          if (j == 0 && r < p.R) p.part[base + r] = float2{m, l};
+        }
+        __syncthreads();
+      }
+    }
+  };
+  // pass 1, one block: add the lane's exponentials against the running
+  // reference st.x (log2 units); take the block maximum only where no
+  // reference exists yet or the block would overflow it
+  auto stats = [&](bool clean, f32x16 (&acc)[kT], int key0, int r, float2& s) {
+    if (!clean) {
+      // wave-uniform branch: keys past the prefix and rows past R take -inf.
+      // Element (t, e) is key key0 + 4hb + off(t, e) with a constant offset;
+      // it is masked when off >= lim (every element of a row past R)
+      const int lim = r < p.R ? p.n - key0 - 4 * hb : INT_MIN;
+#pragma unroll
+      for (int t = 0; t < kT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (32 * t + 8 * (e >> 2) + (e & 3) >= lim) acc[t][e] = -INFINITY;
+    }
+    const float mref = s.x;
+    const float mrs = (mref == -INFINITY) ? 0.f : mref;
+    float l = 0.f;
+    bool redo = mref == -INFINITY;   // no reference yet: take the block maximum directly
+    if (!__ballot(redo)) {
+#pragma unroll
+      for (int t = 0; t < kT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) l += fast_exp2(fmaf(acc[t][e], cc, -mrs));
+      redo = !(l < 0x1p64f);   // a key far above the reference: rescale
+    }
+    if (__ballot(redo)) {
+      if (redo) {
+        float mx = acc[0][0];
+#pragma unroll
+        for (int t = 0; t < kT; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[t][e]);
+        const float m2 = fmaxf(mref, mx * cc);
+        const float m2s = (m2 == -INFINITY) ? 0.f : m2;
+        l = 0.f;
+#pragma unroll
+        for (int t = 0; t < kT; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) l += fast_exp2(fmaf(acc[t][e], cc, -m2s));
+        s.y *= fast_exp2(mrs - m2s);   // s.y = 0 while no reference exists
+        s.x = m2;
+      }
+    }
+    s.y += l;
+  };
+
+  if (n_units > 0) load_tiles(unit_at(0), 0, std::integral_constant<int, kT>{}, kf);
+#pragma unroll 1
+  for (int it = 0; it < n_units; ++it) {
+    const int u = unit_at(it);
+    const int head = u / p.nblk, blk = u - head * p.nblk;
+    const int layer = head / p.Hkv;
+    if (head != cur) {
+      if (!kPass2 && cur >= 0) flush(cur);
+      __syncthreads();   // every wave is done with the previous rows
+      stage(head);
+      __syncthreads();
+      cur = head;
+      const float alpha = p.layer_scales ? p.layer_scales[layer] : p.scale;
+      cc = alpha * kLog2e;
+      if (!kPass2) {
+#pragma unroll
+        for (int qb = 0; qb < kCB; ++qb) st[qb] = float2{-INFINITY, 0.f};
+      }
+    }
+    if (it != 0 && kPF > 0) {
+#pragma unroll
+      for (int t = 0; t < kPF; ++t)
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) kf[t][s2] = kn[t][s2];
+    }
+    // this unit's tiles are in (tiles [kPF, kT) were loaded into kf during the
+    // previous unit's last block); the next unit's first kPF tiles go in
+    // flight (unconditionally -- the last unit reloads itself -- so nothing
+    // below waits on them)
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    if (kPF > 0)
+      load_tiles(unit_at(min(it + 1, n_units - 1)), 0, std::integral_constant<int, (kPF > 0 ? kPF : 1)>{}, kn);
+    // once the last block's MFMAs have read this unit's tiles, tiles [kPF, kT)
+    // of the next unit are loaded into their registers (the next unit's wait
+    // above covers them)
+    auto tail_prefetch = [&] {
+      if (it + 1 < n_units) load_tiles(unit_at(it + 1), kPF, std::integral_constant<int, kT - kPF>{}, kf + kPF);
+    };
+    const int key0 = blk * kKeysPerUnit + wave * kKeysPerWave;
+    const bool wave_full = key0 + kKeysPerWave <= p.n;
+    read_q(0);
+    if (!kPass2) {
+      const bool clean = wave_full && nb * 32 == p.R;
+      static_for<0, kCB>([&](auto qb_c) {
+        constexpr int qb = decltype(qb_c)::value;
+        if (qb < nb) {
+          f32x16 acc[kT];
+          mfma_block(acc);
+          if (qb + 1 < nb) read_q(qb + 1);
+          if (qb == kCB - 1) tail_prefetch();
+          stats(clean, acc, key0, qb * 32 + col, st[qb]);
+        }
+      });
+      if (nb < kCB) tail_prefetch();
+    } else {
+#pragma unroll
+      for (int t = 0; t < kT; ++t) colacc[t] = f32x16{};
+      // the last block is peeled: its vector phase issues the tail prefetch,
+      // and a load issued inside the loop would make the compiler wait for
+      // the outstanding prefetches before the loop's MFMAs
+      auto block2 = [&](int qb, bool last) {
+        f32x16 acc[kT];
+        mfma_block(acc);
+        const float rc = rcs[qb * 32 + col];   // +inf for rows past R: adds 0
+        if (last)
+          tail_prefetch();
+        else
+          read_q(qb + 1);
+#pragma unroll
+        for (int t = 0; t < kT; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) colacc[t][e] += fast_exp2(fmaf(acc[t][e], cc, -rc));
+      };
+#pragma unroll 1
+      for (int qb = 0; qb < nb - 1; ++qb) block2(qb, false);
+      block2(nb - 1, true);
+      // sum each key column over the 32 query lanes of its half-wave
+      float* out = p.imp + (int64_t)head * p.n;
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        float mine = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float v = colacc[t][e];
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 8);
+          v += __shfl_xor(v, 4);
+          v += __shfl_xor(v, 2);
+          v += __shfl_xor(v, 1);
+          if (col == e) mine = v;
+        }
+        if (col < 16) {
+          const int key = key0 + 32 * t + 8 * (col >> 2) + 4 * hb + (col & 3);
+          if (key < p.n) out[key] = mine * p.inv_w;
+        }
+      }
+    }
+  }
+  if (!kPass2 && cur >= 0) flush(cur);
+}
+
 // Fold the per-unit partials of each query row into
 // rowc = m + log2(sum_b l_b * 2^(m_b - m)).  A workgroup takes kRows
 // consecutive rows of one head; its 256/kRows thread groups each fold every
@@ -497,8 +845,10 @@ __global__ __launch_bounds__(256) void score_combine(ScoreParams p, int heads) {
   float m = -INFINITY, l = 0.f;
   if (head < heads && r < p.R) {
     const float2* pp = p.part + (int64_t)head * p.nblk * p.R + r;
-    // causal: only the units this row's position can see were scored for it
-    const int nb_row = p.causal_unit ? min(p.nblk, (p.S - p.w + r % p.w) / p.causal_unit + 1) : p.nblk;
+    // causal: only the units this row's position can see were scored for it;
+    // segment mode: one partial per workgroup segment of the head
+    const int nb_row = p.seg_grid ? head_segments(head, p.nblk, heads * p.nblk, p.seg_grid)
+                       : p.causal_unit ? min(p.nblk, (p.S - p.w + r % p.w) / p.causal_unit + 1) : p.nblk;
 #pragma unroll 4
     for (int b = q; b < nb_row; b += kGroups) {
       const float2 a = pp[(int64_t)b * p.R];
@@ -612,6 +962,36 @@ kvc_status launch_score(ScoreParams p, const Plan& pl, hipStream_t s, bool pass2
   return KVC_OK;
 }
 
+// Window scoring for 256 < G*w <= 512 (one 512-row chunk): the segment
+// passes.  Pass 2 folds the segment partials itself while staging when every
+// head has at most kFuseRowcUnits segments; otherwise the combine kernel runs.
+template <int kPF1, int kPF2>
+kvc_status launch_score_seg(ScoreParams p, const Plan& pl, hipStream_t s) {
+  constexpr int kThreads = 8 * kWave;
+  const int units = p.L * p.Hkv * pl.nblk;
+  const int heads = p.L * p.Hkv;
+  const size_t lds1 = score_lds_bytes(pl.chunk_rows, 8, false), lds2 = score_lds_bytes(pl.chunk_rows, 8, true);
+  auto k1 = score_pass_seg<false, kPF1>;
+  auto k2 = score_pass_seg<true, kPF2>;
+  int g1 = 0, g2 = 0;
+  kvc_status st = score_grid(k1, kThreads, lds1, units, &g1);
+  if (st != KVC_OK) return st;
+  st = score_grid(k2, kThreads, lds2, units, &g2);
+  if (st != KVC_OK) return st;
+  p.causal_unit = 0;
+  p.seg_grid = g1;
+  int nseg_max = 0;
+  for (int h = 0; h < heads; ++h) nseg_max = max(nseg_max, head_segments(h, pl.nblk, units, g1));
+  p.fuse_rowc = nseg_max <= kFuseRowcUnits ? 1 : 0;
+  KVC_LAUNCH_SHM("score_pass1", k1, dim3(g1), dim3(kThreads), lds1, s, p);
+  if (!p.fuse_rowc) {
+    const dim3 comb_grid(heads * ((pl.R + 31) / 32));
+    KVC_LAUNCH("score_combine", score_combine<32>, comb_grid, dim3(256), s, p, heads);
+  }
+  KVC_LAUNCH_SHM("score_pass2", k2, dim3(g2), dim3(kThreads), lds2, s, p);
+  return KVC_OK;
+}
+
 }  // namespace
 }  // namespace kvc
 
@@ -668,6 +1048,7 @@ kvc_status score_entry(const kvc_score_args* a, const void* q_obs, const void* k
     return launch_score<false, true, 4, 2, 8, 1, 1>(p, pl, s);
   }
   if (a->gumbel) return launch_score<true, false, 4, 1, 4, 0, 0>(p, pl, s);
+  if (pl.shape.kw == 8 && pl.R <= pl.chunk_rows) return launch_score_seg<0, 1>(p, pl, s);
   if (pl.shape.kw == 8) return launch_score<false, false, 8, 2, 16, 1, 2>(p, pl, s);
   if (pl.R >= 128) return launch_score<false, false, 4, 2, 8, 2, 2>(p, pl, s);
   return launch_score<false, false, 4, 2, 8, 1, 1>(p, pl, s);
