@@ -29,17 +29,22 @@ METRIC = "prompt KV tokens compressed/sec (score+top-k+gather); % of HBM rooflin
 DECODE_METRIC = "Keyformer decode tokens/sec for one layer (score accumulation + eviction on the kept cache)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-# vector ALU: 256 CUs x 4 SIMDs x 32 lane-operations per clock x 2.4 GHz (the
-# published unpacked fp32 / fp64 vector rate, 78.6 T FMA/s)
-VALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
-# vector operations per noisy tempered logit that the Gumbel path itself needs:
-# Philox4x32-10 (10 rounds of 2 wide products and 2 three-input xors per 4
-# samples: 10), the uniform from a word (3), -ln(-ln u) (2 logs, 2 scalings:
-# 4), (x c + g) / tau (2); then pass 1's max, shift, exp2, add (4) or pass 2's
-# shift, exp2, add (3).  Transcendentals count as one operation although the
-# hardware issues them at a lower rate, so the fraction is a lower bound.
-GUMBEL_OPS_PASS1 = 10 + 3 + 4 + 2 + 4
-GUMBEL_OPS_PASS2 = 10 + 3 + 4 + 2 + 3
+CLOCK_HZ = 2.4e9                # MI355X peak engine clock, published
+# Vector ALU roof in lane instructions: the published unpacked fp32 rate,
+# 78.6 TFLOP/s, counts an FMA as 2 flops, i.e. 256 CUs x 4 SIMDs x 16 lanes x
+# 2.4 GHz = 39.3 T lane-FMAs/s.  Other instruction classes are converted to
+# FMA-equivalents by their cost per wave64 instruction relative to v_fma_f32,
+# measured on the box by libkvc_peak in the same run (measure_peaks).
+VALU_PEAK_TLANE = 256 * 4 * 16 * CLOCK_HZ / 1e12
+# Lane instructions per noisy tempered logit of the Gumbel passes, by class:
+#   philox_pair -- Philox4x32-10: 10 rounds x (2 v_mad_u64_u32 + 2 v_bitop3_b32)
+#                  per 4 samples = 5 (product, three-input xor) pairs per sample;
+#   trans       -- the two logs of -ln(-ln u) and the exp2 of the softmax;
+#   simple      -- the uniform from a word (3), two scalings of the noise (2),
+#                  (x c + g) / tau (2), and the softmax's max, shift and add in
+#                  pass 1 (3) or shift and add in pass 2 (2).
+GUMBEL_MIX_PASS1 = {"philox_pair": 5, "trans": 3, "simple": 10}
+GUMBEL_MIX_PASS2 = {"philox_pair": 5, "trans": 3, "simple": 9}
 MALL_BYTES = 256 * 2 ** 20
 
 
@@ -54,6 +59,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure the on-box peaks (and read bandwidth over buffer sizes)")
     return ap.parse_args()
 
 
@@ -68,6 +75,89 @@ def calibrate_copy(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
+
+
+def _mix(mix, logits):
+    """Lane instructions per class for `logits` noisy tempered logits."""
+    return {c: n * logits for c, n in mix.items()}
+
+
+def fma_equivalents(mix_counts, peaks):
+    """Lane instructions of several classes -> v_fma_f32 equivalents, each class
+    weighted by its measured cycles per wave64 instruction relative to FMA."""
+    cyc = peaks["valu_cycles_per_wave_instr"]
+    cost = {"simple": 1.0, "trans": cyc["exp2"] / cyc["fma"], "philox_pair": cyc["mad_u64+bitop3"] / cyc["fma"]}
+    return sum(n * cost[c] for c, n in mix_counts.items())
+
+
+def measure_peaks(dev, stream, sweep=False):
+    """On-box peaks from libkvc_peak (its own probe kernels, timed with events on
+    `stream`): HBM read stream over 2 GiB, Infinity Cache read over 96 MiB, dense
+    bf16 MFMA, and the issue cost of each vector instruction class."""
+    import ctypes
+
+    import torch
+
+    from kv_cache_compression_bf16_amd import build_lib
+
+    lib = ctypes.CDLL(build_lib.PEAK_LIB)
+    P, SZ, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.kvc_peak_read.argtypes = [P, SZ, P, P]
+    lib.kvc_peak_mfma.argtypes = [P, I, P]
+    lib.kvc_peak_valu.argtypes = [I, P, I, P]
+    for f in ("kvc_peak_read_sink_words", "kvc_peak_mfma_sink_words", "kvc_peak_valu_sink_words"):
+        getattr(lib, f).restype = SZ
+    lib.kvc_peak_mfma_flops.restype = ctypes.c_double
+    lib.kvc_peak_valu_wave_instructions.restype = ctypes.c_double
+    lib.kvc_peak_mfma_flops.argtypes = [I]
+    lib.kvc_peak_valu_wave_instructions.argtypes = [I]
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    cus = lib.kvc_peak_cus()
+
+    def timed(launch, reps):
+        assert launch() == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3          # seconds per launch
+
+    out = {"cus": cus}
+    sink = torch.empty(max(lib.kvc_peak_read_sink_words(), lib.kvc_peak_mfma_sink_words(),
+                           lib.kvc_peak_valu_sink_words()), dtype=torch.int32, device=dev)
+    big = 2 << 30
+    buf = torch.empty(big, dtype=torch.uint8, device=dev)
+    t = timed(lambda: lib.kvc_peak_read(P(buf.data_ptr()), big, P(sink.data_ptr()), sp), 5)
+    out["hbm_read_GBs"] = big / t / 1e9
+    small = 96 << 20
+    t = timed(lambda: lib.kvc_peak_read(P(buf.data_ptr()), small, P(sink.data_ptr()), sp), 20)
+    out["infinity_cache_read_GBs"] = small / t / 1e9
+    del buf
+    iters = 4096
+    t = timed(lambda: lib.kvc_peak_mfma(P(sink.data_ptr()), iters, sp), 3)
+    out["mfma_bf16_TFLOPs"] = lib.kvc_peak_mfma_flops(iters) / t / 1e12
+    cyc = {}
+    for op, name in enumerate(("fma", "add", "exp2", "log2", "mad_u64+bitop3", "bitop3")):
+        it = 2048
+        t = timed(lambda: lib.kvc_peak_valu(op, P(sink.data_ptr()), it, sp), 3)
+        per_simd = lib.kvc_peak_valu_wave_instructions(it) / (cus * 4)
+        cyc[name] = t * CLOCK_HZ / per_simd             # at the published 2.4 GHz clock
+    out["valu_cycles_per_wave_instr"] = cyc
+    out["valu_fma_Tlane"] = 64 * 4 * cus * CLOCK_HZ / cyc["fma"] / 1e12
+    if sweep:
+        # read bandwidth against the buffer size: L2 (4 MB per XCD), Infinity Cache
+        # (256 MB), HBM
+        buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+        out["read_GBs_by_MiB"] = {}
+        for mib in (16, 32, 64, 128, 192, 256, 512, 1024, 2048):
+            n = mib << 20
+            t = timed(lambda: lib.kvc_peak_read(P(buf.data_ptr()), n, P(sink.data_ptr()), sp), max(3, 2048 // mib))
+            out["read_GBs_by_MiB"][mib] = round(n / t / 1e9)
+        del buf
+    return out
 
 
 def algorithmic(wl, kept_rows=None):
@@ -115,10 +205,10 @@ def algorithmic(wl, kept_rows=None):
     per_kernel = {
         "score_pass1": ("mfma", flops_pass, q_bytes + k_prefix),
         "score_pass2": ("mfma", flops_pass, q_bytes + k_prefix + imp),
-        "score_pass1_gumbel": ("mfma", flops_pass, q_bytes + k_prefix, GUMBEL_OPS_PASS1 * logits),
-        "score_pass2_gumbel": ("mfma", flops_pass, q_bytes + k_prefix + imp, GUMBEL_OPS_PASS2 * logits),
-        "score_causal_pass1_gumbel": ("mfma", flops_pass, q_bytes + k_prefix, GUMBEL_OPS_PASS1 * logits),
-        "score_causal_pass2_gumbel": ("mfma", flops_pass, q_bytes + k_prefix + imp, GUMBEL_OPS_PASS2 * logits),
+        "score_pass1_gumbel": ("mfma", flops_pass, q_bytes + k_prefix, _mix(GUMBEL_MIX_PASS1, logits)),
+        "score_pass2_gumbel": ("mfma", flops_pass, q_bytes + k_prefix + imp, _mix(GUMBEL_MIX_PASS2, logits)),
+        "score_causal_pass1_gumbel": ("mfma", flops_pass, q_bytes + k_prefix, _mix(GUMBEL_MIX_PASS1, logits)),
+        "score_causal_pass2_gumbel": ("mfma", flops_pass, q_bytes + k_prefix + imp, _mix(GUMBEL_MIX_PASS2, logits)),
         "score_causal_pass1": ("mfma", flops_pass, q_bytes + k_prefix),
         "score_causal_pass2": ("mfma", flops_pass, q_bytes + k_prefix + imp),
         "select_topk": ("hbm", 0.0, imp + B_total * 4),
@@ -323,6 +413,12 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
+    if args.peaks:
+        import torch
+
+        dev = torch.device("cuda:0")
+        print(json.dumps({"measured_peaks": measure_peaks(dev, torch.cuda.current_stream(dev), sweep=True)}))
+        return
 
     import numpy as np
     import torch
@@ -392,6 +488,7 @@ def main():
     kt = kvc.kvc_timing_read()
     kvc.kvc_timing_enable(False)
 
+    peaks = measure_peaks(dev, stream)
     tokens = 1 if wl.decode_steps else wl.L * wl.S    # decode: one token of one layer per step
     value = tokens / (ms_step / 1e3)
     kept_rows = int(plan.offsets[-1].item()) if wl.threshold > 0 else None   # after the timed region
@@ -400,37 +497,40 @@ def main():
     dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
     avg_s = kernels[dom]["avg_us"] / 1e6
     per_launch = args.steps / kernels[dom]["launches"]     # one step's figure -> one launch's
-    bound, flops, nbytes, ops = (per_kernel.get(dom, ("hbm", 0.0, 0)) + (0.0,))[:4]
+    bound, flops, nbytes, mix = (per_kernel.get(dom, ("hbm", 0.0, 0)) + ({},))[:4]
+    ops = fma_equivalents(mix, peaks) if mix else 0.0
     # the roofline that binds this kernel: the longest of its MFMA, HBM and
     # vector-ALU times at peak (a scoring pass over few query rows moves more
     # bytes per flop than the chip's ratio and is HBM-bound; the Gumbel passes
     # spend more on Philox and logs than on their MFMA work)
     t_roof = {"mfma": flops / (MFMA_BF16_PEAK_TFLOPS * 1e12), "hbm": nbytes / (HBM_PEAK_GBS * 1e9),
-              "alu": ops / (VALU_PEAK_TOPS * 1e12)}
+              "alu": ops / (VALU_PEAK_TLANE * 1e12)}
     if bound == "mfma":
         bound = max(t_roof, key=t_roof.get)
     traffic = measured_traffic(dom, wl.name)
     if bound == "alu":
         achieved = ops * per_launch / avg_s / 1e12
-        roof = {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS, "unit": "Tops/s",
-                "frac": achieved / VALU_PEAK_TOPS, "traffic": traffic}
+        roof = {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TLANE, "unit": "T lane-FMA-equivalents/s",
+                "frac": achieved / VALU_PEAK_TLANE, "traffic": traffic, "measured_peak": peaks["valu_fma_Tlane"]}
     elif bound == "mfma":
         achieved = flops * per_launch / avg_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
+                "measured_peak": peaks["mfma_bf16_TFLOPs"]}
     else:
         achieved = nbytes * per_launch / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "measured_peak": peaks["hbm_read_GBs"]}
+    roof["frac_of_measured_peak"] = roof["achieved"] / roof["measured_peak"]
     roof["kernel"] = dom
     roof["alg_bytes_per_launch"] = nbytes * per_launch
     for name, kk in kernels.items():
-        b, f, nb, op = (per_kernel.get(name, ("", 0.0, 0)) + (0.0,))[:4]
+        b, f, nb, mx = (per_kernel.get(name, ("", 0.0, 0)) + ({},))[:4]
         pl = args.steps / kk["launches"]
         kk["alg_TFLOPs"] = round(f * pl / (kk["avg_us"] / 1e6) / 1e12, 2) if f else None
         kk["alg_GBs"] = round(nb * pl / (kk["avg_us"] / 1e6) / 1e9, 1) if nb else None
-        if op:
-            kk["alg_Tops"] = round(op * pl / (kk["avg_us"] / 1e6) / 1e12, 2)
+        if mx:
+            kk["alg_T_lane_fma_eq"] = round(fma_equivalents(mx, peaks) * pl / (kk["avg_us"] / 1e6) / 1e12, 2)
         kk["avg_us"] = round(kk["avg_us"], 2)
 
     config = {"workload": wl.name, "layers": wl.L, "q_heads": wl.H, "kv_heads": wl.Hkv, "seq_len": wl.S,
@@ -447,6 +547,9 @@ def main():
         "hbm_frac_step": step_bytes / (ms_step / 1e3) / (HBM_PEAK_GBS * 1e9),
         "alg_bytes_step": step_bytes, "alg_flops_score_pass": flops_pass,
         "roofline": roof, "kernels": kernels, "cpu_baseline": cpu,
+        "measured_peaks": peaks,
+        "published_peaks": {"hbm_GBs": HBM_PEAK_GBS, "mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                            "valu_T_lane_fma": VALU_PEAK_TLANE},
     }
     print(json.dumps(out))
 

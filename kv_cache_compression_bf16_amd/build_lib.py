@@ -18,6 +18,9 @@ LIB = os.path.join(PKG, "libkvc.so")
 
 SOURCES = ["kvc_common.hip", "score.hip", "pool.hip", "select.hip", "threshold.hip", "compact.hip", "budget.hip",
            "think.hip", "decode.hip"]
+# the benchmark's peak probes: a library of their own, not part of the path
+PEAK_SOURCES = ["peak.hip"]
+PEAK_LIB = os.path.join(PKG, "libkvc_peak.so")
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -49,25 +52,33 @@ def _compile(src, extra=(), build_dir=BUILD):
     return obj, r.stderr
 
 
-def build(verbose=False, jobs=None, extra_flags=(), out=LIB, build_dir=BUILD):
-    """Compile every source and link ``out``; ``extra_flags`` (e.g. -D switches)
-    build an alternative variant of the library for A/B measurements."""
-    os.makedirs(build_dir, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(lambda src: _compile(src, extra_flags, build_dir), SOURCES))
-    objs = [o for o, _ in results]
-    if verbose:
-        for (_, err), src in zip(results, SOURCES):
-            warn = "\n".join(l for l in err.splitlines() if "packed-fp32-ops" not in l and l.strip())
-            if warn:
-                print(f"[{src}] {warn}", file=sys.stderr)
+def _link(objs, out):
     tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
+
+
+def build(verbose=False, jobs=None, extra_flags=(), out=LIB, build_dir=BUILD, peak=True):
+    """Compile every source and link ``out`` (and, with ``peak``, the probe
+    library libkvc_peak.so); ``extra_flags`` (e.g. -D switches) build an
+    alternative variant of the library for A/B measurements."""
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = SOURCES + (PEAK_SOURCES if peak else [])
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(lambda src: _compile(src, extra_flags, build_dir), srcs))
+    objs = dict(zip(srcs, (o for o, _ in results)))
+    if verbose:
+        for (_, err), src in zip(results, srcs):
+            warn = "\n".join(l for l in err.splitlines() if "packed-fp32-ops" not in l and l.strip())
+            if warn:
+                print(f"[{src}] {warn}", file=sys.stderr)
+    _link([objs[s] for s in SOURCES], out)
+    if peak:
+        _link([objs[s] for s in PEAK_SOURCES], PEAK_LIB)
     return out
 
 

@@ -358,3 +358,22 @@ def test_timing_api_without_launches():
     assert lib.kvc_timing_enable(1) == E.KVC_OK
     assert lib.kvc_timing_count() == 0
     assert lib.kvc_timing_enable(0) == E.KVC_OK
+
+
+def test_peak_probe_library_exports_its_header():
+    # the benchmark's probe library (libkvc_peak.so, include/kvc_peak.h) loads and
+    # exports every function its header declares; bad arguments are rejected on
+    # the host (return 1) before any launch
+    from kv_cache_compression_bf16_amd import build_lib
+    if not os.path.exists(build_lib.PEAK_LIB):
+        pytest.skip("libkvc_peak.so not built")
+    peak = ctypes.CDLL(build_lib.PEAK_LIB)
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "kvc_peak.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(kvc_peak_[a-z0-9_]+)\s*\(", src)))
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(peak, n), f"{n} declared in kvc_peak.h but not exported"
+    peak.kvc_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    peak.kvc_peak_valu.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert peak.kvc_peak_read(None, 16, None, None) == 1
+    assert peak.kvc_peak_valu(0, None, 1, None) == 1

@@ -146,3 +146,30 @@ def test_score_causal_matches_oracle(H, Hkv, S, w, gumbel, tau):
                                          w=w, scale=scale, gumbel=gumbel, tau=tau, seed=77)
     worst = check_importance(imp.cpu().numpy(), ref, H // Hkv, "causal")
     print("worst relative error:", worst)
+
+
+def test_long_prompt_gumbel_every_head_keeps_its_noise():
+    # 8 KV heads x 80000 prefix keys with Keyformer noise: many units per head, and
+    # the noise of every head keyed by its own head index
+    H = Hkv = 8
+    w, S = 32, 80000
+    qb, kb = _draw(H, Hkv, w, S, seed=81)
+    gpu = _gpu_importance(qb, kb, w=w, S=S, gumbel=True, tau=1.0, seed=7)
+    assert np.allclose(gpu.astype(np.float64).sum(axis=1), 1.0, rtol=1e-5, atol=0)
+    ref = oracle.score.importance(oracle.score.bf16_bits_to_f64(qb), oracle.score.bf16_bits_to_f64(kb), S=S, w=w,
+                                  scale=F32_ALPHA, gumbel=True, tau=1.0, seed=7, kv_heads=[1, 5, 6])
+    for g in (1, 5, 6):
+        check_importance(gpu[g][None], ref[g][None], 1, f"long gumbel head {g}")
+
+
+def test_many_layers_with_layer_scales():
+    # 6 layers x 4 KV heads x 40000 keys, each layer with its own logit scale
+    L, H, Hkv, w, S = 6, 8, 4, 48, 40000
+    qb, kb = _draw(H, Hkv, w, S, seed=82, L=L)
+    scales = (np.linspace(0.5, 3.0, L) / math.sqrt(128)).astype(np.float32)
+    ls = torch.from_numpy(scales).to(dev())
+    gpu = _gpu_importance(qb, kb, w=w, S=S, L=L, layer_scales=ls)
+    assert np.allclose(gpu.astype(np.float64).sum(axis=-1), H // Hkv, rtol=1e-5, atol=0)
+    for l, g in ((0, 1), (4, 2), (5, 3)):
+        ref = _oracle(qb[l], kb[l], w=w, S=S, scale=float(scales[l]), kv_heads=[g])
+        check_importance(gpu[l, g][None], ref[g][None], H // Hkv, f"layer {l} head {g}")
