@@ -83,10 +83,14 @@ inline size_t score_lds_bytes(int rows, int kw, bool pass2) {
   return (size_t)rows * kRowPitch + (pass2 ? (size_t)rows * sizeof(float) : (size_t)4 * 32 * kw * 2 * sizeof(float2));
 }
 
+
 // Most units per head for which pass 2 folds the row constants itself: one
 // step of loads per row.  Beyond it the fold's chain of round trips to
 // memory, which pass 2 must wait for, costs more than the combine launch.
 constexpr int kFuseRowcUnits = 32;
+// Most segment partials per row that the segment passes' pass 2 folds itself
+// (kFuseRowcUnits loads in flight per step).
+constexpr int kFuseRowcSegments = 64;
 
 struct ScoreParams {
   const uint16_t* q;
@@ -528,10 +532,14 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <bool kPass2, int kPF>
-__global__ __launch_bounds__(512, 1) void score_pass_seg(ScoreParams p) {
+// kPreQ: read the next block's query fragments during the current block's
+// exponentials (else at the start of each block, which frees their registers
+// for a deeper key prefetch).  kTag only separates the instantiation that the
+// ThinK value path runs for row constants alone (its own name in profiles).
+template <bool kPass2, int kW, int kT, int kCB, int kPF, bool kPreQ, int kTag>
+__global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  constexpr int kW = 8, kT = 2, kCB = 16, kThreads = kW * kWave;
+  constexpr int kThreads = kW * kWave;
   constexpr int kKeysPerWave = 32 * kT, kKeysPerUnit = kKeysPerWave * kW, kFoldBlocks = 4;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hb = lane >> 5, col = lane & 31;
@@ -613,21 +621,27 @@ __global__ __launch_bounds__(512, 1) void score_pass_seg(ScoreParams p) {
         for (int i = tid; i < nrows; i += kThreads) rcs[i] = i < p.R ? p.rowc[head_row0 + i] : INFINITY;
       } else {
         // rowc = m + log2(sum_s l_s 2^(m_s - m)) over the head's segments, one
-        // thread per row, every segment's load in flight at once (<= 32)
+        // thread per row, kFuseRowcUnits segment loads in flight per step, the
+        // steps folded in order
         const int nseg = head_segments(head, p.nblk, total, p.seg_grid);
         for (int i = tid; i < nrows; i += kThreads) {
           const int r = min(i, p.R - 1);
           const float2* pp = p.part + head_row0 * p.nblk + r;
-          float2 a[kFuseRowcUnits];
+          float m = -INFINITY, l = 0.f;
+          for (int b0 = 0; b0 < nseg; b0 += kFuseRowcUnits) {
+            float2 a[kFuseRowcUnits];
 #pragma unroll
-          for (int e = 0; e < kFuseRowcUnits; ++e) a[e] = pp[(int64_t)min(e, nseg - 1) * p.R];
-          float m = -INFINITY;
+            for (int e = 0; e < kFuseRowcUnits; ++e) a[e] = pp[(int64_t)min(b0 + e, nseg - 1) * p.R];
+            float mn = m;
 #pragma unroll
-          for (int e = 0; e < kFuseRowcUnits; ++e) m = fmaxf(m, e < nseg ? a[e].x : -INFINITY);
-          const float ms = (m == -INFINITY) ? 0.f : m;
-          float l = 0.f;
+            for (int e = 0; e < kFuseRowcUnits; ++e) mn = fmaxf(mn, b0 + e < nseg ? a[e].x : -INFINITY);
+            const float ms = (mn == -INFINITY) ? 0.f : mn;
+            float acc = l * fast_exp2(m - ms);
 #pragma unroll
-          for (int e = 0; e < kFuseRowcUnits; ++e) l += e < nseg ? a[e].y * fast_exp2(a[e].x - ms) : 0.f;
+            for (int e = 0; e < kFuseRowcUnits; ++e) acc += b0 + e < nseg ? a[e].y * fast_exp2(a[e].x - ms) : 0.f;
+            m = mn;
+            l = acc;
+          }
           rcs[i] = (i < p.R && l > 0.f) ? m + log2f(l) : INFINITY;
         }
       }
@@ -768,15 +782,16 @@ __global__ __launch_bounds__(512, 1) void score_pass_seg(ScoreParams p) {
     };
     const int key0 = blk * kKeysPerUnit + wave * kKeysPerWave;
     const bool wave_full = key0 + kKeysPerWave <= p.n;
-    read_q(0);
+    if (kPreQ) read_q(0);
     if (!kPass2) {
       const bool clean = wave_full && nb * 32 == p.R;
       static_for<0, kCB>([&](auto qb_c) {
         constexpr int qb = decltype(qb_c)::value;
         if (qb < nb) {
           f32x16 acc[kT];
+          if (!kPreQ) read_q(qb);
           mfma_block(acc);
-          if (qb + 1 < nb) read_q(qb + 1);
+          if (kPreQ && qb + 1 < nb) read_q(qb + 1);
           if (qb == kCB - 1) tail_prefetch();
           stats(clean, acc, key0, qb * 32 + col, st[qb]);
         }
@@ -790,11 +805,12 @@ __global__ __launch_bounds__(512, 1) void score_pass_seg(ScoreParams p) {
       // the outstanding prefetches before the loop's MFMAs
       auto block2 = [&](int qb, bool last) {
         f32x16 acc[kT];
+        if (!kPreQ) read_q(qb);
         mfma_block(acc);
         const float rc = rcs[qb * 32 + col];   // +inf for rows past R: adds 0
         if (last)
           tail_prefetch();
-        else
+        else if (kPreQ)
           read_q(qb + 1);
 #pragma unroll
         for (int t = 0; t < kT; ++t)
@@ -962,17 +978,19 @@ kvc_status launch_score(ScoreParams p, const Plan& pl, hipStream_t s, bool pass2
   return KVC_OK;
 }
 
-// Window scoring for 256 < G*w <= 512 (one 512-row chunk): the segment
-// passes.  Pass 2 folds the segment partials itself while staging when every
-// head has at most kFuseRowcUnits segments; otherwise the combine kernel runs.
-template <int kPF1, int kPF2>
-kvc_status launch_score_seg(ScoreParams p, const Plan& pl, hipStream_t s) {
-  constexpr int kThreads = 8 * kWave;
+// Window scoring whose G*w rows fit one staged chunk: the segment passes.
+// Pass 2 folds the segment partials itself while staging when every head has
+// at most kFuseRowcUnits segments; otherwise the combine kernel runs.
+// pass2 == false: pass 1 and the row constants only (the ThinK value path),
+// from an instantiation of its own (kTag 1).
+template <int kW, int kT, int kCB, int kPF1, bool kPreQ1, int kPF2, bool kPreQ2>
+kvc_status launch_score_seg(ScoreParams p, const Plan& pl, hipStream_t s, bool pass2 = true) {
+  constexpr int kThreads = kW * kWave;
   const int units = p.L * p.Hkv * pl.nblk;
   const int heads = p.L * p.Hkv;
-  const size_t lds1 = score_lds_bytes(pl.chunk_rows, 8, false), lds2 = score_lds_bytes(pl.chunk_rows, 8, true);
-  auto k1 = score_pass_seg<false, kPF1>;
-  auto k2 = score_pass_seg<true, kPF2>;
+  const size_t lds1 = score_lds_bytes(pl.chunk_rows, kW, false), lds2 = score_lds_bytes(pl.chunk_rows, kW, true);
+  auto k1 = pass2 ? score_pass_seg<false, kW, kT, kCB, kPF1, kPreQ1, 0> : score_pass_seg<false, kW, kT, kCB, kPF1, kPreQ1, 1>;
+  auto k2 = score_pass_seg<true, kW, kT, kCB, kPF2, kPreQ2, 0>;
   int g1 = 0, g2 = 0;
   kvc_status st = score_grid(k1, kThreads, lds1, units, &g1);
   if (st != KVC_OK) return st;
@@ -982,12 +1000,15 @@ kvc_status launch_score_seg(ScoreParams p, const Plan& pl, hipStream_t s) {
   p.seg_grid = g1;
   int nseg_max = 0;
   for (int h = 0; h < heads; ++h) nseg_max = max(nseg_max, head_segments(h, pl.nblk, units, g1));
-  p.fuse_rowc = nseg_max <= kFuseRowcUnits ? 1 : 0;
-  KVC_LAUNCH_SHM("score_pass1", k1, dim3(g1), dim3(kThreads), lds1, s, p);
-  if (!p.fuse_rowc) {
-    const dim3 comb_grid(heads * ((pl.R + 31) / 32));
-    KVC_LAUNCH("score_combine", score_combine<32>, comb_grid, dim3(256), s, p, heads);
+  p.fuse_rowc = (pass2 && nseg_max <= kFuseRowcSegments) ? 1 : 0;
+  const dim3 comb_grid(heads * ((pl.R + 31) / 32));
+  if (!pass2) {
+    KVC_LAUNCH_SHM("think_rowc_pass1", k1, dim3(g1), dim3(kThreads), lds1, s, p);
+    KVC_LAUNCH("think_rowc_combine", score_combine<32>, comb_grid, dim3(256), s, p, heads);
+    return KVC_OK;
   }
+  KVC_LAUNCH_SHM("score_pass1", k1, dim3(g1), dim3(kThreads), lds1, s, p);
+  if (!p.fuse_rowc) KVC_LAUNCH("score_combine", score_combine<32>, comb_grid, dim3(256), s, p, heads);
   KVC_LAUNCH_SHM("score_pass2", k2, dim3(g2), dim3(kThreads), lds2, s, p);
   return KVC_OK;
 }
@@ -1048,10 +1069,9 @@ kvc_status score_entry(const kvc_score_args* a, const void* q_obs, const void* k
     return launch_score<false, true, 4, 2, 8, 1, 1>(p, pl, s);
   }
   if (a->gumbel) return launch_score<true, false, 4, 1, 4, 0, 0>(p, pl, s);
-  if (pl.shape.kw == 8 && pl.R <= pl.chunk_rows) return launch_score_seg<0, 1>(p, pl, s);
+  if (pl.shape.kw == 8 && pl.R <= pl.chunk_rows) return launch_score_seg<8, 2, 16, 0, true, 1, true>(p, pl, s);
   if (pl.shape.kw == 8) return launch_score<false, false, 8, 2, 16, 1, 2>(p, pl, s);
-  if (pl.R >= 128) return launch_score<false, false, 4, 2, 8, 2, 2>(p, pl, s);
-  return launch_score<false, false, 4, 2, 8, 1, 1>(p, pl, s);
+  return launch_score_seg<4, 2, 8, 2, true, 1, true>(p, pl, s);
 }
 
 }  // namespace
@@ -1127,9 +1147,9 @@ kvc_status score_rowc(const uint16_t* q, int64_t q_hs, const uint16_t* k, int64_
   p.nblk = pl.nblk;
   p.chunk_rows = pl.chunk_rows;
   *rowc = p.rowc;
+  if (pl.shape.kw == 8 && pl.R <= pl.chunk_rows) return launch_score_seg<8, 2, 16, 0, true, 1, true>(p, pl, s, false);
   if (pl.shape.kw == 8) return launch_score<false, false, 8, 2, 16, 1, 2>(p, pl, s, false);
-  if (pl.R >= 128) return launch_score<false, false, 4, 2, 8, 2, 2>(p, pl, s, false);
-  return launch_score<false, false, 4, 2, 8, 1, 1>(p, pl, s, false);
+  return launch_score_seg<4, 2, 8, 2, true, 1, true>(p, pl, s, false);
 }
 
 }  // namespace kvc
