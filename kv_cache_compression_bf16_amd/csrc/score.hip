@@ -126,6 +126,33 @@ __host__ __device__ inline int head_segments(int h, int nblk, int total, int gri
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// For each of the 16 values v[e] of a lane, the sum over the 32 lanes of its
+// half-wave, with DPP moves only (no LDS round trip): xor 1 and xor 2 quad
+// permutations, then the half-row and row mirrors give every lane its 16-lane
+// row sum, and a row broadcast of lane 15 adds row 0's sum into row 1 (row 2's
+// into row 3).  Lane col >= 16 of a half-wave returns the total of value
+// col - 16.  A fixed order: bit-reproducible.
+__device__ __forceinline__ float half_wave_sum16_dpp(const f32x16& v, int col) {
+  auto add_dpp = [](float x, auto ctrl_c, auto row_mask_c) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl_c)::value,
+                                                          decltype(row_mask_c)::value, 0xF, false));
+  };
+  using All = std::integral_constant<int, 0xF>;
+  using OddRows = std::integral_constant<int, 0xA>;   // rows 1 and 3 receive the broadcast
+  float mine = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float x = v[e];
+    x = add_dpp(x, std::integral_constant<int, 0xB1>{}, All{});    // quad_perm [1,0,3,2]: lane ^ 1
+    x = add_dpp(x, std::integral_constant<int, 0x4E>{}, All{});    // quad_perm [2,3,0,1]: lane ^ 2
+    x = add_dpp(x, std::integral_constant<int, 0x141>{}, All{});   // row_half_mirror: 8-lane sums
+    x = add_dpp(x, std::integral_constant<int, 0x140>{}, All{});   // row_mirror: 16-lane sums
+    x = add_dpp(x, std::integral_constant<int, 0x142>{}, OddRows{});   // row_bcast15: 32-lane sums
+    if (col == 16 + e) mine = x;
+  }
+  return mine;
+}
+
 // kCausal: keys [0, S) and window row i (position S - w + i) sees the keys at
 // positions <= its own; w % 32 == 0, so no 32-row query block spans two heads.
 // kPF: tiles of the next unit's keys prefetched during this unit (0..kT).
@@ -820,23 +847,15 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
 #pragma unroll 1
       for (int qb = 0; qb < nb - 1; ++qb) block2(qb, false);
       block2(nb - 1, true);
-      // sum each key column over the 32 query lanes of its half-wave
+      // sum each key column over the 32 query lanes of its half-wave (lane
+      // col >= 16 receives the total of value col - 16)
       float* out = p.imp + (int64_t)head * p.n;
 #pragma unroll
       for (int t = 0; t < kT; ++t) {
-        float mine = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float v = colacc[t][e];
-          v += __shfl_xor(v, 16);
-          v += __shfl_xor(v, 8);
-          v += __shfl_xor(v, 4);
-          v += __shfl_xor(v, 2);
-          v += __shfl_xor(v, 1);
-          if (col == e) mine = v;
-        }
-        if (col < 16) {
-          const int key = key0 + 32 * t + 8 * (col >> 2) + 4 * hb + (col & 3);
+        const float mine = half_wave_sum16_dpp(colacc[t], col);
+        if (col >= 16) {
+          const int e = col - 16;
+          const int key = key0 + 32 * t + 8 * (e >> 2) + 4 * hb + (e & 3);
           if (key < p.n) out[key] = mine * p.inv_w;
         }
       }
