@@ -504,23 +504,15 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
     }
 
     if (kPass2) {
-      // sum each key column over the 32 query lanes of its half-wave
+      // sum each key column over the 32 query lanes of its half-wave (lane
+      // col >= 16 receives the total of value col - 16)
       float* out = p.imp + (int64_t)head * p.n;
 #pragma unroll
       for (int t = 0; t < kT; ++t) {
-        float mine = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float v = colacc[t][e];
-          v += __shfl_xor(v, 16);
-          v += __shfl_xor(v, 8);
-          v += __shfl_xor(v, 4);
-          v += __shfl_xor(v, 2);
-          v += __shfl_xor(v, 1);
-          if (col == e) mine = v;
-        }
-        if (col < 16) {
-          const int key = key0 + 32 * t + 8 * (col >> 2) + 4 * hb + (col & 3);
+        const float mine = half_wave_sum16_dpp(colacc[t], col);
+        if (col >= 16) {
+          const int e = col - 16;
+          const int key = key0 + 32 * t + 8 * (e >> 2) + 4 * hb + (e & 3);
           if (key < p.n) out[key] = mine * p.inv_w;
         }
       }
