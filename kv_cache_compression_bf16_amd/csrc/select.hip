@@ -76,13 +76,31 @@ constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kBPT = kBins / kSelThreads;   // histogram bins per thread in the scan
 
 // Workgroup-wide (min, max); every thread receives the result.
+// Within each 16-lane row, DPP moves (xor 1, xor 2, half-row mirror, row
+// mirror) leave every lane with the row's (min, max); lanes 0, 16, 32 and 48
+// are then read into scalar registers.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kCtrl, 0xF, 0xF, false);
+}
+__device__ __forceinline__ void wave_min_max(uint32_t& lo, uint32_t& hi) {
+  lo = min(lo, dpp_u32<0xB1>(lo));
+  hi = max(hi, dpp_u32<0xB1>(hi));
+  lo = min(lo, dpp_u32<0x4E>(lo));
+  hi = max(hi, dpp_u32<0x4E>(hi));
+  lo = min(lo, dpp_u32<0x141>(lo));
+  hi = max(hi, dpp_u32<0x141>(hi));
+  lo = min(lo, dpp_u32<0x140>(lo));
+  hi = max(hi, dpp_u32<0x140>(hi));
+  lo = min(min((uint32_t)__builtin_amdgcn_readlane((int)lo, 0), (uint32_t)__builtin_amdgcn_readlane((int)lo, 16)),
+           min((uint32_t)__builtin_amdgcn_readlane((int)lo, 32), (uint32_t)__builtin_amdgcn_readlane((int)lo, 48)));
+  hi = max(max((uint32_t)__builtin_amdgcn_readlane((int)hi, 0), (uint32_t)__builtin_amdgcn_readlane((int)hi, 16)),
+           max((uint32_t)__builtin_amdgcn_readlane((int)hi, 32), (uint32_t)__builtin_amdgcn_readlane((int)hi, 48)));
+}
+
 __device__ __forceinline__ void block_min_max(uint32_t& lo, uint32_t& hi, uint32_t* wlo, uint32_t* whi) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor(lo, o));
-    hi = max(hi, (uint32_t)__shfl_xor(hi, o));
-  }
+  wave_min_max(lo, hi);
   if (lane == 0) {
     wlo[wid] = lo;
     whi[wid] = hi;

@@ -48,25 +48,26 @@ def test_rejects_even_kernel():
 
 
 @pytest.mark.parametrize("mode", [AVG, MAX])
-def test_pool_multi_row_keeps_each_row_apart(mode):
-    # importance [2, 3, n]: row (a, b) holds one spike of height (a+1)(b+1) at its own
-    # position p = 5a + 7b + 3, so each pooled row must show that row's plateau
-    # [p - h, p + h] at that row's height (ZigZagKV page, SnapKV section: pooling runs
-    # along the keys of each head separately), nothing else, and the shape is kept.
+@pytest.mark.parametrize("lead", [(2, 3), (3,)])
+def test_pool_multi_row_keeps_each_row_apart(mode, lead):
+    # importance [2, 3, n] (layers, heads) or [3, n] (heads): row r holds one spike of
+    # height r+1 at its own position p = 7r + 3, so each pooled row must show that row's
+    # plateau [p - h, p + h] at that row's height (ZigZagKV page, SnapKV section: pooling
+    # runs along the keys of each head separately), nothing else, and the shape is kept.
     n, k = 40, 5
     h = k // 2
-    x = np.zeros((2, 3, n))
-    for a in range(2):
-        for b in range(3):
-            x[a, b, 5 * a + 7 * b + 3] = (a + 1) * (b + 1)
+    x = np.zeros(lead + (n,))
+    rows = x.reshape(-1, n)
+    for r in range(rows.shape[0]):
+        rows[r, 7 * r + 3] = r + 1
     out = oracle.pool.pool(x, k, mode)
     assert out.shape == x.shape
-    for a in range(2):
-        for b in range(3):
-            p, v = 5 * a + 7 * b + 3, (a + 1) * (b + 1)
-            want = np.zeros(n)
-            want[p - h:p + h + 1] = v / k if mode == AVG else v
-            assert np.allclose(out[a, b], want, rtol=0, atol=1e-15), (a, b)
+    got = out.reshape(-1, n)
+    for r in range(rows.shape[0]):
+        p, v = 7 * r + 3, r + 1
+        want = np.zeros(n)
+        want[p - h:p + h + 1] = v / k if mode == AVG else v
+        assert np.allclose(got[r], want, rtol=0, atol=1e-15), r
 
 
 def test_pool_single_row_input_stays_one_dimensional():
