@@ -38,8 +38,10 @@ constexpr int kBins = 2048;
 
 // fp32 -> uint32 with the same order (-0 folded onto +0).
 __device__ __forceinline__ uint32_t order_key(uint32_t b) {
-  if (b == 0x80000000u) b = 0u;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  // sign set: all bits flipped; clear: the sign bit set.  -0 lands on
+  // 0x7FFFFFFF (no other input does) and is moved onto +0's key.
+  const uint32_t k = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+  return k == 0x7FFFFFFFu ? 0x80000000u : k;
 }
 
 // Exclusive prefix sum over a workgroup of kThreadsT threads; *total receives
@@ -125,9 +127,19 @@ constexpr int kRound = kSelWaves * kSpan;
 
 __device__ __forceinline__ void load_round(const uint32_t* v, int c, int r, uint32_t (&key)[kVPL]) {
   const int base = r * kRound + (int)(threadIdx.x >> 6) * kSpan + (int)(threadIdx.x & 63);
+  uint32_t raw[kVPL];
+  if (r * kRound + (int)(threadIdx.x >> 6) * kSpan + kSpan <= c) {
+    // a wave whose whole span is candidates: one base address and immediate
+    // offsets, no range test
+    const uint32_t* vb = v + base;
+#pragma unroll
+    for (int i = 0; i < kVPL; ++i) raw[i] = vb[64 * i];
+#pragma unroll
+    for (int i = 0; i < kVPL; ++i) key[i] = order_key(raw[i]);
+    return;
+  }
   // Unconditional loads from a clamped address (then masked): a guarded load
   // would be a branch, and the wait at each branch merge would serialize them.
-  uint32_t raw[kVPL];
 #pragma unroll
   for (int i = 0; i < kVPL; ++i) {
     const int j = base + 64 * i;
