@@ -127,30 +127,41 @@ __host__ __device__ inline int head_segments(int h, int nblk, int total, int gri
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // For each of the 16 values v[e] of a lane, the sum over the 32 lanes of its
-// half-wave, with DPP moves only (no LDS round trip): xor 1 and xor 2 quad
-// permutations, then the half-row and row mirrors give every lane its 16-lane
-// row sum, and a row broadcast of lane 15 adds row 0's sum into row 1 (row 2's
-// into row 3).  Lane col >= 16 of a half-wave returns the total of value
-// col - 16.  A fixed order: bit-reproducible.
+// half-wave, as a butterfly of DPP moves (no LDS round trip).  Four steps
+// within each 16-lane row -- row mirror, half-row mirror, quad xor 2, quad
+// xor 1 -- each pair two lanes that hold the same set of partial values; each
+// lane keeps the half of the set its position selects and adds its partner's
+// copy of that half, so position i of a row ends with the row sum of value i.
+// One exchange between the two rows of the half-wave completes the sum.  Lane
+// col of a half-wave returns the total of value col & 15.  A fixed order:
+// bit-reproducible.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float half_wave_sum16_dpp(const f32x16& v, int col) {
-  auto add_dpp = [](float x, auto ctrl_c, auto row_mask_c) {
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl_c)::value,
-                                                          decltype(row_mask_c)::value, 0xF, false));
+  const int i = col & 15;
+  const bool k1 = i & 8, k2 = i & 4, k3 = i & 2, k4 = i & 1;
+  // keep + partner's copy of it: the partner (opposite selector) sends what
+  // this lane keeps.  The selects act on the operands, before the move, so
+  // every lane runs every move.
+  auto step = [](bool k, float a, float b, auto ctrl_c) {
+    const float keep = k ? b : a, send = k ? a : b;
+    return keep + dpp_f32<decltype(ctrl_c)::value>(send);
   };
-  using All = std::integral_constant<int, 0xF>;
-  using OddRows = std::integral_constant<int, 0xA>;   // rows 1 and 3 receive the broadcast
-  float mine = 0.f;
+  using Mirror = std::integral_constant<int, 0x140>;      // row mirror: lane i with 15 - i
+  using HalfMirror = std::integral_constant<int, 0x141>;  // half-row mirror: i with 7 - i in each half
+  using Xor2 = std::integral_constant<int, 0x4E>;         // quad_perm [2,3,0,1]
+  using Xor1 = std::integral_constant<int, 0xB1>;         // quad_perm [1,0,3,2]
+  float w[8], x[4], y[2];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    float x = v[e];
-    x = add_dpp(x, std::integral_constant<int, 0xB1>{}, All{});    // quad_perm [1,0,3,2]: lane ^ 1
-    x = add_dpp(x, std::integral_constant<int, 0x4E>{}, All{});    // quad_perm [2,3,0,1]: lane ^ 2
-    x = add_dpp(x, std::integral_constant<int, 0x141>{}, All{});   // row_half_mirror: 8-lane sums
-    x = add_dpp(x, std::integral_constant<int, 0x140>{}, All{});   // row_mirror: 16-lane sums
-    x = add_dpp(x, std::integral_constant<int, 0x142>{}, OddRows{});   // row_bcast15: 32-lane sums
-    if (col == 16 + e) mine = x;
-  }
-  return mine;
+  for (int e = 0; e < 8; ++e) w[e] = step(k1, v[e], v[e + 8], Mirror{});
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = step(k2, w[e], w[e + 4], HalfMirror{});
+#pragma unroll
+  for (int e = 0; e < 2; ++e) y[e] = step(k3, x[e], x[e + 2], Xor2{});
+  const float z = step(k4, y[0], y[1], Xor1{});
+  return z + __shfl_xor(z, 16);
 }
 
 // kCausal: keys [0, S) and window row i (position S - w + i) sees the keys at
@@ -505,13 +516,13 @@ __global__ __launch_bounds__(kW * kWave, kGumbel ? 3 : 1) void score_pass(ScoreP
 
     if (kPass2) {
       // sum each key column over the 32 query lanes of its half-wave (lane
-      // col >= 16 receives the total of value col - 16)
+      // col receives the total of value col & 15; the first row stores it)
       float* out = p.imp + (int64_t)head * p.n;
 #pragma unroll
       for (int t = 0; t < kT; ++t) {
         const float mine = half_wave_sum16_dpp(colacc[t], col);
-        if (col >= 16) {
-          const int e = col - 16;
+        if (col < 16) {
+          const int e = col;
           const int key = key0 + 32 * t + 8 * (e >> 2) + 4 * hb + (e & 3);
           if (key < p.n) out[key] = mine * p.inv_w;
         }
@@ -840,13 +851,13 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
       for (int qb = 0; qb < nb - 1; ++qb) block2(qb, false);
       block2(nb - 1, true);
       // sum each key column over the 32 query lanes of its half-wave (lane
-      // col >= 16 receives the total of value col - 16)
+      // col receives the total of value col & 15; the first row stores it)
       float* out = p.imp + (int64_t)head * p.n;
 #pragma unroll
       for (int t = 0; t < kT; ++t) {
         const float mine = half_wave_sum16_dpp(colacc[t], col);
-        if (col >= 16) {
-          const int e = col - 16;
+        if (col < 16) {
+          const int e = col;
           const int key = key0 + 32 * t + 8 * (e >> 2) + 4 * hb + (e & 3);
           if (key < p.n) out[key] = mine * p.inv_w;
         }
