@@ -131,6 +131,9 @@ __global__ __launch_bounds__(256) void think_qpartial(const uint16_t* q, int64_t
 }
 
 // qpart == nullptr: magnitude score; else the query-driven score (squared).
+// kTag only separates the value path's instantiation (its own name in
+// profiles).
+template <int kTag>
 __global__ __launch_bounds__(kD * kSelGroups) void think_select(const float* part, int nchunk, const float* qpart,
                                                                int G, int T, int32_t* channels, uint8_t* mask) {
   __shared__ float red[kSelGroups][kD];
@@ -198,8 +201,8 @@ __global__ __launch_bounds__(kD * kSelGroups) void think_select(const float* par
 
 // kPairs: T even and the output 4-byte aligned (lane l < T/2 stores output
 // channels 2l and 2l+1 as one 4-byte word); else lanes l and l+64 store one
-// bf16 each.
-template <bool kPairs>
+// bf16 each.  kTag as for think_select.
+template <bool kPairs, int kTag>
 __global__ __launch_bounds__(256) void think_gather(const uint16_t* kc, int budget, int rows, int T,
                                                    const int32_t* channels, uint16_t* out) {
   constexpr int kRows = 8;   // rows per wave per step, loads in flight
@@ -499,17 +502,17 @@ kvc_status channel_prune(const void* k_c, const void* q, int32_t G, int32_t w, i
   if (q)
     KVC_LAUNCH("think_qpartial", think_qpartial, dim3(G, Hkv), dim3(256), s, static_cast<const uint16_t*>(q),
                q_hs, G, w, qpart);
-  KVC_LAUNCH("think_select", think_select, dim3(Hkv), dim3(kD * kSelGroups), s, part, nchunk, qpart, G, T,
+  KVC_LAUNCH("think_select", think_select<0>, dim3(Hkv), dim3(kD * kSelGroups), s, part, nchunk, qpart, G, T,
              channels, mask);
   if (rows > 0) {
     int gx = (rows + 31) / 32;   // 4 waves x 8 rows per workgroup step
     if (gx > 1024) gx = 1024;
     uint16_t* kp = static_cast<uint16_t*>(k_pruned);
     if ((T & 1) == 0 && (reinterpret_cast<uintptr_t>(k_pruned) & 3) == 0)
-      KVC_LAUNCH("think_gather", think_gather<true>, dim3(gx, Hkv), dim3(256), s, kcp, budget, rows, T, channels,
+      KVC_LAUNCH("think_gather", think_gather<true, 0>, dim3(gx, Hkv), dim3(256), s, kcp, budget, rows, T, channels,
                  kp);
     else
-      KVC_LAUNCH("think_gather", think_gather<false>, dim3(gx, Hkv), dim3(256), s, kcp, budget, rows, T, channels,
+      KVC_LAUNCH("think_gather", think_gather<false, 0>, dim3(gx, Hkv), dim3(256), s, kcp, budget, rows, T, channels,
                  kp);
   }
   return KVC_OK;
@@ -618,17 +621,17 @@ extern "C" kvc_status kvc_channel_prune_value(const void* k_c, const void* v_c, 
                q_head_stride, G, w, kp, vp, budget, rows, rowc, scale * kLog2e, L.nsplit, opart);
   }
   KVC_LAUNCH("think_vnorm", think_vnorm, dim3(L.nrg, Hkv), dim3(kD * kVNormRows), s, opart, L.nsplit, R, vpart);
-  KVC_LAUNCH("think_select_v", think_select, dim3(Hkv), dim3(kD * kSelGroups), s, vpart, L.nrg, nullptr, 0, T,
+  KVC_LAUNCH("think_select_v", think_select<1>, dim3(Hkv), dim3(kD * kSelGroups), s, vpart, L.nrg, nullptr, 0, T,
              channels, mask);
   if (rows > 0) {
     int gx = (rows + 31) / 32;
     if (gx > 1024) gx = 1024;
     uint16_t* out = static_cast<uint16_t*>(v_pruned);
     if ((T & 1) == 0 && (reinterpret_cast<uintptr_t>(v_pruned) & 3) == 0)
-      KVC_LAUNCH("think_gather_v", think_gather<true>, dim3(gx, Hkv), dim3(256), s, vp, budget, rows, T, channels,
+      KVC_LAUNCH("think_gather_v", think_gather<true, 1>, dim3(gx, Hkv), dim3(256), s, vp, budget, rows, T, channels,
                  out);
     else
-      KVC_LAUNCH("think_gather_v", think_gather<false>, dim3(gx, Hkv), dim3(256), s, vp, budget, rows, T, channels,
+      KVC_LAUNCH("think_gather_v", think_gather<false, 1>, dim3(gx, Hkv), dim3(256), s, vp, budget, rows, T, channels,
                  out);
   }
   return KVC_OK;
