@@ -509,10 +509,10 @@ kvc_status channel_prune(const void* k_c, const void* q, int32_t G, int32_t w, i
     if (gx > 1024) gx = 1024;
     uint16_t* kp = static_cast<uint16_t*>(k_pruned);
     if ((T & 1) == 0 && (reinterpret_cast<uintptr_t>(k_pruned) & 3) == 0)
-      KVC_LAUNCH("think_gather", think_gather<true, 0>, dim3(gx, Hkv), dim3(256), s, kcp, budget, rows, T, channels,
+      KVC_LAUNCH("think_gather", (think_gather<true, 0>), dim3(gx, Hkv), dim3(256), s, kcp, budget, rows, T, channels,
                  kp);
     else
-      KVC_LAUNCH("think_gather", think_gather<false, 0>, dim3(gx, Hkv), dim3(256), s, kcp, budget, rows, T, channels,
+      KVC_LAUNCH("think_gather", (think_gather<false, 0>), dim3(gx, Hkv), dim3(256), s, kcp, budget, rows, T, channels,
                  kp);
   }
   return KVC_OK;
@@ -628,10 +628,10 @@ extern "C" kvc_status kvc_channel_prune_value(const void* k_c, const void* v_c, 
     if (gx > 1024) gx = 1024;
     uint16_t* out = static_cast<uint16_t*>(v_pruned);
     if ((T & 1) == 0 && (reinterpret_cast<uintptr_t>(v_pruned) & 3) == 0)
-      KVC_LAUNCH("think_gather_v", think_gather<true, 1>, dim3(gx, Hkv), dim3(256), s, vp, budget, rows, T, channels,
+      KVC_LAUNCH("think_gather_v", (think_gather<true, 1>), dim3(gx, Hkv), dim3(256), s, vp, budget, rows, T, channels,
                  out);
     else
-      KVC_LAUNCH("think_gather_v", think_gather<false, 1>, dim3(gx, Hkv), dim3(256), s, vp, budget, rows, T, channels,
+      KVC_LAUNCH("think_gather_v", (think_gather<false, 1>), dim3(gx, Hkv), dim3(256), s, vp, budget, rows, T, channels,
                  out);
   }
   return KVC_OK;
