@@ -873,7 +873,9 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
 // (256/kRows)-th unit online (coalesced reads along the rows), and the group
 // results are folded in a fixed order, so the result is bit-reproducible.
 // Rows with many units use 8 rows x 32 groups, the rest 32 rows x 8 groups.
-template <int kRows>
+// kTag only separates the ThinK value path's row-constant fold (its own name
+// in profiles).
+template <int kRows, int kTag = 0>
 __global__ __launch_bounds__(256) void score_combine(ScoreParams p, int heads) {
   constexpr int kGroups = 256 / kRows;
   __shared__ float2 sg[kGroups][kRows];
@@ -987,7 +989,8 @@ kvc_status launch_score(ScoreParams p, const Plan& pl, hipStream_t s, bool pass2
   if (st != KVC_OK) return st;
   if (!pass2) {   // row constants only (ThinK value scores): named apart from the scoring pass
     KVC_LAUNCH_SHM("think_rowc_pass1", k1, dim3(g1), dim3(kThreads), lds1, s, p);
-    KVC_LAUNCH("think_rowc_combine", kc, comb_grid, dim3(256), s, p, heads);
+    KVC_LAUNCH("think_rowc_combine", wide ? (score_combine<8, 1>) : (score_combine<32, 1>), comb_grid, dim3(256),
+               s, p, heads);
     return KVC_OK;
   }
   KVC_LAUNCH_SHM(kCausal ? (kGumbel ? "score_causal_pass1_gumbel" : "score_causal_pass1")
@@ -1026,7 +1029,7 @@ kvc_status launch_score_seg(ScoreParams p, const Plan& pl, hipStream_t s, bool p
   const dim3 comb_grid(heads * ((pl.R + 31) / 32));
   if (!pass2) {
     KVC_LAUNCH_SHM("think_rowc_pass1", k1, dim3(g1), dim3(kThreads), lds1, s, p);
-    KVC_LAUNCH("think_rowc_combine", score_combine<32>, comb_grid, dim3(256), s, p, heads);
+    KVC_LAUNCH("think_rowc_combine", (score_combine<32, 1>), comb_grid, dim3(256), s, p, heads);
     return KVC_OK;
   }
   KVC_LAUNCH_SHM("score_pass1", k1, dim3(g1), dim3(kThreads), lds1, s, p);
