@@ -678,7 +678,11 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
     }
   };
 
-  float2 st[kCB];
+  // per query block (reference, sum) of the lane's row, indexed by the
+  // wave-uniform block number: register vectors, so the block loop can be a
+  // runtime loop (no scratch, a short loop body)
+  using stvec = float __attribute__((ext_vector_type(kCB)));
+  stvec stm, stl;
   f32x16 colacc[kT];
   int cur = -1;
   float cc = 0.f;
@@ -691,7 +695,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
     for (int f0 = 0; f0 < kCB; f0 += kFoldBlocks) {
       if (f0 < nb) {
 #pragma unroll
-        for (int qq = 0; qq < kFoldBlocks; ++qq) fold[((wave * kFoldBlocks + qq) * 32 + col) * 2 + hb] = st[f0 + qq];
+        for (int qq = 0; qq < kFoldBlocks; ++qq) fold[((wave * kFoldBlocks + qq) * 32 + col) * 2 + hb] = float2{stm[f0 + qq], stl[f0 + qq]};
         __syncthreads();
         {
           constexpr int kTPR = kThreads / (kFoldBlocks * 32);
@@ -765,7 +769,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
         for (int t = 0; t < kT; ++t)
 #pragma unroll
           for (int e = 0; e < 16; ++e) l += fast_exp2(fmaf(acc[t][e], cc, -m2s));
-        s.y *= fast_exp2(mrs - m2s);   // s.y = 0 while no reference exists
+        if (mref != -INFINITY) s.y *= fast_exp2(mrs - m2s);   // (s.y = 0 while no reference exists)
         s.x = m2;
       }
     }
@@ -788,7 +792,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
       cc = alpha * kLog2e;
       if (!kPass2) {
 #pragma unroll
-        for (int qb = 0; qb < kCB; ++qb) st[qb] = float2{-INFINITY, 0.f};
+        for (int qb = 0; qb < kCB; ++qb) {
+          stm[qb] = -INFINITY;
+          stl[qb] = 0.f;
+        }
       }
     }
     if (it != 0 && kPF > 0) {
@@ -815,18 +822,32 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
     if (kPreQ) read_q(0);
     if (!kPass2) {
       const bool clean = wave_full && nb * 32 == p.R;
-      static_for<0, kCB>([&](auto qb_c) {
-        constexpr int qb = decltype(qb_c)::value;
-        if (qb < nb) {
-          f32x16 acc[kT];
-          if (!kPreQ) read_q(qb);
-          mfma_block(acc);
-          if (kPreQ && qb + 1 < nb) read_q(qb + 1);
-          if (qb == kCB - 1) tail_prefetch();
-          stats(clean, acc, key0, qb * 32 + col, st[qb]);
-        }
-      });
-      if (nb < kCB) tail_prefetch();
+      auto block1 = [&](int qb, bool last) {
+        f32x16 acc[kT];
+        if (!kPreQ) read_q(qb);
+        mfma_block(acc);
+        if (last)
+          tail_prefetch();
+        else if (kPreQ)
+          read_q(qb + 1);
+        float2 sq = float2{stm[qb], stl[qb]};
+        stats(clean, acc, key0, qb * 32 + col, sq);
+        stm[qb] = sq.x;
+        stl[qb] = sq.y;
+      };
+      if constexpr (kW == 8) {
+        // a runtime loop (the 16-block unrolled body was 48 KB of code); the
+        // last block is peeled, as in pass 2, to issue the tail prefetch
+#pragma unroll 1
+        for (int qb = 0; qb < nb - 1; ++qb) block1(qb, false);
+        block1(nb - 1, true);
+      } else {
+        // unrolled: the runtime loop's indexing registers would pass 256 VGPRs
+        static_for<0, kCB>([&](auto qb_c) {
+          constexpr int qb = decltype(qb_c)::value;
+          if (qb < nb) block1(qb, qb == nb - 1);
+        });
+      }
     } else {
 #pragma unroll
       for (int t = 0; t < kT; ++t) colacc[t] = f32x16{};
