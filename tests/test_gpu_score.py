@@ -75,6 +75,23 @@ def test_outlier_channels_and_explicit_scale():
     check_importance(gpu, ref, 4, "outliers")
 
 
+@pytest.mark.parametrize("H,Hkv,w,S", [(8, 2, 32, 1100), (32, 8, 128, 2100)])
+def test_far_negative_logits(H, Hkv, w, S):
+    # Q near -3 and K near +3 in every channel: every logit is near -1150 * alpha, about
+    # -147 in log2 units, so a block's exponentials against its own maximum are fine but
+    # 2^(0 - max) overflows fp32.  A row's first block (no reference yet) must not
+    # rescale its empty sum by that factor (0 * inf).  Both the 4-wave (R = 128) and the
+    # 8-wave (R = 512) segment passes.
+    rng = np.random.default_rng(17)
+    q = -3.0 + 0.25 * rng.standard_normal((H, w, 128), dtype=np.float32)
+    k = 3.0 + 0.25 * rng.standard_normal((Hkv, S, 128), dtype=np.float32)
+    qb, kb = wk.f32_to_bf16_bits(q), wk.f32_to_bf16_bits(k)
+    gpu = _gpu_importance(qb, kb, w=w, S=S)
+    assert np.isfinite(gpu).all()
+    ref = _oracle(qb, kb, w=w, S=S, scale=F32_ALPHA)
+    check_importance(gpu, ref, H // Hkv, f"far negative H={H} Hkv={Hkv} w={w} S={S}")
+
+
 def test_minimal_prefix_of_one_key():
     qb, kb = _draw(4, 2, 1, 2, seed=1)
     gpu = _gpu_importance(qb, kb, w=1, S=2)
