@@ -678,9 +678,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
     }
   };
 
-  // per query block (reference, sum) of the lane's row, indexed by the
-  // wave-uniform block number: register vectors, so the block loop can be a
-  // runtime loop (no scratch, a short loop body)
+  // per query block (reference, sum) of the lane's row (the blocks are
+  // unrolled, so every index is a constant)
   using stvec = float __attribute__((ext_vector_type(kCB)));
   stvec stm, stl;
   f32x16 colacc[kT];
@@ -835,19 +834,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
         stm[qb] = sq.x;
         stl[qb] = sq.y;
       };
-      if constexpr (kW == 8) {
-        // a runtime loop (the 16-block unrolled body was 48 KB of code); the
-        // last block is peeled, as in pass 2, to issue the tail prefetch
-#pragma unroll 1
-        for (int qb = 0; qb < nb - 1; ++qb) block1(qb, false);
-        block1(nb - 1, true);
-      } else {
-        // unrolled: the runtime loop's indexing registers would pass 256 VGPRs
-        static_for<0, kCB>([&](auto qb_c) {
-          constexpr int qb = decltype(qb_c)::value;
-          if (qb < nb) block1(qb, qb == nb - 1);
-        });
-      }
+      static_for<0, kCB>([&](auto qb_c) {
+        constexpr int qb = decltype(qb_c)::value;
+        if (qb < nb) block1(qb, qb == nb - 1);
+      });
     } else {
 #pragma unroll
       for (int t = 0; t < kT; ++t) colacc[t] = f32x16{};
@@ -886,6 +876,193 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
     }
   }
   if (!kPass2 && cur >= 0) flush(cur);
+}
+
+// Pass 1, query-stationary form (8 waves, R <= 512): wave w keeps query rows
+// [64w, 64w + 64) of the head in registers as two B-operand blocks, so each
+// lane carries the statistics of just two rows, in fixed registers, for the
+// whole segment.  The keys stream through LDS: half-units of 256 keys (8
+// tiles of 32) are copied by global_load_lds_dwordx4 into a two-buffer ring,
+// one buffer filling while the other is read, one barrier per half-unit.  A
+// key row's 16-byte chunk c lands at position c ^ (row & 15) of its 256-byte
+// LDS row, so the A-operand reads of 8 or 16 consecutive keys hit distinct
+// banks.  Per tile a wave runs 16 MFMAs (2 row blocks x 8 depth steps).  At
+// the end of a head's segment each row's two half-wave (reference, sum) pairs
+// are merged with one lane exchange; no cross-wave fold, so the segment's
+// partials are written without LDS or barriers.
+constexpr int kQsHalfKeys = 256;                           // keys per ring buffer
+constexpr int kQsTiles = kQsHalfKeys / 32;                 // 32-key tiles per buffer
+constexpr int kQsBufBytes = kQsHalfKeys * kD * 2;          // 64 KB
+constexpr int kQsLds = 2 * kQsBufBytes;
+
+template <int kTag>
+__global__ __launch_bounds__(512, 1) void score_pass1_qs(ScoreParams p) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int kThreads = 512, kKeysPerUnit = 512;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hb = lane >> 5, col = lane & 31;
+  const int heads = p.L * p.Hkv, total = heads * p.nblk;
+  const int nwg = (int)gridDim.x, bid = (int)blockIdx.x;
+  const int per = total / nwg, extra = total % nwg;
+  const int u_first = bid * per + min(bid, extra);
+  const int n_units = per + (bid < extra ? 1 : 0);
+  if (n_units <= 0) return;   // uniform over the workgroup: no barrier is skipped by part of it
+  const int n_half = 2 * n_units;
+  const float inv_w = 1.0f / (float)p.w;
+  auto split_row = [&](int r, int& hh, int& ii) {
+    hh = (int)((float)r * inv_w);
+    ii = r - hh * p.w;
+    if (ii < 0) { --hh; ii += p.w; }
+    if (ii >= p.w) { ++hh; ii -= p.w; }
+  };
+
+  // copy half-unit h (keys key0 .. key0 + 255 of its head, clamped to n - 1)
+  // into ring buffer h & 1: this wave's 8 of the 64 one-KB instructions
+  auto issue_copy = [&](int h) {
+    const int u = u_first + (h >> 1);
+    const int head = u / p.nblk, blk = u - head * p.nblk;
+    const int layer = head / p.Hkv, g = head - layer * p.Hkv;
+    const uint16_t* kb = p.k + layer * p.k_ls + g * p.k_hs;
+    const int key0 = blk * kKeysPerUnit + (h & 1) * kQsHalfKeys;
+    char* buf = lds + (h & 1) * kQsBufBytes;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int blk1k = wave * 8 + i;                    // which KB of the buffer
+      const int row = blk1k * 4 + (lane >> 4);           // key row within the half-unit
+      const int chunk = (lane & 15) ^ (row & 15);        // logical chunk stored at this lane's slot
+      const int key = min(key0 + row, p.n - 1);
+      __builtin_amdgcn_global_load_lds(kb + (int64_t)key * kD + chunk * 8, buf + blk1k * 1024, 16, 0, 0);
+    }
+  };
+
+  // A-operand byte offsets within a tile: lane (col, hb) reads logical chunk
+  // 2 s2 + hb of key row col, stored at position (2 s2 + hb) ^ (col & 15)
+  int aoff[8];
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) aoff[s2] = col * 256 + (((2 * s2) | hb) ^ (col & 15)) * 16;
+
+  bf16x8 qf[2][8];
+  float stm[2], stl[2];
+  int cur = -1;
+  float cc = 0.f;
+  const int row0 = wave * 64;   // this wave's first query row
+
+  auto load_q = [&](int head) {
+    const int layer = head / p.Hkv, g = head - layer * p.Hkv;
+    const uint16_t* qg = p.q + layer * p.q_ls + (int64_t)g * p.G * p.q_hs;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int r = min(row0 + 32 * b + col, p.R - 1);
+      int hh, ii;
+      split_row(r, hh, ii);
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(qg + hh * p.q_hs + (int64_t)ii * kD) + hb;
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) qf[b][s2] = src[2 * s2];
+    }
+  };
+  // merge the two half-waves' (reference, sum) of each row and write the
+  // segment's partial for rows < R
+  auto flush = [&](int head) {
+    const int seg = bid - unit_owner(head * p.nblk, total, nwg);
+    const int64_t base = ((int64_t)head * p.nblk + seg) * p.R;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const float m = stm[b], l = stl[b];
+      const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
+      const float m2 = fmaxf(m, mo);
+      const float m2s = (m2 == -INFINITY) ? 0.f : m2;
+      const float l2 = (m == -INFINITY ? 0.f : l * fast_exp2(m - m2s)) + (mo == -INFINITY ? 0.f : lo * fast_exp2(mo - m2s));
+      const int r = row0 + 32 * b + col;
+      if (hb == 0 && r < p.R) p.part[base + r] = float2{m2, l2};
+    }
+  };
+  // one tile's statistics for both row blocks, against each lane's running
+  // reference (log2 units); a block takes its own maximum where the lane has
+  // no reference yet or the sum would leave fp32 range
+  auto stats = [&](f32x16 (&acc)[2], int key_t, bool clean) {
+    if (!clean) {
+      const int lim = p.n - key_t - 4 * hb;   // element (e) is key key_t + 4hb + 8(e/4) + e%4
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const bool row_ok = row0 + 32 * b + col < p.R;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (!row_ok || 8 * (e >> 2) + (e & 3) >= lim) acc[b][e] = -INFINITY;
+      }
+    }
+    float l[2] = {0.f, 0.f};
+    bool redo[2] = {stm[0] == -INFINITY, stm[1] == -INFINITY};
+    if (!__ballot(redo[0] || redo[1])) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) l[b] += fast_exp2(fmaf(acc[b][e], cc, -stm[b]));
+        redo[b] = !(l[b] < 0x1p64f);
+      }
+    }
+    if (__ballot(redo[0] || redo[1])) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        if (redo[b]) {
+          float mx = acc[b][0];
+#pragma unroll
+          for (int e = 1; e < 16; ++e) mx = fmaxf(mx, acc[b][e]);
+          const float mref = stm[b];
+          const float m2 = fmaxf(mref, mx * cc);
+          const float m2s = (m2 == -INFINITY) ? 0.f : m2;
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s += fast_exp2(fmaf(acc[b][e], cc, -m2s));
+          l[b] = s;
+          if (mref != -INFINITY) stl[b] *= fast_exp2(mref - m2s);   // (no reference: the sum is 0)
+          stm[b] = m2;
+        }
+      }
+    }
+    stl[0] += l[0];
+    stl[1] += l[1];
+  };
+
+  issue_copy(0);
+#pragma unroll 1
+  for (int h = 0; h < n_half; ++h) {
+    const int u = u_first + (h >> 1);
+    const int head = u / p.nblk, blk = u - head * p.nblk;
+    if (head != cur) {
+      if (cur >= 0) flush(cur);
+      load_q(head);
+      cur = head;
+      const int layer = head / p.Hkv;
+      cc = (p.layer_scales ? p.layer_scales[layer] : p.scale) * kLog2e;
+      stm[0] = stm[1] = -INFINITY;
+      stl[0] = stl[1] = 0.f;
+    }
+    // this wave's part of half-unit h (and the head's rows) have landed; the
+    // barrier makes every wave's part visible and ends every wave's reads of
+    // the other buffer, which the next copy then refills
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (h + 1 < n_half) issue_copy(h + 1);
+    const char* buf = lds + (h & 1) * kQsBufBytes;
+    const int key_h = blk * kKeysPerUnit + (h & 1) * kQsHalfKeys;
+    const bool rows_full = row0 + 64 <= p.R;
+    static_for<0, kQsTiles>([&](auto t_c) {
+      constexpr int t = decltype(t_c)::value;
+      bf16x8 kfr[8];
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) kfr[s2] = *reinterpret_cast<const bf16x8*>(buf + t * 32 * 256 + aoff[s2]);
+      f32x16 acc[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[b] = f32x16{};
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[s2], qf[b][s2], acc[b], 0, 0, 0);
+      const int key_t = key_h + 32 * t;
+      stats(acc, key_t, rows_full && key_t + 32 <= p.n);
+    });
+  }
+  flush(cur);
 }
 
 // Fold the per-unit partials of each query row into
@@ -1034,8 +1211,18 @@ kvc_status launch_score_seg(ScoreParams p, const Plan& pl, hipStream_t s, bool p
   constexpr int kThreads = kW * kWave;
   const int units = p.L * p.Hkv * pl.nblk;
   const int heads = p.L * p.Hkv;
-  const size_t lds1 = score_lds_bytes(pl.chunk_rows, kW, false), lds2 = score_lds_bytes(pl.chunk_rows, kW, true);
-  auto k1 = pass2 ? score_pass_seg<false, kW, kT, kCB, kPF1, kPreQ1, 0> : score_pass_seg<false, kW, kT, kCB, kPF1, kPreQ1, 1>;
+  // the 8-wave shape's pass 1 is the query-stationary kernel (same units,
+  // segments and partials; kPF1 and kPreQ1 do not apply to it)
+  constexpr bool kQs = kW == 8;
+  const size_t lds1 = kQs ? (size_t)kQsLds : score_lds_bytes(pl.chunk_rows, kW, false);
+  const size_t lds2 = score_lds_bytes(pl.chunk_rows, kW, true);
+  auto pick_pass1 = [pass2]() {
+    if constexpr (kQs)
+      return pass2 ? score_pass1_qs<0> : score_pass1_qs<1>;
+    else
+      return pass2 ? score_pass_seg<false, kW, kT, kCB, kPF1, kPreQ1, 0> : score_pass_seg<false, kW, kT, kCB, kPF1, kPreQ1, 1>;
+  };
+  auto k1 = pick_pass1();
   auto k2 = score_pass_seg<true, kW, kT, kCB, kPF2, kPreQ2, 0>;
   int g1 = 0, g2 = 0;
   kvc_status st = score_grid(k1, kThreads, lds1, units, &g1);
