@@ -745,15 +745,15 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
     }
     const float mref = s.x;
     const float mrs = (mref == -INFINITY) ? 0.f : mref;
+    // every lane sums against its own reference, also while other lanes of
+    // the wave have none (rows past R never get one); a lane without one, or
+    // whose sum leaves fp32 range, redoes the block against its maximum
     float l = 0.f;
-    bool redo = mref == -INFINITY;   // no reference yet: take the block maximum directly
-    if (!__ballot(redo)) {
 #pragma unroll
-      for (int t = 0; t < kT; ++t)
+    for (int t = 0; t < kT; ++t)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) l += fast_exp2(fmaf(acc[t][e], cc, -mrs));
-      redo = !(l < 0x1p64f);   // a key far above the reference: rescale
-    }
+      for (int e = 0; e < 16; ++e) l += fast_exp2(fmaf(acc[t][e], cc, -mrs));
+    const bool redo = mref == -INFINITY || !(l < 0x1p64f);
     if (__ballot(redo)) {
       if (redo) {
         float mx = acc[0][0];
@@ -990,15 +990,16 @@ __global__ __launch_bounds__(512, 1) void score_pass1_qs(ScoreParams p) {
           if (!row_ok || 8 * (e >> 2) + (e & 3) >= lim) acc[b][e] = -INFINITY;
       }
     }
+    // every lane sums against its own references, also while other lanes
+    // of the wave have none (rows past R never get one)
     float l[2] = {0.f, 0.f};
-    bool redo[2] = {stm[0] == -INFINITY, stm[1] == -INFINITY};
-    if (!__ballot(redo[0] || redo[1])) {
+    bool redo[2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 2; ++b) {
+      const float mrs = (stm[b] == -INFINITY) ? 0.f : stm[b];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) l[b] += fast_exp2(fmaf(acc[b][e], cc, -stm[b]));
-        redo[b] = !(l[b] < 0x1p64f);
-      }
+      for (int e = 0; e < 16; ++e) l[b] += fast_exp2(fmaf(acc[b][e], cc, -mrs));
+      redo[b] = stm[b] == -INFINITY || !(l[b] < 0x1p64f);
     }
     if (__ballot(redo[0] || redo[1])) {
 #pragma unroll

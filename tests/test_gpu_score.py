@@ -75,6 +75,20 @@ def test_outlier_channels_and_explicit_scale():
     check_importance(gpu, ref, 4, "outliers")
 
 
+@pytest.mark.parametrize("H,Hkv,w,S", [
+    (8, 2, 20, 300000),    # R = 80, 4-wave shape: rows 80..95 of the last block are past R; ~4.6 units per workgroup
+    (8, 2, 75, 150000),    # R = 300, 8-wave shape: wave 4 part-filled, waves 5..7 empty; ~2.3 units per workgroup
+])
+def test_ragged_rows_many_units(H, Hkv, w, S):
+    """Rows past R never get a reference maximum.  The lanes holding valid rows
+    of the same wave must still add every later tile's exponentials, so the
+    segments have to run several units each (long prefixes)."""
+    qb, kb = _draw(H, Hkv, w, S, seed=w * 7 + S)
+    gpu = _gpu_importance(qb, kb, w=w, S=S)
+    ref = _oracle(qb, kb, w=w, S=S, scale=F32_ALPHA)
+    check_importance(gpu, ref, H // Hkv, f"ragged rows H={H} Hkv={Hkv} w={w} S={S}")
+
+
 @pytest.mark.parametrize("H,Hkv,w,S", [(8, 2, 32, 1100), (32, 8, 128, 2100)])
 def test_far_negative_logits(H, Hkv, w, S):
     # Q near -3 and K near +3 in every channel: every logit is near -1150 * alpha, about
