@@ -111,6 +111,19 @@ struct ScoreParams {
                      // this many workgroups (score_pass_seg); 0: one partial per (head, unit)
 };
 
+// Workgroup i runs on XCD i % 8.  With the grid a multiple of 8, the 8-wave
+// segment passes number their workgroups XCD-major, so each XCD takes a
+// contiguous eighth of the units: its L2 then holds the query rows and row
+// partials of about an eighth of the heads (on the 32K-token GQA layer each
+// XCD's workgroups load one head's 128 KB of rows instead of all eight), and
+// a workgroup of pass 2 still finds the keys the same-numbered workgroup of
+// pass 1 read last in its own L2.  The 4-wave passes keep the plain order,
+// which measured faster there (131K-token layer, 64 rows per head).
+__device__ inline int xcd_major_block(int nwg) {
+  const int b = (int)blockIdx.x;
+  return (nwg & 7) == 0 ? (b & 7) * (nwg >> 3) + (b >> 3) : b;
+}
+
 // Contiguous unit ranges over a grid of `grid` workgroups: the workgroup that
 // owns unit u (every workgroup owns per or per + 1 consecutive units).
 __host__ __device__ inline int unit_owner(int u, int total, int grid) {
@@ -587,9 +600,11 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
   };
   const int heads = p.L * p.Hkv;
   const int total = heads * p.nblk;
-  const int per = total / (int)gridDim.x, extra = total % (int)gridDim.x;
-  const int u_first = (int)blockIdx.x * per + min((int)blockIdx.x, extra);
-  const int n_units = per + ((int)blockIdx.x < extra ? 1 : 0);
+  // the 8-wave pass 2 numbers its workgroups like the query-stationary pass 1
+  const int nwg = (int)gridDim.x, bid = kW == 8 ? xcd_major_block(nwg) : (int)blockIdx.x;
+  const int per = total / nwg, extra = total % nwg;
+  const int u_first = bid * per + min(bid, extra);
+  const int n_units = per + (bid < extra ? 1 : 0);
   // pass 2 walks its range backwards: its first keys are the ones pass 1 read last
   auto unit_at = [&](int it) { return kPass2 ? u_first + n_units - 1 - it : u_first + it; };
 
@@ -688,7 +703,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void score_pass_seg(ScoreParams p) {
   // pass 1: fold each lane's per-block (max, sum) over the 2*kW half-waves of
   // every row, kFoldBlocks query blocks at a time through LDS, in a fixed order
   auto flush = [&](int head) {
-    const int seg = (int)blockIdx.x - unit_owner(head * p.nblk, total, (int)gridDim.x);
+    const int seg = bid - unit_owner(head * p.nblk, total, nwg);
     const int64_t base = ((int64_t)head * p.nblk + seg) * p.R;
 #pragma unroll
     for (int f0 = 0; f0 < kCB; f0 += kFoldBlocks) {
@@ -902,7 +917,7 @@ __global__ __launch_bounds__(512, 1) void score_pass1_qs(ScoreParams p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hb = lane >> 5, col = lane & 31;
   const int heads = p.L * p.Hkv, total = heads * p.nblk;
-  const int nwg = (int)gridDim.x, bid = (int)blockIdx.x;
+  const int nwg = (int)gridDim.x, bid = xcd_major_block(nwg);
   const int per = total / nwg, extra = total % nwg;
   const int u_first = bid * per + min(bid, extra);
   const int n_units = per + (bid < extra ? 1 : 0);
@@ -916,23 +931,29 @@ __global__ __launch_bounds__(512, 1) void score_pass1_qs(ScoreParams p) {
     if (ii >= p.w) { ++hh; ii -= p.w; }
   };
 
-  // copy half-unit h (keys key0 .. key0 + 255 of its head, clamped to n - 1)
-  // into ring buffer h & 1: this wave's 8 of the 64 one-KB instructions
+  // copy half-unit h (keys key0 .. key0 + 255 of its head) into ring buffer
+  // h & 1: copy instruction i of wave w moves the KB holding keys
+  // 32i + 4w .. 32i + 4w + 3 (tile i), so a lane's key row differs between
+  // its instructions by 32 and its chunk (lane & 15) ^ (row & 15) not at all;
+  // the key base and LDS slot are uniform
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int cp_row = 4 * wave_u + (lane >> 4);                 // + 32 i
+  const int cp_off = (cp_row * kD + (((lane & 15) ^ (cp_row & 15)) * 8)) * 2;   // bytes
   auto issue_copy = [&](int h) {
     const int u = u_first + (h >> 1);
     const int head = u / p.nblk, blk = u - head * p.nblk;
     const int layer = head / p.Hkv, g = head - layer * p.Hkv;
-    const uint16_t* kb = p.k + layer * p.k_ls + g * p.k_hs;
     const int key0 = blk * kKeysPerUnit + (h & 1) * kQsHalfKeys;
-    char* buf = lds + (h & 1) * kQsBufBytes;
+    const uint16_t* kb = p.k + layer * p.k_ls + g * p.k_hs + (int64_t)key0 * kD;
+    // a buffer over the half-unit's keys inside the prefix: rows past it
+    // read as zeros (the statistics mask them)
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, min(kQsHalfKeys, p.n - key0) * kD * 2, 0x00020000);
+    char* buf = lds + (h & 1) * kQsBufBytes + wave_u * 1024;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int blk1k = wave * 8 + i;                    // which KB of the buffer
-      const int row = blk1k * 4 + (lane >> 4);           // key row within the half-unit
-      const int chunk = (lane & 15) ^ (row & 15);        // logical chunk stored at this lane's slot
-      const int key = min(key0 + row, p.n - 1);
-      __builtin_amdgcn_global_load_lds(kb + (int64_t)key * kD + chunk * 8, buf + blk1k * 1024, 16, 0, 0);
-    }
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(buf + i * 8192), 16,
+                                               cp_off + i * 32 * kD * 2, 0, 0, 0);
   };
 
   // A-operand byte offsets within a tile: lane (col, hb) reads logical chunk
@@ -977,44 +998,43 @@ __global__ __launch_bounds__(512, 1) void score_pass1_qs(ScoreParams p) {
     }
   };
   // one tile's statistics for both row blocks, against each lane's running
-  // reference (log2 units); a block takes its own maximum where the lane has
-  // no reference yet or the sum would leave fp32 range
-  auto stats = [&](f32x16 (&acc)[2], int key_t, bool clean) {
-    if (!clean) {
-      const int lim = p.n - key_t - 4 * hb;   // element (e) is key key_t + 4hb + 8(e/4) + e%4
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const bool row_ok = row0 + 32 * b + col < p.R;
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (!row_ok || 8 * (e >> 2) + (e & 3) >= lim) acc[b][e] = -INFINITY;
-      }
-    }
-    // every lane sums against its own references, also while other lanes
-    // of the wave have none (rows past R never get one)
-    float l[2] = {0.f, 0.f};
-    bool redo[2];
+  // reference (log2 units).  stats_sum is branch-free: every lane sums
+  // against its own references, also while other lanes of the wave have none
+  // (rows past R never get one); stats_fix lets a block take its own maximum
+  // where the lane has no reference yet or the sum left fp32 range
+  auto stats_sum = [&](const f32x16 (&acc)[2], float (&l)[2], bool& redo) {
+    redo = false;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const float mrs = (stm[b] == -INFINITY) ? 0.f : stm[b];
+      float s0 = fast_exp2(fmaf(acc[b][0], cc, -mrs)), s1 = fast_exp2(fmaf(acc[b][1], cc, -mrs));
 #pragma unroll
-      for (int e = 0; e < 16; ++e) l[b] += fast_exp2(fmaf(acc[b][e], cc, -mrs));
-      redo[b] = stm[b] == -INFINITY || !(l[b] < 0x1p64f);
+      for (int e = 2; e < 16; e += 2) {
+        s0 += fast_exp2(fmaf(acc[b][e], cc, -mrs));
+        s1 += fast_exp2(fmaf(acc[b][e + 1], cc, -mrs));
+      }
+      l[b] = s0 + s1;
+      redo = redo || stm[b] == -INFINITY || !(l[b] < 0x1p64f);
     }
-    if (__ballot(redo[0] || redo[1])) {
+  };
+  auto stats_fix = [&](const f32x16 (&acc)[2], float (&l)[2], bool redo) {
+    if (__ballot(redo)) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        if (redo[b]) {
+        if (stm[b] == -INFINITY || !(l[b] < 0x1p64f)) {
           float mx = acc[b][0];
 #pragma unroll
           for (int e = 1; e < 16; ++e) mx = fmaxf(mx, acc[b][e]);
           const float mref = stm[b];
           const float m2 = fmaxf(mref, mx * cc);
           const float m2s = (m2 == -INFINITY) ? 0.f : m2;
-          float s = 0.f;
+          float s0 = fast_exp2(fmaf(acc[b][0], cc, -m2s)), s1 = fast_exp2(fmaf(acc[b][1], cc, -m2s));
 #pragma unroll
-          for (int e = 0; e < 16; ++e) s += fast_exp2(fmaf(acc[b][e], cc, -m2s));
-          l[b] = s;
+          for (int e = 2; e < 16; e += 2) {
+            s0 += fast_exp2(fmaf(acc[b][e], cc, -m2s));
+            s1 += fast_exp2(fmaf(acc[b][e + 1], cc, -m2s));
+          }
+          l[b] = s0 + s1;
           if (mref != -INFINITY) stl[b] *= fast_exp2(mref - m2s);   // (no reference: the sum is 0)
           stm[b] = m2;
         }
@@ -1023,20 +1043,65 @@ __global__ __launch_bounds__(512, 1) void score_pass1_qs(ScoreParams p) {
     stl[0] += l[0];
     stl[1] += l[1];
   };
+  auto stats = [&](f32x16 (&acc)[2]) {
+    float l[2];
+    bool redo;
+    stats_sum(acc, l, redo);
+    stats_fix(acc, l, redo);
+  };
+  auto load_tile = [&](bf16x8 (&kf)[8], const char* tp) {
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) kf[s2] = *reinterpret_cast<const bf16x8*>(tp + aoff[s2]);
+  };
+  auto mfma_tile = [&](f32x16 (&acc)[2], const bf16x8 (&kf)[8]) {
+    acc[0] = f32x16{};
+    acc[1] = f32x16{};
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s2], qf[b][s2], acc[b], 0, 0, 0);
+  };
 
+  // Half-units whose 256 keys are all in the prefix run as a software
+  // pipeline: each step issues tile t's MFMAs (into acc2[t & 1]), the LDS
+  // reads of tile t + 1 and the statistics of tile t - 1, with no branch
+  // between them but the rare redo, so the MFMAs run under the vector work.
+  // The last tile's statistics are pending into the next half-unit (pend).
+  // Rows past R need no mask: their query rows are copies of row R - 1 and
+  // flush skips them.
+  f32x16 acc2[2][2];
+  bf16x8 kf2[2][8];
+  bool pend = false;
+  auto drain = [&] {
+    if (pend) stats(acc2[1]);
+    pend = false;
+  };
+  auto step = [&](auto t_c, auto pend_c, const char* buf) {
+    constexpr int t = decltype(t_c)::value, c = t & 1, o = c ^ 1;
+    constexpr bool kPend = decltype(pend_c)::value;
+    if (t + 1 < kQsTiles) load_tile(kf2[o], buf + (t + 1) * 32 * 256);
+    mfma_tile(acc2[c], kf2[c]);
+    if (kPend) stats(acc2[o]);
+  };
+
+  auto set_head = [&](int head) {
+    load_q(head);
+    cur = head;
+    const int layer = head / p.Hkv;
+    cc = (p.layer_scales ? p.layer_scales[layer] : p.scale) * kLog2e;
+    stm[0] = stm[1] = -INFINITY;
+    stl[0] = stl[1] = 0.f;
+  };
+  set_head(u_first / p.nblk);
   issue_copy(0);
 #pragma unroll 1
   for (int h = 0; h < n_half; ++h) {
     const int u = u_first + (h >> 1);
     const int head = u / p.nblk, blk = u - head * p.nblk;
     if (head != cur) {
-      if (cur >= 0) flush(cur);
-      load_q(head);
-      cur = head;
-      const int layer = head / p.Hkv;
-      cc = (p.layer_scales ? p.layer_scales[layer] : p.scale) * kLog2e;
-      stm[0] = stm[1] = -INFINITY;
-      stl[0] = stl[1] = 0.f;
+      drain();
+      flush(cur);
+      set_head(head);
     }
     // this wave's part of half-unit h (and the head's rows) have landed; the
     // barrier makes every wave's part visible and ends every wave's reads of
@@ -1046,23 +1111,40 @@ __global__ __launch_bounds__(512, 1) void score_pass1_qs(ScoreParams p) {
     if (h + 1 < n_half) issue_copy(h + 1);
     const char* buf = lds + (h & 1) * kQsBufBytes;
     const int key_h = blk * kKeysPerUnit + (h & 1) * kQsHalfKeys;
-    const bool rows_full = row0 + 64 <= p.R;
-    static_for<0, kQsTiles>([&](auto t_c) {
-      constexpr int t = decltype(t_c)::value;
-      bf16x8 kfr[8];
+    if (key_h + kQsHalfKeys <= p.n) {
+      load_tile(kf2[0], buf);
+      if (pend)
+        step(std::integral_constant<int, 0>{}, std::true_type{}, buf);
+      else
+        step(std::integral_constant<int, 0>{}, std::false_type{}, buf);
+      static_for<1, kQsTiles>([&](auto t_c) { step(t_c, std::true_type{}, buf); });
+      pend = true;
+    } else {
+      // the head's last, part-filled half-unit, tile by tile: keys past the
+      // prefix take -inf
+      drain();
+      static_for<0, kQsTiles>([&](auto t_c) {
+        constexpr int t = decltype(t_c)::value;
+        const int key_t = key_h + 32 * t;
+        if (key_t < p.n) {
+          bf16x8 kfr[8];
+          load_tile(kfr, buf + t * 32 * 256);
+          f32x16 acc[2];
+          mfma_tile(acc, kfr);
+          if (key_t + 32 > p.n) {
+            const int lim = p.n - key_t - 4 * hb;   // element (e) is key key_t + 4hb + 8(e/4) + e%4
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) kfr[s2] = *reinterpret_cast<const bf16x8*>(buf + t * 32 * 256 + aoff[s2]);
-      f32x16 acc[2];
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) acc[b] = f32x16{};
-#pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[s2], qf[b][s2], acc[b], 0, 0, 0);
-      const int key_t = key_h + 32 * t;
-      stats(acc, key_t, rows_full && key_t + 32 <= p.n);
-    });
+              for (int e = 0; e < 16; ++e)
+                if (8 * (e >> 2) + (e & 3) >= lim) acc[b][e] = -INFINITY;
+          }
+          stats(acc);
+        }
+      });
+    }
   }
+  drain();
   flush(cur);
 }
 
