@@ -1387,7 +1387,7 @@ kvc_status score_entry(const kvc_score_args* a, const void* q_obs, const void* k
   if (a->gumbel) return launch_score<true, false, 4, 1, 4, 0, 0>(p, pl, s);
   if (pl.shape.kw == 8 && pl.R <= pl.chunk_rows) return launch_score_seg<8, 2, 16, 0, true, 1, true>(p, pl, s);
   if (pl.shape.kw == 8) return launch_score<false, false, 8, 2, 16, 1, 2>(p, pl, s);
-  return launch_score_seg<4, 2, 8, 2, true, 1, true>(p, pl, s);
+  return launch_score_seg<4, 2, 8, 1, true, 1, true>(p, pl, s);
 }
 
 }  // namespace
@@ -1465,7 +1465,7 @@ kvc_status score_rowc(const uint16_t* q, int64_t q_hs, const uint16_t* k, int64_
   *rowc = p.rowc;
   if (pl.shape.kw == 8 && pl.R <= pl.chunk_rows) return launch_score_seg<8, 2, 16, 0, true, 1, true>(p, pl, s, false);
   if (pl.shape.kw == 8) return launch_score<false, false, 8, 2, 16, 1, 2>(p, pl, s, false);
-  return launch_score_seg<4, 2, 8, 2, true, 1, true>(p, pl, s, false);
+  return launch_score_seg<4, 2, 8, 1, true, 1, true>(p, pl, s, false);
 }
 
 }  // namespace kvc
