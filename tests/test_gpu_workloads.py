@@ -91,14 +91,15 @@ def test_snapkv_mha8_s2048():
 def test_gqa32x8_s32768():
     wl = wk.WORKLOADS["gqa32x8_s32768"]
     plan, (q, k, v), sc = _run(wl)
-    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=[0, 5])
+    # every head: each is scored by its own 32 of the 256 workgroups
+    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=range(wl.Hkv))
     print("selection:", kinds)
 
 
 def test_gqa32x8_s32768_pool7():
     wl = wk.WORKLOADS["gqa32x8_s32768_pool7"]
     plan, (q, k, v), sc = _run(wl)
-    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=[3])
+    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=range(wl.Hkv))
     print("selection:", kinds)
 
 
@@ -106,14 +107,15 @@ def test_gqa32x8_s32768_pool7():
 def test_keyformer_mha32_s8192(tau):
     wl = wk.WORKLOADS["keyformer_mha32_s8192"]
     plan, (q, k, v), sc = _run(wl, tau=tau)
-    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=[0, 17], tau=tau)
+    # one KV head per eighth of the 32 (each its own noise stream)
+    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=[0, 5, 9, 14, 17, 22, 26, 31], tau=tau)
     print("selection:", kinds)
 
 
 def test_think_s131072():
     wl = wk.WORKLOADS["think_s131072"]
     plan, (q, k, v), sc = _run(wl)
-    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=[3])
+    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=range(wl.Hkv))
     print("selection:", kinds)
     # ThinK on the GPU's compacted keys, every head
     kc = bits_of(plan.kc)
@@ -134,7 +136,7 @@ def test_think_s131072():
 def test_think_s131072_query():
     wl = wk.WORKLOADS["think_s131072_query"]
     plan, (q, k, v), sc = _run(wl)
-    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=[5])
+    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=[2, 5])
     print("selection:", kinds)
     # query-driven ThinK on the GPU's compacted keys and the window queries, every head
     kc = bits_of(plan.kc)
@@ -156,7 +158,7 @@ def test_think_s131072_query():
 def test_think_s131072_kv():
     wl = wk.WORKLOADS["think_s131072_kv"]
     plan, (q, k, v), sc = _run(wl)
-    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=[1])
+    kinds = _check_uniform_budget_layer(wl, plan, q, k, v, sc[0], heads=[1, 6])
     print("selection:", kinds)
     f64 = oracle.score.bf16_bits_to_f64
     kc, vc = bits_of(plan.kc), bits_of(plan.vc)
@@ -268,18 +270,20 @@ def test_gqa32x8_s32768_thr2():
     # packed compaction, every head: bit-exact against the gather at the GPU's indices
     assert np.array_equal(bits_of(plan.kc_flat[:total]), oracle.threshold.compact_ragged(k, ri, ro))
     assert np.array_equal(bits_of(plan.vc_flat[:total]), oracle.threshold.compact_ragged(v, ri, ro))
-    # a sampled head against the oracle's own importance: the keep decision may
+    # sampled heads against the oracle's own importance: the keep decision may
     # differ only for candidates within the importance tolerance of theta
-    g = 2
-    ref = _oracle_imp(wl, q, k, sc[0], [g])[g]
-    check_importance(imp[g][None], ref[None], wl.G, f"head {g}")
+    heads = [2, 6]
+    refs = _oracle_imp(wl, q, k, sc[0], heads)
     c = wl.n_candidates
-    mine = set(gi[go[g]:go[g + 1]].tolist())
-    theirs = set(oracle.threshold.select_threshold(ref, S=wl.S, w=wl.w, recent=wl.recent,
-                                                   theta=float(theta)).tolist())
-    for j in mine ^ theirs:
-        assert j < c and abs(ref[j] - float(theta)) <= 1e-3 * ref[j], f"candidate {j} decided away from theta"
-    print("decisions that differ near theta:", len(mine ^ theirs))
+    for g in heads:
+        ref = refs[g]
+        check_importance(imp[g][None], ref[None], wl.G, f"head {g}")
+        mine = set(gi[go[g]:go[g + 1]].tolist())
+        theirs = set(oracle.threshold.select_threshold(ref, S=wl.S, w=wl.w, recent=wl.recent,
+                                                       theta=float(theta)).tolist())
+        for j in mine ^ theirs:
+            assert j < c and abs(ref[j] - float(theta)) <= 1e-3 * ref[j], f"candidate {j} decided away from theta"
+        print(f"head {g}: decisions that differ near theta:", len(mine ^ theirs))
 
 
 def test_zigzag_l32_s16384():
@@ -306,7 +310,7 @@ def test_zigzag_l32_s16384():
         assert np.array_equal(bits_of(kc_t), oracle.compact.compact(k[l], idx))
         assert np.array_equal(bits_of(vc_t), oracle.compact.compact(v[l], idx))
     # sampled (layer, head) rows against the oracle's own importance, incl. MBA
-    for l, g in [(0, 0), (13, 5), (31, 7)]:
+    for l, g in [(0, 0), (4, 1), (9, 2), (13, 5), (18, 3), (22, 6), (27, 4), (31, 7)]:
         ref = _oracle_imp(wl, q[l], k[l], scales[l], [g])[g]
         check_importance(imp[l, g][None], ref[None], 1, f"layer {l} head {g}")
         m_ref = oracle.budget.mba(ref, wl.mass)
