@@ -81,8 +81,11 @@ int launch_begin(const char* name, hipStream_t s) {
   (void)hipGetLastError();  // start from a clean error state
   if (!g_timing) return -1;
   Record r{name, nullptr, nullptr};
-  if (hipEventCreate(&r.start) != hipSuccess) return -1;
-  if (hipEventCreate(&r.stop) != hipSuccess) {
+  // timing-only events: no system-scope fence (an L2 writeback and
+  // invalidate) when they signal, which would slow the launch being timed
+  // and the one after it
+  if (hipEventCreateWithFlags(&r.start, hipEventDisableSystemFence) != hipSuccess) return -1;
+  if (hipEventCreateWithFlags(&r.stop, hipEventDisableSystemFence) != hipSuccess) {
     (void)hipEventDestroy(r.start);
     return -1;
   }
