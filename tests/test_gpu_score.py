@@ -204,3 +204,16 @@ def test_many_layers_with_layer_scales():
     for l, g in ((0, 1), (4, 2), (5, 3)):
         ref = _oracle(qb[l], kb[l], w=w, S=S, scale=float(scales[l]), kv_heads=[g])
         check_importance(gpu[l, g][None], ref[g][None], H // Hkv, f"layer {l} head {g}")
+
+
+@pytest.mark.parametrize("gumbel", [False, True])
+def test_largest_query_group_accepted(gumbel):
+    """G * w = 65536 query rows per KV head, the most the boundary accepts:
+    128 staged chunks of 512 rows (Keyformer noise: 512 chunks of 128) for
+    every unit of a 333-key prefix (a ragged last unit)."""
+    H, Hkv, w, S = 64, 1, 1024, 1024 + 333
+    qb, kb = _draw(H, Hkv, w, S, seed=65536 + gumbel)
+    kw = dict(gumbel=True, tau=1.0, seed=5) if gumbel else {}
+    gpu = _gpu_importance(qb, kb, w=w, S=S, **kw)
+    ref = _oracle(qb, kb, w=w, S=S, scale=F32_ALPHA, **kw)
+    check_importance(gpu, ref, H // Hkv, f"G*w = 65536, gumbel={gumbel}")
