@@ -102,7 +102,7 @@ int kvc_think_channels(int D, double lambda);
  *   tau > 0 (+inf allowed, NaN rejected) when gumbel != 0, and q_obs / k are
  *   16-byte aligned, importance 4-byte aligned; KVC_E_SHAPE unless
  *   H % Hkv == 0, 1 <= w < S, G * w <= 65536 (G = H / Hkv), L <= 65535,
- *   Hkv <= 65535, q_head_stride >= w*D, k_head_stride >= S*D and, for L > 1,
+ *   Hkv <= 65535, L * Hkv * ceil(n / 128) < 2^31, q_head_stride >= w*D, k_head_stride >= S*D and, for L > 1,
  *   q_layer_stride >= H*q_head_stride and k_layer_stride >= Hkv*k_head_stride;
  *   KVC_E_WORKSPACE if the workspace is missing, short or not 16-byte aligned.
  *   Up to 512 (Keyformer noise: 128) of a KV head's G*w query rows are staged

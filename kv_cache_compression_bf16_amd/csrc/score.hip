@@ -1216,6 +1216,8 @@ kvc_status plan(const kvc_score_args* a, Plan* pl, bool causal = false) {
   if (!a->layer_scales && !(a->scale > 0.f && isfinite(a->scale))) return KVC_E_ARG;
   if (a->gumbel && !(a->tau > 0.f)) return KVC_E_ARG;   // rejects NaN; +inf allowed
   pl->n = causal ? a->S : a->S - a->w;
+  // units of work (at least 128 keys each) are counted in 32-bit integers
+  if ((int64_t)a->L * a->Hkv * ((pl->n + 127) / 128) > INT32_MAX) return KVC_E_SHAPE;
   pl->G = (int)G;
   pl->R = (int)(G * a->w);
   pl->shape = score_shape(pl->R, a->gumbel != 0);

@@ -87,6 +87,9 @@ FAKE2 = ctypes.c_void_p(1 << 21)
     (dict(gumbel=1, tau=float("nan")), E.KVC_E_ARG),
     (dict(k_head_stride=100), E.KVC_E_SHAPE),
     (dict(q_head_stride=32 * 128 + 4), E.KVC_E_ARG),
+    # 65535 layers of 65535 KV heads: more units of work than 32-bit counters hold
+    (dict(L=65535, H=65535, Hkv=65535, q_layer_stride=65535 * 32 * 128, k_layer_stride=65535 * 2048 * 128),
+     E.KVC_E_SHAPE),
 ])
 def test_score_validation(over, status):
     a = _args(**over)
