@@ -120,7 +120,10 @@ __device__ __forceinline__ void block_min_max(uint32_t& lo, uint32_t& hi, uint32
 // [w*kSpan, (w+1)*kSpan) and lane l holds candidates w*kSpan + 64*i + l
 // (i < kVPL), so every load instruction reads 256 contiguous bytes and a lane
 // keeps kVPL loads in flight.  The keys are loaded once and stay in registers
-// for every radix level and the emission.
+// for every radix level and the emission.  They come back as bits ^ 2^31,
+// which is order_key for every value whose sign bit is clear (scores of
+// softmax means always are); the caller redoes them with order_key when a
+// candidate's sign bit is set.
 constexpr int kVPL = 32768 / kSelThreads;          // candidates per lane per round
 constexpr int kSpan = kVPL * kWave;                 // candidates per wave per round
 constexpr int kRound = kSelWaves * kSpan;
@@ -135,7 +138,7 @@ __device__ __forceinline__ void load_round(const uint32_t* v, int c, int r, uint
 #pragma unroll
     for (int i = 0; i < kVPL; ++i) raw[i] = vb[64 * i];
 #pragma unroll
-    for (int i = 0; i < kVPL; ++i) key[i] = order_key(raw[i]);
+    for (int i = 0; i < kVPL; ++i) key[i] = raw[i] ^ 0x80000000u;
     return;
   }
   // Unconditional loads from a clamped address (then masked): a guarded load
@@ -146,7 +149,7 @@ __device__ __forceinline__ void load_round(const uint32_t* v, int c, int r, uint
     raw[i] = v[j < c ? j : c - 1];
   }
 #pragma unroll
-  for (int i = 0; i < kVPL; ++i) key[i] = (base + 64 * i < c) ? order_key(raw[i]) : 0u;
+  for (int i = 0; i < kVPL; ++i) key[i] = (base + 64 * i < c) ? raw[i] ^ 0x80000000u : 0u;
 }
 
 // Keys of the threshold bin are ranked directly once a level leaves at most
@@ -209,21 +212,38 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const float* i
 
   // ---- key range of the candidates (slots past them hold key 0: no effect
   // on the max; the min skips them)
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  if (wave_full) {
+  uint32_t kmin, kmax;
+  auto key_range = [&] {
+    kmin = 0xFFFFFFFFu;
+    kmax = 0u;
+    if (wave_full) {
 #pragma unroll
-    for (int i = 0; i < kVPL; i += 2) {
-      kmin = min(kmin, min(key[i], key[i + 1]));
-      kmax = max(kmax, max(key[i], key[i + 1]));
-    }
-  } else if (!wave_empty) {
+      for (int i = 0; i < kVPL; i += 2) {
+        kmin = min(kmin, min(key[i], key[i + 1]));
+        kmax = max(kmax, max(key[i], key[i + 1]));
+      }
+    } else if (!wave_empty) {
 #pragma unroll
-    for (int i = 0; i < kVPL; ++i) {
-      kmin = min(kmin, lbase + 64 * i < c ? key[i] : 0xFFFFFFFFu);
-      kmax = max(kmax, key[i]);
+      for (int i = 0; i < kVPL; ++i) {
+        kmin = min(kmin, lbase + 64 * i < c ? key[i] : 0xFFFFFFFFu);
+        kmax = max(kmax, key[i]);
+      }
     }
+    block_min_max(kmin, kmax, wsum, wsum2);
+  };
+  key_range();
+  if (kmin < 0x80000000u) {
+    // a candidate's sign bit is set (a negative value, -0 or a negative
+    // NaN): the full order key, and the range again
+    if (wave_full) {
+#pragma unroll
+      for (int i = 0; i < kVPL; ++i) key[i] = order_key(key[i] ^ 0x80000000u);
+    } else if (!wave_empty) {
+#pragma unroll
+      for (int i = 0; i < kVPL; ++i) key[i] = lbase + 64 * i < c ? order_key(key[i] ^ 0x80000000u) : 0u;
+    }
+    key_range();
   }
-  block_min_max(kmin, kmax, wsum, wsum2);
   // From here on key[i] holds d = key - kmin.  The partial wave's slots past
   // the candidates take d = 0: they follow every candidate in position order
   // and no candidate is smaller, so they are never kept (ties are taken in
