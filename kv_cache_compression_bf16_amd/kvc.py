@@ -109,11 +109,16 @@ def _stream(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _workspace(nbytes, device, ws):
+def _workspace(nbytes, device, ws, stream):
     if nbytes == 0:
         return ws, 0
     if ws is None:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if stream is not None:
+            # allocated on the current stream, used on `stream`: without this the
+            # allocator could hand the block to a later call while the kernels
+            # queued on `stream` still use it
+            ws.record_stream(stream)
     return ws, ws.numel() * ws.element_size()
 
 
@@ -176,7 +181,7 @@ def kvc_score(q_obs, k, importance, *, w, S, scale=None, layer_scales=None, gumb
     if importance.dtype != torch.float32 or not importance.is_contiguous() \
             or importance.numel() != a.L * a.Hkv * (S - w):
         raise ValueError("importance must be contiguous float32 with L*Hkv*(S-w) elements")
-    ws, nbytes = _workspace(_lib.kvc_score_workspace_size(ctypes.byref(a)), k.device, workspace)
+    ws, nbytes = _workspace(_lib.kvc_score_workspace_size(ctypes.byref(a)), k.device, workspace, stream)
     _check(_lib.kvc_score(ctypes.byref(a), _ptr(q_obs), _ptr(k), _ptr(importance), _ptr(ws), nbytes,
                           _stream(stream, k.device)), "kvc_score")
     return importance
@@ -213,7 +218,7 @@ def kvc_score_causal(q_obs, k, importance, *, w, S, scale=None, layer_scales=Non
     if importance.dtype != torch.float32 or not importance.is_contiguous() \
             or importance.numel() != a.L * a.Hkv * S:
         raise ValueError("importance must be contiguous float32 with L*Hkv*S elements")
-    ws, nbytes = _workspace(_lib.kvc_score_causal_workspace_size(ctypes.byref(a)), k.device, workspace)
+    ws, nbytes = _workspace(_lib.kvc_score_causal_workspace_size(ctypes.byref(a)), k.device, workspace, stream)
     _check(_lib.kvc_score_causal(ctypes.byref(a), _ptr(q_obs), _ptr(k), _ptr(importance), _ptr(ws), nbytes,
                                  _stream(stream, k.device)), "kvc_score_causal")
     return importance
@@ -228,7 +233,7 @@ def kvc_lmba_budget(importance, budgets, *, total_budget, floor_per_layer, capac
         raise ValueError("importance must be contiguous float32 [L, Hkv, n]")
     ws, nbytes = (workspace, 0)
     if mba is None:
-        ws, nbytes = _workspace(_lib.kvc_lmba_budget_workspace_size(L, Hkv, n), importance.device, workspace)
+        ws, nbytes = _workspace(_lib.kvc_lmba_budget_workspace_size(L, Hkv, n), importance.device, workspace, stream)
     _check(_lib.kvc_lmba_budget(_ptr(importance), L, Hkv, n, float(mass), int(total_budget),
                                 int(floor_per_layer), int(capacity), _ptr(mba), _ptr(budgets), _ptr(ws),
                                 nbytes, _stream(stream, importance.device)), "kvc_lmba_budget")
@@ -262,7 +267,7 @@ def kvc_select_topk(importance, indices, *, S, w, recent, budget, workspace=None
         raise ValueError("importance rows must be float32 with unit stride")
     if indices.dtype != torch.int32 or not indices.is_contiguous() or indices.numel() != Hkv * budget:
         raise ValueError("indices must be contiguous int32 [Hkv, budget]")
-    ws, nbytes = _workspace(_lib.kvc_select_topk_workspace_size(Hkv, S - w), importance.device, workspace)
+    ws, nbytes = _workspace(_lib.kvc_select_topk_workspace_size(Hkv, S - w), importance.device, workspace, stream)
     _check(_lib.kvc_select_topk(_ptr(importance), importance.stride(0), Hkv, S, w, recent, budget,
                                 _ptr(indices), _ptr(ws), nbytes, _stream(stream, importance.device)),
            "kvc_select_topk")
@@ -335,7 +340,8 @@ def kvc_select_threshold(scores, indices, offsets, *, S, w, recent, threshold, w
     c = min(S - w, S - recent)
     if offsets.numel() != Hkv + 1 or indices.numel() < Hkv * (c + recent):
         raise ValueError(f"offsets needs {Hkv + 1} entries and indices {Hkv * (c + recent)}")
-    ws, nbytes = _workspace(_lib.kvc_select_threshold_workspace_size(Hkv, S, w, recent), scores.device, workspace)
+    ws, nbytes = _workspace(_lib.kvc_select_threshold_workspace_size(Hkv, S, w, recent), scores.device,
+                            workspace, stream)
     _check(_lib.kvc_select_threshold(_ptr(scores), scores.stride(0), Hkv, S, w, recent, float(threshold),
                                      _ptr(indices), _ptr(offsets), _ptr(ws), nbytes,
                                      _stream(stream, scores.device)), "kvc_select_threshold")
@@ -368,7 +374,7 @@ def kvc_channel_prune(k_c, channels, k_pruned, *, recent, lam, p=2, mask=None, w
     Hkv, budget, D = k_c.shape
     if not k_c.is_contiguous():
         raise ValueError("k_c must be contiguous")
-    ws, nbytes = _workspace(_lib.kvc_channel_prune_workspace_size(Hkv, budget, D), k_c.device, workspace)
+    ws, nbytes = _workspace(_lib.kvc_channel_prune_workspace_size(Hkv, budget, D), k_c.device, workspace, stream)
     _check(_lib.kvc_channel_prune(_ptr(k_c), Hkv, budget, D, recent, float(lam), int(p), _ptr(channels),
                                   _ptr(mask), _ptr(k_pruned), _ptr(ws), nbytes, _stream(stream, k_c.device)),
            "kvc_channel_prune")
@@ -388,7 +394,7 @@ def kvc_channel_prune_query(k_c, q_obs, channels, k_pruned, *, recent, lam, mask
         raise ValueError(f"shape mismatch: q_obs {tuple(q_obs.shape)}, k_c {tuple(k_c.shape)}")
     G = H // Hkv
     ws, nbytes = _workspace(_lib.kvc_channel_prune_query_workspace_size(Hkv, G, budget, D), k_c.device,
-                            workspace)
+                            workspace, stream)
     _check(_lib.kvc_channel_prune_query(_ptr(k_c), _ptr(q_obs), Hkv, G, w, q_obs.stride(0), budget, D, recent,
                                         float(lam), _ptr(channels), _ptr(mask), _ptr(k_pruned), _ptr(ws), nbytes,
                                         _stream(stream, k_c.device)), "kvc_channel_prune_query")
@@ -409,7 +415,7 @@ def kvc_channel_prune_value(k_c, v_c, q_obs, channels, v_pruned, *, recent, lam,
     G = H // Hkv
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     ws, nbytes = _workspace(_lib.kvc_channel_prune_value_workspace_size(Hkv, G, w, budget, recent, D), k_c.device,
-                            workspace)
+                            workspace, stream)
     _check(_lib.kvc_channel_prune_value(_ptr(k_c), _ptr(v_c), _ptr(q_obs), Hkv, G, w, q_obs.stride(0), budget, D,
                                         recent, float(lam), float(scale), _ptr(channels), _ptr(mask),
                                         _ptr(v_pruned), _ptr(ws), nbytes, _stream(stream, k_c.device)),
@@ -448,7 +454,7 @@ def kvc_keyformer_decode_step(q, k_new, v_new, k_cache, v_cache, pos, acc, *, t,
         raise ValueError("pos must be int32 and acc float32, both [Hkv, B]")
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     ws, nbytes = _workspace(_lib.kvc_keyformer_decode_step_workspace_size(Hkv, H // Hkv, B), k_cache.device,
-                            workspace)
+                            workspace, stream)
     _check(_lib.kvc_keyformer_decode_step(_ptr(q), q.stride(0), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                                           _ptr(v_cache), _ptr(pos), _ptr(acc), Hkv, H // Hkv, B, D, int(t),
                                           int(recent), float(scale), float(tau), int(seed) & (2 ** 64 - 1),

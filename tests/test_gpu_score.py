@@ -155,6 +155,25 @@ def test_deterministic_bytes():
     assert a.tobytes() == b.tobytes()
 
 
+def test_calls_on_two_streams_at_once():
+    """The library keeps no per-call state of its own: two calls in flight on
+    two streams, each with its own workspace (the 8-wave and 4-wave shapes),
+    give the bytes the same calls give one after the other."""
+    kvc = _kvc()
+    cases = [(_draw(32, 8, 128, 9000, seed=41), 128, 9000), (_draw(8, 2, 40, 20000, seed=42), 40, 20000)]
+    dev_in = [(to_dev(qb), to_dev(kb), w, S) for (qb, kb), w, S in cases]
+    ref = [_gpu_importance(qb, kb, w=w, S=S) for (qb, kb), w, S in cases]
+    outs = [torch.full((kb.shape[0], S - w), float("nan"), dtype=torch.float32, device=dev())
+            for (_, kb, w, S) in dev_in]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for (q, k, w, S), out, st in zip(dev_in, outs, streams):
+        kvc.kvc_score(q, k, out, w=w, S=S, stream=st)
+    torch.cuda.synchronize()
+    for out, r in zip(outs, ref):
+        assert out.cpu().numpy().tobytes() == r.tobytes()
+
+
 # ---------------------------------------------------------------- causal (whole-prompt) scoring
 @pytest.mark.parametrize("H,Hkv,S,w,gumbel,tau", [
     (4, 4, 640, 640, True, 1.0),       # every position a query; 5 row chunks x 5 key units, Gumbel shape
