@@ -143,8 +143,10 @@ kvc_status kvc_score(const kvc_score_args* args /* host */, const void* q_obs, c
  * library runs on until the process ends.  Neither this call nor its kernels
  * allocate or free memory.
  * Errors: as kvc_score; KVC_E_WORKSPACE, before any device call, when
- *   kvc_score_workspace_size(args) exceeds the scratch; KVC_E_DEVICE if the
- *   scratch address of the current device cannot be obtained.
+ *   kvc_score_workspace_size(args) exceeds the scratch; KVC_E_ARG if `stream`
+ *   belongs to a device other than the current one (the scratch used is the
+ *   current device's); KVC_E_DEVICE if the scratch address of the current
+ *   device cannot be obtained.
  * Concurrency: all calls on one device share its scratch, which keeps the last
  *   call's contents (every byte a call reads it has written first).  Calls
  *   that overlap in time on one device -- other streams, other host threads --

@@ -1505,6 +1505,14 @@ extern "C" kvc_status kvc_score_noalloc(const kvc_score_args* a, const void* q_o
   kvc_status st = kvc::plan(a, &pl);
   if (st != KVC_OK) return st;
   if (pl.total > kScoreScratchBytes) return KVC_E_WORKSPACE;   // checked before any device call
+  if (stream) {
+    // the scratch is the current device's: the kernels must run there
+    hipDevice_t sdev = -1;
+    int cur = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess || hipGetDevice(&cur) != hipSuccess)
+      return KVC_E_DEVICE;
+    if (sdev != cur) return KVC_E_ARG;
+  }
   void* ws = nullptr;
   st = kvc::score_scratch_ptr(&ws);
   if (st != KVC_OK) return st;
