@@ -236,3 +236,20 @@ def test_largest_query_group_accepted(gumbel):
     gpu = _gpu_importance(qb, kb, w=w, S=S, **kw)
     ref = _oracle(qb, kb, w=w, S=S, scale=F32_ALPHA, **kw)
     check_importance(gpu, ref, H // Hkv, f"G*w = 65536, gumbel={gumbel}")
+
+
+def test_many_heads_per_workgroup_eight_wave_shape():
+    """R = 384 (the 8-wave shape) over 64 layers x 8 KV heads with two units
+    per head (the second ragged): 1024 units on at most 256 workgroups, so
+    every workgroup crosses a head boundary (pass 1 flushes a head's partial
+    mid-range, pass 2 re-stages rows and folds that head's segments), each
+    layer with its own scale."""
+    L, H, Hkv, w, S = 64, 32, 8, 96, 96 + 700
+    qb, kb = _draw(H, Hkv, w, S, seed=384, L=L)
+    scales = (np.linspace(0.6, 2.5, L) / math.sqrt(128)).astype(np.float32)
+    gpu = _gpu_importance(qb, kb, w=w, S=S, L=L, layer_scales=torch.from_numpy(scales).to(dev()))
+    assert np.allclose(gpu.astype(np.float64).sum(axis=-1), H // Hkv, rtol=1e-5, atol=0)
+    for l, g in [(0, 0), (0, 7), (3, 2), (9, 5), (17, 1), (22, 6), (31, 3), (32, 4), (40, 0), (45, 7), (50, 2),
+                 (55, 5), (58, 1), (61, 6), (63, 3), (63, 7)]:
+        ref = _oracle(qb[l], kb[l], w=w, S=S, scale=float(scales[l]), kv_heads=[g])
+        check_importance(gpu[l, g][None], ref[g][None], H // Hkv, f"layer {l} head {g}")
