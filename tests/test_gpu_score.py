@@ -253,3 +253,18 @@ def test_many_heads_per_workgroup_eight_wave_shape():
                  (55, 5), (58, 1), (61, 6), (63, 3), (63, 7)]:
         ref = _oracle(qb[l], kb[l], w=w, S=S, scale=float(scales[l]), kv_heads=[g])
         check_importance(gpu[l, g][None], ref[g][None], H // Hkv, f"layer {l} head {g}")
+
+
+@pytest.mark.parametrize("H,Hkv,w,n", [
+    (4, 1, 96, 41 * 512 + 77),   # 8-wave shape, 42 segments: pass 2 folds them in two steps of 32
+    (4, 1, 96, 70 * 512),        # 8-wave shape, 70 segments (> 64): the combine kernel folds them
+    (4, 1, 32, 41 * 256 + 13),   # 4-wave shape (R = 128), 42 segments in two steps
+])
+def test_segment_fold_steps(H, Hkv, w, n):
+    """One KV head spread over as many workgroups as it has units, so its row
+    statistics arrive as that many segment partials."""
+    S = n + w
+    qb, kb = _draw(H, Hkv, w, S, seed=n)
+    gpu = _gpu_importance(qb, kb, w=w, S=S)
+    ref = _oracle(qb, kb, w=w, S=S, scale=F32_ALPHA)
+    check_importance(gpu, ref, H // Hkv, f"H={H} w={w} n={n}")
