@@ -58,6 +58,9 @@ def _ref_select(imp32, **kw):
     (2, 32768, 128, 64, 2048, "narrow"),        # a tiny key range in one workgroup
     (2, 32768, 128, 0, 30000, "exp"),           # k_top close to the candidate count
     (3, 32767 + 128, 128, 0, 5, "dups"),        # 32767 candidates: the last wave part-filled
+    (2, 32769 + 128, 128, 0, 3000, "exp"),      # 32769 candidates: the first count on the chunked path
+    (2, 9000, 64, 64, 6000, "signed_zeros"),    # +0 and -0 tied at the threshold (one workgroup)
+    (2, 40064, 64, 64, 26000, "signed_zeros"),  # the same on the chunked path
 ])
 def test_select_bit_exact(Hkv, S, w, recent, budget, kind):
     rng = np.random.default_rng(S + budget)
@@ -74,6 +77,13 @@ def test_select_bit_exact(Hkv, S, w, recent, budget, kind):
         imp = ((1.0 + 1e-4 * rng.standard_normal(size=(Hkv, n))) / n).astype(np.float32)
     elif kind == "signed":
         imp = rng.standard_normal(size=(Hkv, n)).astype(np.float32)
+    elif kind == "signed_zeros":
+        # half positive, a third +0.0, the rest -0.0: the kept set ends inside
+        # the zeros, which count as equal (position order)
+        imp = rng.exponential(size=(Hkv, n)).astype(np.float32)
+        u = rng.random(size=(Hkv, n))
+        imp[u < 0.5] = 0.0
+        imp[u < 0.15] = -0.0
     elif kind == "wide":
         imp = rng.choice(np.array([-np.inf, -1e30, -1.0, -0.0, 0.0, 1e-30, 1.0, 1e30, np.inf],
                                   dtype=np.float32), size=(Hkv, n))
